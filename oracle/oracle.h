@@ -1,0 +1,63 @@
+/*
+ * oracle.h - plain, slow CPU reference of the verification hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library includes this
+ * header, links this code or calls it; only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark load liboracle.so.
+ *
+ * Every floating-point operation is one IEEE-754 binary32 operation rounded
+ * to nearest-even, in the order the comments state. The file is compiled with
+ * -O2 -ffp-contract=off -fno-fast-math and no -march, so no FMA is formed
+ * and nothing is reassociated. Denormals are kept.
+ *
+ * Status codes: 0 on success, -1 for an invalid argument.
+ */
+#ifndef SPECV_ORACLE_H
+#define SPECV_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* fp16 <-> fp32. Widening is exact; narrowing rounds to nearest-even with
+ * overflow to infinity and gradual underflow. */
+float orc_f16_to_f32(uint16_t h);
+uint16_t orc_f32_to_f16(float x);
+
+/* The fixed 16-slot summation order used by every fp32 sum of the path. */
+float orc_r16(const float* v, int64_t n);
+
+/* Per-token absmax int8 quantisation of x [T][K] -> xq [T][K], xs [T]. */
+int orc_quantize_act(const float* x, int T, int K, int8_t* xq, float* xs);
+
+/* Exact int32 dot of each 32-input group: d [T][N][K/32]. */
+int orc_group_dots(const uint8_t* wq, const int8_t* xq, int T, int N, int K, int32_t* d);
+
+/* W4A8 linear: y [T][N] from nibbles wq [N][K/2], fp16 scales ws [N][K/32],
+ * codes xq [T][K] and token scales xs [T]. */
+int orc_w4a8_linear(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
+                    const float* xs, float* y, int T, int N, int K);
+
+/* Same, for a list of output rows only: y [T][nrows] holds rows[r]. */
+int orc_w4a8_linear_rows(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
+                         const float* xs, float* y, int T, int N, int K,
+                         const int32_t* rows, int nrows);
+
+/* Lowest index of the maximum of each row of logits [N][V]. */
+int orc_argmax(const float* logits, int N, int64_t V, int32_t* out);
+
+/* Greedy tree acceptance. Returns the accepted depth m >= 0 and fills
+ * path[0..m] and *bonus, or -1 for a malformed tree. */
+int orc_tree_accept(const int32_t* parent, const int32_t* token, const int32_t* amax,
+                    int N, int32_t* path, int32_t* bonus);
+
+/* In-place compaction of one cache [layers][heads][cap][hd] (fp16 bits):
+ * row L+path[j] moves to row L+j for j = 1..m. */
+int orc_kv_compact(uint16_t* cache, int layers, int heads, int cap, int hd,
+                   int L, const int32_t* path, int m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
