@@ -1,0 +1,172 @@
+/*
+ * specv.h - C ABI of the deterministic small-batch verification library
+ * (libspecv.so, HIP for AMD Instinct MI355X / gfx950).
+ *
+ * The operations follow "GPU-Resident Speculative Decoding for In-Browser LLM
+ * Inference with WebGPU" (cited below as [P1] with its section), the packing
+ * of "WebGPU for LLM Inference, in depth" ([P2], quantised matvec kernel) and
+ * the KV transaction model of "Exact Speculative And Assisted Decoding For A
+ * Tiny Draft And Qualified Champion" ([P3]).
+ *
+ * Conventions shared by every call:
+ *  - Pointers are device memory unless marked "host". The caller owns and
+ *    allocates every buffer; the library allocates nothing.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call validates its arguments on the host, enqueues its kernels on
+ *    `stream` and returns without synchronising. Device faults surface at the
+ *    caller's next synchronisation.
+ *  - On invalid arguments a call returns a negative status and enqueues
+ *    nothing. No call aborts, throws or falls back to another code path.
+ *  - Tensors are dense row-major (C order) unless stated otherwise.
+ *  - Results are deterministic: the same inputs give the same bits on every
+ *    run, launch shape and token count.
+ */
+#ifndef SPECV_H
+#define SPECV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SPECV_OK = 0,
+    SPECV_E_INVAL = -1,     /* null pointer, negative size, bad enum value  */
+    SPECV_E_SHAPE = -2,     /* size outside the supported range             */
+    SPECV_E_ALIGN = -3,     /* pointer not aligned as the call requires     */
+    SPECV_E_HIP = -4,       /* the HIP runtime refused a launch             */
+    SPECV_E_WORKSPACE = -5  /* workspace missing or smaller than required   */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* specv_status_string(int status);
+
+/*
+ * Device-resident control state, 32 bytes ([P1], GPU-Resident Speculation
+ * Loop: the committed KV length, the number of valid nodes, the context
+ * length and a termination flag live in a small buffer every kernel reads at
+ * run time). Kernels read these fields from device memory when they run, so a
+ * sequence of steps can be enqueued without host decisions in between.
+ *   committed_len  KV rows [0, committed_len) are committed.
+ *   n_nodes        valid tree nodes of the current step (1..16).
+ *   ctx_len        context limit: a step that leaves committed_len + n_nodes
+ *                  > ctx_len sets done, so the next tree still fits.
+ *   done           non-zero: every step kernel returns without effect.
+ *   accept_len     m, accepted draft nodes of the last step (0 if it was a
+ *                  no-op).
+ *   root_token     token of node 0 of the next step (the last step's bonus).
+ *   step           steps committed so far.
+ *   ring_head      tokens emitted so far (next ring slot = ring_head % cap).
+ */
+typedef struct {
+    int32_t committed_len;
+    int32_t n_nodes;
+    int32_t ctx_len;
+    int32_t done;
+    int32_t accept_len;
+    int32_t root_token;
+    int32_t step;
+    int32_t ring_head;
+} specv_ctrl;
+
+/* Per-step statistics, 12 bytes ([P1], GPU-Resident Speculation Loop; the
+ * controller of Feedback Control of Speculation Width reads the accepted
+ * count and the drafter's best match length). */
+typedef struct {
+    int32_t accepted;    /* m of the step, -1 if the step was a no-op */
+    int32_t best_match;  /* drafter's best candidate length (0 if unknown) */
+    int32_t width;       /* n_nodes of the step */
+} specv_step_stats;
+
+/*
+ * Per-token int8 activation quantisation ([P1], Small-Batch Verification
+ * Kernels: activations become 8-bit integers before every matrix
+ * multiplication; here with one absmax scale per token).
+ *   x   fp32 [T][K]      input activations (finite values).
+ *   xq  int8 [T][K]      codes: round-to-nearest-even of x * (127/absmax),
+ *                        in [-127, 127].
+ *   xs  fp32 [T]         scale absmax/127 (0 for an all-zero token, whose
+ *                        codes are 0).
+ * T in [0, 64], K in [1, 2^24]. T == 0 enqueues nothing.
+ * Alignment: x 4 bytes; xq and xs any.
+ */
+int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs,
+                      void* stream);
+
+/*
+ * W4A8 linear for T = 1..16 tokens ([P1], Small-Batch Verification Kernels
+ * and Implementation; packing of [P2]):
+ *   y[t][n] = xs[t] * R16_g( f32(ws[n][g]) * f32(d[t][n][g]) ),
+ *   d[t][n][g] = sum_{k in group g} (u(n,k) - 8) * xq[t][k]   (exact int32),
+ * where R16 is the fixed 16-slot order (slot s accumulates the groups
+ * g = s, s+16, ... in increasing g starting from +0, then slots combine with
+ * s += s+off for off = 8, 4, 2, 1). The order does not depend on T, so row t
+ * of a T-token call equals a 1-token call on token t bit for bit.
+ *   wq  uint8 [N][K/2]   byte b of row n: input 2b in the low nibble, input
+ *                        2b+1 in the high nibble, each stored as u = q + 8.
+ *   ws  uint16 [N][K/32] fp16 bit patterns, one scale per 32 inputs.
+ *   xq  int8 [T][K], xs fp32 [T]   from w4a8_quantize_act.
+ *   y   fp32 [T][N]
+ * T in [1, 16], N in [0, 2^24], K a multiple of 32 in [32, 2^20],
+ * N*K/2 < 2^31 bytes. N == 0 enqueues nothing.
+ * Alignment: wq and xq 16 bytes, ws 2, xs and y 4.
+ */
+int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
+                  float* y, int32_t T, int32_t N, int32_t K, void* stream);
+
+/*
+ * Greedy argmax per tree node and tree acceptance ([P1], GPU-Resident
+ * Speculation Loop: the acceptance kernel walks the tree from the root and
+ * follows the child whose token equals the greedy prediction of its parent;
+ * the step commits the accepted draft nodes and the prediction after the
+ * last of them). Reads ctrl->n_nodes and ctrl->done when it runs.
+ *   logits  fp32 [n_max][V]  rows >= n_nodes are not read.
+ *   parent  int32 [n_max]    parent[0] = -1, 0 <= parent[i] < i. A node whose
+ *                            parent breaks this is treated as rejected.
+ *   token   int32 [n_max]    token of each node (token[0] is the root).
+ *   argmax  int32 [n_max]    out: lowest index of each row's maximum.
+ *   path    int32 [n_max]    out: path[0..m] = accepted chain from node 0.
+ *   ctrl    in/out, see specv_ctrl. When done is set on entry the call only
+ *           writes accept_len = 0. Otherwise, with w the deepest accepted
+ *           node (lowest index among equally deep ones) and m its depth:
+ *           accept_len = m, committed_len += m + 1, root_token = argmax[w],
+ *           step += 1, ring_head += m + 1, and done = 1 when
+ *           committed_len + n_nodes > ctx_len.
+ *   stats   nullable: one record written for the step.
+ *   ring    nullable int32 [ring_cap]: the emitted tokens token[path[1..m]]
+ *           then argmax[w] go to ring[(ring_head + i) % ring_cap].
+ *   workspace  device buffer of tree_argmax_accept_workspace(V, n_max) bytes,
+ *           4-byte aligned; its contents need no initialisation.
+ * n_max in [1, 16], V in [1, 2^31 - 1]. Alignment: logits 16 bytes.
+ */
+size_t tree_argmax_accept_workspace(int64_t V, int32_t n_max);
+int tree_argmax_accept(const float* logits, int64_t V, int32_t n_max,
+                       const int32_t* parent, const int32_t* token,
+                       int32_t* argmax, int32_t* path, specv_ctrl* ctrl,
+                       specv_step_stats* stats, int32_t* ring, int32_t ring_cap,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KV-cache compaction of the accepted path ([P1], GPU-Resident Speculation
+ * Loop: a compaction kernel moves the keys and values of the accepted path
+ * into place; [P3], KV transaction model: rows past the committed pointer
+ * are dead). Tree node i of the step was written at row L + i. Reads
+ * m = ctrl->accept_len and L = ctrl->committed_len - m - 1 when it runs, i.e.
+ * it runs after tree_argmax_accept of the same step, and moves row
+ * L + path[j] to row L + j for j = 1..m in every layer and KV head, with the
+ * result of doing so in increasing j. m == 0 moves nothing.
+ *   k_cache, v_cache  fp16 bits [n_layers][n_kv_heads][capacity][head_dim]
+ *   path              int32 [m+1] from tree_argmax_accept
+ * head_dim a multiple of 8 in [8, 512]; n_layers, n_kv_heads >= 1;
+ * capacity >= 1. Alignment: caches 16 bytes.
+ */
+int kv_compact(uint16_t* k_cache, uint16_t* v_cache, int32_t n_layers, int32_t n_kv_heads,
+               int32_t capacity, int32_t head_dim, const int32_t* path,
+               const specv_ctrl* ctrl, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECV_H */

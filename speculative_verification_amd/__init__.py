@@ -1,0 +1,105 @@
+"""Deterministic small-batch speculative verification for AMD MI355X.
+
+Thin torch-facing wrappers over libspecv.so (see include/specv.h): they check
+tensor dtypes, devices and shapes, pass raw device pointers and the current
+HIP stream, and raise SpecvError on a non-zero status. All computation runs
+in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import LIB, SpecvError, check
+
+__all__ = ["SpecvError", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
+           "argmax_accept_workspace_bytes", "kv_compact"]
+
+CTRL_FIELDS = ("committed_len", "n_nodes", "ctx_len", "done", "accept_len", "root_token", "step",
+               "ring_head")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def new_ctrl(committed_len: int, n_nodes: int, ctx_len: int, root_token: int = 0,
+             device="cuda") -> torch.Tensor:
+    """int32[8] control block with the layout of specv_ctrl."""
+    v = [committed_len, n_nodes, ctx_len, 0, 0, root_token, 0, 0]
+    return torch.tensor(v, dtype=torch.int32, device=device)
+
+
+def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tensor | None = None):
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device=x.device) if xq is None else xq
+    xs = torch.empty((T,), dtype=torch.float32, device=x.device) if xs is None else xs
+    check("w4a8_quantize_act", LIB.w4a8_quantize_act(_dev(x, "x", torch.float32), T, K,
+                                                     _dev(xq, "xq", torch.int8),
+                                                     _dev(xs, "xs", torch.float32), _stream()))
+    return xq, xs
+
+
+def linear(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
+           y: torch.Tensor | None = None) -> torch.Tensor:
+    """y [T][N] fp32 from nibbles wq uint8 [N][K/2], fp16 scale bits ws
+    (int16/uint16/float16 storage) [N][K/32], codes xq int8 [T][K], xs [T]."""
+    N = wq.shape[0]
+    T, K = xq.shape
+    if wq.shape != (N, K // 2) or ws.shape != (N, K // 32) or xs.shape != (T,):
+        raise ValueError("shape mismatch between wq, ws, xq and xs")
+    if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
+        raise TypeError("ws must hold fp16 bit patterns")
+    y = torch.empty((T, N), dtype=torch.float32, device=xq.device) if y is None else y
+    check("w4a8_linear_T", LIB.w4a8_linear_T(_dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype),
+                                             _dev(xq, "xq", torch.int8), _dev(xs, "xs", torch.float32),
+                                             _dev(y, "y", torch.float32), T, N, K, _stream()))
+    return y
+
+
+def argmax_accept_workspace_bytes(V: int, n_max: int) -> int:
+    return int(LIB.tree_argmax_accept_workspace(V, n_max))
+
+
+def tree_argmax_accept(logits: torch.Tensor, parent: torch.Tensor, token: torch.Tensor,
+                       ctrl: torch.Tensor, argmax: torch.Tensor | None = None,
+                       path: torch.Tensor | None = None, stats: torch.Tensor | None = None,
+                       ring: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    n_max, V = logits.shape
+    dev = logits.device
+    argmax = torch.empty(n_max, dtype=torch.int32, device=dev) if argmax is None else argmax
+    path = torch.zeros(n_max, dtype=torch.int32, device=dev) if path is None else path
+    if workspace is None:
+        workspace = torch.empty(argmax_accept_workspace_bytes(V, n_max), dtype=torch.uint8, device=dev)
+    st = _dev(stats, "stats", torch.int32) if stats is not None else None
+    rp = _dev(ring, "ring", torch.int32) if ring is not None else None
+    check("tree_argmax_accept", LIB.tree_argmax_accept(
+        _dev(logits, "logits", torch.float32), V, n_max, _dev(parent, "parent", torch.int32),
+        _dev(token, "token", torch.int32), _dev(argmax, "argmax", torch.int32),
+        _dev(path, "path", torch.int32), _dev(ctrl, "ctrl", torch.int32), st, rp,
+        ring.numel() if ring is not None else 0, _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream()))
+    return argmax, path
+
+
+def kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, path: torch.Tensor,
+               ctrl: torch.Tensor) -> None:
+    """Caches: fp16 (or int16 bits) [layers][kv_heads][capacity][head_dim]."""
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must share a 4-D shape")
+    if k_cache.element_size() != 2 or v_cache.element_size() != 2:
+        raise TypeError("caches must hold fp16 values (2-byte elements)")
+    layers, heads, cap, hd = k_cache.shape
+    check("kv_compact", LIB.kv_compact(_dev(k_cache, "k_cache", k_cache.dtype),
+                                       _dev(v_cache, "v_cache", v_cache.dtype), layers, heads, cap, hd,
+                                       _dev(path, "path", torch.int32), _dev(ctrl, "ctrl", torch.int32),
+                                       _stream()))

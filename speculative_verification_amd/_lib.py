@@ -1,0 +1,50 @@
+"""ctypes binding of libspecv.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels. There is no
+Python or CPU fallback: if the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+SO = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecv.so")
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+I64 = ctypes.c_int64
+SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/specv.h
+SIGNATURES = {
+    "specv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "w4a8_quantize_act": (ctypes.c_int, [P, I32, I32, P, P, P]),
+    "w4a8_linear_T": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P]),
+    "tree_argmax_accept_workspace": (SZ, [I64, I32]),
+    "tree_argmax_accept": (ctypes.c_int, [P, I64, I32, P, P, P, P, P, P, P, I32, P, SZ, P]),
+    "kv_compact": (ctypes.c_int, [P, P, I32, I32, I32, I32, P, P, P]),
+}
+
+
+class SpecvError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    if not os.path.exists(SO):
+        raise ImportError(f"{SO} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(SO)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+LIB = load()
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SpecvError(fn, status, LIB.specv_status_string(status).decode())

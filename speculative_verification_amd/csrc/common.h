@@ -1,0 +1,46 @@
+// Internal helpers of libspecv: buffer resources with zero-filled
+// out-of-range loads, launch checking, and the fp32 rules every kernel keeps.
+//
+// Every source of the library is compiled with -ffp-contract=off and without
+// fast-math, so each fp32 expression below is one IEEE binary32 operation
+// rounded to nearest-even, with denormals kept and correctly rounded division.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/specv.h"
+
+namespace specv {
+
+// A raw buffer resource over [base, base + bytes). Loads whose offset lies
+// past `bytes` return zeros instead of touching memory, which lets the
+// kernels fill ragged tiles without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // dword 3 = 0x00020000: 32-bit data format, as the CDNA3/CDNA4 ISA uses
+    // for raw (untyped) buffer access.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Offset that is out of range for every buffer the library accepts (all are
+// validated to be smaller than 2^31 bytes).
+constexpr uint32_t kOOB = 0x80000000u;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+inline int launch_status() {
+    return hipGetLastError() == hipSuccess ? SPECV_OK : SPECV_E_HIP;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace specv

@@ -1,0 +1,303 @@
+"""GPU parity: every call of the C ABI against the CPU oracle, bit for bit.
+
+Inputs come from synthgen with the configs' shapes and distributions: int4
+codes uniform in [-8, 7], fp16 scales U(0.005, 0.02), fp32 N(0,1)
+activations. Small and ragged shapes are compared element by element; the
+full-size lm_head shapes are compared on sampled rows the oracle computes one
+by one, plus properties that hold at any size (rows of T equal single-token
+calls, run-to-run identity).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthgen as sg
+
+pytestmark = pytest.mark.gpu
+
+QWEN = {"q": (896, 896), "k": (128, 896), "v": (128, 896), "o": (896, 896),
+        "gate": (4864, 896), "up": (4864, 896), "down": (896, 4864), "lm_head": (151936, 896)}
+LLAMA = {"q": (4096, 4096), "k": (1024, 4096), "v": (1024, 4096), "o": (4096, 4096),
+         "gate": (14336, 4096), "up": (14336, 4096), "down": (4096, 14336), "lm_head": (128256, 4096)}
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_verification_amd as m
+    return m
+
+
+def case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@functools.lru_cache(maxsize=2)
+def _weights(seed, N, K, layer):
+    wq, ws, _ = sg.linear_case(seed, 1, N, K, layer=layer)
+    return wq, ws, to_dev(wq), to_dev(ws)
+
+
+def gpu_quant_linear(sv, wq, ws, x, wq_d=None, ws_d=None):
+    xq, xs = sv.quantize_act(to_dev(x))
+    y = sv.linear(to_dev(wq) if wq_d is None else wq_d, to_dev(ws) if ws_d is None else ws_d, xq, xs)
+    torch.cuda.synchronize()
+    return xq.cpu().numpy(), xs.cpu().numpy(), y.cpu().numpy()
+
+
+def assert_bits(a: np.ndarray, b: np.ndarray, what: str):
+    if a.tobytes() != b.tobytes():
+        a32, b32 = a.view(np.uint32).ravel(), b.view(np.uint32).ravel()
+        bad = np.nonzero(a32 != b32)[0]
+        i = bad[0]
+        rel = np.max(np.abs(a.ravel()[bad] - b.ravel()[bad]) / np.maximum(np.abs(b.ravel()[bad]), 1e-30))
+        raise AssertionError(f"{what}: {bad.size} of {a32.size} differ; first at {i}: "
+                             f"{a.ravel()[i]!r} vs {b.ravel()[i]!r}; max rel diff {rel:.3g}")
+
+
+# ------------------------------------------------------------------ quantisation
+
+@pytest.mark.parametrize("T,K", [(1, 896), (8, 896), (3, 4864), (16, 4096), (8, 14336), (2, 33), (5, 1),
+                                 (64, 96)])
+def test_quantize_parity(sv, T, K):
+    case(f"quantize T={T} K={K}")
+    x = sg.normal_f32(sg.stream_key(40 + T, sg.TID_X), T * K).reshape(T, K)
+    if T >= 2:
+        x[1] = 0.0
+        x[1, ::3] = -0.0
+    if T >= 3:
+        x[2] *= np.float32(1e-39)     # subnormal inputs
+    xq_o, xs_o = oracle.quantize_act(x)
+    xq, xs = sv.quantize_act(to_dev(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert_bits(xs.cpu().numpy(), xs_o, "xs")
+
+
+# ------------------------------------------------------------------ linear, small and ragged
+
+@pytest.mark.parametrize("T,N,K", [(1, 16, 32), (3, 17, 64), (5, 33, 96), (7, 40, 544), (8, 100, 896),
+                                   (16, 50, 4864), (4, 1, 4096), (2, 15, 14336), (9, 31, 512),
+                                   (12, 64, 1024), (6, 48, 160)])
+def test_linear_parity_ragged(sv, T, N, K):
+    case(f"linear ragged T={T} N={N} K={K}")
+    wq, ws, x = sg.linear_case(50 + T, T, N, K)
+    xq_o, xs_o = oracle.quantize_act(x)
+    y_o = oracle.w4a8_linear(wq, ws, xq_o, xs_o)
+    xq, xs, y = gpu_quant_linear(sv, wq, ws, x)
+    assert np.array_equal(xq, xq_o)
+    assert_bits(y, y_o, f"y T={T} N={N} K={K}")
+
+
+def test_linear_config1(sv):
+    """Single linear K = N = 896, T = 1, seed 0."""
+    case("linear config1 896x896 T=1 seed 0")
+    wq, ws, x = sg.linear_case(0, 1, 896, 896)
+    xq_o, xs_o = oracle.quantize_act(x)
+    y_o = oracle.w4a8_linear(wq, ws, xq_o, xs_o)
+    _, _, y = gpu_quant_linear(sv, wq, ws, x)
+    assert_bits(y, y_o, "config1")
+
+
+def _sample_rows(N, seed, n=96):
+    r = (sg.u32(sg.stream_key(seed, 77), n) % np.uint32(N)).astype(np.int32)
+    return np.unique(np.concatenate([r, [0, 1, 15, 16, N // 2, N - 17, N - 16, N - 1]]).astype(np.int32))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+@pytest.mark.parametrize("name", list(QWEN))
+def test_linear_qwen_shapes(sv, name, T):
+    N, K = QWEN[name]
+    for seed in ((0, 1, 2, 3) if T == 8 else (0,)):
+        case(f"linear qwen {name} N={N} K={K} T={T} seed={seed}")
+        wq, ws, wq_d, ws_d = _weights(seed, N, K, list(QWEN).index(name))
+        _, _, x = sg.linear_case(seed, T, 1, K, layer=list(QWEN).index(name))
+        xq_o, xs_o = oracle.quantize_act(x)
+        _, _, y = gpu_quant_linear(sv, wq, ws, x, wq_d, ws_d)
+        if N * K <= 896 * 4864:
+            assert_bits(y, oracle.w4a8_linear(wq, ws, xq_o, xs_o), f"{name} T={T} seed={seed}")
+        else:
+            rows = _sample_rows(N, seed)
+            assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows),
+                        f"{name} T={T} seed={seed} sampled")
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+@pytest.mark.parametrize("name", list(LLAMA))
+def test_linear_llama_shapes_sampled(sv, name, T):
+    N, K = LLAMA[name]
+    seed = 0
+    case(f"linear llama {name} N={N} K={K} T={T}")
+    wq, ws, wq_d, ws_d = _weights(seed, N, K, 100 + list(LLAMA).index(name))
+    _, _, x = sg.linear_case(seed, T, 1, K, layer=100 + list(LLAMA).index(name))
+    xq_o, xs_o = oracle.quantize_act(x)
+    _, _, y = gpu_quant_linear(sv, wq, ws, x, wq_d, ws_d)
+    rows = _sample_rows(N, seed, n=48)
+    assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), f"{name} T={T}")
+
+
+def test_linear_rows_of_T_equal_single_token(sv):
+    """Property at full size: row t of a T-token call equals a 1-token call
+    on token t, for every T bucket, on the 8B-shaped q projection."""
+    N, K = LLAMA["q"]
+    wq, ws, x = sg.linear_case(7, 16, N, K)
+    wq_d, ws_d = to_dev(wq), to_dev(ws)
+    xq, xs = sv.quantize_act(to_dev(x))
+    singles = [sv.linear(wq_d, ws_d, xq[t:t + 1].contiguous(), xs[t:t + 1].contiguous()) for t in range(16)]
+    single = torch.cat(singles, 0).cpu().numpy()
+    for T in range(1, 17):
+        case(f"rows-of-T T={T}")
+        yT = sv.linear(wq_d, ws_d, xq[:T].contiguous(), xs[:T].contiguous()).cpu().numpy()
+        assert_bits(yT, single[:T].copy(), f"T={T} vs single-token")
+
+
+def test_linear_run_to_run_identical(sv):
+    case("determinism lm_head qwen T=8")
+    N, K = QWEN["lm_head"]
+    wq, ws, x = sg.linear_case(8, 8, N, K)
+    wq_d, ws_d = to_dev(wq), to_dev(ws)
+    xq, xs = sv.quantize_act(to_dev(x))
+    a = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
+    b = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
+    assert a.tobytes() == b.tobytes()
+
+
+def test_linear_degenerate_values(sv):
+    """All-zero token, negative and subnormal fp16 scales, tiny activations
+    with subnormal outputs, and an empty matrix."""
+    case("linear degenerate values")
+    T, N, K = 4, 37, 288
+    wq, ws, x = sg.linear_case(9, T, N, K)
+    x[0] = 0.0
+    x[2] *= np.float32(1e-36)
+    ws = ws.copy()
+    ws[::3] ^= np.uint16(0x8000)                 # negative scales
+    ws[5] = np.uint16(1)                          # smallest subnormal fp16
+    ws[6, :2] = np.uint16(0)                      # zero scales
+    xq_o, xs_o = oracle.quantize_act(x)
+    y_o = oracle.w4a8_linear(wq, ws, xq_o, xs_o)
+    _, _, y = gpu_quant_linear(sv, wq, ws, x)
+    assert_bits(y, y_o, "degenerate")
+    empty = sv.linear(torch.zeros((0, 16), dtype=torch.uint8, device="cuda"),
+                      torch.zeros((0, 1), dtype=torch.int16, device="cuda"),
+                      torch.zeros((1, 32), dtype=torch.int8, device="cuda"),
+                      torch.ones(1, device="cuda"))
+    assert empty.shape == (1, 0)
+
+
+# ------------------------------------------------------------------ argmax + acceptance + compaction
+
+def _plant_tree(seed, n, amax_o, V, accept_path):
+    """Random topological tree; drafts along a chosen chain equal the parent's
+    prediction, the rest are random, so the accepted depth is controlled."""
+    key = sg.stream_key(seed, sg.TID_PARENT)
+    parent = sg.random_tree_parents(key, n)
+    token = sg.tokens(sg.stream_key(seed, sg.TID_TOKEN), n, V)
+    if accept_path and n > 1:
+        depth = np.zeros(n, np.int32)
+        for i in range(1, n):
+            depth[i] = depth[parent[i]] + 1
+        w = int(np.argmax(depth))
+        chain = [w]
+        while chain[-1] != 0:
+            chain.append(int(parent[chain[-1]]))
+        for c in chain[:-1]:
+            token[c] = amax_o[parent[c]]
+    return parent, token
+
+
+@pytest.mark.parametrize("V", [151936, 128256, 1000, 1])
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16])
+def test_argmax_accept_compact_parity(sv, V, n):
+    for seed, plant in ((n * 7 + V % 97, True), (n * 11 + 1, False)):
+        case(f"argmax/accept/compact V={V} n={n} seed={seed} planted={plant}")
+        logits = sg.normal_f32(sg.stream_key(seed, sg.TID_LOGITS), n * V).reshape(n, V)
+        if V > 10:
+            logits[0, V // 3] = logits[0, V // 2] = np.float32(9.0)     # tie: lowest index
+            if n > 1:
+                logits[1, :] = np.float32(-1.0)
+                logits[1, 7] = np.float32(-0.0)
+                logits[1, 5] = np.float32(0.0)                           # -0 == +0: index 5
+        amax_o = oracle.argmax(logits)
+        parent, token = _plant_tree(seed, n, amax_o, V, plant)
+        m_o, path_o, bonus_o = oracle.tree_accept(parent, token, amax_o)
+
+        L0, ctx = 1024, 1040
+        layers, heads, cap, hd = 24, 2, 1040, 64
+        kv = sg.u32(sg.stream_key(seed, sg.TID_KV), 2 * layers * heads * cap * hd).astype(np.uint16)
+        kv = kv.reshape(2, layers, heads, cap, hd)
+        ctrl = sv.new_ctrl(committed_len=L0, n_nodes=n, ctx_len=ctx, root_token=int(token[0]))
+        stats = torch.full((3,), 77, dtype=torch.int32, device="cuda")
+        ring = torch.full((5,), -1, dtype=torch.int32, device="cuda")
+        ctrl[7] = 3  # ring_head
+        amax, path = sv.tree_argmax_accept(to_dev(logits), to_dev(parent), to_dev(token), ctrl,
+                                           stats=stats, ring=ring)
+        kc, vc = to_dev(kv[0]), to_dev(kv[1])
+        sv.kv_compact(kc, vc, path, ctrl)
+        torch.cuda.synchronize()
+
+        assert np.array_equal(amax.cpu().numpy(), amax_o)
+        assert np.array_equal(path.cpu().numpy()[: m_o + 1], path_o)
+        c = ctrl.cpu().numpy()
+        L1 = L0 + m_o + 1
+        assert list(c) == [L1, n, ctx, int(L1 + n > ctx), m_o, bonus_o, 1, 3 + m_o + 1]
+        assert list(stats.cpu().numpy()) == [m_o, 77, n]
+        emitted = [int(token[p]) for p in path_o[1:]] + [bonus_o]
+        ring_o = [-1] * 5
+        for i, tkn in enumerate(emitted):
+            ring_o[(3 + i) % 5] = tkn
+        assert list(ring.cpu().numpy()) == ring_o
+        for i, t in enumerate((kc, vc)):
+            ref = kv[i].copy()
+            oracle.kv_compact(ref, L0, path_o, m_o)
+            got = t.cpu().numpy().view(np.uint16)
+            assert np.array_equal(got[:, :, :L1], ref[:, :, :L1])
+
+
+def test_done_step_is_noop(sv):
+    """With done set on entry, acceptance writes only accept_len = 0 and a
+    no-op statistics record, and compaction then moves nothing."""
+    case("done flag no-op")
+    n, V = 8, 4096
+    logits = sg.normal_f32(sg.stream_key(3, sg.TID_LOGITS), n * V).reshape(n, V)
+    parent = sg.random_tree_parents(sg.stream_key(3, sg.TID_PARENT), n)
+    token = sg.tokens(sg.stream_key(3, sg.TID_TOKEN), n, V)
+    ctrl = sv.new_ctrl(100, n, 200)
+    ctrl[3] = 1
+    ctrl[4] = 5
+    before = ctrl.cpu().numpy().copy()
+    kc = torch.arange(2 * 2 * 200 * 8, dtype=torch.int16, device="cuda").reshape(2, 2, 200, 8)
+    vc = kc.clone() + 1
+    k0, v0 = kc.clone(), vc.clone()
+    stats = torch.zeros(3, dtype=torch.int32, device="cuda")
+    _, path = sv.tree_argmax_accept(to_dev(logits), to_dev(parent), to_dev(token), ctrl, stats=stats)
+    sv.kv_compact(kc, vc, path, ctrl)
+    torch.cuda.synchronize()
+    after = ctrl.cpu().numpy()
+    before[4] = 0
+    assert list(after) == list(before)
+    assert list(stats.cpu().numpy()) == [-1, 0, n]
+    assert torch.equal(kc, k0) and torch.equal(vc, v0)
+
+
+def test_context_limit_sets_done(sv):
+    case("ctx limit sets done")
+    n, V = 4, 64
+    logits = np.zeros((n, V), np.float32)
+    logits[:, 3] = 1.0
+    parent = np.array([-1, 0, 1, 2], np.int32)
+    token = np.array([9, 3, 3, 3], np.int32)       # every draft accepted: m = 3
+    ctrl = sv.new_ctrl(10, n, 10 + 4 + n - 1)      # after commit: 14 + 4 > 17
+    sv.tree_argmax_accept(to_dev(logits), to_dev(parent), to_dev(token), ctrl)
+    torch.cuda.synchronize()
+    c = ctrl.cpu().numpy()
+    assert (c[0], c[3], c[4]) == (14, 1, 3)
