@@ -74,18 +74,19 @@ uint16_t orc_f32_to_f16(float x) {
  * The fixed reduction order. [P1, Implementation] requires that every matrix
  * multiplication reduce in one fixed order across all token buckets, so that
  * N-token verification gives the bits of N single-token steps; the pages do
- * not print the order. Reading: the shape of [P2]'s kernel, strided
- * accumulation into a fixed set of partial sums followed by a stride-halving
- * tree, with 16 partial sums:
+ * not print the order. Reading: strided accumulation into a fixed set of
+ * partial sums, as in [P2]'s kernel, with 16 partial sums that are then added
+ * as a balanced binary tree in index order:
  *   slot s (0..15) starts at +0 and adds v[j] for j = s, s+16, ... in order;
- *   then for off = 8, 4, 2, 1: slot s += slot s+off for s < off.
+ *   then for w = 1, 2, 4, 8: slot s += slot s+w for every s divisible by 2w,
+ *   i.e. ((a0+a1)+(a2+a3)) + ((a4+a5)+(a6+a7)), and so on up to a0.
  */
 float orc_r16(const float* v, int64_t n) {
     float a[16];
     for (int s = 0; s < 16; s++) a[s] = 0.0f;
     for (int64_t j = 0; j < n; j++) a[j % 16] = a[j % 16] + v[j];
-    for (int off = 8; off >= 1; off /= 2)
-        for (int s = 0; s < off; s++) a[s] = a[s] + a[s + off];
+    for (int w = 1; w < 16; w *= 2)
+        for (int s = 0; s < 16; s += 2 * w) a[s] = a[s] + a[s + w];
     return a[0];
 }
 
