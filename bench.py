@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark of one deterministic small-batch verification step on one GPU.
+
+A step verifies a T-node tree (default T = 8) through a W4A8 linear stack of
+a Llama-3-8B-shaped model and then accepts on the GPU:
+  per layer (32): quantize + qkv (6144x4096, q/k/v rows concatenated),
+                  quantize + o (4096x4096), quantize + gate_up (28672x4096,
+                  gate/up rows concatenated), quantize + down (4096x14336);
+  then quantize + lm_head (128256x4096), argmax + tree acceptance, and KV
+  compaction of the accepted rows (32 layers x 8 KV heads x head_dim 128).
+Weights are int4 in groups of 32 with fp16 scales U(0.005, 0.02);
+activations fp32 N(0,1). The weights of 4 distinct generated layer sets are
+copied into 32 separate layer buffers plus one lm_head, 4.22 GB in total, so
+every step streams each byte from HBM once (far above the 256 MB
+last-level cache). The step is captured once as a HIP graph and replayed.
+
+Prints one JSON line (rank 0). `value` is the algorithmic bytes of the step
+(weights, activation codes and scales, linear outputs, quantisation traffic,
+logits read by the argmax, compaction moves) divided by the step time, in
+GB/s, at T = 8.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "W4A8 verify GB/s & % HBM peak at T=1..8; T=8/T=1 cost ratio; µs/verify"
+
+MODELS = {
+    "llama3-8b": dict(hidden=4096, layers=32, qkv=4096 + 2 * 1024, inter=14336, vocab=128256,
+                      kv_heads=8, head_dim=128, copies=1, distinct=4),
+    "qwen2.5-0.5b": dict(hidden=896, layers=24, qkv=896 + 2 * 128, inter=4864, vocab=151936,
+                         kv_heads=2, head_dim=64, copies=4, distinct=4),
+}
+
+
+def layer_linears(m):
+    return [("qkv", m["qkv"], m["hidden"]), ("o", m["hidden"], m["hidden"]),
+            ("gate_up", 2 * m["inter"], m["hidden"]), ("down", m["hidden"], m["inter"])]
+
+
+def weight_bytes(N, K):
+    return N * K // 2 + N * (K // 32) * 2
+
+
+def linear_bytes(T, N, K):
+    """Algorithmic bytes of one W4A8 linear launch."""
+    return weight_bytes(N, K) + T * K + 4 * T + 4 * T * N
+
+
+def quant_bytes(T, K):
+    return 4 * T * K + T * K + 4 * T
+
+
+class Model:
+    def __init__(self, name, torch, sv, sg, Tmax):
+        m = MODELS[name]
+        self.m, self.torch, self.sv = m, torch, sv
+        dev = torch.device("cuda")
+        self.copies = []
+        host_sets = []
+        t0 = time.time()
+        for d in range(m["distinct"]):
+            lay = {}
+            for i, (nm, N, K) in enumerate(layer_linears(m)):
+                wq, ws, _ = sg.linear_case(d, 1, N, K, layer=16 * d + i)
+                lay[nm] = (wq, ws)
+            host_sets.append(lay)
+        wq, ws, _ = sg.linear_case(99, 1, m["vocab"], m["hidden"], layer=1000)
+        host_lm = (wq, ws)
+        self.host_sets, self.gen_s = host_sets, time.time() - t0
+        def gm(b):  # scales [N][K/32] -> the library's group-major [K/32][N]
+            return torch.from_numpy(np.ascontiguousarray(b.T).view(np.int16)).to(dev)
+        dev_sets = [{nm: (torch.from_numpy(a).to(dev), gm(b)) for nm, (a, b) in s.items()} for s in host_sets]
+        for c in range(m["copies"]):
+            layers = []
+            for l in range(m["layers"]):
+                src = dev_sets[(l + c) % m["distinct"]]
+                layers.append({nm: (a.clone(), b.clone()) for nm, (a, b) in src.items()})
+            lm = (torch.from_numpy(host_lm[0]).to(dev), gm(host_lm[1]))
+            self.copies.append((layers, lm if c == 0 else (lm[0].clone(), lm[1].clone())))
+        del dev_sets
+        # activations (fp32 inputs of each linear kind), quantisation and output buffers
+        Ks = sorted({K for _, _, K in layer_linears(m)})
+        self.x = {K: torch.from_numpy(sg.normal_f32(sg.stream_key(5, 3 + K), Tmax * K).reshape(Tmax, K)).to(dev)
+                  for K in Ks}
+        self.xq = {K: torch.empty((Tmax, K), dtype=torch.int8, device=dev) for K in Ks}
+        self.xs = {K: torch.empty((Tmax,), dtype=torch.float32, device=dev) for K in Ks}
+        self.y = {nm: torch.empty((Tmax * N,), dtype=torch.float32, device=dev)
+                  for nm, N, _ in layer_linears(m)}
+        self.logits = torch.empty((Tmax * m["vocab"],), dtype=torch.float32, device=dev)
+        # size the shared split-K workspace once, before any graph capture
+        for T in range(1, Tmax + 1):
+            for _, N, K in layer_linears(m) + [("lm_head", m["vocab"], m["hidden"])]:
+                sv.linear_workspace(T, N, K, dev)
+        # tree, control block and KV cache
+        self.L0 = 1024
+        self.cap = self.L0 + 4096
+        self.kc = torch.zeros((m["layers"], m["kv_heads"], self.cap, m["head_dim"]), dtype=torch.int16, device=dev)
+        self.vc = torch.zeros_like(self.kc)
+        self.ws_acc = torch.empty(sv.argmax_accept_workspace_bytes(m["vocab"], 16), dtype=torch.uint8, device=dev)
+        self.argmax = torch.empty(16, dtype=torch.int32, device=dev)
+        self.path = torch.zeros(16, dtype=torch.int32, device=dev)
+        self.stats = torch.zeros(3, dtype=torch.int32, device=dev)
+        self.ring = torch.zeros(4096, dtype=torch.int32, device=dev)
+        self.ctrl = torch.zeros(8, dtype=torch.int32, device=dev)
+        self.sg = sg
+
+    def set_tree(self, T, token_plant=None):
+        torch, sg = self.torch, self.sg
+        parent = sg.random_tree_parents(sg.stream_key(T, sg.TID_PARENT), T)
+        token = sg.tokens(sg.stream_key(T, sg.TID_TOKEN), T, self.m["vocab"])
+        if token_plant is not None:
+            depth = np.zeros(T, np.int32)
+            for i in range(1, T):
+                depth[i] = depth[parent[i]] + 1
+            c = int(np.argmax(depth))
+            while c != 0:
+                token[c] = token_plant[parent[c]]
+                c = int(parent[c])
+        self.parent = torch.from_numpy(parent).cuda()
+        self.token = torch.from_numpy(token).cuda()
+
+    def reset_ctrl(self, T):
+        self.ctrl.copy_(self.torch.tensor([self.L0, T, self.cap - 16, 0, 0, 0, 0, 0], dtype=self.torch.int32))
+
+    def step(self, T, copy=0, events=None):
+        """Enqueue one verify step. events: list to which (start, end, bytes)
+        of each linear launch are appended (eager roofline timing only)."""
+        sv, torch, m = self.sv, self.torch, self.m
+        layers, lm = self.copies[copy]
+
+        def lin(wpair, K, N, y):
+            xq, xs = self.xq[K][:T], self.xs[K][:T]
+            sv.quantize_act(self.x[K][:T], xq, xs)
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            sv.linear(wpair[0], wpair[1], xq, xs, y[: T * N].view(T, N))
+            if events is not None:
+                e1.record()
+                events.append((e0, e1, linear_bytes(T, N, K)))
+
+        for lay in layers:
+            for nm, N, K in layer_linears(m):
+                lin(lay[nm], K, N, self.y[nm])
+        lin(lm, m["hidden"], m["vocab"], self.logits)
+        sv.tree_argmax_accept(self.logits[: T * m["vocab"]].view(T, m["vocab"]), self.parent, self.token,
+                              self.ctrl, argmax=self.argmax, path=self.path, stats=self.stats,
+                              ring=self.ring, workspace=self.ws_acc)
+        sv.kv_compact(self.kc, self.vc, self.path, self.ctrl)
+
+    def step_bytes(self, T, m_acc):
+        m = self.m
+        b = 0
+        for _, N, K in layer_linears(m):
+            b += m["layers"] * (linear_bytes(T, N, K) + quant_bytes(T, K))
+        b += linear_bytes(T, m["vocab"], m["hidden"]) + quant_bytes(T, m["hidden"])
+        b += 4 * T * m["vocab"]                                         # argmax reads the logits
+        b += 2 * 2 * m_acc * m["layers"] * m["kv_heads"] * m["head_dim"] * 2  # K and V rows read + written
+        return b
+
+    def weight_bytes_total(self):
+        m = self.m
+        return m["layers"] * sum(weight_bytes(N, K) for _, N, K in layer_linears(m)) + \
+            weight_bytes(m["vocab"], m["hidden"])
+
+
+def run_T(model, T, steps, warmup, torch):
+    """Graph-captured steps at T nodes: returns ms per step, accepted m,
+    and whether graph replays reproduce the eager logits bit for bit."""
+    copies = len(model.copies)
+    model.set_tree(T)
+    model.reset_ctrl(T)
+    model.step(T)                      # eager step: find the predictions, then plant drafts
+    torch.cuda.synchronize()
+    model.set_tree(T, token_plant=model.argmax[:T].cpu().numpy())
+    model.reset_ctrl(T)
+    model.step(T)
+    torch.cuda.synchronize()
+    eager_logits = model.logits[: T * model.m["vocab"]].clone()
+    m_acc = int(model.ctrl[4].item())
+
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(copies):
+            model.step(T, copy=c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            model.step(T, copy=c)
+        graphs.append(g)
+    model.reset_ctrl(T)
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    replay_ok = bool(torch.equal(model.logits[: T * model.m["vocab"]], eager_logits))
+    model.reset_ctrl(T)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % copies].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    replay_ok = replay_ok and bool(torch.equal(model.logits[: T * model.m["vocab"]], eager_logits))
+    del graphs
+    return ms, m_acc, replay_ok
+
+
+def roofline_linear(model, T, reps, torch):
+    """Live per-launch timing of the W4A8 linear kernel with HIP events on
+    the stream it runs on. A spin kernel first holds the GPU so the host has
+    enqueued every launch before they execute back to back."""
+    durs, byts = [], []
+    model.reset_ctrl(T)
+    for r in range(reps):
+        ev = []
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(200_000_000)
+        model.step(T, copy=r % len(model.copies), events=ev)
+        torch.cuda.synchronize()
+        for a, b, nb in ev:
+            durs.append(a.elapsed_time(b) * 1e-3)
+            byts.append(nb)
+    avg_s = float(np.mean(durs))
+    avg_b = float(np.mean(byts))
+    return avg_b / avg_s / 1e9, avg_s, avg_b, len(durs) // reps
+
+
+def cpu_baseline(model, T, min_seconds=10.0):
+    """The oracle, as it stands, on a bounded sample: quantize + W4A8 linear
+    over the generated layer sets (qkv, o, gate_up, down) at T tokens, one
+    linear after another until at least `min_seconds` have passed, single
+    thread."""
+    import oracle
+    sg = model.sg
+    t0 = time.perf_counter()
+    nbytes, n = 0, 0
+    lins = [(s, nm, N, K) for s in model.host_sets for nm, N, K in layer_linears(model.m)]
+    while n == 0 or time.perf_counter() - t0 < min_seconds:
+        lay, nm, N, K = lins[n % len(lins)]
+        x = sg.normal_f32(sg.stream_key(5, 3 + K), T * K).reshape(T, K)
+        xq, xs = oracle.quantize_act(x)
+        oracle.w4a8_linear(lay[nm][0], lay[nm][1], xq, xs)
+        nbytes += linear_bytes(T, N, K) + quant_bytes(T, K)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"quantize + W4A8 linear, {n} linears of the {model.m['hidden']}-hidden layer sets "
+                      f"(qkv, o, gate_up, down) at T={T}: {nbytes/1e6:.1f} MB algorithmic in {dt:.2f} s, "
+                      f"single thread on {platform.machine()} ({os.cpu_count()} host cpus visible)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--T", type=int, default=8)
+    ap.add_argument("--workload", choices=sorted(MODELS), default="llama3-8b")
+    ap.add_argument("--sweep", default="1,2,4,8", help="T values timed besides --T")
+    ap.add_argument("--roofline-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the verification step of one request runs on one device).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_verification_amd as sv
+    import synthgen as sg
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    Ts = sorted({args.T, *[int(t) for t in args.sweep.split(",") if t]})
+    model = Model(args.workload, torch, sv, sg, max(Ts))
+    print(f"[bench] {args.workload}: weights {model.weight_bytes_total()/1e9:.3f} GB x {len(model.copies)} "
+          f"copies, generated in {model.gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    per_T = {}
+    for T in Ts:
+        ms, m_acc, ok = run_T(model, T, args.steps if T == args.T else max(5, args.steps // 2),
+                              args.warmup, torch)
+        nb = model.step_bytes(T, m_acc)
+        per_T[T] = {"ms": ms, "GB/s": nb / (ms * 1e-3) / 1e9, "accepted": m_acc, "graph_replay_exact": ok,
+                    "bytes": nb}
+        print(f"[bench] T={T}: {ms*1e3:.1f} us/step, {per_T[T]['GB/s']:.0f} GB/s, m={m_acc}, "
+              f"replay exact={ok}", file=sys.stderr, flush=True)
+
+    ach, avg_s, avg_b, nlaunch = roofline_linear(model, args.T, args.roofline_reps, torch)
+    main_T = per_T[args.T]
+    out = {
+        "metric": METRIC,
+        "value": round(main_T["GB/s"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_T["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xint8->int32,fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.workload}-shaped verify step: {MODELS[args.workload]['layers']} x (qkv, o, "
+                         f"gate_up, down) + lm_head W4A8 g32, argmax + tree accept + KV compaction, "
+                         f"T={args.T} tree nodes, HIP-graph replay"),
+            "T": args.T,
+            "weight_bytes": model.weight_bytes_total(),
+            "step_bytes": main_T["bytes"],
+        },
+        "pct_hbm_peak": round(100 * main_T["GB/s"] / HBM_PEAK_GBS, 2),
+        "us_per_verify": round(main_T["ms"] * 1e3, 2),
+        "t8_over_t1": round(per_T[8]["ms"] / per_T[1]["ms"], 4) if 8 in per_T and 1 in per_T else None,
+        "per_T": {str(T): {"us": round(v["ms"] * 1e3, 2), "GB/s": round(v["GB/s"], 1),
+                           "pct_hbm_peak": round(100 * v["GB/s"] / HBM_PEAK_GBS, 2),
+                           "accepted": v["accepted"], "graph_replay_exact": v["graph_replay_exact"]}
+                  for T, v in per_T.items()},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"w4a8_linear_kernel<{args.T},S> (all K-split variants)",
+                     "avg_launch_us": round(avg_s * 1e6, 3),
+                     "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(model, args.T),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

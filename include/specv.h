@@ -98,23 +98,35 @@ int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* x
 /*
  * W4A8 linear for T = 1..16 tokens ([P1], Small-Batch Verification Kernels
  * and Implementation; packing of [P2]):
- *   y[t][n] = xs[t] * R16_g( f32(ws[n][g]) * f32(d[t][n][g]) ),
+ *   y[t][n] = xs[t] * R16_g( f32(ws[g][n]) * f32(d[t][n][g]) ),
  *   d[t][n][g] = sum_{k in group g} (u(n,k) - 8) * xq[t][k]   (exact int32),
- * where R16 is the fixed 16-slot order (slot s accumulates the groups
- * g = s, s+16, ... in increasing g starting from +0, then slots combine with
- * s += s+off for off = 8, 4, 2, 1). The order does not depend on T, so row t
- * of a T-token call equals a 1-token call on token t bit for bit.
+ * where R16 is the fixed 16-slot order: slot s accumulates the groups
+ * g = s, s+16, ... in increasing g starting from +0, then the 16 slots are
+ * added as a binary tree in index order (slot s += slot s+w for s divisible
+ * by 2w, w = 1, 2, 4, 8). The order does not depend on T, so row t of a
+ * T-token call equals a 1-token call on token t bit for bit.
  *   wq  uint8 [N][K/2]   byte b of row n: input 2b in the low nibble, input
  *                        2b+1 in the high nibble, each stored as u = q + 8.
- *   ws  uint16 [N][K/32] fp16 bit patterns, one scale per 32 inputs.
+ *   ws  uint16 [K/32][N] fp16 bit patterns, one scale per 32 inputs, stored
+ *                        group-major (the scales of group g for all rows are
+ *                        contiguous).
  *   xq  int8 [T][K], xs fp32 [T]   from w4a8_quantize_act.
  *   y   fp32 [T][N]
+ *   workspace  device buffer of w4a8_linear_workspace(T, N, K) bytes
+ *              (may be 0, then NULL is accepted), 256-byte aligned: a 1 MiB
+ *              region of split-K counters followed by partial sums. It must
+ *              be zero-filled before its first use; every call returns the
+ *              counters it used to zero, so one buffer, sized for the
+ *              largest shape, serves any sequence of calls on one stream.
+ *              Calls that run concurrently need separate workspaces.
  * T in [1, 16], N in [0, 2^24], K a multiple of 32 in [32, 2^20],
  * N*K/2 < 2^31 bytes. N == 0 enqueues nothing.
  * Alignment: wq and xq 16 bytes, ws 2, xs and y 4.
  */
+size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K);
 int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
-                  float* y, int32_t T, int32_t N, int32_t K, void* stream);
+                  float* y, int32_t T, int32_t N, int32_t K, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /*
  * Greedy argmax per tree node and tree acceptance ([P1], GPU-Resident

@@ -12,7 +12,7 @@ import torch
 from ._lib import LIB, SpecvError, check
 
 __all__ = ["SpecvError", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
-           "argmax_accept_workspace_bytes", "kv_compact"]
+           "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace"]
 
 CTRL_FIELDS = ("committed_len", "n_nodes", "ctx_len", "done", "accept_len", "root_token", "step",
                "ring_head")
@@ -49,20 +49,42 @@ def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tens
     return xq, xs
 
 
+_WORKSPACES: dict = {}
+
+
+def linear_workspace(T: int, N: int, K: int, device) -> torch.Tensor | None:
+    """A zero-filled workspace for w4a8_linear_T on `device`, shared by calls
+    on one stream (the library leaves it zeroed after every call)."""
+    need = int(LIB.w4a8_linear_workspace(T, N, K))
+    if need == 0:
+        return None
+    dev = torch.device(device)
+    ws = _WORKSPACES.get(dev)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=dev)
+        _WORKSPACES[dev] = ws
+    return ws
+
+
 def linear(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
-           y: torch.Tensor | None = None) -> torch.Tensor:
-    """y [T][N] fp32 from nibbles wq uint8 [N][K/2], fp16 scale bits ws
-    (int16/uint16/float16 storage) [N][K/32], codes xq int8 [T][K], xs [T]."""
+           y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y [T][N] fp32 from nibbles wq uint8 [N][K/2], group-major fp16 scale
+    bits ws (int16/uint16/float16 storage) [K/32][N], codes xq int8 [T][K]
+    and token scales xs [T]."""
     N = wq.shape[0]
     T, K = xq.shape
-    if wq.shape != (N, K // 2) or ws.shape != (N, K // 32) or xs.shape != (T,):
-        raise ValueError("shape mismatch between wq, ws, xq and xs")
+    if wq.shape != (N, K // 2) or ws.shape != (K // 32, N) or xs.shape != (T,):
+        raise ValueError("shape mismatch between wq, ws (group-major), xq and xs")
     if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
         raise TypeError("ws must hold fp16 bit patterns")
     y = torch.empty((T, N), dtype=torch.float32, device=xq.device) if y is None else y
+    if workspace is None:
+        workspace = linear_workspace(T, N, K, xq.device)
+    wsp = _dev(workspace, "workspace", torch.uint8) if workspace is not None else None
+    wsb = workspace.numel() if workspace is not None else 0
     check("w4a8_linear_T", LIB.w4a8_linear_T(_dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype),
                                              _dev(xq, "xq", torch.int8), _dev(xs, "xs", torch.float32),
-                                             _dev(y, "y", torch.float32), T, N, K, _stream()))
+                                             _dev(y, "y", torch.float32), T, N, K, wsp, wsb, _stream()))
     return y
 
 

@@ -37,6 +37,11 @@ __device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
+// Reinterpret one 32-bit lane of a loaded vector as fp32. The element is
+// taken by value first: clang lowers __builtin_bit_cast applied directly to
+// an ext-vector element expression as a cast of element 0.
+__device__ __forceinline__ float lane_f32(int v) { return __builtin_bit_cast(float, v); }
+
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? SPECV_OK : SPECV_E_HIP;
 }

@@ -3,29 +3,41 @@
 // Operation (GPU-Resident Speculative Decoding for In-Browser LLM Inference
 // with WebGPU, Small-Batch Verification Kernels and Implementation):
 //   d[t][n][g] = sum_{k in group g} q(n,k) * xq[t][k]   exact int32
-//   p_g        = f32(scale[n][g]) * f32(d)               one rounding
+//   p_g        = f32(scale[g][n]) * f32(d)               one rounding
 //   y[t][n]    = xs[t] * R16(p_0 .. p_{G-1})             fixed order
 // R16: slot s in 0..15 accumulates the groups g = s, s+16, s+32, ... in
-// increasing g from +0, then slot s += slot s+off for off = 8, 4, 2, 1.
+// increasing g from +0; the 16 slots are then added as a binary tree in
+// index order (slot s += slot s+w for s divisible by 2w, w = 1, 2, 4, 8).
 //
-// Work decomposition. A workgroup owns 16 output rows and all K. Its four
-// waves split the 16 R16 slots: wave w owns slots 4w..4w+3, so in iteration j
-// it reads groups 16j+4w .. 16j+4w+3 of each row, 64 contiguous bytes per row
-// (the four waves together stream 256 contiguous bytes per row per
-// iteration). Lane l of a wave holds row l%16 and slot 4w + l/16, i.e. one
-// 16-byte group of nibbles and its scale, and keeps that slot's running fp32
-// sum for every token. The slot sums of the 16 slots meet in LDS at the end
-// and combine in the R16 tree, then xs[t] scales the result.
+// Work decomposition, three layouts chosen per shape:
+//  narrow: a workgroup owns 16 rows and all K; its four waves take the four
+//          slot quads (wave w: groups 16j + 4w + 0..3 in iteration j, 64
+//          contiguous bytes per row), and the quad sums meet in LDS, where
+//          the tree levels w = 4, 8 add them. Used when the matrix has few
+//          rows: every CU gets work without splitting K.
+//  wide:   a workgroup owns 64 rows (4 waves x 16) and all K; each wave takes
+//          all four slot quads of its rows and finishes the tree in
+//          registers. Used for tall matrices: 4x more rows share each staged
+//          activation byte.
+//  split:  64 rows and one of S K-slices (the Q = 4/S quads pQ..pQ+Q-1);
+//          each slice reduces its own slots, and the last workgroup of a row
+//          group to finish adds the S partials in tree order. The S
+//          workgroups of a row group are numbered so that the hardware's
+//          round-robin placement puts them on one XCD, whose L2 serves the
+//          lines they share. Used when the staged activations of a whole row
+//          would not fit in LDS.
+// In all layouts a workgroup stages the activation codes it needs in LDS
+// once, and every wave load covers 16 rows x 64 contiguous bytes.
 //
 // Integer dots. One v_mfma_i32_16x16x32_i8 computes, for 16 rows, the dots
-// of one 8-input chunk of each of the wave's four groups against up to four
+// of one 8-input chunk of each group of a slot quad against up to four
 // tokens: B (32x16) carries the weights, lane quarter q supplying the chunk of
-// slot 4w+q for row l%16; A (16x32) carries the activations block-diagonally,
-// row m = 4h+t holding token t's chunk of slot 4w+h in k-quarter h and zeros
-// elsewhere. Output element (m, n) = (4h+t, row) is then exactly the chunk
-// dot of row n, slot 4w+h, token t, and it lands in lane 16h + n, register t:
-// the lane that loaded that row's group and scale. Four chunks accumulate in
-// the int32 accumulator, giving the exact group dot.
+// slot q of the quad for row l%16; A (16x32) carries the activations
+// block-diagonally, row m = 4h+t holding token t's chunk of slot h in
+// k-quarter h and zeros elsewhere. Output element (m, n) = (4h+t, row) is then
+// exactly the chunk dot of row n, slot h, token t, and it lands in lane
+// 16h + n, register t: the lane that loaded that row's group and scale. Four
+// chunks accumulate in the int32 accumulator, giving the exact group dot.
 //
 // Nibble decode. Codes are stored u = q + 8. Flipping bit 3 of each nibble
 // gives the 4-bit two's complement of q; moving it into the high half of a
@@ -35,146 +47,340 @@
 // as f32(scale) * f32(d) and rounds identically.
 //
 // Ragged shapes. All global loads go through buffer resources; a lane whose
-// row or group is out of range, or whose activation row is a padding token,
-// uses an out-of-range offset and receives zeros. A zero group contributes
-// +0 to a slot, which never changes it (a slot is never -0).
+// row or group is out of range uses an out-of-range offset and receives
+// zeros, and staged activations of groups past K are zeros. A zero group
+// contributes +0 to a slot, which never changes it (a slot is never -0).
 #include "common.h"
 
 namespace specv {
 
-template <int T>
-struct Stage {
-    static constexpr int TT = (T + 3) / 4;
-    v4i w;          // 16 bytes of nibbles: one group of one row
-    uint16_t s;     // its fp16 scale
-    v4i a[TT][2];   // 32 activation codes of one token per tile (or zeros)
+// Stages of weight loads kept in flight per wave. A narrow layout runs about
+// one workgroup per CU, so it keeps many stages in flight to cover memory
+// latency; the other layouts rely on several resident workgroups per CU.
+#ifndef SPECV_NARROW_STAGES
+#define SPECV_NARROW_STAGES 4
+#endif
+#ifndef SPECV_LINEAR_STAGES
+#define SPECV_LINEAR_STAGES 2
+#endif
+
+template <int Q>
+struct WStage {
+    v4i w[Q];       // per slot quad: 16 bytes of nibbles (one group of one row)
+    uint16_t s[Q];  // and its fp16 scale
 };
 
 __device__ __forceinline__ long mk64(int lo, int hi) {
     return (long)(((unsigned long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-template <int T, int P>
-__global__ __launch_bounds__(256) void w4a8_linear_kernel(const uint8_t* __restrict__ wq,
-                                                          const uint16_t* __restrict__ ws,
-                                                          const int8_t* __restrict__ xq,
-                                                          const float* __restrict__ xs,
-                                                          float* __restrict__ y, int N, int K) {
+// Staged activation layout in LDS: [t][j][Q*128 bytes] (the slice's groups of
+// iteration j for token t), followed by 32 zero bytes that lanes whose A
+// operand must be zero read instead.
+enum { kNarrow = 0, kWide = 1 };  // modes; a split layout is MODE = S in {2, 4}
+
+template <int T, int MODE>
+__global__ __launch_bounds__(256) void w4a8_linear_kernel(
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq,
+    const float* __restrict__ xs, float* __restrict__ y, float* __restrict__ part, int* __restrict__ cnt,
+    int N, int K) {
+    constexpr int S = MODE == kNarrow || MODE == kWide ? 1 : MODE;  // K-slices
+    constexpr int QS = 4 / S;                        // slot quads staged per workgroup
+    constexpr int Q = MODE == kNarrow ? 1 : QS;      // slot quads per wave
+    constexpr int ROWS = MODE == kNarrow ? 16 : 64;  // rows per workgroup
     constexpr int TT = (T + 3) / 4;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int r = lane & 15;        // output row within the block; MFMA column n
-    const int q = lane >> 4;        // slot within the wave; k-quarter of B
-    const int h = (lane & 15) >> 2; // slot of this lane's A row
-    const int tp = lane & 3;        // token of this lane's A row within a tile
-    const int row = blockIdx.x * 16 + r;
+    constexpr int P = MODE == kNarrow ? SPECV_NARROW_STAGES : SPECV_LINEAR_STAGES;
+    extern __shared__ __attribute__((aligned(16))) int8_t act[];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r = lane & 15;         // row within the wave's 16; MFMA column n
+    const int q = lane >> 4;         // slot within the quad; k-quarter of B
+    const int h = (lane & 15) >> 2;  // slot of this lane's A row
+    const int tp = lane & 3;         // token of this lane's A row within a tile
     const int G = K >> 5;
     const int J = (G + 15) >> 4;
-    const int slot = 4 * wave + q;
+    const int NG = (N + ROWS - 1) / ROWS;
+
+    int rg, p;
+    if (S == 1) {
+        rg = blockIdx.x;
+        p = 0;
+    } else {
+        const int b = blockIdx.x, i = b >> 3;
+        p = i % S;
+        rg = (i / S) * 8 + (b & 7);
+    }
+    if (rg >= NG) return;
+    const int row = rg * ROWS + (MODE == kNarrow ? 0 : wave * 16) + r;
     const bool row_ok = row < N;
-    const bool a_active = (q == h);
+    // first slot quad of this wave
+    const int quad0 = MODE == kNarrow ? wave : p * QS;
 
     const auto rw = make_rsrc(wq, (uint32_t)((int64_t)N * (K / 2)));
-    const auto rs = make_rsrc(ws, (uint32_t)((int64_t)N * G * 2));
+    const auto rs = make_rsrc(wsg, (uint32_t)((int64_t)G * N * 2));
     const auto rx = make_rsrc(xq, (uint32_t)(T * K));
 
-    auto load_stage = [&](Stage<T>& st, int j) {
-        const int g = 16 * j + slot;
-        const bool ok = row_ok && g < G;
-        st.w = load16(rw, ok ? (uint32_t)(row * (K / 2) + 16 * g) : kOOB);
-        st.s = load2(rs, ok ? (uint32_t)((row * G + g) * 2) : kOOB);
+    // Offsets are built without branches: an out-of-range lane ORs in the
+    // out-of-range bit, so loads issue unconditionally and in program order,
+    // which lets the compiler wait for exactly one stage at a time.
+    const uint32_t wbase = (uint32_t)row * (uint32_t)(K / 2);
+    auto load_stage = [&](WStage<Q>& st, int j) {
 #pragma unroll
-        for (int tt = 0; tt < TT; tt++) {
-            const int t = 4 * tt + tp;
-            const bool aok = a_active && t < T && g < G;
-            const uint32_t off = aok ? (uint32_t)(t * K + 32 * g) : kOOB;
-            st.a[tt][0] = load16(rx, off);
-            st.a[tt][1] = load16(rx, off + 16u);
+        for (int qq = 0; qq < Q; qq++) {
+            const int g = 16 * j + 4 * (quad0 + qq) + q;
+            const uint32_t bad = (uint32_t)(!(row_ok && g < G)) << 31;
+            st.w[qq] = load16(rw, (wbase + 16u * (uint32_t)g) | bad);
+            st.s[qq] = load2(rs, (((uint32_t)g * (uint32_t)N + (uint32_t)row) * 2u) | bad);
         }
     };
 
-    float acc[T];
+    WStage<Q> st[P];
 #pragma unroll
-    for (int t = 0; t < T; t++) acc[t] = 0.0f;
+    for (int pp = 0; pp < P; pp++) {
+        load_stage(st[pp], pp);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    auto compute = [&](const Stage<T>& st) {
-        long b[4];
+    // Stage the slice's activations: all loads of a round first, then the
+    // LDS writes, so a round costs one L2 round trip.
+    const int nchunks = T * J * QS * 8;  // 16-byte chunks
+    constexpr int U = 8;
+    for (int base = 0; base < nchunks; base += 256 * U) {
+        v4i v[U];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const unsigned W = (unsigned)st.w[c] ^ 0x88888888u;
-            const unsigned lo = (W << 4) & 0xF0F0F0F0u;  // even inputs, as 16q
-            const unsigned hi = W & 0xF0F0F0F0u;         // odd inputs, as 16q
-            const unsigned b0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-            const unsigned b1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-            b[c] = mk64((int)b0, (int)b1);
+        for (int u = 0; u < U; u++) {
+            const int i = base + u * 256 + tid;
+            const int c = i % (QS * 8);
+            const int tj = i / (QS * 8);
+            const int j = tj % J;
+            const int t = tj / J;
+            const int g = 16 * j + 4 * p * QS + (c >> 1);
+            const bool ok = i < nchunks && g < G;
+            v[u] = load16(rx, ((uint32_t)(t * K + 32 * g + 16 * (c & 1))) | ((uint32_t)!ok << 31));
         }
-        v4i d[TT];
 #pragma unroll
-        for (int tt = 0; tt < TT; tt++) d[tt] = v4i{0, 0, 0, 0};
+        for (int u = 0; u < U; u++) {
+            const int i = base + u * 256 + tid;
+            if (i < nchunks) *reinterpret_cast<v4i*>(act + 16 * i) = v[u];
+        }
+    }
+    const int zero_off = nchunks * 16;
+    if (tid < 2) *reinterpret_cast<v4i*>(act + zero_off + 16 * tid) = v4i{0, 0, 0, 0};
+    __syncthreads();
+
+    float acc[Q][T];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
+    for (int qq = 0; qq < Q; qq++)
+#pragma unroll
+        for (int t = 0; t < T; t++) acc[qq][t] = 0.0f;
+
+    const bool a_active = (q == h);
+    auto compute = [&](const WStage<Q>& stg, int j) {
+#pragma unroll
+        for (int qq = 0; qq < Q; qq++) {
+            long b[4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const unsigned W = (unsigned)stg.w[qq][c] ^ 0x88888888u;
+                const unsigned lo = (W << 4) & 0xF0F0F0F0u;  // even inputs, as 16q
+                const unsigned hi = W & 0xF0F0F0F0u;         // odd inputs, as 16q
+                b[c] = mk64((int)__builtin_amdgcn_perm(hi, lo, 0x05010400u),
+                            (int)__builtin_amdgcn_perm(hi, lo, 0x07030602u));
+            }
+            v4i a0[TT], a1[TT];
 #pragma unroll
             for (int tt = 0; tt < TT; tt++) {
-                const v4i& a = st.a[tt][c >> 1];
-                const long av = (c & 1) ? mk64(a[2], a[3]) : mk64(a[0], a[1]);
-                d[tt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, b[c], d[tt], 0, 0, 0);
+                const int t = 4 * tt + tp;
+                const bool ok = a_active && t < T && j < J;
+                const int off = ok ? ((t * J + j) * QS + (quad0 - p * QS) + qq) * 128 + h * 32 : zero_off;
+                a0[tt] = *reinterpret_cast<const v4i*>(act + off);
+                a1[tt] = *reinterpret_cast<const v4i*>(act + off + 16);
             }
+            v4i d[TT];
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++) d[tt] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+#pragma unroll
+                for (int tt = 0; tt < TT; tt++) {
+                    const v4i& a = (c < 2) ? a0[tt] : a1[tt];
+                    const long av = (c & 1) ? mk64(a[2], a[3]) : mk64(a[0], a[1]);
+                    d[tt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, b[c], d[tt], 0, 0, 0);
+                }
+            const float s16 = (float)__builtin_bit_cast(_Float16, stg.s[qq]) * 0.0625f;
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++)
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    if (4 * tt + v < T) acc[qq][4 * tt + v] = acc[qq][4 * tt + v] + s16 * (float)d[tt][v];
         }
-        const float s16 = (float)__builtin_bit_cast(_Float16, st.s) * 0.0625f;
-#pragma unroll
-        for (int tt = 0; tt < TT; tt++)
-#pragma unroll
-            for (int v = 0; v < 4; v++)
-                if (4 * tt + v < T) acc[4 * tt + v] = acc[4 * tt + v] + s16 * (float)d[tt][v];
     };
 
-    Stage<T> st[P];
-#pragma unroll
-    for (int p = 0; p < P; p++)
-        if (p < J) load_stage(st[p], p);
+    // P stages in flight; stages past the last group read zeros and add +0,
+    // so the loop runs a whole number of P-blocks with no guards. The
+    // scheduling barriers keep each stage's use ahead of its refill.
     for (int j0 = 0; j0 < J; j0 += P) {
 #pragma unroll
-        for (int p = 0; p < P; p++) {
-            const int j = j0 + p;
-            if (j < J) {
-                compute(st[p]);
-                if (j + P < J) load_stage(st[p], j + P);
-            }
+        for (int pp = 0; pp < P; pp++) {
+            compute(st[pp], j0 + pp);
+            __builtin_amdgcn_sched_barrier(0);
+            load_stage(st[pp], j0 + pp + P);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    __shared__ float red[16][T][16];  // [slot][token][row]
+    // Tree levels w = 1, 2 pair the four slots of a quad: lanes q^1, then q^2.
+    float val[Q][T];
 #pragma unroll
-    for (int t = 0; t < T; t++) red[slot][t][r] = acc[t];
-    __syncthreads();
-    if (threadIdx.x < 16 * T) {
-        const int t = threadIdx.x >> 4;
-        const int rr = threadIdx.x & 15;
-        float a[16];
+    for (int qq = 0; qq < Q; qq++)
 #pragma unroll
-        for (int s = 0; s < 16; s++) a[s] = red[s][t][rr];
+        for (int t = 0; t < T; t++) {
+            float v = acc[qq][t];
+            v = v + __shfl_xor(v, 16, 64);
+            v = v + __shfl_xor(v, 32, 64);
+            val[qq][t] = v;
+        }
+
+    if (MODE == kNarrow) {  // levels w = 4, 8 across the four waves, in LDS
+        __shared__ float red[4][T][16];
+        if (q == 0)
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1)
-#pragma unroll
-            for (int s = 0; s < off; s++) a[s] = a[s] + a[s + off];
-        const int orow = blockIdx.x * 16 + rr;
-        if (orow < N) y[(int64_t)t * N + orow] = xs[t] * a[0];
+            for (int t = 0; t < T; t++) red[wave][t][r] = val[0][t];
+        __syncthreads();
+        if (tid < 16 * T) {
+            const int t = tid >> 4, rr = tid & 15;
+            const int orow = rg * ROWS + rr;
+            if (orow < N)
+                y[(int64_t)t * N + orow] = xs[t] * ((red[0][t][rr] + red[1][t][rr]) + (red[2][t][rr] + red[3][t][rr]));
+        }
+        return;
     }
+    if (MODE == kWide) {  // levels w = 4, 8 inside the lane, then the token scale
+        if (q == 0 && row_ok)
+#pragma unroll
+            for (int t = 0; t < T; t++)
+                y[(int64_t)t * N + row] =
+                    xs[t] * ((val[0][t] + val[1 % Q][t]) + (val[2 % Q][t] + val[3 % Q][t]));
+        return;
+    }
+
+    // S > 1: this slice's partial (level w = 4 inside the lane when Q = 2).
+    // Partials and counters use device-scope relaxed atomic accesses: they
+    // are coherent across the XCDs' separate L2 caches without a
+    // device-scope fence (which would write back the whole L2). All partial
+    // stores of the workgroup complete (s_waitcnt, then the barrier) before
+    // its counter increment, so the workgroup that observes the final count
+    // reads every partial.
+    if (q == 0 && row_ok)
+#pragma unroll
+        for (int t = 0; t < T; t++)
+            __hip_atomic_store(&part[((int64_t)p * T + t) * N + row],
+                               (Q == 2) ? (val[0][t] + val[1 % Q][t]) : val[0][t], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        s_last = (__hip_atomic_fetch_add(&cnt[rg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1);
+    __syncthreads();
+    if (!s_last) return;
+    const int64_t ps = (int64_t)T * N;
+    for (int idx = tid; idx < ROWS * T; idx += 256) {
+        const int t = idx / ROWS;
+        const int orow = rg * ROWS + idx % ROWS;
+        if (orow >= N) continue;
+        float* pp = part + (int64_t)t * N + orow;
+        float v[S];
+#pragma unroll
+        for (int k = 0; k < S; k++) v[k] = __hip_atomic_load(pp + k * ps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float tot = (S == 2) ? v[0] + v[1 % S] : (v[0] + v[1 % S]) + (v[2 % S] + v[3 % S]);
+        y[(int64_t)t * N + orow] = xs[t] * tot;
+    }
+    if (tid == 0) __hip_atomic_store(&cnt[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Staged activation bytes of a workgroup in a given mode.
+inline size_t linear_lds_bytes(int T, int K, int mode) {
+    const int J = (K / 32 + 15) / 16;
+    const int qs = (mode == kNarrow || mode == kWide) ? 4 : 4 / mode;
+    return (size_t)T * J * qs * 128 + 32;
+}
+
+constexpr size_t kLdsBudget = 150 * 1024;
+
+// Layout for a shape: wide when there are enough 64-row groups to fill the
+// chip, narrow otherwise, split when the staged activations of whole rows
+// would not fit in LDS.
+inline int linear_mode(int T, int N, int K) {
+#ifdef SPECV_FORCE_LINEAR_MODE
+    if (linear_lds_bytes(T, K, SPECV_FORCE_LINEAR_MODE) <= kLdsBudget) return SPECV_FORCE_LINEAR_MODE;
+#endif
+    const int NG64 = (N + 63) / 64;
+    if (linear_lds_bytes(T, K, kWide) <= kLdsBudget) return NG64 >= 256 ? kWide : kNarrow;
+    return linear_lds_bytes(T, K, 2) <= kLdsBudget && NG64 >= 256 ? 2 : 4;
+}
+
+inline int linear_row_groups_padded(int N) {
+    const int NG = (N + 63) / 64;
+    return (NG + 7) / 8 * 8;
+}
+
+// Split-K workspace: one counter per row group in a fixed region sized for
+// the largest N (so its location never depends on the call), then the
+// partials. Only the counters must start at zero; every call returns the
+// counters it used to zero, and partials are written before they are read.
+constexpr size_t kCounterBytes = (size_t)((1 << 24) / 64) * 4;
+
+template <int T, int MODE>
+static int launch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
+                  float* part, int* cnt, int N, int K, hipStream_t s) {
+    // Dynamic LDS above 64 KB must be enabled per kernel, up to what the
+    // launch needs (the static LDS of the kernel counts towards the limit).
+    static size_t lds_enabled = 64 * 1024;
+    const size_t lds = linear_lds_bytes(T, K, MODE);
+    if (lds > kLdsBudget) return SPECV_E_SHAPE;
+    if (lds > lds_enabled) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a8_linear_kernel<T, MODE>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+            (void)hipGetLastError();
+            return SPECV_E_HIP;
+        }
+        lds_enabled = lds;
+    }
+    const int grid = MODE == kNarrow ? (N + 15) / 16
+                     : MODE == kWide ? (N + 63) / 64
+                                     : MODE * linear_row_groups_padded(N);
+    hipLaunchKernelGGL((w4a8_linear_kernel<T, MODE>), dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, part,
+                       cnt, N, K);
+    return launch_status();
 }
 
 template <int T>
-static void launch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                   int N, int K, hipStream_t s) {
-    constexpr int P = 4;
-    hipLaunchKernelGGL((w4a8_linear_kernel<T, P>), dim3((N + 15) / 16), dim3(256), 0, s, wq, ws, xq,
-                       xs, y, N, K);
+static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
+                    float* part, int* cnt, int N, int K, hipStream_t s) {
+    switch (linear_mode(T, N, K)) {
+        case kNarrow: return launch<T, kNarrow>(wq, ws, xq, xs, y, part, cnt, N, K, s);
+        case kWide: return launch<T, kWide>(wq, ws, xq, xs, y, part, cnt, N, K, s);
+        case 2: return launch<T, 2>(wq, ws, xq, xs, y, part, cnt, N, K, s);
+        default: return launch<T, 4>(wq, ws, xq, xs, y, part, cnt, N, K, s);
+    }
 }
 
 }  // namespace specv
 
-extern "C" int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
-                             const float* xs, float* y, int32_t T, int32_t N, int32_t K,
-                             void* stream) {
+extern "C" size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K) {
+    using namespace specv;
+    if (T < 1 || T > 16 || N < 1 || K < 32 || K % 32) return 0;
+    const int mode = linear_mode(T, N, K);
+    if (mode == kNarrow || mode == kWide) return 0;
+    return kCounterBytes + (size_t)mode * T * N * 4;
+}
+
+extern "C" int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
+                             float* y, int32_t T, int32_t N, int32_t K, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     using namespace specv;
     if (T < 1 || T > 16 || N < 0 || N > (1 << 24) || K < 32 || K > (1 << 20) || K % 32)
         return SPECV_E_SHAPE;
@@ -183,15 +389,19 @@ extern "C" int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t
     if (!wq || !ws || !xq || !xs || !y) return SPECV_E_INVAL;
     if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(ws, 2) || !aligned(xs, 4) || !aligned(y, 4))
         return SPECV_E_ALIGN;
+    const size_t need = w4a8_linear_workspace(T, N, K);
+    if (need && (!workspace || workspace_bytes < need)) return SPECV_E_WORKSPACE;
+    if (need && !aligned(workspace, 256)) return SPECV_E_ALIGN;
+    int* cnt = static_cast<int*>(workspace);
+    float* part = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
     hipStream_t s = (hipStream_t)stream;
     switch (T) {
 #define SPECV_CASE(n) \
-    case n: launch<n>(wq, ws, xq, xs, y, N, K, s); break;
+    case n: return launch_T<n>(wq, ws, xq, xs, y, part, cnt, N, K, s);
         SPECV_CASE(1) SPECV_CASE(2) SPECV_CASE(3) SPECV_CASE(4) SPECV_CASE(5) SPECV_CASE(6)
         SPECV_CASE(7) SPECV_CASE(8) SPECV_CASE(9) SPECV_CASE(10) SPECV_CASE(11) SPECV_CASE(12)
         SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
 #undef SPECV_CASE
         default: return SPECV_E_SHAPE;
     }
-    return launch_status();
 }

@@ -38,6 +38,55 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_kernel(
     }
 }
 
+// Register-resident variant for rows of up to 4*CH*256 values with K % 4 == 0
+// and 16-byte aligned rows: every thread loads its CH float4 at once (one
+// memory round trip), reduces the max, then quantises from registers and
+// stores four codes per 32-bit word.
+template <int CH>
+__global__ __launch_bounds__(kQuantThreads) void quantize_act_reg_kernel(
+    const float* __restrict__ x, int K, int8_t* __restrict__ xq, float* __restrict__ xs) {
+    const int t = blockIdx.x;
+    const int K4 = K >> 2;
+    const auto rx = make_rsrc(x + (int64_t)t * K, (uint32_t)K * 4u);
+    v4i raw[CH];
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+        const int i = c * kQuantThreads + threadIdx.x;
+        raw[c] = load16(rx, ((uint32_t)i * 16u) | ((uint32_t)(i >= K4) << 31));
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; c++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) a = fmaxf(a, fabsf(lane_f32(raw[c][e])));
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    __shared__ float wave_max[kQuantThreads / 64];
+    if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = wave_max[0];
+#pragma unroll
+    for (int w = 1; w < kQuantThreads / 64; w++) a = fmaxf(a, wave_max[w]);
+
+    const bool zero = (a == 0.0f);
+    const float inv = zero ? 0.0f : 127.0f / a;
+    if (threadIdx.x == 0) xs[t] = zero ? 0.0f : a / 127.0f;
+    uint32_t* out = reinterpret_cast<uint32_t*>(xq + (int64_t)t * K);
+#pragma unroll
+    for (int c = 0; c < CH; c++) {
+        const int i = c * kQuantThreads + threadIdx.x;
+        if (i < K4) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float r = __builtin_rintf(lane_f32(raw[c][e]) * inv);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                packed |= ((uint32_t)(int)r & 0xffu) << (8 * e);
+            }
+            out[i] = packed;
+        }
+    }
+}
+
 }  // namespace specv
 
 extern "C" int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs,
@@ -47,7 +96,20 @@ extern "C" int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* x
     if (T == 0) return SPECV_OK;
     if (!x || !xq || !xs) return SPECV_E_INVAL;
     if (!aligned(x, 4) || !aligned(xs, 4)) return SPECV_E_ALIGN;
-    hipLaunchKernelGGL(quantize_act_kernel, dim3(T), dim3(kQuantThreads), 0, (hipStream_t)stream,
-                       x, K, xq, xs);
+    hipStream_t s = (hipStream_t)stream;
+    const int K4 = K / 4;
+    const bool vec = K % 4 == 0 && aligned(x, 16) && aligned(xq, 4);
+    if (vec && K4 <= 1 * kQuantThreads)
+        hipLaunchKernelGGL(quantize_act_reg_kernel<1>, dim3(T), dim3(kQuantThreads), 0, s, x, K, xq, xs);
+    else if (vec && K4 <= 2 * kQuantThreads)
+        hipLaunchKernelGGL(quantize_act_reg_kernel<2>, dim3(T), dim3(kQuantThreads), 0, s, x, K, xq, xs);
+    else if (vec && K4 <= 4 * kQuantThreads)
+        hipLaunchKernelGGL(quantize_act_reg_kernel<4>, dim3(T), dim3(kQuantThreads), 0, s, x, K, xq, xs);
+    else if (vec && K4 <= 8 * kQuantThreads)
+        hipLaunchKernelGGL(quantize_act_reg_kernel<8>, dim3(T), dim3(kQuantThreads), 0, s, x, K, xq, xs);
+    else if (vec && K4 <= 16 * kQuantThreads)
+        hipLaunchKernelGGL(quantize_act_reg_kernel<16>, dim3(T), dim3(kQuantThreads), 0, s, x, K, xq, xs);
+    else
+        hipLaunchKernelGGL(quantize_act_kernel, dim3(T), dim3(kQuantThreads), 0, s, x, K, xq, xs);
     return launch_status();
 }

@@ -57,17 +57,28 @@ A = 0x10000  # a fake, 64 KiB-aligned address: validation never dereferences it
 
 def test_linear_rejects_bad_arguments(lib):
     f = lib.w4a8_linear_T
-    assert f(A, A, A, A, A, 1, 16, 33, None) == E_SHAPE      # K not a multiple of 32
-    assert f(A, A, A, A, A, 0, 16, 64, None) == E_SHAPE      # T < 1
-    assert f(A, A, A, A, A, 17, 16, 64, None) == E_SHAPE     # T > 16
-    assert f(A, A, A, A, A, 1, -1, 64, None) == E_SHAPE
-    assert f(A, A, A, A, A, 1, 1 << 22, 1024, None) == E_SHAPE  # weights >= 2 GiB
-    assert f(None, A, A, A, A, 1, 16, 64, None) == E_INVAL
-    assert f(A, A, A, A, None, 1, 16, 64, None) == E_INVAL
-    assert f(A + 8, A, A, A, A, 1, 16, 64, None) == E_ALIGN   # wq not 16-byte aligned
-    assert f(A, A, A + 4, A, A, 1, 16, 64, None) == E_ALIGN   # xq not 16-byte aligned
-    assert f(A, A + 1, A, A, A, 1, 16, 64, None) == E_ALIGN
-    assert f(None, None, None, None, None, 1, 0, 64, None) == OK  # N == 0: nothing to do
+    W = 1 << 30  # workspace bytes: larger than any shape below needs
+    assert f(A, A, A, A, A, 1, 16, 33, A, W, None) == E_SHAPE      # K not a multiple of 32
+    assert f(A, A, A, A, A, 0, 16, 64, A, W, None) == E_SHAPE      # T < 1
+    assert f(A, A, A, A, A, 17, 16, 64, A, W, None) == E_SHAPE     # T > 16
+    assert f(A, A, A, A, A, 1, -1, 64, A, W, None) == E_SHAPE
+    assert f(A, A, A, A, A, 1, 1 << 22, 1024, A, W, None) == E_SHAPE  # weights >= 2 GiB
+    assert f(None, A, A, A, A, 1, 16, 64, A, W, None) == E_INVAL
+    assert f(A, A, A, A, None, 1, 16, 64, A, W, None) == E_INVAL
+    assert f(A + 8, A, A, A, A, 1, 16, 64, A, W, None) == E_ALIGN   # wq not 16-byte aligned
+    assert f(A, A, A + 4, A, A, 1, 16, 64, A, W, None) == E_ALIGN   # xq not 16-byte aligned
+    assert f(A, A + 1, A, A, A, 1, 16, 64, A, W, None) == E_ALIGN
+    assert f(None, None, None, None, None, 1, 0, 64, None, 0, None) == OK  # N == 0: nothing to do
+    # workspace: only shapes whose staged activations overflow LDS split K
+    need = lib.w4a8_linear_workspace(16, 4096, 14336)
+    assert need == (1 << 20) + 4 * 16 * 4096 * 4                     # 4 slices
+    assert f(A, A, A, A, A, 16, 4096, 14336, None, 0, None) == E_WORKSPACE
+    assert f(A, A, A, A, A, 16, 4096, 14336, A, need - 1, None) == E_WORKSPACE
+    assert f(A, A, A, A, A, 16, 4096, 14336, A + 16, need, None) == E_ALIGN
+    assert lib.w4a8_linear_workspace(16, 16400, 10240) == (1 << 20) + 2 * 16 * 16400 * 4  # 2 slices
+    for T, N, K in ((8, 4096, 4096), (8, 4096, 14336), (8, 28672, 4096), (8, 128256, 4096), (16, 896, 4864)):
+        assert lib.w4a8_linear_workspace(T, N, K) == 0              # narrow or wide: none
+    assert lib.w4a8_linear_workspace(0, 16, 64) == 0
 
 
 def test_quantize_rejects_bad_arguments(lib):

@@ -41,15 +41,20 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def ws_dev(ws: np.ndarray) -> torch.Tensor:
+    """Scales [N][K/32] as generated -> the library's group-major [K/32][N]."""
+    return to_dev(np.ascontiguousarray(ws.T))
+
+
 @functools.lru_cache(maxsize=2)
 def _weights(seed, N, K, layer):
     wq, ws, _ = sg.linear_case(seed, 1, N, K, layer=layer)
-    return wq, ws, to_dev(wq), to_dev(ws)
+    return wq, ws, to_dev(wq), ws_dev(ws)
 
 
 def gpu_quant_linear(sv, wq, ws, x, wq_d=None, ws_d=None):
     xq, xs = sv.quantize_act(to_dev(x))
-    y = sv.linear(to_dev(wq) if wq_d is None else wq_d, to_dev(ws) if ws_d is None else ws_d, xq, xs)
+    y = sv.linear(to_dev(wq) if wq_d is None else wq_d, ws_dev(ws) if ws_d is None else ws_d, xq, xs)
     torch.cuda.synchronize()
     return xq.cpu().numpy(), xs.cpu().numpy(), y.cpu().numpy()
 
@@ -67,7 +72,7 @@ def assert_bits(a: np.ndarray, b: np.ndarray, what: str):
 # ------------------------------------------------------------------ quantisation
 
 @pytest.mark.parametrize("T,K", [(1, 896), (8, 896), (3, 4864), (16, 4096), (8, 14336), (2, 33), (5, 1),
-                                 (64, 96)])
+                                 (64, 96), (3, 16388), (4, 1024), (2, 2048)])
 def test_quantize_parity(sv, T, K):
     case(f"quantize T={T} K={K}")
     x = sg.normal_f32(sg.stream_key(40 + T, sg.TID_X), T * K).reshape(T, K)
@@ -83,11 +88,27 @@ def test_quantize_parity(sv, T, K):
     assert_bits(xs.cpu().numpy(), xs_o, "xs")
 
 
+def test_quantize_misaligned_rows(sv):
+    """Rows that start off a 16-byte boundary take the scalar kernel."""
+    case("quantize misaligned x")
+    T, K = 4, 896
+    x = sg.normal_f32(sg.stream_key(45, sg.TID_X), T * K + 1)
+    xq_o, xs_o = oracle.quantize_act(x[1:].reshape(T, K).copy())
+    xd = to_dev(x)[1:].view(T, K)
+    assert xd.data_ptr() % 16 != 0
+    xq, xs = sv.quantize_act(xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert_bits(xs.cpu().numpy(), xs_o, "xs")
+
+
 # ------------------------------------------------------------------ linear, small and ragged
 
 @pytest.mark.parametrize("T,N,K", [(1, 16, 32), (3, 17, 64), (5, 33, 96), (7, 40, 544), (8, 100, 896),
                                    (16, 50, 4864), (4, 1, 4096), (2, 15, 14336), (9, 31, 512),
-                                   (12, 64, 1024), (6, 48, 160)])
+                                   (12, 64, 1024), (6, 48, 160), (16, 130, 14336),
+                                   # K split in 2 (>= 256 row groups) and unsplit (>= 1024)
+                                   (3, 16400, 96), (8, 16385, 544), (5, 65601, 64), (16, 65600, 160)])
 def test_linear_parity_ragged(sv, T, N, K):
     case(f"linear ragged T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(50 + T, T, N, K)
@@ -150,7 +171,7 @@ def test_linear_rows_of_T_equal_single_token(sv):
     on token t, for every T bucket, on the 8B-shaped q projection."""
     N, K = LLAMA["q"]
     wq, ws, x = sg.linear_case(7, 16, N, K)
-    wq_d, ws_d = to_dev(wq), to_dev(ws)
+    wq_d, ws_d = to_dev(wq), ws_dev(ws)
     xq, xs = sv.quantize_act(to_dev(x))
     singles = [sv.linear(wq_d, ws_d, xq[t:t + 1].contiguous(), xs[t:t + 1].contiguous()) for t in range(16)]
     single = torch.cat(singles, 0).cpu().numpy()
@@ -164,11 +185,42 @@ def test_linear_run_to_run_identical(sv):
     case("determinism lm_head qwen T=8")
     N, K = QWEN["lm_head"]
     wq, ws, x = sg.linear_case(8, 8, N, K)
-    wq_d, ws_d = to_dev(wq), to_dev(ws)
+    wq_d, ws_d = to_dev(wq), ws_dev(ws)
     xq, xs = sv.quantize_act(to_dev(x))
     a = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
     b = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
     assert a.tobytes() == b.tobytes()
+
+
+@pytest.mark.parametrize("T,N,K", [(16, 16400, 10240), (16, 4096, 14336), (8, 4096, 14336), (8, 28672, 4096)])
+def test_linear_layouts_sampled(sv, T, N, K):
+    """Two-slice and four-slice K splits (activations too large for LDS) and
+    the narrow and wide layouts at full size, on sampled rows."""
+    case(f"linear layout T={T} N={N} K={K}")
+    wq, ws, x = sg.linear_case(11, T, N, K)
+    xq_o, xs_o = oracle.quantize_act(x)
+    _, _, y = gpu_quant_linear(sv, wq, ws, x)
+    rows = _sample_rows(N, 11, n=40)
+    assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), f"T={T} N={N} K={K}")
+
+
+@pytest.mark.parametrize("T,N,K", [(16, 4096, 14336), (16, 16400, 10240), (8, 128256, 896)])
+def test_linear_workspace_reuse(sv, T, N, K):
+    """One zeroed workspace serves repeated calls and calls of other shapes:
+    the split-K counters are left at zero by every call."""
+    case(f"workspace reuse T={T} N={N} K={K}")
+    wq, ws, x = sg.linear_case(10, T, N, K)
+    wq_d, ws_d = to_dev(wq), ws_dev(ws)
+    xq, xs = sv.quantize_act(to_dev(x))
+    first = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
+    for T2 in (1, 5, 16):
+        sv.linear(wq_d[: N // 2].contiguous(), ws_d[:, : N // 2].contiguous(), xq[:T2].contiguous(),
+                  xs[:T2].contiguous())
+        again = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
+        assert again.tobytes() == first.tobytes()
+    rows = _sample_rows(N, 10, n=32)
+    xq_o, xs_o = oracle.quantize_act(x)
+    assert_bits(first[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), "reuse sampled")
 
 
 def test_linear_degenerate_values(sv):
@@ -188,7 +240,7 @@ def test_linear_degenerate_values(sv):
     _, _, y = gpu_quant_linear(sv, wq, ws, x)
     assert_bits(y, y_o, "degenerate")
     empty = sv.linear(torch.zeros((0, 16), dtype=torch.uint8, device="cuda"),
-                      torch.zeros((0, 1), dtype=torch.int16, device="cuda"),
+                      torch.zeros((1, 0), dtype=torch.int16, device="cuda"),
                       torch.zeros((1, 32), dtype=torch.int8, device="cuda"),
                       torch.ones(1, device="cuda"))
     assert empty.shape == (1, 0)
