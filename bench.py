@@ -140,7 +140,7 @@ class Model:
         sv, torch, m = self.sv, self.torch, self.m
         layers, lm = self.copies[copy]
 
-        def lin(wpair, K, N, y):
+        def lin(name, wpair, K, N, y):
             xq, xs = self.xq[K][:T], self.xs[K][:T]
             sv.quantize_act(self.x[K][:T], xq, xs)
             if events is not None:
@@ -149,12 +149,12 @@ class Model:
             sv.linear(wpair[0], wpair[1], xq, xs, y[: T * N].view(T, N))
             if events is not None:
                 e1.record()
-                events.append((e0, e1, linear_bytes(T, N, K)))
+                events.append((e0, e1, linear_bytes(T, N, K), name))
 
         for lay in layers:
             for nm, N, K in layer_linears(m):
-                lin(lay[nm], K, N, self.y[nm])
-        lin(lm, m["hidden"], m["vocab"], self.logits)
+                lin(nm, lay[nm], K, N, self.y[nm])
+        lin("lm_head", lm, m["hidden"], m["vocab"], self.logits)
         sv.tree_argmax_accept(self.logits[: T * m["vocab"]].view(T, m["vocab"]), self.parent, self.token,
                               self.ctrl, argmax=self.argmax, path=self.path, stats=self.stats,
                               ring=self.ring, workspace=self.ws_acc)
@@ -227,7 +227,7 @@ def roofline_linear(model, T, reps, torch):
     """Live per-launch timing of the W4A8 linear kernel with HIP events on
     the stream it runs on. A spin kernel first holds the GPU so the host has
     enqueued every launch before they execute back to back."""
-    durs, byts = [], []
+    durs, byts, names = [], [], []
     model.reset_ctrl(T)
     for r in range(reps):
         ev = []
@@ -235,12 +235,18 @@ def roofline_linear(model, T, reps, torch):
             torch.cuda._sleep(200_000_000)
         model.step(T, copy=r % len(model.copies), events=ev)
         torch.cuda.synchronize()
-        for a, b, nb in ev:
+        for a, b, nb, nm in ev:
             durs.append(a.elapsed_time(b) * 1e-3)
             byts.append(nb)
-    avg_s = float(np.mean(durs))
-    avg_b = float(np.mean(byts))
-    return avg_b / avg_s / 1e9, avg_s, avg_b, len(durs) // reps
+            names.append(nm)
+    durs, byts = np.array(durs), np.array(byts, dtype=np.float64)
+    by_shape = {}
+    for nm in dict.fromkeys(names):
+        sel = np.array([n == nm for n in names])
+        us = float(durs[sel].mean() * 1e6)
+        by_shape[nm] = {"us": round(us, 2), "GB/s": round(float(byts[sel].mean()) / us / 1e3, 1)}
+    avg_s, avg_b = float(durs.mean()), float(byts.mean())
+    return avg_b / avg_s / 1e9, avg_s, avg_b, len(durs) // reps, by_shape
 
 
 def cpu_baseline(model, T, min_seconds=10.0):
@@ -313,7 +319,7 @@ def main():
         print(f"[bench] T={T}: {ms*1e3:.1f} us/step, {per_T[T]['GB/s']:.0f} GB/s, m={m_acc}, "
               f"replay exact={ok}", file=sys.stderr, flush=True)
 
-    ach, avg_s, avg_b, nlaunch = roofline_linear(model, args.T, args.roofline_reps, torch)
+    ach, avg_s, avg_b, nlaunch, by_shape = roofline_linear(model, args.T, args.roofline_reps, torch)
     main_T = per_T[args.T]
     out = {
         "metric": METRIC,
@@ -347,7 +353,8 @@ def main():
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": f"w4a8_linear_kernel<{args.T},S> (all K-split variants)",
                      "avg_launch_us": round(avg_s * 1e6, 3),
-                     "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch},
+                     "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
+                     "by_shape": by_shape},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(model, args.T),
     }
     print(json.dumps(out), flush=True)
