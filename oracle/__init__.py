@@ -13,7 +13,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SO = os.path.join(HERE, "liboracle.so")
-SOURCES = ["oracle.c"]
+SOURCES = ["oracle.c", "forward.c"]
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
           "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
@@ -56,8 +56,17 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_argmax.argtypes = [P, I, I64, P]
     L.orc_tree_accept.argtypes = [P, P, P, I, P, P]
     L.orc_kv_compact.argtypes = [P, I, I, I, I, I, P, I]
+    L.orc_det_exp.argtypes, L.orc_det_exp.restype = [ctypes.c_float], ctypes.c_float
+    L.orc_silu.argtypes, L.orc_silu.restype = [ctypes.c_float], ctypes.c_float
+    L.orc_rmsnorm.argtypes, L.orc_rmsnorm.restype = [P, P, I, ctypes.c_float, P], None
+    L.orc_rope_table.argtypes = [P, P, I, I, ctypes.c_double]
+    L.orc_attention.argtypes = [P, P, P, I, P, I, P]
+    L.orc_forward.argtypes = [P, P, P, I, I, I, P, P, P]
+    L.orc_tree_step.argtypes = [P, P, P, I, P, I, P, P, P, P, P, P]
+    L.orc_draft_tree.argtypes = [I, I, ctypes.c_int32, P, I, P, ctypes.c_uint32, I, P, P, P]
     for f in ("orc_quantize_act", "orc_group_dots", "orc_w4a8_linear", "orc_w4a8_linear_rows",
-              "orc_argmax", "orc_tree_accept", "orc_kv_compact"):
+              "orc_argmax", "orc_tree_accept", "orc_kv_compact", "orc_rope_table", "orc_attention",
+              "orc_forward", "orc_tree_step", "orc_draft_tree"):
         getattr(L, f).restype = I
 
 
@@ -148,3 +157,140 @@ def kv_compact(cache: np.ndarray, L: int, path: np.ndarray, m: int) -> None:
     layers, heads, cap, hd = cache.shape
     path = np.ascontiguousarray(path, np.int32)
     _check(lib().orc_kv_compact(_p(cache), layers, heads, cap, hd, L, _p(path), m), "kv_compact")
+
+
+# ---------------------------------------------------------------- forward
+
+def det_exp(x: float) -> np.float32:
+    return np.float32(lib().orc_det_exp(x))
+
+
+def silu(g: float) -> np.float32:
+    return np.float32(lib().orc_silu(g))
+
+
+def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    w = np.ascontiguousarray(w, np.float32)
+    y = np.empty_like(x)
+    lib().orc_rmsnorm(_p(x), _p(w), x.size, eps, _p(y))
+    return y
+
+
+def rope_table(max_pos: int, head_dim: int, theta: float = 1e6):
+    c = np.empty((max_pos, head_dim // 2), np.float32)
+    s = np.empty((max_pos, head_dim // 2), np.float32)
+    _check(lib().orc_rope_table(_p(c), _p(s), max_pos, head_dim, theta), "rope_table")
+    return c, s
+
+
+def attention(q: np.ndarray, kplane: np.ndarray, vplane: np.ndarray, rows) -> np.ndarray:
+    """One query head over rows of one KV head plane [cap][hd] (fp16 bits)."""
+    q = np.ascontiguousarray(q, np.float32)
+    rows = np.ascontiguousarray(rows, np.int32)
+    hd = q.size
+    out = np.empty(hd, np.float32)
+    _check(lib().orc_attention(_p(q), _p(np.ascontiguousarray(kplane)), _p(np.ascontiguousarray(vplane)),
+                               hd, _p(rows), rows.size, _p(out)), "attention")
+    return out
+
+
+class _OrcModel(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim",
+                                            "inter", "vocab", "max_pos")] + [("eps", ctypes.c_float)] + \
+               [(n, ctypes.c_void_p) for n in ("wq", "sq", "wk", "sk", "wv", "sv", "wo", "so", "wg", "sg",
+                                              "wu", "su", "wd", "sd", "norm_attn", "norm_mlp", "norm_final",
+                                              "wlm", "slm", "rope_cos", "rope_sin")]
+
+
+class Model:
+    """Holds a model's host arrays (canonical layouts: nibbles [rows][K/2],
+    scales [rows][K/32]) and the C struct that points into them."""
+
+    def __init__(self, arrays: dict, cfg: dict):
+        self.cfg, self.arrays = cfg, arrays
+        self._keep = []
+        c = _OrcModel()
+        for k in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab", "max_pos"):
+            setattr(c, k, int(cfg[k]))
+        c.eps = float(cfg["eps"])
+        for k in ("wq", "sq", "wk", "sk", "wv", "sv", "wo", "so", "wg", "sg", "wu", "su", "wd", "sd",
+                  "norm_attn", "norm_mlp"):
+            arr = (ctypes.c_void_p * cfg["n_layers"])(*[_p(a) for a in arrays[k]])
+            self._keep.append(arr)
+            setattr(c, k, ctypes.cast(arr, ctypes.c_void_p))
+        for k in ("norm_final", "wlm", "slm", "rope_cos", "rope_sin"):
+            setattr(c, k, _p(arrays[k]))
+        self.c = c
+
+    def ptr(self):
+        return ctypes.addressof(self.c)
+
+
+def forward(model: Model, kc: np.ndarray, vc: np.ndarray, L: int, parent, token) -> np.ndarray:
+    """Forward over a tree; writes K/V rows L+i in place; returns logits [N][V]."""
+    parent = np.ascontiguousarray(parent, np.int32)
+    token = np.ascontiguousarray(token, np.int32)
+    N = parent.size
+    logits = np.empty((N, model.cfg["vocab"]), np.float32)
+    cap = kc.shape[2]
+    _check(lib().orc_forward(model.ptr(), _p(kc), _p(vc), cap, L, N, _p(parent), _p(token), _p(logits)),
+           "forward")
+    return logits
+
+
+def tree_step(model: Model, kc: np.ndarray, vc: np.ndarray, L: int, parent, token, want_logits=False):
+    """Forward + argmax + acceptance + compaction. Returns dict with m, path,
+    bonus, amax, new L (and logits)."""
+    parent = np.ascontiguousarray(parent, np.int32)
+    token = np.ascontiguousarray(token, np.int32)
+    N = parent.size
+    logits = np.empty((N, model.cfg["vocab"]), np.float32) if want_logits else None
+    amax = np.empty(N, np.int32)
+    path = np.zeros(N, np.int32)
+    bonus = np.zeros(1, np.int32)
+    Lb = ctypes.c_int(L)
+    m = lib().orc_tree_step(model.ptr(), _p(kc), _p(vc), kc.shape[2], ctypes.byref(Lb), N, _p(parent),
+                            _p(token), _p(logits) if logits is not None else None, _p(amax), _p(path),
+                            _p(bonus))
+    _check(m, "tree_step")
+    return {"m": m, "path": path[: m + 1].copy(), "bonus": int(bonus[0]), "amax": amax, "L": Lb.value,
+            "logits": logits}
+
+
+def draft_tree(width, L, root_token, greedy, draws, threshold, vocab):
+    greedy = np.ascontiguousarray(greedy, np.int32)
+    draws = np.ascontiguousarray(draws, np.uint32)
+    parent = np.zeros(width, np.int32)
+    token = np.zeros(width, np.int32)
+    bm = ctypes.c_int(0)
+    _check(lib().orc_draft_tree(width, L, root_token, _p(greedy), greedy.size, _p(draws), threshold, vocab,
+                                _p(parent), _p(token), ctypes.byref(bm)), "draft_tree")
+    return parent, token, bm.value
+
+
+def window(model: Model, kc, vc, ctrl: dict, width: int, W: int, greedy, draws_table, threshold):
+    """W speculation steps of the device-resident window, driven by the
+    control state (committed_len, root_token, step, done, ctx_len, ring):
+    each step drafts a tree, verifies it, accepts and compacts. Steps after
+    `done` do nothing. Returns the per-step statistics and emitted tokens."""
+    stats, emitted = [], []
+    for _ in range(W):
+        if ctrl["done"]:
+            stats.append((-1, 0, width))
+            ctrl["accept_len"] = 0
+            continue
+        L = ctrl["committed_len"]
+        parent, token, bm = draft_tree(width, L, ctrl["root_token"], greedy,
+                                       draws_table[ctrl["step"] % len(draws_table)], threshold,
+                                       model.cfg["vocab"])
+        r = tree_step(model, kc, vc, L, parent, token)
+        m = r["m"]
+        out = [int(token[p]) for p in r["path"][1:]] + [r["bonus"]]
+        emitted.extend(out)
+        ctrl.update(committed_len=r["L"], accept_len=m, root_token=r["bonus"], step=ctrl["step"] + 1,
+                    ring_head=ctrl["ring_head"] + m + 1)
+        if r["L"] + width > ctrl["ctx_len"]:
+            ctrl["done"] = 1
+        stats.append((m, bm, width))
+    return stats, emitted

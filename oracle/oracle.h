@@ -60,4 +60,61 @@ int orc_kv_compact(uint16_t* cache, int layers, int heads, int cap, int hd,
 #ifdef __cplusplus
 }
 #endif
+
+/* ------------------------------------------------------------------ forward
+ * Tree-masked forward of a small-batch verification step and the
+ * device-resident speculation window, for a Qwen2.5-shaped decoder. All
+ * weights use the W4A8 format above with row-major scales [rows][K/32]. */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab, max_pos;
+    float eps;
+    /* per layer (arrays of n_layers host pointers) */
+    const uint8_t* const* wq; const uint16_t* const* sq;  /* [nh*hd][H]   */
+    const uint8_t* const* wk; const uint16_t* const* sk;  /* [nkv*hd][H]  */
+    const uint8_t* const* wv; const uint16_t* const* sv;  /* [nkv*hd][H]  */
+    const uint8_t* const* wo; const uint16_t* const* so;  /* [H][nh*hd]   */
+    const uint8_t* const* wg; const uint16_t* const* sg;  /* [I][H]       */
+    const uint8_t* const* wu; const uint16_t* const* su;  /* [I][H]       */
+    const uint8_t* const* wd; const uint16_t* const* sd;  /* [H][I]       */
+    const float* const* norm_attn; const float* const* norm_mlp;  /* [H] */
+    const float* norm_final;                                      /* [H] */
+    const uint8_t* wlm; const uint16_t* slm;                      /* [V][H] */
+    const float* rope_cos; const float* rope_sin;                 /* [max_pos][hd/2] */
+} orc_model;
+
+float orc_det_exp(float x);
+float orc_silu(float g);
+void orc_rmsnorm(const float* x, const float* w, int H, float eps, float* y);
+int orc_rope_table(float* cos_t, float* sin_t, int max_pos, int head_dim, double theta);
+
+/* Chunked attention of one query head (scores scaled by 1/sqrt(hd)) over the KV rows
+ * `rows` (logical order) of one head plane [..][hd] (fp16 bits). */
+int orc_attention(const float* q, const uint16_t* kc, const uint16_t* vc, int hd, const int* rows,
+                  int len, float* out);
+
+/* One forward pass over a tree of N nodes whose root sits at committed
+ * length L: writes K/V rows L+i of every layer and logits [N][V]. */
+int orc_forward(const orc_model* m, uint16_t* kc, uint16_t* vc, int cap, int L, int N,
+                const int32_t* parent, const int32_t* token, float* logits);
+
+/* A full verification step: forward, argmax, acceptance and compaction.
+ * *L advances by m+1; returns m (>= 0) and fills path[0..m], amax[0..N),
+ * *bonus; or -1 on bad arguments. logits may be NULL. */
+int orc_tree_step(const orc_model* m, uint16_t* kc, uint16_t* vc, int cap, int* L, int N,
+                  const int32_t* parent, const int32_t* token, float* logits, int32_t* amax,
+                  int32_t* path, int32_t* bonus);
+
+/* Synthetic drafter of the window: the tree for one step. */
+int orc_draft_tree(int width, int L, int32_t root_token, const int32_t* greedy, int stream_len,
+                   const uint32_t* draws, uint32_t threshold, int vocab, int32_t* parent,
+                   int32_t* token, int* best_match);
+
+#ifdef __cplusplus
+}
+#endif
 #endif

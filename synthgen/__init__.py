@@ -119,3 +119,59 @@ def linear_case(seed: int, T: int, N: int, K: int, layer: int = 0):
     ws = fp16_bits_uniform(stream_key(seed, base + TID_WS), N * (K // 32), 0.005, 0.02)
     x = normal_f32(stream_key(seed, base + TID_X), T * K).reshape(T, K)
     return wq, ws.reshape(N, K // 32), x
+
+
+# ---------------------------------------------------------------- models
+
+QWEN05 = dict(n_layers=24, hidden=896, n_heads=14, n_kv_heads=2, head_dim=64, inter=4864, vocab=151936,
+              eps=1e-6, max_pos=4096 + 64)
+TINY = dict(n_layers=2, hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, inter=96, vocab=300,
+            eps=1e-6, max_pos=640)
+
+
+def model_case(seed: int, cfg: dict, distinct_layers: int | None = None) -> dict:
+    """Random W4A8 model arrays of a Qwen2.5-shaped decoder: int4 g32 weights
+    (codes uniform, fp16 scales U(0.005, 0.02), scales row-major
+    [rows][K/32]), RMSNorm weights U(0.9, 1.1). distinct_layers < n_layers
+    reuses layer l % distinct_layers (the copies are separate arrays)."""
+    H, nh, nkv, hd, I, V = (cfg[k] for k in ("hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab"))
+    nd = distinct_layers or cfg["n_layers"]
+    shapes = {"q": (nh * hd, H), "k": (nkv * hd, H), "v": (nkv * hd, H), "o": (H, nh * hd),
+              "g": (I, H), "u": (I, H), "d": (H, I)}
+    out = {f"{p}{n}": [] for n in shapes for p in ("w", "s")}
+    out["norm_attn"], out["norm_mlp"] = [], []
+    gen = []
+    for l in range(nd):
+        layer = {}
+        for i, (n, (rows, K)) in enumerate(shapes.items()):
+            layer["w" + n] = packed_nibbles(stream_key(seed, 1000 + 40 * l + 2 * i), rows, K)
+            layer["s" + n] = fp16_bits_uniform(stream_key(seed, 1001 + 40 * l + 2 * i), rows * (K // 32),
+                                               0.005, 0.02).reshape(rows, K // 32)
+        layer["norm_attn"] = uniform_f32(stream_key(seed, 1030 + 40 * l), H, 0.9, 1.1)
+        layer["norm_mlp"] = uniform_f32(stream_key(seed, 1031 + 40 * l), H, 0.9, 1.1)
+        gen.append(layer)
+    for l in range(cfg["n_layers"]):
+        src = gen[l % nd]
+        for k, v in src.items():
+            out[k].append(v if l < nd else v.copy())
+    out["norm_final"] = uniform_f32(stream_key(seed, 90), H, 0.9, 1.1)
+    out["wlm"] = packed_nibbles(stream_key(seed, 91), V, H)
+    out["slm"] = fp16_bits_uniform(stream_key(seed, 92), V * (H // 32), 0.005, 0.02).reshape(V, H // 32)
+    return out
+
+
+def kv_prefix(seed: int, cfg: dict, L: int, cap: int):
+    """fp16 K and V caches [layers][kv_heads][cap][hd] whose first L rows are
+    N(0,1) values; rows >= L are zero."""
+    shape = (cfg["n_layers"], cfg["n_kv_heads"], cap, cfg["head_dim"])
+    kc = np.zeros(shape, np.uint16)
+    vc = np.zeros(shape, np.uint16)
+    n = cfg["n_layers"] * cfg["n_kv_heads"] * L * cfg["head_dim"]
+    kc[:, :, :L] = fp16_bits_normal(stream_key(seed, 95), n).reshape(shape[0], shape[1], L, shape[3])
+    vc[:, :, :L] = fp16_bits_normal(stream_key(seed, 96), n).reshape(shape[0], shape[1], L, shape[3])
+    return kc, vc
+
+
+def draft_draws(seed: int, steps: int, width: int = 16) -> np.ndarray:
+    """Per-step, per-node uint32 draws of the synthetic drafter [steps][16]."""
+    return u32(stream_key(seed, 97), steps * width).reshape(steps, width)
