@@ -178,6 +178,73 @@ int kv_compact(uint16_t* k_cache, uint16_t* v_cache, int32_t n_layers, int32_t n
                int32_t capacity, int32_t head_dim, const int32_t* path,
                const specv_ctrl* ctrl, void* stream);
 
+
+/*
+ * A Qwen2.5-shaped decoder in the W4A8 format, for the tree-masked forward
+ * of a verification step ([P1], GPU-Resident Speculation Loop: each step runs
+ * the forward pass over the tree, in which each node attends to the
+ * committed cache and to its ancestors; Small-Batch Verification Kernels:
+ * chunked attention with a merge pass, query heads sharing a KV head read
+ * each key and value once). Host struct of device pointers; per-layer
+ * tensors are stacked along a leading layer axis. With
+ * QKV = (n_heads + 2*n_kv_heads)*head_dim, A = n_heads*head_dim,
+ * H = hidden, I = inter, V = vocab:
+ *   w_qkv  uint8 [layers][QKV][H/2]   q rows, then k rows, then v rows
+ *   s_qkv  uint16 [layers][H/32][QKV] (group-major scales, as w4a8_linear_T)
+ *   w_o    [layers][H][A/2],  s_o    [layers][A/32][H]
+ *   w_gu   [layers][2I][H/2], s_gu   [layers][H/32][2I]  gate rows, then up
+ *   w_down [layers][H][I/2],  s_down [layers][I/32][H]
+ *   norm_attn, norm_mlp  fp32 [layers][H]; norm_final fp32 [H]
+ *   w_lm   [V][H/2], s_lm [H/32][V]; the embedding of a token is its
+ *          dequantised lm_head row (tied weights)
+ *   rope_cos, rope_sin  fp32 [max_pos][head_dim/2] (specv_rope_table)
+ *   k_cache, v_cache    fp16 bits [layers][n_kv_heads][kv_capacity][head_dim]
+ * A step with committed length L and n nodes writes the K/V rows of node i
+ * at row L + i and gives node i the logical position L + depth(i). Scores
+ * are scaled by 1/sqrt(head_dim); attention runs in chunks of 256 logical
+ * positions merged in a second pass; every sum uses the fixed 16-slot order;
+ * exp is a fixed Cody-Waite plus degree-7 polynomial evaluation, so results
+ * are bit-reproducible. Limits: n_heads/n_kv_heads <= 16, head_dim <= 128
+ * and even, 4*(n_heads/n_kv_heads)*(head_dim+256) + 512*head_dim <= 64 KiB,
+ * hidden, inter and n_heads*head_dim multiples of 32, 4*max(hidden, inter)
+ * <= 64 KiB.
+ */
+typedef struct {
+    int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab, max_pos;
+    float eps;          /* RMSNorm epsilon */
+    int32_t kv_capacity;
+    const uint8_t* w_qkv;  const uint16_t* s_qkv;
+    const uint8_t* w_o;    const uint16_t* s_o;
+    const uint8_t* w_gu;   const uint16_t* s_gu;
+    const uint8_t* w_down; const uint16_t* s_down;
+    const float* norm_attn; const float* norm_mlp; const float* norm_final;
+    const uint8_t* w_lm;   const uint16_t* s_lm;
+    const float* rope_cos; const float* rope_sin;
+    uint16_t* k_cache; uint16_t* v_cache;
+} specv_model;
+
+/* Rotary table (host memory): for position p < max_pos and pair i < hd/2,
+ * the angle p * theta^(-2i/hd) evaluated in double, cos and sin rounded to
+ * fp32. Copy the tables to the device for specv_model. */
+int specv_rope_table(float* cos_host, float* sin_host, int32_t max_pos, int32_t head_dim, double theta);
+
+/* Workspace bytes of one step with up to n_max nodes (0 on bad arguments). */
+size_t spec_step_workspace(const specv_model* m, int32_t n_max);
+
+/*
+ * One verification step: the tree-masked forward over ctrl->n_nodes nodes
+ * (parent/token as in tree_argmax_accept), then tree_argmax_accept and
+ * kv_compact, with the same control-state semantics.
+ *   logits  fp32 [n_max][V] out (16-byte aligned); argmax, path int32 [n_max].
+ *   workspace  spec_step_workspace(m, n_max) bytes, 256-byte aligned,
+ *              zero-filled before its first use (as for w4a8_linear_T).
+ * n_max in [1, 16].
+ */
+int spec_tree_step(const specv_model* m, specv_ctrl* ctrl, const int32_t* parent,
+                   const int32_t* token, int32_t n_max, float* logits, int32_t* argmax,
+                   int32_t* path, specv_step_stats* stats, int32_t* ring, int32_t ring_cap,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,8 +10,9 @@ from __future__ import annotations
 import torch
 
 from ._lib import LIB, SpecvError, check
+from .model import DeviceModel
 
-__all__ = ["SpecvError", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
+__all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
            "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace"]
 
 CTRL_FIELDS = ("committed_len", "n_nodes", "ctx_len", "done", "accept_len", "root_token", "step",

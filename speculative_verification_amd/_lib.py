@@ -24,7 +24,20 @@ SIGNATURES = {
     "tree_argmax_accept_workspace": (SZ, [I64, I32]),
     "tree_argmax_accept": (ctypes.c_int, [P, I64, I32, P, P, P, P, P, P, P, I32, P, SZ, P]),
     "kv_compact": (ctypes.c_int, [P, P, I32, I32, I32, I32, P, P, P]),
+    "specv_rope_table": (ctypes.c_int, [P, P, I32, I32, ctypes.c_double]),
+    "spec_step_workspace": (SZ, [P, I32]),
+    "spec_tree_step": (ctypes.c_int, [P, P, P, P, I32, P, P, P, P, P, I32, P, SZ, P]),
 }
+
+
+class SpecvModel(ctypes.Structure):
+    """Mirror of specv_model."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim",
+                                              "inter", "vocab", "max_pos")] + \
+               [("eps", ctypes.c_float), ("kv_capacity", ctypes.c_int32)] + \
+               [(n, ctypes.c_void_p) for n in ("w_qkv", "s_qkv", "w_o", "s_o", "w_gu", "s_gu", "w_down", "s_down",
+                                              "norm_attn", "norm_mlp", "norm_final", "w_lm", "s_lm", "rope_cos",
+                                              "rope_sin", "k_cache", "v_cache")]
 
 
 class SpecvError(RuntimeError):

@@ -15,6 +15,7 @@
 //     commits the step in ctrl, appends the emitted tokens to the ring and
 //     writes the step statistics.
 #include "common.h"
+#include "internal.h"
 
 namespace specv {
 
@@ -77,14 +78,17 @@ __global__ __launch_bounds__(kArgThreads) void argmax_partial_kernel(
 __global__ __launch_bounds__(kArgThreads) void accept_kernel(
     const Best* __restrict__ part, int chunks, int n_max, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ token, int32_t* __restrict__ argmax_out, int32_t* __restrict__ path,
-    specv_ctrl* __restrict__ ctrl, specv_step_stats* __restrict__ stats, int32_t* __restrict__ ring,
-    int ring_cap) {
+    specv_ctrl* __restrict__ ctrl, specv_step_stats* __restrict__ stats_base, int32_t* __restrict__ wcounter,
+    int32_t* __restrict__ ring, int ring_cap) {
     __shared__ int s_amax[kMaxNodes];
     __shared__ int s_acc[kMaxNodes];
     __shared__ int s_depth[kMaxNodes];
     const int done = ctrl->done;
     int n = ctrl->n_nodes;
     n = n < 1 ? 1 : (n > n_max ? n_max : n);
+    // Statistics of a window step go to the record its counter names.
+    specv_step_stats* stats = stats_base ? stats_base + (wcounter ? *wcounter : 0) : nullptr;
+    __syncthreads();
     if (done) {
         if (threadIdx.x == 0) {
             ctrl->accept_len = 0;
@@ -92,6 +96,7 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
                 stats->accepted = -1;
                 stats->width = n;
             }
+            if (wcounter) *wcounter = *wcounter + 1;
         }
         return;
     }
@@ -151,6 +156,7 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
         stats->accepted = m;
         stats->width = n;
     }
+    if (wcounter) *wcounter = *wcounter + 1;
 }
 
 inline int argmax_chunks(int64_t V) { return (int)((V + kArgChunk - 1) / kArgChunk); }
@@ -161,6 +167,25 @@ extern "C" size_t tree_argmax_accept_workspace(int64_t V, int32_t n_max) {
     if (V < 1 || n_max < 1) return 0;
     return (size_t)n_max * (size_t)specv::argmax_chunks(V) * sizeof(specv::Best);
 }
+
+namespace specv {
+
+int enqueue_argmax_accept(const float* logits, int64_t V, int n_max, const int32_t* parent,
+                          const int32_t* token, int32_t* argmax, int32_t* path, specv_ctrl* ctrl,
+                          specv_step_stats* stats, int32_t* wcounter, int32_t* ring, int32_t ring_cap,
+                          void* partials, hipStream_t s) {
+    const int chunks = argmax_chunks(V);
+    Best* part = static_cast<Best*>(partials);
+    hipLaunchKernelGGL(argmax_partial_kernel, dim3(chunks, n_max), dim3(kArgThreads), 0, s, logits, V, ctrl,
+                       part, chunks);
+    const int rc = launch_status();
+    if (rc != SPECV_OK) return rc;
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kArgThreads), 0, s, part, chunks, n_max, parent, token,
+                       argmax, path, ctrl, stats, wcounter, ring, ring_cap);
+    return launch_status();
+}
+
+}  // namespace specv
 
 extern "C" int tree_argmax_accept(const float* logits, int64_t V, int32_t n_max,
                                   const int32_t* parent, const int32_t* token, int32_t* argmax,
@@ -177,14 +202,6 @@ extern "C" int tree_argmax_accept(const float* logits, int64_t V, int32_t n_max,
     const size_t need = tree_argmax_accept_workspace(V, n_max);
     if (!workspace || workspace_bytes < need) return SPECV_E_WORKSPACE;
     if (!aligned(workspace, 4)) return SPECV_E_ALIGN;
-    const int chunks = argmax_chunks(V);
-    hipStream_t s = (hipStream_t)stream;
-    Best* part = static_cast<Best*>(workspace);
-    hipLaunchKernelGGL(argmax_partial_kernel, dim3(chunks, n_max), dim3(kArgThreads), 0, s, logits, V,
-                       ctrl, part, chunks);
-    int rc = launch_status();
-    if (rc != SPECV_OK) return rc;
-    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kArgThreads), 0, s, part, chunks, n_max, parent,
-                       token, argmax, path, ctrl, stats, ring, ring_cap);
-    return launch_status();
+    return enqueue_argmax_accept(logits, V, n_max, parent, token, argmax, path, ctrl, stats, nullptr, ring,
+                                 ring_cap, workspace, (hipStream_t)stream);
 }

@@ -1,0 +1,571 @@
+// Tree-masked forward of one verification step (GPU-Resident Speculative
+// Decoding for In-Browser LLM Inference with WebGPU, Small-Batch
+// Verification Kernels and GPU-Resident Speculation Loop) for a
+// Qwen2.5-shaped decoder in the W4A8 format, plus the step that follows it
+// (argmax, acceptance, compaction).
+//
+// All step kernels read the committed length, the node count and the done
+// flag from the device control block when they run, so one enqueued (or
+// graph-captured) step serves every step of a window.
+//
+// Arithmetic rules shared with every kernel of the library: single IEEE fp32
+// operations in the written order, no contraction; every sum over a vector
+// uses the 16-slot order (slot s takes indices s, s+16, ... in order, then
+// the slots are added as a binary tree in index order). The xor butterfly
+// over 16 lanes used below computes exactly that tree: after level w every
+// aligned block of 2w lanes holds its block sum in every lane.
+#include <cmath>
+#include <cstring>
+
+#include "common.h"
+#include "internal.h"
+
+namespace specv {
+
+// ---------------------------------------------------------------- exp
+
+// Deterministic exp: Cody-Waite reduction x = n*ln2 + r with ln2 split in
+// C1 (9 significant bits, n*C1 exact for |n| <= 128) and C2 = fl(ln2 - C1),
+// a degree-7 Taylor polynomial in r by Horner's rule (separate multiply and
+// add), and 2^n assembled from its exponent bits.
+__device__ __forceinline__ float det_exp(float x) {
+    if (x > 88.0f) return __builtin_inff();
+    if (x < -87.0f) return 0.0f;
+    const float inv_ln2 = 0x1.715476p+0f;
+    const float C1 = 0x1.63p-1f;
+    const float C2 = -0x1.bd0106p-13f;
+    const float n = __builtin_rintf(x * inv_ln2);
+    const float r = (x - n * C1) - n * C2;
+    float p = 0x1.a01a02p-13f;         // 1/7!
+    p = p * r + 0x1.6c16c2p-10f;       // 1/6!
+    p = p * r + 0x1.111112p-7f;        // 1/5!
+    p = p * r + 0x1.555556p-5f;        // 1/4!
+    p = p * r + 0x1.555556p-3f;        // 1/3!
+    p = p * r + 0x1.0p-1f;             // 1/2!
+    p = p * r + 1.0f;                  // 1/1!
+    p = p * r + 1.0f;                  // 1/0!
+    const int ni = (int)n;
+    return p * __builtin_bit_cast(float, (uint32_t)(ni + 127) << 23);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + det_exp(-g)); }
+
+// Sum of one value per lane over 16 aligned lanes, in the tree order.
+__device__ __forceinline__ float tree16(float v) {
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1) v = v + __shfl_xor(v, w, 16);
+    return v;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+}
+
+// Depth of node i in a topologically ordered parent array (a node whose
+// parent breaks the order counts as a root).
+__device__ __forceinline__ int node_depth(const int32_t* parent, int i) {
+    int d = 0;
+    for (int x = i, guard = 0; x > 0 && guard < 64; guard++) {
+        const int p = parent[x];
+        if (p < 0 || p >= x) break;
+        x = p;
+        d++;
+    }
+    return d;
+}
+
+constexpr int kFwdThreads = 256;
+
+// Block-wide max of non-negative values (order-free).
+__device__ __forceinline__ float block_max(float a, float* scratch4) {
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    if ((threadIdx.x & 63) == 0) scratch4[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(scratch4[0], scratch4[1]), fmaxf(scratch4[2], scratch4[3]));
+    __syncthreads();
+    return a;
+}
+
+// Quantise a row held in LDS to per-token int8 (absmax scale, codes rounded
+// to nearest-even, symmetric 127), writing xq[0..K) and *xs.
+__device__ void quantize_row(const float* row, int K, int8_t* xq, float* xs, float* scratch4) {
+    float a = 0.0f;
+    for (int k = threadIdx.x; k < K; k += kFwdThreads) a = fmaxf(a, fabsf(row[k]));
+    a = block_max(a, scratch4);
+    if (a == 0.0f) {
+        if (threadIdx.x == 0) *xs = 0.0f;
+        for (int k = threadIdx.x; k < K; k += kFwdThreads) xq[k] = 0;
+        return;
+    }
+    const float inv = 127.0f / a;
+    if (threadIdx.x == 0) *xs = a / 127.0f;
+    for (int k = threadIdx.x; k < K; k += kFwdThreads) {
+        float r = __builtin_rintf(row[k] * inv);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        xq[k] = (int8_t)(int)r;
+    }
+}
+
+// Rows of nodes past the live count quantise to zero, so the linears that
+// follow produce exact zeros for them.
+__device__ void zero_row(int8_t* xq, float* xs, int K) {
+    if (threadIdx.x == 0) *xs = 0.0f;
+    for (int k = threadIdx.x; k < K; k += kFwdThreads) xq[k] = 0;
+}
+
+// ---------------------------------------------------------------- kernels
+
+// Embedding tied to the lm_head: h[i][k] = f32(scale[k/32][tok]) * code(tok, k)
+// (exact: an 11-bit significand times a 4-bit integer).
+__global__ __launch_bounds__(kFwdThreads) void embed_kernel(const int32_t* __restrict__ token,
+                                                            const uint8_t* __restrict__ wlm,
+                                                            const uint16_t* __restrict__ slm, int H, int V,
+                                                            float* __restrict__ h, const specv_ctrl* ctrl) {
+    const int i = blockIdx.x;
+    if (ctrl->done || i >= ctrl->n_nodes) return;
+    int tok = token[i];
+    tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+    const uint8_t* wr = wlm + (size_t)tok * (H / 2);
+    for (int k = threadIdx.x; k < H; k += kFwdThreads) {
+        const uint8_t b = wr[k >> 1];
+        const int code = ((k & 1) ? (b >> 4) : (b & 15)) - 8;
+        h[(size_t)i * H + k] = f16_to_f32(slm[(size_t)(k >> 5) * V + tok]) * (float)code;
+    }
+}
+
+// Optional residual (h += resid, written back), RMSNorm with weight w, then
+// per-token int8 quantisation. RMSNorm: ss = R16(x*x), ms = ss / H,
+// rs = 1 / sqrt(ms + eps), y = (x * rs) * w.
+__global__ __launch_bounds__(kFwdThreads) void rmsnorm_quant_kernel(float* __restrict__ h,
+                                                                    const float* __restrict__ resid,
+                                                                    const float* __restrict__ w, int H,
+                                                                    float eps, int8_t* __restrict__ xq,
+                                                                    float* __restrict__ xs,
+                                                                    const specv_ctrl* ctrl) {
+    extern __shared__ float row[];  // H floats
+    __shared__ float scratch4[4];
+    __shared__ float s_ss;
+    const int i = blockIdx.x;
+    if (ctrl->done) return;
+    if (i >= ctrl->n_nodes) {
+        zero_row(xq + (size_t)i * H, xs + i, H);
+        return;
+    }
+    float* hr = h + (size_t)i * H;
+    for (int k = threadIdx.x; k < H; k += kFwdThreads) {
+        float v = hr[k];
+        if (resid) {
+            v = v + resid[(size_t)i * H + k];
+            hr[k] = v;
+        }
+        row[k] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        float acc = 0.0f;
+        for (int k = threadIdx.x; k < H; k += 16) acc = acc + row[k] * row[k];
+        acc = tree16(acc);
+        if (threadIdx.x == 0) s_ss = acc;
+    }
+    __syncthreads();
+    const float ms = s_ss / (float)H;
+    const float rs = 1.0f / sqrtf(ms + eps);
+    for (int k = threadIdx.x; k < H; k += kFwdThreads) row[k] = (row[k] * rs) * w[k];
+    __syncthreads();
+    quantize_row(row, H, xq + (size_t)i * H, xs + i, scratch4);
+}
+
+// z = silu(gate) * up over a [n][2I] gate/up output, then quantisation.
+__global__ __launch_bounds__(kFwdThreads) void silu_mul_quant_kernel(const float* __restrict__ gu, int I,
+                                                                     int8_t* __restrict__ xq,
+                                                                     float* __restrict__ xs,
+                                                                     const specv_ctrl* ctrl) {
+    extern __shared__ float row[];  // I floats
+    __shared__ float scratch4[4];
+    const int i = blockIdx.x;
+    if (ctrl->done) return;
+    if (i >= ctrl->n_nodes) {
+        zero_row(xq + (size_t)i * I, xs + i, I);
+        return;
+    }
+    const float* g = gu + (size_t)i * 2 * I;
+    for (int k = threadIdx.x; k < I; k += kFwdThreads) row[k] = silu(g[k]) * g[I + k];
+    __syncthreads();
+    quantize_row(row, I, xq + (size_t)i * I, xs + i, scratch4);
+}
+
+// Rotary positions at L + depth(i) on the q and k heads of node i; k and v
+// go to the fp16 caches at physical row L + i of this layer.
+// Rotate-half: x'_d = x_d c - x_{d+h} s, x'_{d+h} = x_{d+h} c + x_d s.
+__global__ __launch_bounds__(64) void rope_kv_kernel(const float* __restrict__ qkv, const int32_t* __restrict__ parent,
+                                                     const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+                                                     int max_pos, int hd, int nh, int nkv, float* __restrict__ qrot,
+                                                     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int layer,
+                                                     int cap, const specv_ctrl* ctrl) {
+    const int i = blockIdx.x, head = blockIdx.y;
+    if (ctrl->done || i >= ctrl->n_nodes) return;
+    const int L = ctrl->committed_len;
+    const int pos = L + node_depth(parent, i);
+    const int half = hd / 2, d = threadIdx.x;
+    const int QKV = (nh + 2 * nkv) * hd;
+    if (d >= half || pos >= max_pos || L + i >= cap) return;
+    const float c = cos_t[(size_t)pos * half + d], s = sin_t[(size_t)pos * half + d];
+    const float* src = qkv + (size_t)i * QKV + head * hd;
+    const float a = src[d], b = src[d + half];
+    const float ra = a * c - b * s;
+    const float rb = b * c + a * s;
+    if (head < nh) {
+        float* dst = qrot + ((size_t)i * nh + head) * hd;
+        dst[d] = ra;
+        dst[d + half] = rb;
+    } else {
+        const int g = head - nh;
+        const size_t row = (((size_t)layer * nkv + g) * cap + (L + i)) * hd;
+        kc[row + d] = f32_to_f16(ra);
+        kc[row + d + half] = f32_to_f16(rb);
+        const float* vs = qkv + (size_t)i * QKV + (nh + nkv) * hd + g * hd;
+        vc[row + d] = f32_to_f16(vs[d]);
+        vc[row + d + half] = f32_to_f16(vs[d + half]);
+    }
+}
+
+constexpr int kAttnChunk = 256;   // logical positions per chunk
+constexpr int kMaxHeadDim = 128;
+constexpr int kMaxGroup = 16;     // query heads per KV head
+
+inline size_t attn_lds_bytes(int hpg, int hd) {
+    return (size_t)4 * hpg * (hd + kAttnChunk) + (size_t)2 * kAttnChunk * hd;
+}
+
+// One chunk of the visible sequence of one node, for all query heads of one
+// KV head, which therefore read each key and value of the chunk once.
+// Logical position j < L is cache row j; position L + t is the physical row
+// of the node's ancestor at depth t (the node itself last). Per head:
+// s_j = R16_d(q_d * K_jd) * scale, m = max s_j, e_j = E(s_j - m),
+// l = R16_j(e_j), o_d = R16_j(e_j * V_jd), sums over the chunk's positions
+// in logical order. Output per (node, head, chunk): m, l, o[hd].
+__global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
+    const float* __restrict__ qrot, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ parent, int layer, int cap, int nh, int nkv, int hd, float scale,
+    float* __restrict__ part, int nchunk_max, const specv_ctrl* ctrl) {
+    const int c = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+    if (ctrl->done || i >= ctrl->n_nodes) return;
+    const int L = ctrl->committed_len;
+    const int hpg = nh / nkv;
+    __shared__ int anc[64];
+    __shared__ float mh[kMaxGroup];
+    __shared__ float scratch4[4];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float* qs = reinterpret_cast<float*>(smem);                      // [hpg][hd]
+    float* S = qs + hpg * hd;                                        // [hpg][256]
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(S + hpg * kAttnChunk);  // [256][hd]
+
+    if (L + i >= cap) return;  // its rows were not written (no room left)
+    const int depth = node_depth(parent, i);
+    const int len = L + depth + 1;
+    const int j0 = c * kAttnChunk;
+    if (j0 >= len) return;
+    const int cnt = len - j0 < kAttnChunk ? len - j0 : kAttnChunk;
+    if (threadIdx.x == 0) {
+        int x = i;
+        for (int t = depth; t >= 0; t--) {
+            anc[t] = x;
+            const int p = parent[x];
+            x = (p >= 0 && p < x) ? p : 0;
+        }
+    }
+    for (int idx = threadIdx.x; idx < hpg * hd; idx += kFwdThreads)
+        qs[idx] = qrot[((size_t)i * nh + g * hpg) * hd + idx];
+    __syncthreads();
+
+    const size_t plane = (((size_t)layer * nkv + g) * cap) * hd;
+    const int jj = threadIdx.x;
+    if (jj < cnt) {
+        const int j = j0 + jj;
+        const int row = j < L ? j : L + anc[j - L];
+        const uint16_t* kr = kc + plane + (size_t)row * hd;
+        const uint16_t* vr = vc + plane + (size_t)row * hd;
+        for (int d = 0; d < hd; d++) Vs[jj * hd + d] = vr[d];
+        for (int hh = 0; hh < hpg; hh++) {
+            float slot[16];
+#pragma unroll
+            for (int s = 0; s < 16; s++) slot[s] = 0.0f;
+            for (int d0 = 0; d0 < hd; d0 += 16)
+#pragma unroll
+                for (int s = 0; s < 16; s++)
+                    if (d0 + s < hd) slot[s] = slot[s] + qs[hh * hd + d0 + s] * f16_to_f32(kr[d0 + s]);
+#pragma unroll
+            for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+                for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
+            S[hh * kAttnChunk + jj] = slot[0] * scale;
+        }
+    }
+    __syncthreads();
+    for (int hh = 0; hh < hpg; hh++) {
+        // max over the chunk (order-free; only +0/-0 ties can differ, and a
+        // difference against either gives the same exp input up to its sign)
+        float a = jj < cnt ? S[hh * kAttnChunk + jj] : -__builtin_inff();
+        for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+        if ((threadIdx.x & 63) == 0) scratch4[threadIdx.x >> 6] = a;
+        __syncthreads();
+        if (threadIdx.x == 0) mh[hh] = fmaxf(fmaxf(scratch4[0], scratch4[1]), fmaxf(scratch4[2], scratch4[3]));
+        __syncthreads();
+    }
+    if (jj < cnt)
+        for (int hh = 0; hh < hpg; hh++) S[hh * kAttnChunk + jj] = det_exp(S[hh * kAttnChunk + jj] - mh[hh]);
+    __syncthreads();
+
+    float* out = part;  // [n][nh][nchunk_max][hd + 2]
+    const int stride = hd + 2;
+    // l = R16 over the chunk: 16 lanes per head, lane s sums positions s, s+16, ...
+    if (threadIdx.x < hpg * 16) {
+        const int hh = threadIdx.x >> 4, s = threadIdx.x & 15;
+        float acc = 0.0f;
+        for (int p = s; p < cnt; p += 16) acc = acc + S[hh * kAttnChunk + p];
+        acc = tree16(acc);
+        if (s == 0) {
+            float* o = out + (((size_t)i * nh + g * hpg + hh) * nchunk_max + c) * stride;
+            o[0] = mh[hh];
+            o[1] = acc;
+        }
+    }
+    // o_d = R16 over the chunk of e_j * V_jd, one (head, d) per thread
+    for (int idx = threadIdx.x; idx < hpg * hd; idx += kFwdThreads) {
+        const int hh = idx / hd, d = idx % hd;
+        float slot[16];
+#pragma unroll
+        for (int s = 0; s < 16; s++) slot[s] = 0.0f;
+        for (int p0 = 0; p0 < cnt; p0 += 16)
+#pragma unroll
+            for (int s = 0; s < 16; s++)
+                if (p0 + s < cnt) slot[s] = slot[s] + S[hh * kAttnChunk + p0 + s] * f16_to_f32(Vs[(p0 + s) * hd + d]);
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+            for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
+        out[(((size_t)i * nh + g * hpg + hh) * nchunk_max + c) * stride + 2 + d] = slot[0];
+    }
+}
+
+// Merge of the chunks of each head of node i: m = max_c m_c,
+// w_c = E(m_c - m), l = R16_c(w_c * l_c), o_d = R16_c(w_c * o_cd),
+// out_d = o_d / l; then the attention output row [nh*hd] is quantised for
+// the output projection.
+__global__ __launch_bounds__(kFwdThreads) void attn_merge_quant_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ parent, int nh, int hd, int nchunk_max,
+    int8_t* __restrict__ xq, float* __restrict__ xs, const specv_ctrl* ctrl) {
+    extern __shared__ float row[];  // nh*hd floats
+    __shared__ float scratch4[4];
+    const int i = blockIdx.x;
+    const int K = nh * hd;
+    if (ctrl->done) return;
+    if (i >= ctrl->n_nodes) {
+        zero_row(xq + (size_t)i * K, xs + i, K);
+        return;
+    }
+    const int len = ctrl->committed_len + node_depth(parent, i) + 1;
+    const int nch_len = (len + kAttnChunk - 1) / kAttnChunk;
+    const int nch = nch_len < nchunk_max ? nch_len : nchunk_max;
+    const int stride = hd + 2;
+    for (int idx = threadIdx.x; idx < K; idx += kFwdThreads) {
+        const int hh = idx / hd, d = idx % hd;
+        const float* ph = part + ((size_t)i * nh + hh) * nchunk_max * stride;
+        float m = -__builtin_inff();
+        for (int c = 0; c < nch; c++) m = fmaxf(m, ph[(size_t)c * stride]);
+        float sl[16], so[16];
+#pragma unroll
+        for (int s = 0; s < 16; s++) sl[s] = so[s] = 0.0f;
+        for (int c0 = 0; c0 < nch; c0 += 16)
+#pragma unroll
+            for (int s = 0; s < 16; s++)
+                if (c0 + s < nch) {
+                    const float* pc = ph + (size_t)(c0 + s) * stride;
+                    const float wc = det_exp(pc[0] - m);
+                    sl[s] = sl[s] + wc * pc[1];
+                    so[s] = so[s] + wc * pc[2 + d];
+                }
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+            for (int s = 0; s < 16; s += 2 * w) {
+                sl[s] = sl[s] + sl[s + w];
+                so[s] = so[s] + so[s + w];
+            }
+        row[idx] = so[0] / sl[0];
+    }
+    __syncthreads();
+    quantize_row(row, K, xq + (size_t)i * K, xs + i, scratch4);
+}
+
+// ---------------------------------------------------------------- host
+
+static inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+StepLayout step_layout(const specv_model* m, int n) {
+    StepLayout s{};
+    const size_t H = m->hidden, I = m->inter, V = m->vocab;
+    const size_t QKV = (size_t)(m->n_heads + 2 * m->n_kv_heads) * m->head_dim;
+    const size_t A = (size_t)m->n_heads * m->head_dim;
+    const size_t xq_cols = std::max(std::max(H, I), A);
+    const int nch = (m->kv_capacity + kAttnChunk - 1) / kAttnChunk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    s.nchunk_max = nch;
+    s.h = take(4 * n * H);
+    s.delta = take(4 * n * H);
+    s.xq = take(n * xq_cols);
+    s.xs = take(4 * n);
+    s.qkv = take(4 * n * QKV);
+    s.qrot = take(4 * n * A);
+    s.attn = take(4 * (size_t)n * m->n_heads * nch * (m->head_dim + 2));
+    s.gu = take(4 * n * 2 * I);
+    s.logits = take(4 * n * V);
+    s.argmax_part = take(tree_argmax_accept_workspace(V, n));
+    s.tree = take(4 * 16 * 4);  // parent, token, argmax, path for up to 16 nodes
+    s.wcounter = take(4);
+    size_t lin = 0;
+    for (size_t Nk : {QKV, H, 2 * I}) lin = std::max(lin, w4a8_linear_workspace(n, (int)Nk, (int)H));
+    lin = std::max(lin, w4a8_linear_workspace(n, (int)H, (int)A));
+    lin = std::max(lin, w4a8_linear_workspace(n, (int)H, (int)I));
+    lin = std::max(lin, w4a8_linear_workspace(n, (int)V, (int)H));
+    s.linear = take(lin);
+    s.linear_bytes = lin;
+    s.total = off;
+    return s;
+}
+
+int validate_model(const specv_model* m) {
+    if (!m) return SPECV_E_INVAL;
+    if (m->n_layers < 1 || m->hidden < 32 || m->hidden % 32 || m->n_heads < 1 || m->n_kv_heads < 1 ||
+        m->n_heads % m->n_kv_heads || m->n_heads / m->n_kv_heads > kMaxGroup || m->head_dim < 2 ||
+        m->head_dim % 2 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
+        m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || !(m->eps >= 0.0f) ||
+        attn_lds_bytes(m->n_heads / m->n_kv_heads, m->head_dim) > 64 * 1024 ||
+        (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024)
+        return SPECV_E_SHAPE;
+    if (!m->w_qkv || !m->s_qkv || !m->w_o || !m->s_o || !m->w_gu || !m->s_gu || !m->w_down || !m->s_down ||
+        !m->norm_attn || !m->norm_mlp || !m->norm_final || !m->w_lm || !m->s_lm || !m->rope_cos ||
+        !m->rope_sin || !m->k_cache || !m->v_cache)
+        return SPECV_E_INVAL;
+    if (!aligned(m->k_cache, 16) || !aligned(m->v_cache, 16)) return SPECV_E_ALIGN;
+    return SPECV_OK;
+}
+
+#define SPECV_TRY(expr)            \
+    do {                           \
+        const int rc_ = (expr);    \
+        if (rc_ != SPECV_OK) return rc_; \
+    } while (0)
+
+int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const int32_t* token, float* logits,
+                    specv_ctrl* ctrl, char* ws, const StepLayout& lay, hipStream_t s) {
+    const int H = m->hidden, I = m->inter, V = m->vocab, nh = m->n_heads, nkv = m->n_kv_heads, hd = m->head_dim;
+    const int QKV = (nh + 2 * nkv) * hd, A = nh * hd, cap = m->kv_capacity;
+    float* h = reinterpret_cast<float*>(ws + lay.h);
+    float* delta = reinterpret_cast<float*>(ws + lay.delta);
+    int8_t* xq = reinterpret_cast<int8_t*>(ws + lay.xq);
+    float* xs = reinterpret_cast<float*>(ws + lay.xs);
+    float* qkv = reinterpret_cast<float*>(ws + lay.qkv);
+    float* qrot = reinterpret_cast<float*>(ws + lay.qrot);
+    float* attn = reinterpret_cast<float*>(ws + lay.attn);
+    float* gu = reinterpret_cast<float*>(ws + lay.gu);
+    void* lin = lay.linear_bytes ? ws + lay.linear : nullptr;
+    const size_t linb = lay.linear_bytes;
+    const float scale = (float)(1.0 / std::sqrt((double)hd));
+
+    hipLaunchKernelGGL(embed_kernel, dim3(n), dim3(kFwdThreads), 0, s, token, m->w_lm, m->s_lm, H, V, h, ctrl);
+    SPECV_TRY(launch_status());
+    for (int l = 0; l < m->n_layers; l++) {
+        const uint8_t* wqkv = m->w_qkv + (size_t)l * QKV * (H / 2);
+        const uint16_t* sqkv = m->s_qkv + (size_t)l * (H / 32) * QKV;
+        const uint8_t* wo = m->w_o + (size_t)l * H * (A / 2);
+        const uint16_t* so = m->s_o + (size_t)l * (A / 32) * H;
+        const uint8_t* wgu = m->w_gu + (size_t)l * 2 * I * (H / 2);
+        const uint16_t* sgu = m->s_gu + (size_t)l * (H / 32) * 2 * I;
+        const uint8_t* wd = m->w_down + (size_t)l * H * (I / 2);
+        const uint16_t* sd = m->s_down + (size_t)l * (I / 32) * H;
+
+        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kFwdThreads), H * sizeof(float), s, h,
+                           l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, H, m->eps, xq, xs, ctrl);
+        SPECV_TRY(launch_status());
+        SPECV_TRY(w4a8_linear_T(wqkv, sqkv, xq, xs, qkv, n, QKV, H, lin, linb, s));
+        hipLaunchKernelGGL(rope_kv_kernel, dim3(n, nh + nkv), dim3(64), 0, s, qkv, parent, m->rope_cos,
+                           m->rope_sin, m->max_pos, hd, nh, nkv, qrot, m->k_cache, m->v_cache, l, cap, ctrl);
+        SPECV_TRY(launch_status());
+        hipLaunchKernelGGL(attn_chunk_kernel, dim3(lay.nchunk_max, nkv, n), dim3(kFwdThreads),
+                           attn_lds_bytes(nh / nkv, hd), s, qrot,
+                           m->k_cache, m->v_cache, parent, l, cap, nh, nkv, hd, scale, attn, lay.nchunk_max, ctrl);
+        SPECV_TRY(launch_status());
+        hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kFwdThreads), A * sizeof(float), s, attn,
+                           parent, nh, hd, lay.nchunk_max, xq, xs, ctrl);
+        SPECV_TRY(launch_status());
+        SPECV_TRY(w4a8_linear_T(wo, so, xq, xs, delta, n, H, A, lin, linb, s));
+        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kFwdThreads), H * sizeof(float), s, h, delta,
+                           m->norm_mlp + (size_t)l * H, H, m->eps, xq, xs, ctrl);
+        SPECV_TRY(launch_status());
+        SPECV_TRY(w4a8_linear_T(wgu, sgu, xq, xs, gu, n, 2 * I, H, lin, linb, s));
+        hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(n), dim3(kFwdThreads), I * sizeof(float), s, gu, I, xq,
+                           xs, ctrl);
+        SPECV_TRY(launch_status());
+        SPECV_TRY(w4a8_linear_T(wd, sd, xq, xs, delta, n, H, I, lin, linb, s));
+    }
+    hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kFwdThreads), H * sizeof(float), s, h, delta,
+                       m->norm_final, H, m->eps, xq, xs, ctrl);
+    SPECV_TRY(launch_status());
+    return w4a8_linear_T(m->w_lm, m->s_lm, xq, xs, logits, n, V, H, lin, linb, s);
+}
+
+int enqueue_step(const specv_model* m, int n, const int32_t* parent, const int32_t* token, float* logits,
+                 int32_t* argmax, int32_t* path, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* wcounter,
+                 int32_t* ring, int32_t ring_cap, char* ws, const StepLayout& lay, hipStream_t s) {
+    SPECV_TRY(enqueue_forward(m, n, parent, token, logits, ctrl, ws, lay, s));
+    SPECV_TRY(enqueue_argmax_accept(logits, m->vocab, n, parent, token, argmax, path, ctrl, stats, wcounter, ring,
+                                    ring_cap, ws + lay.argmax_part, s));
+    return kv_compact(m->k_cache, m->v_cache, m->n_layers, m->n_kv_heads, m->kv_capacity, m->head_dim, path, ctrl,
+                      s);
+}
+
+}  // namespace specv
+
+extern "C" int specv_rope_table(float* cos_host, float* sin_host, int32_t max_pos, int32_t head_dim,
+                                double theta) {
+    if (!cos_host || !sin_host) return SPECV_E_INVAL;
+    if (max_pos < 1 || head_dim < 2 || head_dim % 2 || !(theta > 0)) return SPECV_E_SHAPE;
+    const int half = head_dim / 2;
+    for (int p = 0; p < max_pos; p++)
+        for (int i = 0; i < half; i++) {
+            const double a = (double)p * std::pow(theta, -2.0 * i / head_dim);
+            cos_host[(size_t)p * half + i] = (float)std::cos(a);
+            sin_host[(size_t)p * half + i] = (float)std::sin(a);
+        }
+    return SPECV_OK;
+}
+
+extern "C" size_t spec_step_workspace(const specv_model* m, int32_t n_max) {
+    using namespace specv;
+    if (validate_model(m) != SPECV_OK || n_max < 1 || n_max > 16) return 0;
+    return step_layout(m, n_max).total;
+}
+
+extern "C" int spec_tree_step(const specv_model* m, specv_ctrl* ctrl, const int32_t* parent,
+                              const int32_t* token, int32_t n_max, float* logits, int32_t* argmax,
+                              int32_t* path, specv_step_stats* stats, int32_t* ring, int32_t ring_cap,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    using namespace specv;
+    SPECV_TRY(validate_model(m));
+    if (n_max < 1 || n_max > 16) return SPECV_E_SHAPE;
+    if (!ctrl || !parent || !token || !logits || !argmax || !path) return SPECV_E_INVAL;
+    if (ring && ring_cap < 1) return SPECV_E_INVAL;
+    if (!aligned(ctrl, 4) || !aligned(parent, 4) || !aligned(token, 4) || !aligned(logits, 16) ||
+        !aligned(argmax, 4) || !aligned(path, 4))
+        return SPECV_E_ALIGN;
+    const StepLayout lay = step_layout(m, n_max);
+    if (!workspace || workspace_bytes < lay.total) return SPECV_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return SPECV_E_ALIGN;
+    return enqueue_step(m, n_max, parent, token, logits, argmax, path, ctrl, stats, nullptr, ring, ring_cap,
+                        static_cast<char*>(workspace), lay, (hipStream_t)stream);
+}

@@ -1,0 +1,103 @@
+"""Device model for the tree-masked verification step.
+
+Packs a decoder given in the interchange layout (per layer: nibbles
+[rows][K/2] and scales [rows][K/32] for q, k, v, o, gate, up, down; norms;
+lm_head) into the library's device layout (layers stacked, q/k/v and
+gate/up rows concatenated, scales group-major), and exposes the step.
+Layout conversion only: all arithmetic runs in libspecv.so.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import LIB, SpecvModel, check
+
+CFG_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab", "max_pos")
+
+
+def _gm(s: np.ndarray) -> np.ndarray:
+    """Scales [rows][K/32] -> group-major [K/32][rows]."""
+    return np.ascontiguousarray(s.T)
+
+
+class DeviceModel:
+    def __init__(self, arrays: dict, cfg: dict, kv_capacity: int, k_cache=None, v_cache=None,
+                 rope_theta: float = 1e6, device="cuda"):
+        self.cfg = dict(cfg)
+        dev = torch.device(device)
+        nl = cfg["n_layers"]
+
+        def stack(fn):
+            return torch.from_numpy(np.ascontiguousarray(np.stack([fn(l) for l in range(nl)]))).to(dev)
+
+        def as_i16(a):
+            return a.view(np.int16)
+
+        self.w_qkv = stack(lambda l: np.concatenate([arrays["wq"][l], arrays["wk"][l], arrays["wv"][l]]))
+        self.s_qkv = stack(lambda l: as_i16(_gm(np.concatenate([arrays["sq"][l], arrays["sk"][l], arrays["sv"][l]]))))
+        self.w_o = stack(lambda l: arrays["wo"][l])
+        self.s_o = stack(lambda l: as_i16(_gm(arrays["so"][l])))
+        self.w_gu = stack(lambda l: np.concatenate([arrays["wg"][l], arrays["wu"][l]]))
+        self.s_gu = stack(lambda l: as_i16(_gm(np.concatenate([arrays["sg"][l], arrays["su"][l]]))))
+        self.w_down = stack(lambda l: arrays["wd"][l])
+        self.s_down = stack(lambda l: as_i16(_gm(arrays["sd"][l])))
+        self.norm_attn = stack(lambda l: arrays["norm_attn"][l])
+        self.norm_mlp = stack(lambda l: arrays["norm_mlp"][l])
+        self.norm_final = torch.from_numpy(arrays["norm_final"]).to(dev)
+        self.w_lm = torch.from_numpy(arrays["wlm"]).to(dev)
+        self.s_lm = torch.from_numpy(as_i16(_gm(arrays["slm"]))).to(dev)
+        half = cfg["head_dim"] // 2
+        c = np.empty((cfg["max_pos"], half), np.float32)
+        s = np.empty((cfg["max_pos"], half), np.float32)
+        check("specv_rope_table", LIB.specv_rope_table(c.ctypes.data, s.ctypes.data, cfg["max_pos"],
+                                                       cfg["head_dim"], rope_theta))
+        self.rope_cos = torch.from_numpy(c).to(dev)
+        self.rope_sin = torch.from_numpy(s).to(dev)
+        shape = (nl, cfg["n_kv_heads"], kv_capacity, cfg["head_dim"])
+        self.k_cache = (torch.from_numpy(k_cache.view(np.int16)).to(dev) if k_cache is not None
+                        else torch.zeros(shape, dtype=torch.int16, device=dev))
+        self.v_cache = (torch.from_numpy(v_cache.view(np.int16)).to(dev) if v_cache is not None
+                        else torch.zeros(shape, dtype=torch.int16, device=dev))
+        assert tuple(self.k_cache.shape) == shape and tuple(self.v_cache.shape) == shape
+        m = SpecvModel()
+        for k in CFG_KEYS:
+            setattr(m, k, int(cfg[k]))
+        m.eps = float(cfg["eps"])
+        m.kv_capacity = kv_capacity
+        for k in ("w_qkv", "s_qkv", "w_o", "s_o", "w_gu", "s_gu", "w_down", "s_down", "norm_attn", "norm_mlp",
+                  "norm_final", "w_lm", "s_lm", "rope_cos", "rope_sin", "k_cache", "v_cache"):
+            setattr(m, k, getattr(self, k).data_ptr())
+        self.c = m
+        self._ws = {}
+
+    def ptr(self):
+        return ctypes.addressof(self.c)
+
+    def workspace(self, n_max: int) -> torch.Tensor:
+        need = int(LIB.spec_step_workspace(self.ptr(), n_max))
+        if need == 0:
+            raise ValueError("model or n_max rejected by spec_step_workspace")
+        ws = self._ws.get(n_max)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(need, dtype=torch.uint8, device=self.k_cache.device)
+            self._ws[n_max] = ws
+        return ws
+
+    def tree_step(self, ctrl: torch.Tensor, parent: torch.Tensor, token: torch.Tensor, n_max: int,
+                  logits: torch.Tensor | None = None, stats: torch.Tensor | None = None,
+                  ring: torch.Tensor | None = None):
+        dev = self.k_cache.device
+        V = self.cfg["vocab"]
+        logits = torch.empty((n_max, V), dtype=torch.float32, device=dev) if logits is None else logits
+        argmax = torch.empty(n_max, dtype=torch.int32, device=dev)
+        path = torch.zeros(n_max, dtype=torch.int32, device=dev)
+        ws = self.workspace(n_max)
+        check("spec_tree_step", LIB.spec_tree_step(
+            self.ptr(), ctrl.data_ptr(), parent.data_ptr(), token.data_ptr(), n_max, logits.data_ptr(),
+            argmax.data_ptr(), path.data_ptr(), stats.data_ptr() if stats is not None else None,
+            ring.data_ptr() if ring is not None else None, ring.numel() if ring is not None else 0,
+            ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
+        return logits, argmax, path

@@ -39,12 +39,15 @@ def test_every_declared_symbol_is_exported(lib):
 def test_struct_sizes(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text('#include "specv.h"\n#include <stdio.h>\n#include <stddef.h>\n'
-                   'int main(void){printf("%zu %zu %zu\\n", sizeof(specv_ctrl), sizeof(specv_step_stats),'
-                   ' offsetof(specv_ctrl, ring_head)); return 0;}\n')
+                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(specv_ctrl), sizeof(specv_step_stats),'
+                   ' offsetof(specv_ctrl, ring_head), sizeof(specv_model), offsetof(specv_model, w_qkv));'
+                   ' return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
-    assert out == ["32", "12", "28"]
+    import ctypes
+    from speculative_verification_amd._lib import SpecvModel
+    assert out == ["32", "12", "28", str(ctypes.sizeof(SpecvModel)), str(SpecvModel.w_qkv.offset)]
 
 
 def test_status_strings(lib):
@@ -109,3 +112,25 @@ def test_compact_rejects_bad_arguments(lib):
     assert f(A, A, 0, 2, 1040, 64, A, A, None) == E_SHAPE
     assert f(A, None, 24, 2, 1040, 64, A, A, None) == E_INVAL
     assert f(A + 8, A, 24, 2, 1040, 64, A, A, None) == E_ALIGN
+
+
+def test_rope_table_matches_oracle(lib, orc):
+    """The library's host rotary table and the oracle's are written
+    separately; both evaluate the angle in double with libm, so they agree
+    bit for bit."""
+    import numpy as np
+    c = np.empty((700, 32), np.float32)
+    s_ = np.empty((700, 32), np.float32)
+    assert lib.specv_rope_table(c.ctypes.data, s_.ctypes.data, 700, 64, 1e6) == OK
+    oc, os_ = orc.rope_table(700, 64, 1e6)
+    assert np.array_equal(c, oc) and np.array_equal(s_, os_)
+    assert lib.specv_rope_table(c.ctypes.data, s_.ctypes.data, 700, 63, 1e6) == E_SHAPE
+
+
+def test_step_rejects_bad_model(lib):
+    from speculative_verification_amd._lib import SpecvModel
+    import ctypes
+    m = SpecvModel()
+    assert lib.spec_step_workspace(ctypes.addressof(m), 8) == 0          # all sizes zero
+    assert lib.spec_tree_step(ctypes.addressof(m), A, A, A, 8, A, A, A, None, None, 0, A, 1 << 30, None) == E_SHAPE
+    assert lib.spec_tree_step(None, A, A, A, 8, A, A, A, None, None, 0, A, 1 << 30, None) == E_INVAL

@@ -1,0 +1,181 @@
+"""GPU parity of the tree-masked verification step (spec_tree_step) against
+the CPU oracle, bit for bit: logits, greedy predictions, accepted path,
+control state and the whole fp16 KV caches after compaction. Also the
+property that a tree step reproduces single-token steps along every node's
+path, on the GPU itself at full size (24-layer Qwen2.5-0.5B shape, 1024
+committed rows, 8-node tree)."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthgen as sg
+
+pytestmark = pytest.mark.gpu
+
+
+def case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_verification_amd as m
+    return m
+
+
+@functools.lru_cache(maxsize=2)
+def model_pair(name):
+    cfg = sg.TINY if name == "tiny" else sg.QWEN05
+    arrays = sg.model_case(7 if name == "tiny" else 3, cfg)
+    c, s = oracle.rope_table(cfg["max_pos"], cfg["head_dim"], 1e6)
+    arrays = dict(arrays, rope_cos=c, rope_sin=s)
+    return cfg, arrays, oracle.Model(arrays, cfg)
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+
+
+def planted_tree(seed, N, L, cfg, orc_model, kc, vc):
+    """Random tree; drafts along the deepest chain follow the oracle's greedy
+    continuation so acceptance and compaction are exercised."""
+    parent = sg.random_tree_parents(sg.stream_key(seed, sg.TID_PARENT), N)
+    token = sg.tokens(sg.stream_key(seed, sg.TID_TOKEN), N, cfg["vocab"])
+    if N > 1:
+        depth = np.zeros(N, np.int32)
+        for i in range(1, N):
+            depth[i] = depth[parent[i]] + 1
+        w = int(np.argmax(depth))
+        chain = [w]
+        while chain[-1] != 0:
+            chain.append(int(parent[chain[-1]]))
+        chain.reverse()
+        ks, vs = kc.copy(), vc.copy()
+        for d, node in enumerate(chain[:-1]):
+            lg = oracle.forward(orc_model, ks, vs, L + d, np.array([-1], np.int32),
+                                np.array([token[node]], np.int32))
+            token[chain[d + 1]] = int(np.argmax(lg[0]))
+    return parent, token
+
+
+def compare_step(sv, name, seed, N, L, plant=True):
+    cfg, arrays, om = model_pair(name)
+    cap = L + N + 8
+    kc0, vc0 = sg.kv_prefix(seed, cfg, L, cap)
+    if plant:
+        parent, token = planted_tree(seed, N, L, cfg, om, kc0, vc0)
+    else:
+        parent = sg.random_tree_parents(sg.stream_key(seed, sg.TID_PARENT), N)
+        token = sg.tokens(sg.stream_key(seed, sg.TID_TOKEN), N, cfg["vocab"])
+    kc, vc = kc0.copy(), vc0.copy()
+    ro = oracle.tree_step(om, kc, vc, L, parent, token, want_logits=True)
+
+    dm = sv.DeviceModel(arrays, cfg, cap, kc0, vc0)
+    ctrl = sv.new_ctrl(L, N, cap - N, root_token=int(token[0]))
+    stats = torch.zeros(3, dtype=torch.int32, device="cuda")
+    logits, amax, path = dm.tree_step(ctrl, dev_i32(parent), dev_i32(token), N, stats=stats)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    bad = np.nonzero(lg.view(np.uint32) != ro["logits"].view(np.uint32))
+    assert bad[0].size == 0, f"{bad[0].size} logits differ, first {bad[0][0]},{bad[1][0]}: " \
+                             f"{lg[bad[0][0], bad[1][0]]} vs {ro['logits'][bad[0][0], bad[1][0]]}"
+    assert np.array_equal(amax.cpu().numpy(), ro["amax"])
+    m = ro["m"]
+    assert np.array_equal(path.cpu().numpy()[: m + 1], ro["path"])
+    c = ctrl.cpu().numpy()
+    assert (c[0], c[4], c[5], c[6]) == (ro["L"], m, ro["bonus"], 1)
+    assert np.array_equal(dm.k_cache.cpu().numpy().view(np.uint16), kc)
+    assert np.array_equal(dm.v_cache.cpu().numpy().view(np.uint16), vc)
+    return m
+
+
+@pytest.mark.parametrize("seed,N,L", [(1, 8, 300), (2, 6, 40), (3, 16, 511), (4, 1, 256), (5, 5, 0),
+                                      (6, 3, 1), (8, 16, 600), (9, 2, 255)])
+def test_tiny_tree_step_parity(sv, seed, N, L):
+    case(f"tiny tree step seed={seed} N={N} L={L}")
+    compare_step(sv, "tiny", seed, N, L)
+
+
+def test_tiny_unplanted_tree(sv):
+    case("tiny tree step, random drafts")
+    compare_step(sv, "tiny", 12, 8, 130, plant=False)
+
+
+def test_qwen05_tree_step_parity(sv):
+    """Full 8-node tree verification on the 24-layer Qwen2.5-0.5B shape over
+    a 1024-row fp16 cache, against the oracle."""
+    case("qwen0.5b tree step N=8 L=1024")
+    m = compare_step(sv, "qwen", 21, 8, 1024)
+    assert m >= 1
+
+
+def test_qwen05_tree_equals_sequential_on_gpu(sv):
+    """On the GPU alone: each node's logits and K/V equal those of the
+    single-token steps along its root path."""
+    case("qwen0.5b tree vs sequential on gpu")
+    cfg, arrays, _ = model_pair("qwen")
+    L, N = 1024, 8
+    cap = L + N + 8
+    kc0, vc0 = sg.kv_prefix(22, cfg, L, cap)
+    parent = sg.random_tree_parents(sg.stream_key(22, sg.TID_PARENT), N)
+    token = sg.tokens(sg.stream_key(22, sg.TID_TOKEN), N, cfg["vocab"])
+    dm = sv.DeviceModel(arrays, cfg, cap, kc0, vc0)
+    ctrl = sv.new_ctrl(L, N, 10 ** 6)
+    ctrl[3] = 0
+    # forward only: compare logits of every node before acceptance moves rows
+    tree_logits, _, _ = dm.tree_step(ctrl, dev_i32(parent), dev_i32(token), N)
+    tree_logits = tree_logits.cpu().numpy()
+    for i in range(N):
+        chain = [i]
+        while chain[-1] != 0:
+            chain.append(int(parent[chain[-1]]))
+        chain.reverse()
+        ds = sv.DeviceModel(arrays, cfg, cap, kc0, vc0) if i == 0 else ds_reset(ds, kc0, vc0)
+        for d, node in enumerate(chain):
+            c1 = sv.new_ctrl(L + d, 1, 10 ** 6)
+            lg, _, _ = ds.tree_step(c1, dev_i32([-1]), dev_i32([token[node]]), 1)
+        torch.cuda.synchronize()
+        assert lg.cpu().numpy()[0].tobytes() == tree_logits[i].tobytes(), f"node {i}"
+
+
+def ds_reset(ds, kc0, vc0):
+    ds.k_cache.copy_(torch.from_numpy(kc0.view(np.int16)))
+    ds.v_cache.copy_(torch.from_numpy(vc0.view(np.int16)))
+    return ds
+
+
+def test_step_is_run_to_run_identical(sv):
+    case("tiny step determinism")
+    cfg, arrays, _ = model_pair("tiny")
+    L, N, cap = 400, 16, 430
+    kc0, vc0 = sg.kv_prefix(31, cfg, L, cap)
+    parent = sg.random_tree_parents(sg.stream_key(31, sg.TID_PARENT), N)
+    token = sg.tokens(sg.stream_key(31, sg.TID_TOKEN), N, cfg["vocab"])
+    outs = []
+    for _ in range(2):
+        dm = sv.DeviceModel(arrays, cfg, cap, kc0, vc0)
+        ctrl = sv.new_ctrl(L, N, cap - N)
+        lg, _, _ = dm.tree_step(ctrl, dev_i32(parent), dev_i32(token), N)
+        outs.append((lg.cpu().numpy().tobytes(), dm.k_cache.cpu().numpy().tobytes(), ctrl.cpu().numpy().tobytes()))
+    assert outs[0] == outs[1]
+
+
+def test_done_step_leaves_state(sv):
+    case("tiny step with done set")
+    cfg, arrays, _ = model_pair("tiny")
+    L, N, cap = 60, 4, 80
+    kc0, vc0 = sg.kv_prefix(32, cfg, L, cap)
+    dm = sv.DeviceModel(arrays, cfg, cap, kc0, vc0)
+    ctrl = sv.new_ctrl(L, N, cap - N)
+    ctrl[3] = 1
+    before = ctrl.cpu().numpy().copy()
+    dm.tree_step(ctrl, dev_i32([-1, 0, 1, 1]), dev_i32([1, 2, 3, 4]), N)
+    torch.cuda.synchronize()
+    before[4] = 0
+    assert list(ctrl.cpu().numpy()) == list(before)
+    assert np.array_equal(dm.k_cache.cpu().numpy().view(np.uint16), kc0)
+    assert np.array_equal(dm.v_cache.cpu().numpy().view(np.uint16), vc0)
