@@ -245,6 +245,63 @@ int spec_tree_step(const specv_model* m, specv_ctrl* ctrl, const int32_t* parent
                    int32_t* path, specv_step_stats* stats, int32_t* ring, int32_t ring_cap,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Synthetic drafter of the speculation window (stand-in for the drafter of
+ * [P1], Context-Mixing Drafter, which proposes candidates of up to 8 tokens).
+ * With L = ctrl->committed_len, d = draws[ctrl->step % draw_rows] (16 words)
+ * and D = min(width - 1, 8), the tree of a step is: node 0 the root
+ * (ctrl->root_token); nodes 1..D a chain, node k with parent k-1 and token
+ * reference[L + k] when d[k] < accept_threshold, else
+ * (reference[L + k] + 1 + d[k] % (V - 1)) % V, and d[k] % V once
+ * L + k >= reference_len; nodes e in (D, width) get parent (e - D - 1) % D
+ * and token d[e] % V. The best-match statistic of the step is D.
+ *   reference  int32 [reference_len] device; draws uint32 [draw_rows][16]
+ *              device. Both are read while the window runs.
+ * 32 bytes; `reserved` is ignored.
+ */
+typedef struct {
+    const int32_t* reference;
+    int32_t reference_len;
+    int32_t draw_rows;
+    const uint32_t* draws;
+    uint32_t accept_threshold;
+    int32_t reserved;
+} specv_drafter;
+
+/* Workspace bytes of a window of the given width (as spec_step_workspace). */
+size_t spec_window_workspace(const specv_model* m, int32_t width);
+
+/*
+ * Device-resident speculation window ([P1], GPU-Resident Speculation Loop:
+ * draft, tree verification, acceptance and compaction run for W steps with
+ * no host synchronisation; the host reads the control block and per-step
+ * statistics once per window). Each of the W steps drafts a tree of `width`
+ * nodes (sets ctrl->n_nodes = width), then runs spec_tree_step's forward,
+ * acceptance and compaction. A step that finds done set does nothing but
+ * write accept_len = 0 and the record {-1, 0, n_nodes}.
+ *   ctrl       device control block (n_nodes is overwritten per step).
+ *   stats      specv_step_stats [W] device: record s for step s of the window.
+ *   ring       nullable int32 [ring_cap]: the emitted tokens, as in
+ *              tree_argmax_accept.
+ *   d          drafter; may be NULL only when width == 1 (root-only steps).
+ *   width      nodes per step, in [1, 16]; W in [0, 4096], 0 enqueues nothing.
+ *   workspace  spec_window_workspace(m, width) bytes, 256-byte aligned,
+ *              zero-filled before its first use; it holds the step's tree
+ *              and logits, and the window's step counter.
+ *   host_readback  nullable host buffer of 32 + 12*W bytes, best pinned
+ *              (hipHostMalloc): after the window, ctrl then stats[0..W) are
+ *              copied there on `stream`; synchronise before reading.
+ * One step's launches are captured once into a HIP graph (on a stream the
+ * library creates) and replayed W times on `stream`; the executable graph is
+ * kept for the process, keyed by every argument except W and
+ * host_readback (at most 32 kept; the oldest key is released first).
+ * Windows that share a workspace, control block or cache must not overlap.
+ */
+int spec_window_run(const specv_model* m, specv_ctrl* ctrl, specv_step_stats* stats,
+                    int32_t* ring, int32_t ring_cap, const specv_drafter* d, int32_t width,
+                    int32_t W, void* workspace, size_t workspace_bytes, void* host_readback,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

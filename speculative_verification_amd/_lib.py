@@ -27,6 +27,8 @@ SIGNATURES = {
     "specv_rope_table": (ctypes.c_int, [P, P, I32, I32, ctypes.c_double]),
     "spec_step_workspace": (SZ, [P, I32]),
     "spec_tree_step": (ctypes.c_int, [P, P, P, P, I32, P, P, P, P, P, I32, P, SZ, P]),
+    "spec_window_workspace": (SZ, [P, I32]),
+    "spec_window_run": (ctypes.c_int, [P, P, P, P, I32, P, I32, I32, P, SZ, P, P]),
 }
 
 
@@ -38,6 +40,12 @@ class SpecvModel(ctypes.Structure):
                [(n, ctypes.c_void_p) for n in ("w_qkv", "s_qkv", "w_o", "s_o", "w_gu", "s_gu", "w_down", "s_down",
                                               "norm_attn", "norm_mlp", "norm_final", "w_lm", "s_lm", "rope_cos",
                                               "rope_sin", "k_cache", "v_cache")]
+
+
+class SpecvDrafter(ctypes.Structure):
+    """Mirror of specv_drafter."""
+    _fields_ = [("reference", ctypes.c_void_p), ("reference_len", ctypes.c_int32), ("draw_rows", ctypes.c_int32),
+                ("draws", ctypes.c_void_p), ("accept_threshold", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
 
 
 class SpecvError(RuntimeError):

@@ -1,0 +1,211 @@
+// Device-resident speculation window (GPU-Resident Speculative Decoding for
+// In-Browser LLM Inference with WebGPU, GPU-Resident Speculation Loop):
+// W steps of draft -> tree-masked forward -> acceptance -> compaction run
+// back to back with no host decision in between, because every kernel reads
+// its dynamic state (committed length, node count, root token, step, done)
+// from the device control block. The window ends with one copy of the
+// 32-byte control block and 12 bytes of statistics per step to the host.
+//
+// One step is captured once into a HIP graph (its launches never change;
+// only the control block does) and replayed W times on the caller's stream.
+#include <cstring>
+#include <map>
+#include <mutex>
+
+#include "common.h"
+#include "internal.h"
+
+namespace specv {
+
+// Synthetic drafter standing in for the context-mixing drafter (the pages'
+// drafter extends a candidate by at most 8 tokens): node 0 is the root with
+// the last step's bonus token; nodes 1..D (D = min(width-1, 8)) form a chain;
+// chain node k copies the reference token at position L+k when its draw is
+// below the threshold and otherwise takes a different token; the remaining
+// nodes attach round-robin to nodes 0..D-1 with tokens draw mod vocab.
+__global__ void draft_kernel(specv_ctrl* ctrl, int width, const int32_t* __restrict__ ref, int ref_len,
+                             const uint32_t* __restrict__ draws, int draw_rows, uint32_t threshold, int vocab,
+                             int32_t* __restrict__ parent, int32_t* __restrict__ token,
+                             specv_step_stats* __restrict__ stats, const int32_t* __restrict__ wcounter) {
+    if (threadIdx.x != 0) return;
+    if (ctrl->done) {
+        if (stats) stats[*wcounter].best_match = 0;
+        return;
+    }
+    const int L = ctrl->committed_len;
+    const int D = width - 1 < 8 ? width - 1 : 8;
+    const uint32_t* dr = draws + (size_t)((uint32_t)ctrl->step % (uint32_t)draw_rows) * 16;
+    parent[0] = -1;
+    token[0] = ctrl->root_token;
+    for (int k = 1; k <= D; k++) {
+        parent[k] = k - 1;
+        const uint32_t d = dr[k];
+        if (L + k < ref_len) {
+            const int32_t r = ref[L + k];
+            token[k] = d < threshold ? r
+                                     : (int32_t)(((uint32_t)r + 1u + d % (uint32_t)(vocab - 1)) % (uint32_t)vocab);
+        } else {
+            token[k] = (int32_t)(d % (uint32_t)vocab);
+        }
+    }
+    for (int e = D + 1; e < width; e++) {
+        parent[e] = (e - D - 1) % D;
+        token[e] = (int32_t)(dr[e] % (uint32_t)vocab);
+    }
+    ctrl->n_nodes = width;
+    if (stats) stats[*wcounter].best_match = D;
+}
+
+// Width-1 steps need no draft: the tree is the root alone.
+__global__ void root_only_kernel(specv_ctrl* ctrl, int32_t* __restrict__ parent, int32_t* __restrict__ token,
+                                 specv_step_stats* __restrict__ stats, const int32_t* __restrict__ wcounter) {
+    if (threadIdx.x != 0) return;
+    if (ctrl->done) {
+        if (stats) stats[*wcounter].best_match = 0;
+        return;
+    }
+    parent[0] = -1;
+    token[0] = ctrl->root_token;
+    ctrl->n_nodes = 1;
+    if (stats) stats[*wcounter].best_match = 0;
+}
+
+__global__ void window_begin_kernel(int32_t* wcounter) {
+    if (threadIdx.x == 0) *wcounter = 0;
+}
+
+struct WindowKey {
+    specv_model model;
+    specv_ctrl* ctrl;
+    specv_step_stats* stats;
+    int32_t* ring;
+    int32_t ring_cap;
+    int32_t width;
+    specv_drafter drafter;
+    int32_t has_drafter;
+    void* workspace;
+    bool operator<(const WindowKey& o) const { return std::memcmp(this, &o, sizeof(WindowKey)) < 0; }
+};
+
+struct GraphCache {
+    std::mutex mu;
+    std::map<WindowKey, hipGraphExec_t> execs;
+    hipStream_t capture_stream = nullptr;
+};
+
+static GraphCache& graph_cache() {
+    static GraphCache* c = new GraphCache();  // lives for the process
+    return *c;
+}
+
+static int enqueue_window_step(const WindowKey& k, const StepLayout& lay, hipStream_t s) {
+    char* ws = static_cast<char*>(k.workspace);
+    int32_t* tree = reinterpret_cast<int32_t*>(ws + lay.tree);
+    int32_t *parent = tree, *token = tree + 16, *argmax = tree + 32, *path = tree + 48;
+    int32_t* wcounter = reinterpret_cast<int32_t*>(ws + lay.wcounter);
+    float* logits = reinterpret_cast<float*>(ws + lay.logits);
+    if (k.has_drafter)
+        hipLaunchKernelGGL(draft_kernel, dim3(1), dim3(64), 0, s, k.ctrl, k.width, k.drafter.reference,
+                           k.drafter.reference_len, k.drafter.draws, k.drafter.draw_rows,
+                           k.drafter.accept_threshold, k.model.vocab, parent, token, k.stats, wcounter);
+    else
+        hipLaunchKernelGGL(root_only_kernel, dim3(1), dim3(64), 0, s, k.ctrl, parent, token, k.stats, wcounter);
+    const int rc = launch_status();
+    if (rc != SPECV_OK) return rc;
+    return enqueue_step(&k.model, k.width, parent, token, logits, argmax, path, k.ctrl, k.stats, wcounter, k.ring,
+                        k.ring_cap, ws, lay, s);
+}
+
+// Capture one window step into an executable graph (cached by arguments).
+static int window_graph(const WindowKey& k, const StepLayout& lay, hipGraphExec_t* out) {
+    GraphCache& gc = graph_cache();
+    std::lock_guard<std::mutex> lock(gc.mu);
+    auto it = gc.execs.find(k);
+    if (it != gc.execs.end()) {
+        *out = it->second;
+        return SPECV_OK;
+    }
+    if (!gc.capture_stream && hipStreamCreateWithFlags(&gc.capture_stream, hipStreamNonBlocking) != hipSuccess)
+        return SPECV_E_HIP;
+    // Relaxed capture: kernel attributes set while enqueueing (dynamic LDS
+    // limits) are not stream work and may be changed during capture.
+    if (hipStreamBeginCapture(gc.capture_stream, hipStreamCaptureModeRelaxed) != hipSuccess) return SPECV_E_HIP;
+    const int rc = enqueue_window_step(k, lay, gc.capture_stream);
+    hipGraph_t g = nullptr;
+    const bool ended = hipStreamEndCapture(gc.capture_stream, &g) == hipSuccess;
+    if (rc != SPECV_OK || !ended) {
+        if (g) (void)hipGraphDestroy(g);
+        (void)hipGetLastError();
+        return rc != SPECV_OK ? rc : SPECV_E_HIP;
+    }
+    hipGraphExec_t exec = nullptr;
+    const bool inst = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) == hipSuccess;
+    (void)hipGraphDestroy(g);
+    if (!inst) return SPECV_E_HIP;
+    if (gc.execs.size() >= 32) {  // bounded cache
+        (void)hipGraphExecDestroy(gc.execs.begin()->second);
+        gc.execs.erase(gc.execs.begin());
+    }
+    gc.execs.emplace(k, exec);
+    *out = exec;
+    return SPECV_OK;
+}
+
+}  // namespace specv
+
+extern "C" size_t spec_window_workspace(const specv_model* m, int32_t width) {
+    return spec_step_workspace(m, width);
+}
+
+extern "C" int spec_window_run(const specv_model* m, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* ring,
+                               int32_t ring_cap, const specv_drafter* d, int32_t width, int32_t W,
+                               void* workspace, size_t workspace_bytes, void* host_readback, void* stream) {
+    using namespace specv;
+    const int vrc = validate_model(m);
+    if (vrc != SPECV_OK) return vrc;
+    if (width < 1 || width > 16 || W < 0 || W > 4096) return SPECV_E_SHAPE;
+    if (width > 1 && m->vocab < 2) return SPECV_E_SHAPE;  // the drafter reduces modulo V - 1
+    if (!ctrl || !stats) return SPECV_E_INVAL;
+    if (ring && ring_cap < 1) return SPECV_E_INVAL;
+    if (width > 1 && (!d || !d->reference || d->reference_len < 1 || !d->draws || d->draw_rows < 1))
+        return SPECV_E_INVAL;
+    if (!aligned(ctrl, 4) || !aligned(stats, 4) || !aligned(ring, 4)) return SPECV_E_ALIGN;
+    const StepLayout lay = step_layout(m, width);
+    if (!workspace || workspace_bytes < lay.total) return SPECV_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return SPECV_E_ALIGN;
+    if (W == 0) return SPECV_OK;
+
+    WindowKey k;
+    std::memset(&k, 0, sizeof(k));
+    k.model = *m;
+    k.ctrl = ctrl;
+    k.stats = stats;
+    k.ring = ring;
+    k.ring_cap = ring ? ring_cap : 0;
+    k.width = width;
+    k.has_drafter = width > 1;
+    if (k.has_drafter) {
+        k.drafter = *d;
+        k.drafter.reserved = 0;
+    }
+    k.workspace = workspace;
+
+    hipGraphExec_t exec = nullptr;
+    int rc = window_graph(k, lay, &exec);
+    if (rc != SPECV_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* wcounter = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.wcounter);
+    hipLaunchKernelGGL(window_begin_kernel, dim3(1), dim3(64), 0, s, wcounter);
+    rc = launch_status();
+    if (rc != SPECV_OK) return rc;
+    for (int i = 0; i < W; i++)
+        if (hipGraphLaunch(exec, s) != hipSuccess) return SPECV_E_HIP;
+    if (host_readback) {
+        char* hb = static_cast<char*>(host_readback);
+        if (hipMemcpyAsync(hb, ctrl, sizeof(specv_ctrl), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipMemcpyAsync(hb + sizeof(specv_ctrl), stats, sizeof(specv_step_stats) * (size_t)W,
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            return SPECV_E_HIP;
+    }
+    return SPECV_OK;
+}

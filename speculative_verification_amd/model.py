@@ -13,7 +13,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import LIB, SpecvModel, check
+from ._lib import LIB, SpecvDrafter, SpecvModel, check
 
 CFG_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab", "max_pos")
 
@@ -101,3 +101,26 @@ class DeviceModel:
             ring.data_ptr() if ring is not None else None, ring.numel() if ring is not None else 0,
             ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
         return logits, argmax, path
+
+    def window(self, ctrl: torch.Tensor, stats: torch.Tensor, width: int, W: int,
+               reference: torch.Tensor | None = None, draws: torch.Tensor | None = None, threshold: int = 0,
+               ring: torch.Tensor | None = None, readback: torch.Tensor | None = None):
+        """W device-resident speculation steps (spec_window_run). `reference`
+        int32 and `draws` uint32-as-int32 [rows][16] feed the synthetic
+        drafter (not needed for width 1); `stats` is int32 [>= W][3];
+        `readback`, if given, is a pinned uint8 host tensor of >= 32 + 12*W
+        bytes that receives ctrl and stats[0..W) on the current stream."""
+        d = None
+        if reference is not None:
+            assert reference.dtype == torch.int32 and draws.dtype == torch.int32 and draws.shape[-1] == 16
+            d = SpecvDrafter(reference.data_ptr(), reference.numel(), draws.shape[0], draws.data_ptr(),
+                             int(threshold) & 0xFFFFFFFF, 0)
+        assert stats.dtype == torch.int32 and stats.numel() >= 3 * W
+        if readback is not None:
+            assert readback.device.type == "cpu" and readback.numel() * readback.element_size() >= 32 + 12 * W
+        ws = self.workspace(width)
+        check("spec_window_run", LIB.spec_window_run(
+            self.ptr(), ctrl.data_ptr(), stats.data_ptr(), ring.data_ptr() if ring is not None else None,
+            ring.numel() if ring is not None else 0, ctypes.byref(d) if d is not None else None, width, W,
+            ws.data_ptr(), ws.numel(), readback.data_ptr() if readback is not None else None,
+            torch.cuda.current_stream().cuda_stream))

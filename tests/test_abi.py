@@ -39,15 +39,17 @@ def test_every_declared_symbol_is_exported(lib):
 def test_struct_sizes(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text('#include "specv.h"\n#include <stdio.h>\n#include <stddef.h>\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(specv_ctrl), sizeof(specv_step_stats),'
-                   ' offsetof(specv_ctrl, ring_head), sizeof(specv_model), offsetof(specv_model, w_qkv));'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(specv_ctrl), sizeof(specv_step_stats),'
+                   ' offsetof(specv_ctrl, ring_head), sizeof(specv_model), offsetof(specv_model, w_qkv),'
+                   ' sizeof(specv_drafter), offsetof(specv_drafter, draws), offsetof(specv_drafter, accept_threshold));'
                    ' return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
     import ctypes
-    from speculative_verification_amd._lib import SpecvModel
-    assert out == ["32", "12", "28", str(ctypes.sizeof(SpecvModel)), str(SpecvModel.w_qkv.offset)]
+    from speculative_verification_amd._lib import SpecvDrafter, SpecvModel
+    assert out == ["32", "12", "28", str(ctypes.sizeof(SpecvModel)), str(SpecvModel.w_qkv.offset),
+                   "32", str(SpecvDrafter.draws.offset), str(SpecvDrafter.accept_threshold.offset)]
 
 
 def test_status_strings(lib):
@@ -134,3 +136,53 @@ def test_step_rejects_bad_model(lib):
     assert lib.spec_step_workspace(ctypes.addressof(m), 8) == 0          # all sizes zero
     assert lib.spec_tree_step(ctypes.addressof(m), A, A, A, 8, A, A, A, None, None, 0, A, 1 << 30, None) == E_SHAPE
     assert lib.spec_tree_step(None, A, A, A, 8, A, A, A, None, None, 0, A, 1 << 30, None) == E_INVAL
+
+
+def fake_model(**over):
+    """A specv_model of the tiny shape whose pointers are fake, aligned
+    addresses: enough for host validation, never dereferenced."""
+    from speculative_verification_amd._lib import SpecvModel
+    m = SpecvModel()
+    cfg = dict(n_layers=2, hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, inter=96, vocab=300, max_pos=640)
+    cfg.update(over)
+    for k, v in cfg.items():
+        setattr(m, k, v)
+    m.eps, m.kv_capacity = 1e-6, 700
+    for k, _ in SpecvModel._fields_[10:]:
+        setattr(m, k, A)
+    return m
+
+
+def test_window_rejects_bad_arguments(lib):
+    from speculative_verification_amd._lib import SpecvDrafter
+    m = fake_model()
+    mp = ctypes.addressof(m)
+    need = lib.spec_window_workspace(mp, 8)
+    assert need == lib.spec_step_workspace(mp, 8) > 0
+    d = SpecvDrafter(A, 100, 4, A, 1 << 31, 0)
+    dp = ctypes.byref(d)
+    f = lib.spec_window_run
+    assert f(mp, A, A, None, 0, dp, 0, 4, A, need, None, None) == E_SHAPE        # width < 1
+    assert f(mp, A, A, None, 0, dp, 17, 4, A, need, None, None) == E_SHAPE       # width > 16
+    assert f(mp, A, A, None, 0, dp, 8, -1, A, need, None, None) == E_SHAPE       # W < 0
+    assert f(mp, A, A, None, 0, dp, 8, 4097, A, need, None, None) == E_SHAPE
+    assert f(mp, None, A, None, 0, dp, 8, 4, A, need, None, None) == E_INVAL     # no ctrl
+    assert f(mp, A, None, None, 0, dp, 8, 4, A, need, None, None) == E_INVAL     # no stats
+    assert f(mp, A, A, A, 0, dp, 8, 4, A, need, None, None) == E_INVAL           # ring without capacity
+    assert f(mp, A, A, None, 0, None, 8, 4, A, need, None, None) == E_INVAL      # drafter needed
+    bad = SpecvDrafter(A, 0, 4, A, 0, 0)
+    assert f(mp, A, A, None, 0, ctypes.byref(bad), 8, 4, A, need, None, None) == E_INVAL
+    bad = SpecvDrafter(A, 10, 0, A, 0, 0)
+    assert f(mp, A, A, None, 0, ctypes.byref(bad), 8, 4, A, need, None, None) == E_INVAL
+    assert f(mp, A + 2, A, None, 0, dp, 8, 4, A, need, None, None) == E_ALIGN
+    assert f(mp, A, A, None, 0, dp, 8, 4, A, need - 1, None, None) == E_WORKSPACE
+    assert f(mp, A, A, None, 0, dp, 8, 4, None, need, None, None) == E_WORKSPACE
+    assert f(mp, A, A, None, 0, dp, 8, 4, A + 16, need, None, None) == E_ALIGN
+    assert f(mp, A, A, None, 0, dp, 8, 0, A, need, None, None) == OK             # W == 0: nothing to do
+    assert f(mp, A, A, None, 0, None, 1, 0, A, lib.spec_window_workspace(mp, 1), None, None) == OK
+    assert f(None, A, A, None, 0, dp, 8, 4, A, need, None, None) == E_INVAL
+    m1 = fake_model(vocab=1)
+    assert f(ctypes.addressof(m1), A, A, None, 0, dp, 8, 4, A, need, None, None) == E_SHAPE
+    assert f(ctypes.addressof(m1), A, A, None, 0, None, 1, 0, A, need, None, None) == OK
+    m2 = fake_model(head_dim=15)
+    assert f(ctypes.addressof(m2), A, A, None, 0, dp, 8, 4, A, need, None, None) == E_SHAPE
