@@ -273,6 +273,63 @@ def cpu_baseline(model, T, min_seconds=10.0):
                       f"single thread on {platform.machine()} ({os.cpu_count()} host cpus visible)"}
 
 
+def window_bench(torch, sv, sg, widths, W=16, max_windows=400):
+    """Device-resident windows on the Qwen2.5-0.5B shape: W-step windows of
+    draft -> tree verify -> accept -> compact, each ending in a pinned
+    readback of the control block and W statistics records. The context
+    starts from 1024 committed rows and grows until the device sets done at
+    4096. The drafter copies the width-1 greedy stream with per-node
+    acceptance 0.6. Each window is timed with events on the stream; only
+    windows whose W steps all ran (none after done) are counted."""
+    cfg = sg.QWEN05
+    arrays = sg.model_case(3, cfg)
+    L0, ctx, cap, root = 1024, 4096, 4096 + 32, 9
+    kc, vc = sg.kv_prefix(41, cfg, L0, cap)
+    dm = sv.DeviceModel(arrays, cfg, cap, kc, vc)
+    del arrays, kc, vc
+    stats = torch.zeros((W, 3), dtype=torch.int32, device="cuda")
+    ring = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    rb = torch.zeros(32 + 12 * W, dtype=torch.uint8, pin_memory=True)
+    draws = torch.from_numpy(sg.draft_draws(5, 256).view(np.int32)).cuda()
+    ref = torch.zeros(ctx + 64, dtype=torch.int32, device="cuda")
+    out = {}
+    for width in [1] + [w for w in widths if w != 1]:
+        ctrl = sv.new_ctrl(L0, width, ctx, root_token=root)
+        kw = {} if width == 1 else dict(reference=ref, draws=draws, threshold=int(0.6 * 2 ** 32))
+        dm.window(ctrl, stats, width, W, ring=ring, readback=rb, **kw)       # capture + warm
+        torch.cuda.synchronize()
+        ctrl.copy_(sv.new_ctrl(L0, width, ctx, root_token=root))
+        ring.zero_()
+        t_us, steps, tokens = 0.0, 0, 0
+        for _ in range(max_windows):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dm.window(ctrl, stats, width, W, ring=ring, readback=rb, **kw)
+            e1.record()
+            e1.synchronize()
+            st = rb[32:].numpy().view(np.int32).reshape(W, 3)
+            if (st[:, 0] < 0).any():
+                break
+            t_us += e0.elapsed_time(e1) * 1e3
+            steps += W
+            tokens += int(st[:, 0].sum()) + W
+        if width == 1:   # the greedy stream drives the drafter at every other width
+            n = int(rb[:4].numpy().view(np.int32)[0]) - L0
+            ref[L0] = root
+            ref[L0 + 1:L0 + 1 + n] = ring[:n]
+        out[str(width)] = {"us_per_step": round(t_us / max(steps, 1), 2),
+                           "tokens_per_step": round(tokens / max(steps, 1), 3),
+                           "tokens_per_s": round(tokens / (t_us * 1e-6), 1) if t_us else None,
+                           "windows": steps // W}
+        print(f"[bench] window width={width}: {out[str(width)]}", file=sys.stderr, flush=True)
+    t1 = out["1"]["us_per_step"]
+    for v in out.values():
+        v["step_cost_vs_width1"] = round(v["us_per_step"] / t1, 3)
+    return {"workload": f"qwen2.5-0.5b-shaped decoder, {W}-step windows from 1024 to 4096 context, "
+                        f"synthetic drafter at acceptance 0.6, pinned readback of {32 + 12 * W} B per window",
+            "W": W, "by_width": out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +340,8 @@ def main():
     ap.add_argument("--sweep", default="1,2,4,8", help="T values timed besides --T")
     ap.add_argument("--roofline-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window-widths", default="1,2,4,8,16",
+                    help="tree widths of the speculation-window measurement (empty: skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -320,6 +379,8 @@ def main():
               f"replay exact={ok}", file=sys.stderr, flush=True)
 
     ach, avg_s, avg_b, nlaunch, by_shape = roofline_linear(model, args.T, args.roofline_reps, torch)
+    widths = [int(w) for w in args.window_widths.split(",") if w]
+    window = window_bench(torch, sv, sg, widths) if widths else None
     main_T = per_T[args.T]
     out = {
         "metric": METRIC,
@@ -355,6 +416,7 @@ def main():
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
                      "by_shape": by_shape},
+        "window": window,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(model, args.T),
     }
     print(json.dumps(out), flush=True)

@@ -204,10 +204,12 @@ int kv_compact(uint16_t* k_cache, uint16_t* v_cache, int32_t n_layers, int32_t n
  * are scaled by 1/sqrt(head_dim); attention runs in chunks of 256 logical
  * positions merged in a second pass; every sum uses the fixed 16-slot order;
  * exp is a fixed Cody-Waite plus degree-7 polynomial evaluation, so results
- * are bit-reproducible. Limits: n_heads/n_kv_heads <= 16, head_dim <= 128
- * and even, 4*(n_heads/n_kv_heads)*(head_dim+256) + 512*head_dim <= 64 KiB,
- * hidden, inter and n_heads*head_dim multiples of 32, 4*max(hidden, inter)
- * <= 64 KiB.
+ * are bit-reproducible. Limits: n_heads/n_kv_heads <= 16; head_dim a
+ * multiple of 16 in [16, 128]; 4*(n_heads/n_kv_heads)*(head_dim+256) +
+ * 512*(head_dim+8) <= 64 KiB; hidden, inter and n_heads*head_dim multiples
+ * of 32; hidden, inter <= 16384; n_heads*head_dim <= 8192;
+ * 4*n_heads*(ceil(kv_capacity/256)+1) <= 64 KiB. The norm weights are
+ * 16-byte aligned.
  */
 typedef struct {
     int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab, max_pos;

@@ -64,56 +64,77 @@ __device__ __forceinline__ uint16_t f32_to_f16(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
 }
 
-// Depth of node i in a topologically ordered parent array (a node whose
-// parent breaks the order counts as a root).
-__device__ __forceinline__ int node_depth(const int32_t* parent, int i) {
+constexpr int kFwdThreads = 256;   // embedding and attention-chunk workgroups
+constexpr int kRowThreads = 1024;  // row kernels: norms, SiLU, attention merge
+constexpr int kRowRegs = 4;        // float4 chunks per thread: rows up to 16384 values
+constexpr int kMergeRegs = 8;      // values per thread in the merge: rows up to 8192
+constexpr int kMaxNodes = 16;
+
+// Block-wide max of non-negative values over kRowThreads threads (order-free).
+__device__ __forceinline__ float block_max(float a, float* red) {
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kRowThreads / 64; w++) r = fmaxf(r, red[w]);
+    return r;
+}
+
+// Per-token int8 quantisation of a row held in registers (absmax scale,
+// codes rounded to nearest-even, symmetric 127). Thread t holds, for r < R,
+// the V values at columns V*(t + r*kRowThreads) + e.
+template <int R, int V>
+__device__ void quantize_regs(const float (&y)[R][V], int K, int8_t* __restrict__ xrow, float* __restrict__ xs_i,
+                              float* red) {
+    const int tid = threadIdx.x;
+    float a = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        if (V * (tid + r * kRowThreads) < K)
+#pragma unroll
+            for (int e = 0; e < V; e++) a = fmaxf(a, fabsf(y[r][e]));
+    a = block_max(a, red);
+    const float inv = a == 0.0f ? 0.0f : 127.0f / a;
+    if (tid == 0) *xs_i = a == 0.0f ? 0.0f : a / 127.0f;
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int c0 = V * (tid + r * kRowThreads);
+        if (c0 >= K) continue;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < V; e++) {
+            float q = __builtin_rintf(y[r][e] * inv);  // v_rndne_f32: nearest-even
+            q = fminf(fmaxf(q, -127.0f), 127.0f);
+            packed |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
+        }
+        if (V == 4)
+            *reinterpret_cast<uint32_t*>(xrow + c0) = packed;
+        else
+            xrow[c0] = (int8_t)(packed & 0xff);
+    }
+}
+
+// Rows of nodes past the live count quantise to zero, so the linears that
+// follow produce exact zeros for them. K is a multiple of 4.
+__device__ void zero_row(int8_t* xrow, float* xs_i, int K) {
+    if (threadIdx.x == 0) *xs_i = 0.0f;
+    for (int c = threadIdx.x; c < K / 4; c += blockDim.x) reinterpret_cast<uint32_t*>(xrow)[c] = 0;
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// Depth of node i from an LDS copy of the parent array (a node whose parent
+// breaks the topological order counts as a root).
+__device__ __forceinline__ int lds_depth(const int* s_par, int i) {
     int d = 0;
-    for (int x = i, guard = 0; x > 0 && guard < 64; guard++) {
-        const int p = parent[x];
+    for (int x = i; x > 0 && d < kMaxNodes;) {
+        const int p = s_par[x];
         if (p < 0 || p >= x) break;
         x = p;
         d++;
     }
     return d;
-}
-
-constexpr int kFwdThreads = 256;
-
-// Block-wide max of non-negative values (order-free).
-__device__ __forceinline__ float block_max(float a, float* scratch4) {
-    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-    if ((threadIdx.x & 63) == 0) scratch4[threadIdx.x >> 6] = a;
-    __syncthreads();
-    a = fmaxf(fmaxf(scratch4[0], scratch4[1]), fmaxf(scratch4[2], scratch4[3]));
-    __syncthreads();
-    return a;
-}
-
-// Quantise a row held in LDS to per-token int8 (absmax scale, codes rounded
-// to nearest-even, symmetric 127), writing xq[0..K) and *xs.
-__device__ void quantize_row(const float* row, int K, int8_t* xq, float* xs, float* scratch4) {
-    float a = 0.0f;
-    for (int k = threadIdx.x; k < K; k += kFwdThreads) a = fmaxf(a, fabsf(row[k]));
-    a = block_max(a, scratch4);
-    if (a == 0.0f) {
-        if (threadIdx.x == 0) *xs = 0.0f;
-        for (int k = threadIdx.x; k < K; k += kFwdThreads) xq[k] = 0;
-        return;
-    }
-    const float inv = 127.0f / a;
-    if (threadIdx.x == 0) *xs = a / 127.0f;
-    for (int k = threadIdx.x; k < K; k += kFwdThreads) {
-        float r = __builtin_rintf(row[k] * inv);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        xq[k] = (int8_t)(int)r;
-    }
-}
-
-// Rows of nodes past the live count quantise to zero, so the linears that
-// follow produce exact zeros for them.
-__device__ void zero_row(int8_t* xq, float* xs, int K) {
-    if (threadIdx.x == 0) *xs = 0.0f;
-    for (int k = threadIdx.x; k < K; k += kFwdThreads) xq[k] = 0;
 }
 
 // ---------------------------------------------------------------- kernels
@@ -138,63 +159,102 @@ __global__ __launch_bounds__(kFwdThreads) void embed_kernel(const int32_t* __res
 
 // Optional residual (h += resid, written back), RMSNorm with weight w, then
 // per-token int8 quantisation. RMSNorm: ss = R16(x*x), ms = ss / H,
-// rs = 1 / sqrt(ms + eps), y = (x * rs) * w.
-__global__ __launch_bounds__(kFwdThreads) void rmsnorm_quant_kernel(float* __restrict__ h,
+// rs = 1 / sqrt(ms + eps), y = (x * rs) * w. Every global load of the row is
+// issued before the first use, so the kernel pays one memory round trip.
+__global__ __launch_bounds__(kRowThreads) void rmsnorm_quant_kernel(float* __restrict__ h,
                                                                     const float* __restrict__ resid,
                                                                     const float* __restrict__ w, int H,
                                                                     float eps, int8_t* __restrict__ xq,
                                                                     float* __restrict__ xs,
                                                                     const specv_ctrl* ctrl) {
-    extern __shared__ float row[];  // H floats
-    __shared__ float scratch4[4];
+    extern __shared__ float sq[];  // H squares, summed by 16 lanes in slot order
+    __shared__ float red[kRowThreads / 64];
     __shared__ float s_ss;
-    const int i = blockIdx.x;
+    const int i = blockIdx.x, tid = threadIdx.x, H4 = H / 4;
     if (ctrl->done) return;
     if (i >= ctrl->n_nodes) {
         zero_row(xq + (size_t)i * H, xs + i, H);
         return;
     }
     float* hr = h + (size_t)i * H;
-    for (int k = threadIdx.x; k < H; k += kFwdThreads) {
-        float v = hr[k];
-        if (resid) {
-            v = v + resid[(size_t)i * H + k];
-            hr[k] = v;
+    const float* rr = resid ? resid + (size_t)i * H : nullptr;
+    float4 xv[kRowRegs], rv[kRowRegs], wv[kRowRegs];
+#pragma unroll
+    for (int r = 0; r < kRowRegs; r++) {
+        const int c = tid + r * kRowThreads;
+        if (c < H4) {
+            xv[r] = ld4(hr + 4 * c);
+            wv[r] = ld4(w + 4 * c);
+            if (rr) rv[r] = ld4(rr + 4 * c);
         }
-        row[k] = v;
+    }
+    float x[kRowRegs][4];
+#pragma unroll
+    for (int r = 0; r < kRowRegs; r++) {
+        const int c = tid + r * kRowThreads;
+        if (c >= H4) continue;
+        x[r][0] = xv[r].x, x[r][1] = xv[r].y, x[r][2] = xv[r].z, x[r][3] = xv[r].w;
+        if (rr) {
+            x[r][0] = x[r][0] + rv[r].x, x[r][1] = x[r][1] + rv[r].y;
+            x[r][2] = x[r][2] + rv[r].z, x[r][3] = x[r][3] + rv[r].w;
+            *reinterpret_cast<float4*>(hr + 4 * c) = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
+        }
+        *reinterpret_cast<float4*>(sq + 4 * c) =
+            make_float4(x[r][0] * x[r][0], x[r][1] * x[r][1], x[r][2] * x[r][2], x[r][3] * x[r][3]);
     }
     __syncthreads();
-    if (threadIdx.x < 16) {
+    if (tid < 16) {
         float acc = 0.0f;
-        for (int k = threadIdx.x; k < H; k += 16) acc = acc + row[k] * row[k];
+        for (int k = tid; k < H; k += 16) acc = acc + sq[k];
         acc = tree16(acc);
-        if (threadIdx.x == 0) s_ss = acc;
+        if (tid == 0) s_ss = acc;
     }
     __syncthreads();
     const float ms = s_ss / (float)H;
     const float rs = 1.0f / sqrtf(ms + eps);
-    for (int k = threadIdx.x; k < H; k += kFwdThreads) row[k] = (row[k] * rs) * w[k];
-    __syncthreads();
-    quantize_row(row, H, xq + (size_t)i * H, xs + i, scratch4);
+    float y[kRowRegs][4];
+#pragma unroll
+    for (int r = 0; r < kRowRegs; r++) {
+        y[r][0] = (x[r][0] * rs) * wv[r].x;
+        y[r][1] = (x[r][1] * rs) * wv[r].y;
+        y[r][2] = (x[r][2] * rs) * wv[r].z;
+        y[r][3] = (x[r][3] * rs) * wv[r].w;
+    }
+    quantize_regs(y, H, xq + (size_t)i * H, xs + i, red);
 }
 
 // z = silu(gate) * up over a [n][2I] gate/up output, then quantisation.
-__global__ __launch_bounds__(kFwdThreads) void silu_mul_quant_kernel(const float* __restrict__ gu, int I,
+__global__ __launch_bounds__(kRowThreads) void silu_mul_quant_kernel(const float* __restrict__ gu, int I,
                                                                      int8_t* __restrict__ xq,
                                                                      float* __restrict__ xs,
                                                                      const specv_ctrl* ctrl) {
-    extern __shared__ float row[];  // I floats
-    __shared__ float scratch4[4];
-    const int i = blockIdx.x;
+    __shared__ float red[kRowThreads / 64];
+    const int i = blockIdx.x, tid = threadIdx.x, I4 = I / 4;
     if (ctrl->done) return;
     if (i >= ctrl->n_nodes) {
         zero_row(xq + (size_t)i * I, xs + i, I);
         return;
     }
     const float* g = gu + (size_t)i * 2 * I;
-    for (int k = threadIdx.x; k < I; k += kFwdThreads) row[k] = silu(g[k]) * g[I + k];
-    __syncthreads();
-    quantize_row(row, I, xq + (size_t)i * I, xs + i, scratch4);
+    float4 gv[kRowRegs], uv[kRowRegs];
+#pragma unroll
+    for (int r = 0; r < kRowRegs; r++) {
+        const int c = tid + r * kRowThreads;
+        if (c < I4) {
+            gv[r] = ld4(g + 4 * c);
+            uv[r] = ld4(g + I + 4 * c);
+        }
+    }
+    float z[kRowRegs][4];
+#pragma unroll
+    for (int r = 0; r < kRowRegs; r++) {
+        if (tid + r * kRowThreads >= I4) continue;
+        z[r][0] = silu(gv[r].x) * uv[r].x;
+        z[r][1] = silu(gv[r].y) * uv[r].y;
+        z[r][2] = silu(gv[r].z) * uv[r].z;
+        z[r][3] = silu(gv[r].w) * uv[r].w;
+    }
+    quantize_regs(z, I, xq + (size_t)i * I, xs + i, red);
 }
 
 // Rotary positions at L + depth(i) on the q and k heads of node i; k and v
@@ -205,10 +265,13 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* __restrict__ q
                                                      int max_pos, int hd, int nh, int nkv, float* __restrict__ qrot,
                                                      uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int layer,
                                                      int cap, const specv_ctrl* ctrl) {
+    __shared__ int s_par[kMaxNodes];
     const int i = blockIdx.x, head = blockIdx.y;
     if (ctrl->done || i >= ctrl->n_nodes) return;
     const int L = ctrl->committed_len;
-    const int pos = L + node_depth(parent, i);
+    if (threadIdx.x <= i) s_par[threadIdx.x] = parent[threadIdx.x];
+    __syncthreads();
+    const int pos = L + lds_depth(s_par, i);
     const int half = hd / 2, d = threadIdx.x;
     const int QKV = (nh + 2 * nkv) * hd;
     if (d >= half || pos >= max_pos || L + i >= cap) return;
@@ -224,11 +287,12 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* __restrict__ q
     } else {
         const int g = head - nh;
         const size_t row = (((size_t)layer * nkv + g) * cap + (L + i)) * hd;
+        const float* vs = qkv + (size_t)i * QKV + (nh + nkv) * hd + g * hd;
+        const float va = vs[d], vb = vs[d + half];
         kc[row + d] = f32_to_f16(ra);
         kc[row + d + half] = f32_to_f16(rb);
-        const float* vs = qkv + (size_t)i * QKV + (nh + nkv) * hd + g * hd;
-        vc[row + d] = f32_to_f16(vs[d]);
-        vc[row + d + half] = f32_to_f16(vs[d + half]);
+        vc[row + d] = f32_to_f16(va);
+        vc[row + d + half] = f32_to_f16(vb);
     }
 }
 
@@ -236,9 +300,15 @@ constexpr int kAttnChunk = 256;   // logical positions per chunk
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;     // query heads per KV head
 
+// Padded fp16 row of the staged values (8 extra halves spread the rows of a
+// 16-lane group over the LDS banks).
+inline __host__ __device__ int attn_vstride(int hd) { return hd + 8; }
+
 inline size_t attn_lds_bytes(int hpg, int hd) {
-    return (size_t)4 * hpg * (hd + kAttnChunk) + (size_t)2 * kAttnChunk * hd;
+    return (size_t)4 * hpg * (hd + kAttnChunk) + (size_t)2 * kAttnChunk * attn_vstride(hd);
 }
+
+inline size_t merge_lds_bytes(int nh, int nchunk_max) { return (size_t)4 * nh * (nchunk_max + 1); }
 
 // One chunk of the visible sequence of one node, for all query heads of one
 // KV head, which therefore read each key and value of the chunk once.
@@ -247,83 +317,114 @@ inline size_t attn_lds_bytes(int hpg, int hd) {
 // s_j = R16_d(q_d * K_jd) * scale, m = max s_j, e_j = E(s_j - m),
 // l = R16_j(e_j), o_d = R16_j(e_j * V_jd), sums over the chunk's positions
 // in logical order. Output per (node, head, chunk): m, l, o[hd].
+//
+// Thread t owns position t of the chunk: its key row sits in registers as
+// fp32 and its value row is staged in LDS. For the value sums, lane s of a
+// 16-lane group takes R16 slot s (positions s, s+16, ... in order) of
+// HD/16 columns, and the group's xor butterfly adds the slots as the
+// index-order tree.
+template <int HD>
 __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     const float* __restrict__ qrot, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ parent, int layer, int cap, int nh, int nkv, int hd, float scale,
+    const int32_t* __restrict__ parent, int layer, int cap, int nh, int nkv, float scale,
     float* __restrict__ part, int nchunk_max, const specv_ctrl* ctrl) {
-    const int c = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+    constexpr int VS = HD + 8;
+    const int c = blockIdx.x, g = blockIdx.y, i = blockIdx.z, tid = threadIdx.x;
     if (ctrl->done || i >= ctrl->n_nodes) return;
     const int L = ctrl->committed_len;
-    const int hpg = nh / nkv;
-    __shared__ int anc[64];
-    __shared__ float mh[kMaxGroup];
-    __shared__ float scratch4[4];
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    float* qs = reinterpret_cast<float*>(smem);                      // [hpg][hd]
-    float* S = qs + hpg * hd;                                        // [hpg][256]
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(S + hpg * kAttnChunk);  // [256][hd]
-
     if (L + i >= cap) return;  // its rows were not written (no room left)
-    const int depth = node_depth(parent, i);
+    const int hpg = nh / nkv;
+    __shared__ int s_par[kMaxNodes];
+    __shared__ int anc[kMaxNodes];
+    __shared__ float wmax[kFwdThreads / 64][kMaxGroup];
+    __shared__ float mh[kMaxGroup];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float* qs = reinterpret_cast<float*>(smem);                      // [hpg][HD]
+    float* S = qs + hpg * HD;                                        // [hpg][256]
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(S + hpg * kAttnChunk);  // [256][VS]
+
+    if (tid <= i) s_par[tid] = parent[tid];
+    const float* qsrc = qrot + ((size_t)i * nh + g * hpg) * HD;
+    for (int x = tid; x < hpg * HD / 4; x += kFwdThreads)
+        *reinterpret_cast<float4*>(qs + 4 * x) = ld4(qsrc + 4 * x);
+    __syncthreads();
+    const int depth = lds_depth(s_par, i);
     const int len = L + depth + 1;
     const int j0 = c * kAttnChunk;
     if (j0 >= len) return;
     const int cnt = len - j0 < kAttnChunk ? len - j0 : kAttnChunk;
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         int x = i;
         for (int t = depth; t >= 0; t--) {
             anc[t] = x;
-            const int p = parent[x];
+            const int p = s_par[x];
             x = (p >= 0 && p < x) ? p : 0;
         }
     }
-    for (int idx = threadIdx.x; idx < hpg * hd; idx += kFwdThreads)
-        qs[idx] = qrot[((size_t)i * nh + g * hpg) * hd + idx];
     __syncthreads();
 
-    const size_t plane = (((size_t)layer * nkv + g) * cap) * hd;
-    const int jj = threadIdx.x;
-    if (jj < cnt) {
-        const int j = j0 + jj;
-        const int row = j < L ? j : L + anc[j - L];
-        const uint16_t* kr = kc + plane + (size_t)row * hd;
-        const uint16_t* vr = vc + plane + (size_t)row * hd;
-        for (int d = 0; d < hd; d++) Vs[jj * hd + d] = vr[d];
-        for (int hh = 0; hh < hpg; hh++) {
+    const size_t plane = (((size_t)layer * nkv + g) * cap) * HD;
+    const bool live = tid < cnt;
+    const int j = j0 + tid;
+    const int row = live ? (j < L ? j : L + anc[j - L]) : 0;
+    float kf[HD];
+    if (live) {
+        uint4 kr[HD / 8], vr[HD / 8];
+        const uint4* ksrc = reinterpret_cast<const uint4*>(kc + plane + (size_t)row * HD);
+        const uint4* vsrc = reinterpret_cast<const uint4*>(vc + plane + (size_t)row * HD);
+#pragma unroll
+        for (int t = 0; t < HD / 8; t++) {
+            kr[t] = ksrc[t];
+            vr[t] = vsrc[t];
+        }
+#pragma unroll
+        for (int t = 0; t < HD / 8; t++) {
+            *reinterpret_cast<uint4*>(Vs + tid * VS + 8 * t) = vr[t];
+            const uint32_t wd[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                kf[8 * t + 2 * e] = f16_to_f32((uint16_t)(wd[e] & 0xffff));
+                kf[8 * t + 2 * e + 1] = f16_to_f32((uint16_t)(wd[e] >> 16));
+            }
+        }
+    }
+    // scores, then the chunk max of each head
+    for (int hh = 0; hh < hpg; hh++) {
+        float sc = -__builtin_inff();
+        if (live) {
             float slot[16];
 #pragma unroll
             for (int s = 0; s < 16; s++) slot[s] = 0.0f;
-            for (int d0 = 0; d0 < hd; d0 += 16)
 #pragma unroll
-                for (int s = 0; s < 16; s++)
-                    if (d0 + s < hd) slot[s] = slot[s] + qs[hh * hd + d0 + s] * f16_to_f32(kr[d0 + s]);
+            for (int d0 = 0; d0 < HD; d0 += 16)
+#pragma unroll
+                for (int s = 0; s < 16; s++) slot[s] = slot[s] + qs[hh * HD + d0 + s] * kf[d0 + s];
 #pragma unroll
             for (int w = 1; w < 16; w <<= 1)
 #pragma unroll
                 for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
-            S[hh * kAttnChunk + jj] = slot[0] * scale;
+            sc = slot[0] * scale;
         }
+        S[hh * kAttnChunk + tid] = sc;
+        // max over the chunk (order-free; only +0/-0 ties can differ, and a
+        // difference against either gives the same exp input up to its sign)
+        float a = sc;
+        for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+        if ((tid & 63) == 0) wmax[tid >> 6][hh] = a;
     }
     __syncthreads();
     for (int hh = 0; hh < hpg; hh++) {
-        // max over the chunk (order-free; only +0/-0 ties can differ, and a
-        // difference against either gives the same exp input up to its sign)
-        float a = jj < cnt ? S[hh * kAttnChunk + jj] : -__builtin_inff();
-        for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-        if ((threadIdx.x & 63) == 0) scratch4[threadIdx.x >> 6] = a;
-        __syncthreads();
-        if (threadIdx.x == 0) mh[hh] = fmaxf(fmaxf(scratch4[0], scratch4[1]), fmaxf(scratch4[2], scratch4[3]));
-        __syncthreads();
+        const float m = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
+        S[hh * kAttnChunk + tid] = live ? det_exp(S[hh * kAttnChunk + tid] - m) : 0.0f;
+        if (tid == 0) mh[hh] = m;
     }
-    if (jj < cnt)
-        for (int hh = 0; hh < hpg; hh++) S[hh * kAttnChunk + jj] = det_exp(S[hh * kAttnChunk + jj] - mh[hh]);
     __syncthreads();
 
-    float* out = part;  // [n][nh][nchunk_max][hd + 2]
-    const int stride = hd + 2;
+    float* out = part;  // [n][nh][nchunk_max][HD + 2]
+    const int stride = HD + 2;
     // l = R16 over the chunk: 16 lanes per head, lane s sums positions s, s+16, ...
-    if (threadIdx.x < hpg * 16) {
-        const int hh = threadIdx.x >> 4, s = threadIdx.x & 15;
+    if (tid < hpg * 16) {
+        const int hh = tid >> 4, s = tid & 15;
         float acc = 0.0f;
         for (int p = s; p < cnt; p += 16) acc = acc + S[hh * kAttnChunk + p];
         acc = tree16(acc);
@@ -333,72 +434,103 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
             o[1] = acc;
         }
     }
-    // o_d = R16 over the chunk of e_j * V_jd, one (head, d) per thread
-    for (int idx = threadIdx.x; idx < hpg * hd; idx += kFwdThreads) {
-        const int hh = idx / hd, d = idx % hd;
-        float slot[16];
+    // o_d = R16 over the chunk of e_j * V_jd: lane s of group q owns slot s of
+    // columns q, q + 16, ... (HD/16 of them).
+    {
+        const int s = tid & 15, q = tid >> 4;
+        constexpr int NC = HD / 16;
+        float vv[NC][16];
 #pragma unroll
-        for (int s = 0; s < 16; s++) slot[s] = 0.0f;
-        for (int p0 = 0; p0 < cnt; p0 += 16)
+        for (int m = 0; m < 16; m++) {
+            const int p = s + 16 * m;
 #pragma unroll
-            for (int s = 0; s < 16; s++)
-                if (p0 + s < cnt) slot[s] = slot[s] + S[hh * kAttnChunk + p0 + s] * f16_to_f32(Vs[(p0 + s) * hd + d]);
+            for (int k = 0; k < NC; k++) vv[k][m] = p < cnt ? f16_to_f32(Vs[p * VS + q + 16 * k]) : 0.0f;
+        }
+        for (int hh = 0; hh < hpg; hh++) {
+            float e[16];
 #pragma unroll
-        for (int w = 1; w < 16; w <<= 1)
+            for (int m = 0; m < 16; m++) e[m] = S[hh * kAttnChunk + s + 16 * m];
 #pragma unroll
-            for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
-        out[(((size_t)i * nh + g * hpg + hh) * nchunk_max + c) * stride + 2 + d] = slot[0];
+            for (int k = 0; k < NC; k++) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 16; m++)
+                    if (s + 16 * m < cnt) acc = acc + e[m] * vv[k][m];
+                acc = tree16(acc);
+                if (s == 0) out[(((size_t)i * nh + g * hpg + hh) * nchunk_max + c) * stride + 2 + q + 16 * k] = acc;
+            }
+        }
     }
 }
 
 // Merge of the chunks of each head of node i: m = max_c m_c,
 // w_c = E(m_c - m), l = R16_c(w_c * l_c), o_d = R16_c(w_c * o_cd),
 // out_d = o_d / l; then the attention output row [nh*hd] is quantised for
-// the output projection.
-__global__ __launch_bounds__(kFwdThreads) void attn_merge_quant_kernel(
+// the output projection. The chunk weights are computed once per
+// (head, chunk) by 16 lanes per head and shared through LDS.
+__global__ __launch_bounds__(kRowThreads) void attn_merge_quant_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ parent, int nh, int hd, int nchunk_max,
     int8_t* __restrict__ xq, float* __restrict__ xs, const specv_ctrl* ctrl) {
-    extern __shared__ float row[];  // nh*hd floats
-    __shared__ float scratch4[4];
-    const int i = blockIdx.x;
+    extern __shared__ float wts[];  // [nh][nchunk_max] chunk weights, then l[nh]
+    __shared__ float red[kRowThreads / 64];
+    __shared__ int s_par[kMaxNodes];
+    const int i = blockIdx.x, tid = threadIdx.x;
     const int K = nh * hd;
     if (ctrl->done) return;
     if (i >= ctrl->n_nodes) {
         zero_row(xq + (size_t)i * K, xs + i, K);
         return;
     }
-    const int len = ctrl->committed_len + node_depth(parent, i) + 1;
+    float* lsum = wts + (size_t)nh * nchunk_max;
+    if (tid <= i) s_par[tid] = parent[tid];
+    __syncthreads();
+    const int len = ctrl->committed_len + lds_depth(s_par, i) + 1;
     const int nch_len = (len + kAttnChunk - 1) / kAttnChunk;
     const int nch = nch_len < nchunk_max ? nch_len : nchunk_max;
     const int stride = hd + 2;
-    for (int idx = threadIdx.x; idx < K; idx += kFwdThreads) {
-        const int hh = idx / hd, d = idx % hd;
+    for (int hh = tid >> 4; hh < nh; hh += kRowThreads / 16) {
+        const int s = tid & 15;
         const float* ph = part + ((size_t)i * nh + hh) * nchunk_max * stride;
         float m = -__builtin_inff();
-        for (int c = 0; c < nch; c++) m = fmaxf(m, ph[(size_t)c * stride]);
-        float sl[16], so[16];
+        for (int c = s; c < nch; c += 16) m = fmaxf(m, ph[(size_t)c * stride]);
+        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+        float acc = 0.0f;
+        for (int c = s; c < nch; c += 16) {
+            const float wc = det_exp(ph[(size_t)c * stride] - m);
+            wts[hh * nchunk_max + c] = wc;
+            acc = acc + wc * ph[(size_t)c * stride + 1];
+        }
+        acc = tree16(acc);
+        if (s == 0) lsum[hh] = acc;
+    }
+    __syncthreads();
+    float y[kMergeRegs][1];
 #pragma unroll
-        for (int s = 0; s < 16; s++) sl[s] = so[s] = 0.0f;
-        for (int c0 = 0; c0 < nch; c0 += 16)
+    for (int r = 0; r < kMergeRegs; r++) {
+        const int idx = tid + r * kRowThreads;
+        y[r][0] = 0.0f;
+        if (idx >= K) continue;
+        const int hh = idx / hd, d = idx - hh * hd;
+        const float* ph = part + ((size_t)i * nh + hh) * nchunk_max * stride + 2 + d;
+        const float* wh = wts + hh * nchunk_max;
+        float slot[16];
+#pragma unroll
+        for (int s = 0; s < 16; s++) slot[s] = 0.0f;
+        for (int c0 = 0; c0 < nch; c0 += 16) {
+            float ov[16];
+#pragma unroll
+            for (int s = 0; s < 16; s++) ov[s] = c0 + s < nch ? ph[(size_t)(c0 + s) * stride] : 0.0f;
 #pragma unroll
             for (int s = 0; s < 16; s++)
-                if (c0 + s < nch) {
-                    const float* pc = ph + (size_t)(c0 + s) * stride;
-                    const float wc = det_exp(pc[0] - m);
-                    sl[s] = sl[s] + wc * pc[1];
-                    so[s] = so[s] + wc * pc[2 + d];
-                }
+                if (c0 + s < nch) slot[s] = slot[s] + wh[c0 + s] * ov[s];
+        }
 #pragma unroll
         for (int w = 1; w < 16; w <<= 1)
 #pragma unroll
-            for (int s = 0; s < 16; s += 2 * w) {
-                sl[s] = sl[s] + sl[s + w];
-                so[s] = so[s] + so[s + w];
-            }
-        row[idx] = so[0] / sl[0];
+            for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
+        y[r][0] = slot[0] / lsum[hh];
     }
-    __syncthreads();
-    quantize_row(row, K, xq + (size_t)i * K, xs + i, scratch4);
+    quantize_regs(y, K, xq + (size_t)i * K, xs + i, red);
 }
 
 // ---------------------------------------------------------------- host
@@ -441,17 +573,21 @@ StepLayout step_layout(const specv_model* m, int n) {
 int validate_model(const specv_model* m) {
     if (!m) return SPECV_E_INVAL;
     if (m->n_layers < 1 || m->hidden < 32 || m->hidden % 32 || m->n_heads < 1 || m->n_kv_heads < 1 ||
-        m->n_heads % m->n_kv_heads || m->n_heads / m->n_kv_heads > kMaxGroup || m->head_dim < 2 ||
-        m->head_dim % 2 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
+        m->n_heads % m->n_kv_heads || m->n_heads / m->n_kv_heads > kMaxGroup || m->head_dim < 16 ||
+        m->head_dim % 16 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
         m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || !(m->eps >= 0.0f) ||
         attn_lds_bytes(m->n_heads / m->n_kv_heads, m->head_dim) > 64 * 1024 ||
-        (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024)
+        (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024 ||
+        (size_t)m->n_heads * m->head_dim > (size_t)kMergeRegs * kRowThreads ||
+        merge_lds_bytes(m->n_heads, (m->kv_capacity + kAttnChunk - 1) / kAttnChunk) > 64 * 1024)
         return SPECV_E_SHAPE;
     if (!m->w_qkv || !m->s_qkv || !m->w_o || !m->s_o || !m->w_gu || !m->s_gu || !m->w_down || !m->s_down ||
         !m->norm_attn || !m->norm_mlp || !m->norm_final || !m->w_lm || !m->s_lm || !m->rope_cos ||
         !m->rope_sin || !m->k_cache || !m->v_cache)
         return SPECV_E_INVAL;
-    if (!aligned(m->k_cache, 16) || !aligned(m->v_cache, 16)) return SPECV_E_ALIGN;
+    if (!aligned(m->k_cache, 16) || !aligned(m->v_cache, 16) || !aligned(m->norm_attn, 16) ||
+        !aligned(m->norm_mlp, 16) || !aligned(m->norm_final, 16))
+        return SPECV_E_ALIGN;
     return SPECV_OK;
 }
 
@@ -460,6 +596,22 @@ int validate_model(const specv_model* m) {
         const int rc_ = (expr);    \
         if (rc_ != SPECV_OK) return rc_; \
     } while (0)
+
+static int launch_attn_chunk(int hd, dim3 grid, size_t lds, hipStream_t s, const float* qrot,
+                             const uint16_t* kc, const uint16_t* vc, const int32_t* parent, int layer, int cap,
+                             int nh, int nkv, float scale, float* part, int nchunk_max, const specv_ctrl* ctrl) {
+    switch (hd) {
+#define SPECV_ATTN(HDV)                                                                                   \
+    case HDV:                                                                                             \
+        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), lds, s, qrot, kc, vc, parent, \
+                           layer, cap, nh, nkv, scale, part, nchunk_max, ctrl);                         \
+        return launch_status();
+        SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
+        SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
+#undef SPECV_ATTN
+        default: return SPECV_E_SHAPE;
+    }
+}
 
 int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const int32_t* token, float* logits,
                     specv_ctrl* ctrl, char* ws, const StepLayout& lay, hipStream_t s) {
@@ -489,31 +641,30 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
         const uint8_t* wd = m->w_down + (size_t)l * H * (I / 2);
         const uint16_t* sd = m->s_down + (size_t)l * (I / 32) * H;
 
-        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kFwdThreads), H * sizeof(float), s, h,
+        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, h,
                            l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, H, m->eps, xq, xs, ctrl);
         SPECV_TRY(launch_status());
         SPECV_TRY(w4a8_linear_T(wqkv, sqkv, xq, xs, qkv, n, QKV, H, lin, linb, s));
         hipLaunchKernelGGL(rope_kv_kernel, dim3(n, nh + nkv), dim3(64), 0, s, qkv, parent, m->rope_cos,
                            m->rope_sin, m->max_pos, hd, nh, nkv, qrot, m->k_cache, m->v_cache, l, cap, ctrl);
         SPECV_TRY(launch_status());
-        hipLaunchKernelGGL(attn_chunk_kernel, dim3(lay.nchunk_max, nkv, n), dim3(kFwdThreads),
-                           attn_lds_bytes(nh / nkv, hd), s, qrot,
-                           m->k_cache, m->v_cache, parent, l, cap, nh, nkv, hd, scale, attn, lay.nchunk_max, ctrl);
-        SPECV_TRY(launch_status());
-        hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kFwdThreads), A * sizeof(float), s, attn,
-                           parent, nh, hd, lay.nchunk_max, xq, xs, ctrl);
+        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nkv, n), attn_lds_bytes(nh / nkv, hd), s, qrot,
+                                    m->k_cache, m->v_cache, parent, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
+                                    ctrl));
+        hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kRowThreads),
+                           merge_lds_bytes(nh, lay.nchunk_max), s, attn, parent, nh, hd, lay.nchunk_max, xq, xs,
+                           ctrl);
         SPECV_TRY(launch_status());
         SPECV_TRY(w4a8_linear_T(wo, so, xq, xs, delta, n, H, A, lin, linb, s));
-        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kFwdThreads), H * sizeof(float), s, h, delta,
+        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, h, delta,
                            m->norm_mlp + (size_t)l * H, H, m->eps, xq, xs, ctrl);
         SPECV_TRY(launch_status());
         SPECV_TRY(w4a8_linear_T(wgu, sgu, xq, xs, gu, n, 2 * I, H, lin, linb, s));
-        hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(n), dim3(kFwdThreads), I * sizeof(float), s, gu, I, xq,
-                           xs, ctrl);
+        hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(n), dim3(kRowThreads), 0, s, gu, I, xq, xs, ctrl);
         SPECV_TRY(launch_status());
         SPECV_TRY(w4a8_linear_T(wd, sd, xq, xs, delta, n, H, I, lin, linb, s));
     }
-    hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kFwdThreads), H * sizeof(float), s, h, delta,
+    hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, h, delta,
                        m->norm_final, H, m->eps, xq, xs, ctrl);
     SPECV_TRY(launch_status());
     return w4a8_linear_T(m->w_lm, m->s_lm, xq, xs, logits, n, V, H, lin, linb, s);
