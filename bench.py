@@ -3,16 +3,18 @@
 
 A step verifies a T-node tree (default T = 8) through a W4A8 linear stack of
 a Llama-3-8B-shaped model and then accepts on the GPU:
-  per layer (32): quantize + qkv (6144x4096, q/k/v rows concatenated),
-                  quantize + o (4096x4096), quantize + gate_up (28672x4096,
-                  gate/up rows concatenated), quantize + down (4096x14336);
-  then quantize + lm_head (128256x4096), argmax + tree acceptance, and KV
-  compaction of the accepted rows (32 layers x 8 KV heads x head_dim 128).
-Weights are int4 in groups of 32 with fp16 scales U(0.005, 0.02);
-activations fp32 N(0,1). The weights of 4 distinct generated layer sets are
-copied into 32 separate layer buffers plus one lm_head, 4.22 GB in total, so
-every step streams each byte from HBM once (far above the 256 MB
-last-level cache). The step is captured once as a HIP graph and replayed.
+  the per-token int8 quantisation of every input row of the step (each
+  linear has its own fp32 N(0,1) input; one launch per input width K, as a
+  model fuses this quantisation into the kernel producing the activations);
+  per layer (32): qkv (6144x4096, q/k/v rows concatenated), o (4096x4096),
+  gate_up (28672x4096, gate/up rows concatenated), down (4096x14336);
+  then lm_head (128256x4096), argmax + tree acceptance, and KV compaction of
+  the accepted rows (32 layers x 8 KV heads x head_dim 128).
+Weights are int4 in groups of 32 with fp16 scales U(0.005, 0.02). The
+weights of 4 distinct generated layer sets are copied into 32 separate layer
+buffers plus one lm_head, 4.22 GB in total, so every step streams each byte
+from HBM once (far above the 256 MB last-level cache). The step is captured
+once as a HIP graph and replayed.
 
 Prints one JSON line (rank 0). `value` is the algorithmic bytes of the step
 (weights, activation codes and scales, linear outputs, quantisation traffic,
@@ -62,6 +64,15 @@ def quant_bytes(T, K):
     return 4 * T * K + T * K + 4 * T
 
 
+def timing_events(torch):
+    """A pair of timing events, created now (torch creates events lazily at
+    their first record) so their handles can be passed to the library."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    return e0, e1
+
+
 class Model:
     def __init__(self, name, torch, sv, sg, Tmax):
         m = MODELS[name]
@@ -90,12 +101,21 @@ class Model:
             lm = (torch.from_numpy(host_lm[0]).to(dev), gm(host_lm[1]))
             self.copies.append((layers, lm if c == 0 else (lm[0].clone(), lm[1].clone())))
         del dev_sets
-        # activations (fp32 inputs of each linear kind), quantisation and output buffers
-        Ks = sorted({K for _, _, K in layer_linears(m)})
-        self.x = {K: torch.from_numpy(sg.normal_f32(sg.stream_key(5, 3 + K), Tmax * K).reshape(Tmax, K)).to(dev)
-                  for K in Ks}
-        self.xq = {K: torch.empty((Tmax, K), dtype=torch.int8, device=dev) for K in Ks}
-        self.xs = {K: torch.empty((Tmax,), dtype=torch.float32, device=dev) for K in Ks}
+        # activations: every linear of the step has its own fp32 input rows,
+        # generated once per K as [inputs][Tmax][K]
+        self.inputs = {}   # K -> number of linears of the step that consume K-wide rows
+        self.in_index = []  # per layer: {linear name: input index within its K}
+        for l in range(m["layers"]):
+            idx = {}
+            for nm, _, K in layer_linears(m):
+                idx[nm] = self.inputs.get(K, 0)
+                self.inputs[K] = idx[nm] + 1
+            self.in_index.append(idx)
+        self.lm_index = self.inputs.get(m["hidden"], 0)
+        self.inputs[m["hidden"]] = self.lm_index + 1
+        self.host_x = {K: sg.normal_f32(sg.stream_key(5, 3 + K), n * Tmax * K).reshape(n, Tmax, K)
+                       for K, n in self.inputs.items()}
+        self.act_T = None
         self.y = {nm: torch.empty((Tmax * N,), dtype=torch.float32, device=dev)
                   for nm, N, _ in layer_linears(m)}
         self.logits = torch.empty((Tmax * m["vocab"],), dtype=torch.float32, device=dev)
@@ -131,30 +151,46 @@ class Model:
         self.parent = torch.from_numpy(parent).cuda()
         self.token = torch.from_numpy(token).cuda()
 
+    def prepare_acts(self, T):
+        """Device copies of the step's fp32 inputs at T tokens, [inputs][T][K]
+        contiguous, and their quantised buffers."""
+        torch = self.torch
+        if self.act_T == T:
+            return
+        dev = torch.device("cuda")
+        self.xa = {K: torch.from_numpy(np.ascontiguousarray(hx[:, :T])).to(dev) for K, hx in self.host_x.items()}
+        self.xqa = {K: torch.empty(tuple(x.shape), dtype=torch.int8, device=dev) for K, x in self.xa.items()}
+        self.xsa = {K: torch.empty(tuple(x.shape[:2]), dtype=torch.float32, device=dev) for K, x in self.xa.items()}
+        self.act_T = T
+
     def reset_ctrl(self, T):
         self.ctrl.copy_(self.torch.tensor([self.L0, T, self.cap - 16, 0, 0, 0, 0, 0], dtype=self.torch.int32))
 
     def step(self, T, copy=0, events=None):
-        """Enqueue one verify step. events: list to which (start, end, bytes)
-        of each linear launch are appended (eager roofline timing only)."""
+        """Enqueue one verify step: the quantisation of every input row of the
+        step (one launch per K), the linears, argmax + acceptance, compaction.
+        events: list to which (start, end, bytes, name) of each linear launch
+        are appended (eager roofline timing only)."""
         sv, torch, m = self.sv, self.torch, self.m
         layers, lm = self.copies[copy]
+        self.prepare_acts(T)
+        for K, x in self.xa.items():
+            n = x.shape[0]
+            sv.quantize_act(x.view(n * T, K), self.xqa[K].view(n * T, K), self.xsa[K].view(n * T))
 
-        def lin(name, wpair, K, N, y):
-            xq, xs = self.xq[K][:T], self.xs[K][:T]
-            sv.quantize_act(self.x[K][:T], xq, xs)
-            if events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
+        def lin(name, wpair, K, N, y, i):
+            xq, xs = self.xqa[K][i], self.xsa[K][i]
+            if events is not None:   # kernel begin/end timestamps of this launch
+                e0, e1 = timing_events(torch)
+                sv.check("specv_time_next_linear", sv.LIB.specv_time_next_linear(e0.cuda_event, e1.cuda_event))
             sv.linear(wpair[0], wpair[1], xq, xs, y[: T * N].view(T, N))
             if events is not None:
-                e1.record()
                 events.append((e0, e1, linear_bytes(T, N, K), name))
 
-        for lay in layers:
+        for l, lay in enumerate(layers):
             for nm, N, K in layer_linears(m):
-                lin(nm, lay[nm], K, N, self.y[nm])
-        lin("lm_head", lm, m["hidden"], m["vocab"], self.logits)
+                lin(nm, lay[nm], K, N, self.y[nm], self.in_index[l][nm])
+        lin("lm_head", lm, m["hidden"], m["vocab"], self.logits, self.lm_index)
         sv.tree_argmax_accept(self.logits[: T * m["vocab"]].view(T, m["vocab"]), self.parent, self.token,
                               self.ctrl, argmax=self.argmax, path=self.path, stats=self.stats,
                               ring=self.ring, workspace=self.ws_acc)
@@ -180,6 +216,7 @@ def run_T(model, T, steps, warmup, torch):
     """Graph-captured steps at T nodes: returns ms per step, accepted m,
     and whether graph replays reproduce the eager logits bit for bit."""
     copies = len(model.copies)
+    model.prepare_acts(T)
     model.set_tree(T)
     model.reset_ctrl(T)
     model.step(T)                      # eager step: find the predictions, then plant drafts
@@ -224,9 +261,11 @@ def run_T(model, T, steps, warmup, torch):
 
 
 def roofline_linear(model, T, reps, torch):
-    """Live per-launch timing of the W4A8 linear kernel with HIP events on
-    the stream it runs on. A spin kernel first holds the GPU so the host has
-    enqueued every launch before they execute back to back."""
+    """Live per-launch timing of the W4A8 linear kernel: each launch of an
+    eager step records a pair of HIP events at its kernel's begin and end
+    (hipExtLaunchKernel on the stream the kernel runs on). A spin kernel
+    first holds the GPU so the host has enqueued every launch before they
+    execute back to back."""
     durs, byts, names = [], [], []
     model.reset_ctrl(T)
     for r in range(reps):

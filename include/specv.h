@@ -89,7 +89,8 @@ typedef struct {
  *                        in [-127, 127].
  *   xs  fp32 [T]         scale absmax/127 (0 for an all-zero token, whose
  *                        codes are 0).
- * T in [0, 64], K in [1, 2^24]. T == 0 enqueues nothing.
+ * T in [0, 2^20] rows (one workgroup each), K in [1, 2^24]. T == 0 enqueues
+ * nothing.
  * Alignment: x 4 bytes; xq and xs any.
  */
 int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs,
@@ -127,6 +128,17 @@ size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K);
 int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
                   float* y, int32_t T, int32_t N, int32_t K, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * Timing diagnostic (not part of the computation): the next w4a8_linear_T
+ * launch made by the calling host thread records `start_event` and
+ * `stop_event` (hipEvent_t created with timing) at the beginning and end of
+ * its kernel (hipExtLaunchKernel), so a benchmark can time one kernel without
+ * the queue's event packets around it. Both NULL cancels a pending request;
+ * exactly one NULL returns SPECV_E_INVAL. A call that returns an error
+ * before launching leaves the request pending.
+ */
+int specv_time_next_linear(void* start_event, void* stop_event);
 
 /*
  * Greedy argmax per tree node and tree acceptance ([P1], GPU-Resident

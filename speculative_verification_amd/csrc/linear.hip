@@ -50,6 +50,8 @@
 // row or group is out of range uses an out-of-range offset and receives
 // zeros, and staged activations of groups past K are zeros. A zero group
 // contributes +0 to a slot, which never changes it (a slot is never -0).
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace specv {
@@ -333,6 +335,9 @@ inline int linear_row_groups_padded(int N) {
 // counters it used to zero, and partials are written before they are read.
 constexpr size_t kCounterBytes = (size_t)((1 << 24) / 64) * 4;
 
+// Events for the next linear launch of this host thread (timing diagnostics).
+static thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+
 template <int T, int MODE>
 static int launch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
                   float* part, int* cnt, int N, int K, hipStream_t s) {
@@ -352,8 +357,14 @@ static int launch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const
     const int grid = MODE == kNarrow ? (N + 15) / 16
                      : MODE == kWide ? (N + 63) / 64
                                      : MODE * linear_row_groups_padded(N);
-    hipLaunchKernelGGL((w4a8_linear_kernel<T, MODE>), dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, part,
-                       cnt, N, K);
+    if (g_time_start) {
+        hipExtLaunchKernelGGL((w4a8_linear_kernel<T, MODE>), dim3(grid), dim3(256), lds, s, g_time_start,
+                              g_time_stop, 0, wq, ws, xq, xs, y, part, cnt, N, K);
+        g_time_start = g_time_stop = nullptr;
+    } else {
+        hipLaunchKernelGGL((w4a8_linear_kernel<T, MODE>), dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, part,
+                           cnt, N, K);
+    }
     return launch_status();
 }
 
@@ -369,6 +380,13 @@ static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, con
 }
 
 }  // namespace specv
+
+extern "C" int specv_time_next_linear(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return SPECV_E_INVAL;
+    specv::g_time_start = static_cast<hipEvent_t>(start_event);
+    specv::g_time_stop = static_cast<hipEvent_t>(stop_event);
+    return SPECV_OK;
+}
 
 extern "C" size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K) {
     using namespace specv;

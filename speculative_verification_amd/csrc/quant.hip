@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_reg_kernel(
 extern "C" int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs,
                                  void* stream) {
     using namespace specv;
-    if (T < 0 || T > 64 || K < 1 || K > (1 << 24)) return SPECV_E_SHAPE;
+    if (T < 0 || T > (1 << 20) || K < 1 || K > (1 << 24)) return SPECV_E_SHAPE;
     if (T == 0) return SPECV_OK;
     if (!x || !xq || !xs) return SPECV_E_INVAL;
     if (!aligned(x, 4) || !aligned(xs, 4)) return SPECV_E_ALIGN;

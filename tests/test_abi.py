@@ -86,11 +86,17 @@ def test_linear_rejects_bad_arguments(lib):
     assert lib.w4a8_linear_workspace(0, 16, 64) == 0
 
 
+def test_time_next_linear_arguments(lib):
+    assert lib.specv_time_next_linear(A, None) == E_INVAL
+    assert lib.specv_time_next_linear(None, A) == E_INVAL
+    assert lib.specv_time_next_linear(None, None) == OK
+
+
 def test_quantize_rejects_bad_arguments(lib):
     f = lib.w4a8_quantize_act
     assert f(A, 0, 64, A, A, None) == OK                      # T == 0: nothing to do
     assert f(A, 1, 0, A, A, None) == E_SHAPE
-    assert f(A, 65, 64, A, A, None) == E_SHAPE
+    assert f(A, (1 << 20) + 1, 64, A, A, None) == E_SHAPE
     assert f(None, 1, 64, A, A, None) == E_INVAL
     assert f(A + 2, 1, 64, A, A, None) == E_ALIGN
 
