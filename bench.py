@@ -36,6 +36,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
+# WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
+# valid for the kernel source they were taken on.
+LINEAR_TRAFFIC = {"source_sha256": "d406c62cddf1d5142f918e1128ff124c5da2f3aeabe4a3b984fbe3b08fd955c6",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33646738}
+
+
+def linear_traffic(T, workload):
+    """Counter-measured bytes per launch, or None when the kernel source has
+    changed since the counters were taken (or the workload differs)."""
+    import hashlib
+    src = os.path.join(ROOT, "speculative_verification_amd", "csrc", "linear.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    ok = h == LINEAR_TRAFFIC["source_sha256"] and T == LINEAR_TRAFFIC["T"] and workload == LINEAR_TRAFFIC["workload"]
+    return LINEAR_TRAFFIC["bytes_per_launch"] if ok else None
 METRIC = "W4A8 verify GB/s & % HBM peak at T=1..8; T=8/T=1 cost ratio; µs/verify"
 
 MODELS = {
@@ -450,7 +466,7 @@ def main():
                            "accepted": v["accepted"], "graph_replay_exact": v["graph_replay_exact"]}
                   for T, v in per_T.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": linear_traffic(args.T, args.workload),
                      "kernel": f"w4a8_linear_kernel<{args.T},S> (all K-split variants)",
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,

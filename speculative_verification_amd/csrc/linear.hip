@@ -14,7 +14,8 @@
 //          slot quads (wave w: groups 16j + 4w + 0..3 in iteration j, 64
 //          contiguous bytes per row), and the quad sums meet in LDS, where
 //          the tree levels w = 4, 8 add them. Used when the matrix has few
-//          rows: every CU gets work without splitting K.
+//          rows: every CU gets work without splitting K. The four workgroups
+//          of a 64-row block run on one XCD (they share scale lines).
 //  wide:   a workgroup owns 64 rows (4 waves x 16) and all K; each wave takes
 //          all four slot quads of its rows and finishes the tree in
 //          registers. Used for tall matrices: 4x more rows share each staged
@@ -107,7 +108,15 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
     const int NG = (N + ROWS - 1) / ROWS;
 
     int rg, p;
-    if (S == 1) {
+    if (MODE == kNarrow) {
+        // The four 16-row groups of a 64-row block share the 128-byte lines of
+        // their group-major scales: number them so the hardware's round-robin
+        // placement (workgroup b on XCD b mod 8) puts all four on one XCD,
+        // whose L2 then fetches each line once.
+        const int b = blockIdx.x, i = b >> 3;
+        rg = 4 * ((i >> 2) * 8 + (b & 7)) + (i & 3);
+        p = 0;
+    } else if (S == 1) {
         rg = blockIdx.x;
         p = 0;
     } else {
@@ -354,7 +363,7 @@ static int launch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const
         }
         lds_enabled = lds;
     }
-    const int grid = MODE == kNarrow ? (N + 15) / 16
+    const int grid = MODE == kNarrow ? ((N + 15) / 16 + 31) / 32 * 32
                      : MODE == kWide ? (N + 63) / 64
                                      : MODE * linear_row_groups_padded(N);
     if (g_time_start) {
