@@ -42,15 +42,19 @@
 //
 // Nibble decode. Codes are stored u = q + 8. Flipping bit 3 of each nibble
 // gives the 4-bit two's complement of q; moving it into the high half of a
-// byte gives the int8 value 16q. The dots therefore come out as 16d (exact,
+// byte gives the int8 value 16q: the even inputs of a word come out of its
+// low nibbles, the odd inputs out of its high nibbles, with no byte permute,
+// because the staged activations of each 8-input chunk are stored in the same
+// even-then-odd order. The dots therefore come out as 16d (exact,
 // |16d| < 2^20), and the scale is pre-divided by 16 (exact: a power of two on
 // a widened fp16 value), so f32(scale/16) * f32(16d) is the same real product
 // as f32(scale) * f32(d) and rounds identically.
 //
-// Ragged shapes. All global loads go through buffer resources; a lane whose
-// row or group is out of range uses an out-of-range offset and receives
-// zeros, and staged activations of groups past K are zeros. A zero group
-// contributes +0 to a slot, which never changes it (a slot is never -0).
+// Ragged shapes. All global loads go through buffer resources, whose range
+// check returns zeros. Rows past N lie past the end of the weights; groups
+// past G read zeros (an out-of-range offset in a ragged last iteration, no
+// load in the padding iterations) against zero staged activations, so they
+// add +0, which never changes a slot (a slot is never -0).
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -77,10 +81,12 @@ __device__ __forceinline__ long mk64(int lo, int hi) {
     return (long)(((unsigned long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-// Staged activation layout in LDS: [t][j][Q*128 bytes] (the slice's groups of
-// iteration j for token t), followed by 32 zero bytes that lanes whose A
-// operand must be zero read instead.
+// Staged activation layout in LDS: [t][j][QS*128 bytes] (the slice's groups
+// of iteration j for token t) for j below J rounded up to whole blocks of P
+// stages (zeros past the last group), followed by kZeroBytes of zeros that
+// lanes whose A operand must be zero read instead.
 enum { kNarrow = 0, kWide = 1 };  // modes; a split layout is MODE = S in {2, 4}
+constexpr int kZeroBytes = 512;    // zero area after the staged activations
 
 template <int T, int MODE>
 __global__ __launch_bounds__(256) void w4a8_linear_kernel(
@@ -104,7 +110,8 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
     const int h = (lane & 15) >> 2;  // slot of this lane's A row
     const int tp = lane & 3;         // token of this lane's A row within a tile
     const int G = K >> 5;
-    const int J = (G + 15) >> 4;
+    const int J = (G + 15) >> 4;            // iterations of 16 groups
+    const int JP = (J + P - 1) / P * P;     // staged iterations: whole blocks of P stages
     const int NG = (N + ROWS - 1) / ROWS;
 
     int rg, p;
@@ -134,17 +141,38 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
     const auto rs = make_rsrc(wsg, (uint32_t)((int64_t)G * N * 2));
     const auto rx = make_rsrc(xq, (uint32_t)(T * K));
 
-    // Offsets are built without branches: an out-of-range lane ORs in the
-    // out-of-range bit, so loads issue unconditionally and in program order,
-    // which lets the compiler wait for exactly one stage at a time.
-    const uint32_t wbase = (uint32_t)row * (uint32_t)(K / 2);
-    auto load_stage = [&](WStage<Q>& st, int j) {
+    // Stage loads carry almost no bounds logic. A row past N starts past the
+    // end of the weights, so its loads return zeros. Iterations past the
+    // last one (the pipeline's look-ahead and the padding of the last block)
+    // load nothing: their stages are zeroed, and their staged activations are
+    // zeros, so they add +0, which never changes a slot. Only in a ragged
+    // last iteration (G not a multiple of 16) do lanes past G take an
+    // out-of-range offset. The branches are uniform. Every offset is below
+    // 2^32: the weights and scales are each under 2^31 bytes.
+    const uint32_t wlane = (uint32_t)row * (uint32_t)(K / 2) + 16u * (uint32_t)(4 * quad0 + q);
+    const uint32_t slane = ((uint32_t)(4 * quad0 + q) * (uint32_t)N + (uint32_t)row) * 2u;
+    const bool ragged = (G & 15) != 0;
+    auto load_fast = [&](WStage<Q>& st, int j) {  // j < J, and not a ragged last iteration
+        const uint32_t wo = wlane + 256u * (uint32_t)j;
+        const uint32_t so = slane + 32u * (uint32_t)N * (uint32_t)j;
 #pragma unroll
         for (int qq = 0; qq < Q; qq++) {
-            const int g = 16 * j + 4 * (quad0 + qq) + q;
-            const uint32_t bad = (uint32_t)(!(row_ok && g < G)) << 31;
-            st.w[qq] = load16(rw, (wbase + 16u * (uint32_t)g) | bad);
-            st.s[qq] = load2(rs, (((uint32_t)g * (uint32_t)N + (uint32_t)row) * 2u) | bad);
+            st.w[qq] = load16(rw, wo + 64u * (uint32_t)qq);
+            st.s[qq] = load2(rs, so + 8u * (uint32_t)N * (uint32_t)qq);
+        }
+    };
+    // Checked loads for the last block or two: past the last iteration the
+    // whole wave takes the out-of-range bit (the loads return zeros without
+    // touching memory); in a ragged last iteration, the lanes past G do.
+    auto load_stage = [&](WStage<Q>& st, int j) {
+        const uint32_t wo = wlane + 256u * (uint32_t)j;
+        const uint32_t so = slane + 32u * (uint32_t)N * (uint32_t)j;
+        const uint32_t past = j >= J ? kOOB : 0u;
+#pragma unroll
+        for (int qq = 0; qq < Q; qq++) {
+            const uint32_t bad = past | ((uint32_t)(16 * j + 4 * (quad0 + qq) + q >= G) << 31);
+            st.w[qq] = load16(rw, (wo + 64u * (uint32_t)qq) | bad);
+            st.s[qq] = load2(rs, (so + 8u * (uint32_t)N * (uint32_t)qq) | bad);
         }
     };
 
@@ -155,31 +183,60 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Stage the slice's activations: all loads of a round first, then the
-    // LDS writes, so a round costs one L2 round trip.
-    const int nchunks = T * J * QS * 8;  // 16-byte chunks
-    constexpr int U = 8;
-    for (int base = 0; base < nchunks; base += 256 * U) {
-        v4i v[U];
+    // Stage the slice's activations in rounds of U chunks per thread; the
+    // loads of round r + 1 are issued before the LDS writes of round r, so
+    // the rounds' L2 round trips overlap. Inside every 8-input chunk the
+    // codes are stored as inputs 0, 2, 4, 6, 1, 3, 5, 7: the order in which
+    // the nibble decode below produces the weights, so the integer dot pairs
+    // the same inputs (an exact integer sum in any order).
+    const int nchunks = T * JP * QS * 8;  // 16-byte chunks
+    // A narrow workgroup has its CU to itself and may hold 16 chunks per
+    // round; chunks past the row are skipped by uniform branches, not loaded.
+    constexpr int U = MODE == kNarrow && T >= 4 ? 16 : 8;
+    auto stage_load = [&](v4i (&v)[U], int base) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            if (base + u * 256 >= nchunks) break;
             const int i = base + u * 256 + tid;
             const int c = i % (QS * 8);
             const int tj = i / (QS * 8);
-            const int j = tj % J;
-            const int t = tj / J;
+            const int j = tj % JP;
+            const int t = tj / JP;
             const int g = 16 * j + 4 * p * QS + (c >> 1);
             const bool ok = i < nchunks && g < G;
             v[u] = load16(rx, ((uint32_t)(t * K + 32 * g + 16 * (c & 1))) | ((uint32_t)!ok << 31));
         }
+    };
+    auto stage_store = [&](const v4i (&v)[U], int base) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            if (base + u * 256 >= nchunks) break;
             const int i = base + u * 256 + tid;
-            if (i < nchunks) *reinterpret_cast<v4i*>(act + 16 * i) = v[u];
+            if (i < nchunks) {
+                const v4i a = v[u];
+                const v4i e = {(int)__builtin_amdgcn_perm(a[1], a[0], 0x06040200u),
+                               (int)__builtin_amdgcn_perm(a[1], a[0], 0x07050301u),
+                               (int)__builtin_amdgcn_perm(a[3], a[2], 0x06040200u),
+                               (int)__builtin_amdgcn_perm(a[3], a[2], 0x07050301u)};
+                *reinterpret_cast<v4i*>(act + 16 * i) = e;
+            }
+        }
+    };
+    {
+        v4i va[U], vb[U];
+        stage_load(va, 0);
+        for (int base = 0; base < nchunks; base += 512 * U) {
+            const bool more = base + 256 * U < nchunks;
+            if (more) stage_load(vb, base + 256 * U);
+            stage_store(va, base);
+            if (!more) break;
+            if (base + 512 * U < nchunks) stage_load(va, base + 512 * U);
+            stage_store(vb, base + 256 * U);
         }
     }
+    // zeros read by lanes whose A operand is zero (at most Q*128 bytes on)
     const int zero_off = nchunks * 16;
-    if (tid < 2) *reinterpret_cast<v4i*>(act + zero_off + 16 * tid) = v4i{0, 0, 0, 0};
+    if (tid < kZeroBytes / 16) *reinterpret_cast<v4i*>(act + zero_off + 16 * tid) = v4i{0, 0, 0, 0};
     __syncthreads();
 
     float acc[Q][T];
@@ -188,25 +245,34 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
 #pragma unroll
         for (int t = 0; t < T; t++) acc[qq][t] = 0.0f;
 
-    const bool a_active = (q == h);
+    // A operand addresses: token t = 4tt + tp of slot h, advanced by one
+    // staged iteration per j; lanes whose A row is zero stay on the zeros.
+    int abase[TT], astep[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; tt++) {
+        const int t = 4 * tt + tp;
+        const bool ok = q == h && t < T;
+        abase[tt] = ok ? (t * JP * QS + (quad0 - p * QS)) * 128 + h * 32 : zero_off;
+        astep[tt] = ok ? QS * 128 : 0;
+    }
     auto compute = [&](const WStage<Q>& stg, int j) {
 #pragma unroll
         for (int qq = 0; qq < Q; qq++) {
+            // u = q + 8 in each nibble: flipping bit 3 gives q in 4-bit two's
+            // complement; in the high half of a byte it is the int8 16q.
+            // Even inputs come from the low nibbles, odd from the high ones.
             long b[4];
 #pragma unroll
             for (int c = 0; c < 4; c++) {
-                const unsigned W = (unsigned)stg.w[qq][c] ^ 0x88888888u;
-                const unsigned lo = (W << 4) & 0xF0F0F0F0u;  // even inputs, as 16q
-                const unsigned hi = W & 0xF0F0F0F0u;         // odd inputs, as 16q
-                b[c] = mk64((int)__builtin_amdgcn_perm(hi, lo, 0x05010400u),
-                            (int)__builtin_amdgcn_perm(hi, lo, 0x07030602u));
+                const unsigned W = (unsigned)stg.w[qq][c];
+                const unsigned lo = ((W << 4) ^ 0x80808080u) & 0xF0F0F0F0u;  // inputs 0, 2, 4, 6
+                const unsigned hi = (W ^ 0x80808080u) & 0xF0F0F0F0u;         // inputs 1, 3, 5, 7
+                b[c] = mk64((int)lo, (int)hi);
             }
             v4i a0[TT], a1[TT];
 #pragma unroll
             for (int tt = 0; tt < TT; tt++) {
-                const int t = 4 * tt + tp;
-                const bool ok = a_active && t < T && j < J;
-                const int off = ok ? ((t * J + j) * QS + (quad0 - p * QS) + qq) * 128 + h * 32 : zero_off;
+                const int off = abase[tt] + j * astep[tt] + qq * 128;
                 a0[tt] = *reinterpret_cast<const v4i*>(act + off);
                 a1[tt] = *reinterpret_cast<const v4i*>(act + off + 16);
             }
@@ -230,10 +296,23 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
         }
     };
 
-    // P stages in flight; stages past the last group read zeros and add +0,
-    // so the loop runs a whole number of P-blocks with no guards. The
+    // P stages in flight. The steady loop's look-ahead loads are all plain
+    // (in range, not a ragged last iteration); the last block or two take the
+    // checked loads. Stages past the last iteration read zeros and their
+    // staged activations are zeros, so the final block adds +0 for them. The
     // scheduling barriers keep each stage's use ahead of its refill.
-    for (int j0 = 0; j0 < J; j0 += P) {
+    const int Jsafe = ragged ? J - 1 : J;
+    int j0 = 0;
+    for (; j0 + 2 * P <= Jsafe; j0 += P) {
+#pragma unroll
+        for (int pp = 0; pp < P; pp++) {
+            compute(st[pp], j0 + pp);
+            __builtin_amdgcn_sched_barrier(0);
+            load_fast(st[pp], j0 + pp + P);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    for (; j0 < J; j0 += P) {
 #pragma unroll
         for (int pp = 0; pp < P; pp++) {
             compute(st[pp], j0 + pp);
@@ -315,8 +394,10 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
 // Staged activation bytes of a workgroup in a given mode.
 inline size_t linear_lds_bytes(int T, int K, int mode) {
     const int J = (K / 32 + 15) / 16;
+    const int P = mode == kNarrow ? SPECV_NARROW_STAGES : SPECV_LINEAR_STAGES;
+    const int JP = (J + P - 1) / P * P;
     const int qs = (mode == kNarrow || mode == kWide) ? 4 : 4 / mode;
-    return (size_t)T * J * qs * 128 + 32;
+    return (size_t)T * JP * qs * 128 + kZeroBytes;
 }
 
 constexpr size_t kLdsBudget = 150 * 1024;
