@@ -40,8 +40,8 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "d406c62cddf1d5142f918e1128ff124c5da2f3aeabe4a3b984fbe3b08fd955c6",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33646738}
+LINEAR_TRAFFIC = {"source_sha256": "62f1122edbe63826659b1ead0da95cb96827db2d43d11e3f2ce1b0144c591ffe",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33739484}
 
 
 def linear_traffic(T, workload):
