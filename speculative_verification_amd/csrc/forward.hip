@@ -50,10 +50,34 @@ __device__ __forceinline__ float det_exp(float x) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + det_exp(-g)); }
 
-// Sum of one value per lane over 16 aligned lanes, in the tree order.
+// Value of another lane of the same 16-lane row, by a DPP control: 0xB1 and
+// 0x4E are the quad permutes of lane ^ 1 and lane ^ 2, 0x141 mirrors each
+// half row (l <-> 7 - l), 0x140 the whole row (l <-> 15 - l).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
+}
+
+// Sum of one value per lane over 16 aligned lanes, in the tree order. After
+// the xor-1 and xor-2 levels every lane of a quad holds the quad's sum, so the
+// half-row mirror brings each lane the other quad's sum (level w = 4) and the
+// row mirror the other half's (w = 8): every lane ends with the same bits,
+// the adjacent-pair tree.
 __device__ __forceinline__ float tree16(float v) {
-#pragma unroll
-    for (int w = 1; w < 16; w <<= 1) v = v + __shfl_xor(v, w, 16);
+    v = v + dpp_f32<0xB1>(v);
+    v = v + dpp_f32<0x4E>(v);
+    v = v + dpp_f32<0x141>(v);
+    v = v + dpp_f32<0x140>(v);
+    return v;
+}
+
+// Max over 16 aligned lanes (order-free), same exchanges as tree16.
+__device__ __forceinline__ float max16(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
     return v;
 }
 
@@ -72,7 +96,9 @@ constexpr int kMaxNodes = 16;
 
 // Block-wide max of non-negative values over kRowThreads threads (order-free).
 __device__ __forceinline__ float block_max(float a, float* red) {
-    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    a = max16(a);
+    a = fmaxf(a, __shfl_xor(a, 16, 64));
+    a = fmaxf(a, __shfl_xor(a, 32, 64));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
     float r = red[0];
@@ -124,17 +150,13 @@ __device__ void zero_row(int8_t* xrow, float* xs_i, int K) {
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// Depth of node i from an LDS copy of the parent array (a node whose parent
-// breaks the topological order counts as a root).
-__device__ __forceinline__ int lds_depth(const int* s_par, int i) {
-    int d = 0;
-    for (int x = i; x > 0 && d < kMaxNodes;) {
-        const int p = s_par[x];
-        if (p < 0 || p >= x) break;
-        x = p;
-        d++;
-    }
-    return d;
+// Tree info of a step, written once by the embedding kernel: depth[i], then
+// anc[i][t] = the node at depth t on the path from the root to node i
+// (anc[i][depth[i]] = i). A node whose parent breaks the topological order
+// counts as a root.
+constexpr int kTreeInfoInts = kMaxNodes + kMaxNodes * kMaxNodes;
+__device__ __forceinline__ const int32_t* tinfo_anc(const int32_t* tinfo, int i) {
+    return tinfo + kMaxNodes + i * kMaxNodes;
 }
 
 // ---------------------------------------------------------------- kernels
@@ -142,11 +164,15 @@ __device__ __forceinline__ int lds_depth(const int* s_par, int i) {
 // Embedding tied to the lm_head: h[i][k] = f32(scale[k/32][tok]) * code(tok, k)
 // (exact: an 11-bit significand times a 4-bit integer).
 __global__ __launch_bounds__(kFwdThreads) void embed_kernel(const int32_t* __restrict__ token,
+                                                            const int32_t* __restrict__ parent,
                                                             const uint8_t* __restrict__ wlm,
                                                             const uint16_t* __restrict__ slm, int H, int V,
-                                                            float* __restrict__ h, const specv_ctrl* ctrl) {
+                                                            float* __restrict__ h, int32_t* __restrict__ tinfo,
+                                                            const specv_ctrl* ctrl) {
+    __shared__ int s_par[kMaxNodes];
     const int i = blockIdx.x;
     if (ctrl->done || i >= ctrl->n_nodes) return;
+    if (threadIdx.x <= i) s_par[threadIdx.x] = parent[threadIdx.x];
     int tok = token[i];
     tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
     const uint8_t* wr = wlm + (size_t)tok * (H / 2);
@@ -154,6 +180,23 @@ __global__ __launch_bounds__(kFwdThreads) void embed_kernel(const int32_t* __res
         const uint8_t b = wr[k >> 1];
         const int code = ((k & 1) ? (b >> 4) : (b & 15)) - 8;
         h[(size_t)i * H + k] = f16_to_f32(slm[(size_t)(k >> 5) * V + tok]) * (float)code;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int d = 0;
+        for (int x = i; x > 0;) {
+            const int p = s_par[x];
+            if (p < 0 || p >= x) break;
+            x = p;
+            d++;
+        }
+        tinfo[i] = d;
+        int32_t* anc = tinfo + kMaxNodes + i * kMaxNodes;
+        for (int t = d, x = i; t >= 0; t--) {
+            anc[t] = x;
+            const int p = s_par[x];
+            x = (p >= 0 && p < x) ? p : 0;
+        }
     }
 }
 
@@ -260,18 +303,15 @@ __global__ __launch_bounds__(kRowThreads) void silu_mul_quant_kernel(const float
 // Rotary positions at L + depth(i) on the q and k heads of node i; k and v
 // go to the fp16 caches at physical row L + i of this layer.
 // Rotate-half: x'_d = x_d c - x_{d+h} s, x'_{d+h} = x_{d+h} c + x_d s.
-__global__ __launch_bounds__(64) void rope_kv_kernel(const float* __restrict__ qkv, const int32_t* __restrict__ parent,
+__global__ __launch_bounds__(64) void rope_kv_kernel(const float* __restrict__ qkv, const int32_t* __restrict__ tinfo,
                                                      const float* __restrict__ cos_t, const float* __restrict__ sin_t,
                                                      int max_pos, int hd, int nh, int nkv, float* __restrict__ qrot,
                                                      uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int layer,
                                                      int cap, const specv_ctrl* ctrl) {
-    __shared__ int s_par[kMaxNodes];
     const int i = blockIdx.x, head = blockIdx.y;
     if (ctrl->done || i >= ctrl->n_nodes) return;
     const int L = ctrl->committed_len;
-    if (threadIdx.x <= i) s_par[threadIdx.x] = parent[threadIdx.x];
-    __syncthreads();
-    const int pos = L + lds_depth(s_par, i);
+    const int pos = L + min(max(tinfo[i], 0), i);
     const int half = hd / 2, d = threadIdx.x;
     const int QKV = (nh + 2 * nkv) * hd;
     if (d >= half || pos >= max_pos || L + i >= cap) return;
@@ -304,162 +344,159 @@ constexpr int kMaxGroup = 16;     // query heads per KV head
 // 16-lane group over the LDS banks).
 inline __host__ __device__ int attn_vstride(int hd) { return hd + 8; }
 
-inline size_t attn_lds_bytes(int hpg, int hd) {
-    return (size_t)4 * hpg * (hd + kAttnChunk) + (size_t)2 * kAttnChunk * attn_vstride(hd);
+inline size_t attn_lds_bytes(int hpg, int hd) {  // dynamic part: the staged value rows
+    (void)hpg;
+    return (size_t)2 * kAttnChunk * attn_vstride(hd);
 }
 
 inline size_t merge_lds_bytes(int nh, int nchunk_max) { return (size_t)4 * nh * (nchunk_max + 1); }
 
-// One chunk of the visible sequence of one node, for all query heads of one
-// KV head, which therefore read each key and value of the chunk once.
-// Logical position j < L is cache row j; position L + t is the physical row
-// of the node's ancestor at depth t (the node itself last). Per head:
+// One chunk of the visible sequence of one node for one query head. Logical
+// position j < L is cache row j; position L + t is the physical row of the
+// node's ancestor at depth t (the node itself last). For the head:
 // s_j = R16_d(q_d * K_jd) * scale, m = max s_j, e_j = E(s_j - m),
 // l = R16_j(e_j), o_d = R16_j(e_j * V_jd), sums over the chunk's positions
 // in logical order. Output per (node, head, chunk): m, l, o[hd].
 //
-// Thread t owns position t of the chunk: its key row sits in registers as
-// fp32 and its value row is staged in LDS. For the value sums, lane s of a
-// 16-lane group takes R16 slot s (positions s, s+16, ... in order) of
-// HD/16 columns, and the group's xor butterfly adds the slots as the
+// One workgroup per (chunk, query head, node): the query heads that share a
+// KV head read the same rows, which the L2 serves after the first; one head
+// per workgroup keeps each workgroup's dependent chains short and gives the
+// chip more of them. Thread t owns position t of the chunk, its key row in
+// registers as fp32 and its value row staged in LDS. The query is loaded
+// first and committed rows right after it, so neither waits for the other;
+// only the tree positions wait for the ancestor list. For the value sums,
+// lane s of a 16-lane group takes R16 slot s (positions s, s+16, ... in
+// order) of HD/16 columns, and the group's butterfly adds the slots as the
 // index-order tree.
 template <int HD>
 __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     const float* __restrict__ qrot, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ parent, int layer, int cap, int nh, int nkv, float scale,
+    const int32_t* __restrict__ tinfo, int layer, int cap, int nh, int nkv, float scale,
     float* __restrict__ part, int nchunk_max, const specv_ctrl* ctrl) {
     constexpr int VS = HD + 8;
-    const int c = blockIdx.x, g = blockIdx.y, i = blockIdx.z, tid = threadIdx.x;
+    const int c = blockIdx.x, hq = blockIdx.y, i = blockIdx.z, tid = threadIdx.x;
+    const int depth_raw = tinfo[i];  // issued with the control loads (i < 16)
     if (ctrl->done || i >= ctrl->n_nodes) return;
     const int L = ctrl->committed_len;
     if (L + i >= cap) return;  // its rows were not written (no room left)
-    const int hpg = nh / nkv;
-    __shared__ int s_par[kMaxNodes];
-    __shared__ int anc[kMaxNodes];
-    __shared__ float wmax[kFwdThreads / 64][kMaxGroup];
-    __shared__ float mh[kMaxGroup];
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    float* qs = reinterpret_cast<float*>(smem);                      // [hpg][HD]
-    float* S = qs + hpg * HD;                                        // [hpg][256]
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(S + hpg * kAttnChunk);  // [256][VS]
-
-    if (tid <= i) s_par[tid] = parent[tid];
-    const float* qsrc = qrot + ((size_t)i * nh + g * hpg) * HD;
-    for (int x = tid; x < hpg * HD / 4; x += kFwdThreads)
-        *reinterpret_cast<float4*>(qs + 4 * x) = ld4(qsrc + 4 * x);
-    __syncthreads();
-    const int depth = lds_depth(s_par, i);
+    const int depth = min(max(depth_raw, 0), i);  // depth <= i in a topological tree
     const int len = L + depth + 1;
     const int j0 = c * kAttnChunk;
     if (j0 >= len) return;
     const int cnt = len - j0 < kAttnChunk ? len - j0 : kAttnChunk;
-    if (tid == 0) {
-        int x = i;
-        for (int t = depth; t >= 0; t--) {
-            anc[t] = x;
-            const int p = s_par[x];
-            x = (p >= 0 && p < x) ? p : 0;
-        }
-    }
-    __syncthreads();
+    const int g = hq / (nh / nkv);
+    __shared__ int anc[kMaxNodes];
+    __shared__ float qs[HD];
+    __shared__ float S[kAttnChunk];
+    __shared__ float s_m;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][VS]
 
+    if (tid < HD / 4) *reinterpret_cast<float4*>(qs + 4 * tid) = ld4(qrot + ((size_t)i * nh + hq) * HD + 4 * tid);
     const size_t plane = (((size_t)layer * nkv + g) * cap) * HD;
     const bool live = tid < cnt;
     const int j = j0 + tid;
-    const int row = live ? (j < L ? j : L + anc[j - L]) : 0;
-    float kf[HD];
-    if (live) {
-        uint4 kr[HD / 8], vr[HD / 8];
-        const uint4* ksrc = reinterpret_cast<const uint4*>(kc + plane + (size_t)row * HD);
-        const uint4* vsrc = reinterpret_cast<const uint4*>(vc + plane + (size_t)row * HD);
+    v4i kr[HD / 8], vr[HD / 8];
+    const bool early = live && j < L;
+    if (early) {
+        const v4i* ksrc = reinterpret_cast<const v4i*>(kc + plane + (size_t)j * HD);
+        const v4i* vsrc = reinterpret_cast<const v4i*>(vc + plane + (size_t)j * HD);
 #pragma unroll
         for (int t = 0; t < HD / 8; t++) {
             kr[t] = ksrc[t];
             vr[t] = vsrc[t];
         }
+    }
+    if (tid <= depth) anc[tid] = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
+    __syncthreads();
+    if (live && !early) {
+        const int row = L + anc[j - L];
+        const v4i* ksrc = reinterpret_cast<const v4i*>(kc + plane + (size_t)row * HD);
+        const v4i* vsrc = reinterpret_cast<const v4i*>(vc + plane + (size_t)row * HD);
 #pragma unroll
         for (int t = 0; t < HD / 8; t++) {
-            *reinterpret_cast<uint4*>(Vs + tid * VS + 8 * t) = vr[t];
-            const uint32_t wd[4] = {kr[t].x, kr[t].y, kr[t].z, kr[t].w};
+            kr[t] = ksrc[t];
+            vr[t] = vsrc[t];
+        }
+    }
+    // score of this thread's position
+    float sc = -__builtin_inff();
+    if (live) {
+        float slot[16];
+#pragma unroll
+        for (int s = 0; s < 16; s++) slot[s] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < HD / 8; t++) {
+            *reinterpret_cast<v4i*>(Vs + tid * VS + 8 * t) = vr[t];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                kf[8 * t + 2 * e] = f16_to_f32((uint16_t)(wd[e] & 0xffff));
-                kf[8 * t + 2 * e + 1] = f16_to_f32((uint16_t)(wd[e] >> 16));
+                const uint32_t wd = (uint32_t)kr[t][e];
+                const int d = 8 * t + 2 * e;
+                slot[d & 15] = slot[d & 15] + qs[d] * f16_to_f32((uint16_t)(wd & 0xffff));
+                slot[(d + 1) & 15] = slot[(d + 1) & 15] + qs[d + 1] * f16_to_f32((uint16_t)(wd >> 16));
             }
         }
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+            for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
+        sc = slot[0] * scale;
     }
-    // scores, then the chunk max of each head
-    for (int hh = 0; hh < hpg; hh++) {
-        float sc = -__builtin_inff();
-        if (live) {
-            float slot[16];
-#pragma unroll
-            for (int s = 0; s < 16; s++) slot[s] = 0.0f;
-#pragma unroll
-            for (int d0 = 0; d0 < HD; d0 += 16)
-#pragma unroll
-                for (int s = 0; s < 16; s++) slot[s] = slot[s] + qs[hh * HD + d0 + s] * kf[d0 + s];
-#pragma unroll
-            for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-                for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
-            sc = slot[0] * scale;
-        }
-        S[hh * kAttnChunk + tid] = sc;
-        // max over the chunk (order-free; only +0/-0 ties can differ, and a
-        // difference against either gives the same exp input up to its sign)
-        float a = sc;
-        for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-        if ((tid & 63) == 0) wmax[tid >> 6][hh] = a;
-    }
+    S[tid] = sc;
     __syncthreads();
-    for (int hh = 0; hh < hpg; hh++) {
-        const float m = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
-        S[hh * kAttnChunk + tid] = live ? det_exp(S[hh * kAttnChunk + tid] - m) : 0.0f;
-        if (tid == 0) mh[hh] = m;
-    }
+    // max over the chunk, taken by every 16-lane group for itself (order-free;
+    // only +0/-0 ties can differ, and a difference against either gives the
+    // same exp input up to its sign)
+    const int s = tid & 15, q = tid >> 4;
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < 16; k++)
+        if (s + 16 * k < cnt) m = fmaxf(m, S[s + 16 * k]);
+    m = max16(m);
+    __syncthreads();
+    S[tid] = live ? det_exp(sc - m) : 0.0f;
     __syncthreads();
 
-    float* out = part;  // [n][nh][nchunk_max][HD + 2]
-    const int stride = HD + 2;
-    // l = R16 over the chunk: 16 lanes per head, lane s sums positions s, s+16, ...
-    if (tid < hpg * 16) {
-        const int hh = tid >> 4, s = tid & 15;
-        float acc = 0.0f;
-        for (int p = s; p < cnt; p += 16) acc = acc + S[hh * kAttnChunk + p];
-        acc = tree16(acc);
-        if (s == 0) {
-            float* o = out + (((size_t)i * nh + g * hpg + hh) * nchunk_max + c) * stride;
-            o[0] = mh[hh];
-            o[1] = acc;
-        }
+    // Lane s of group q owns R16 slot s (positions s, s+16, ... in order) of
+    // l and of the columns 4q..4q+3 (group q + 16, ... for head dims above
+    // 64), read as one 8-byte word per position; the group's butterfly adds
+    // the slots as the index-order tree. Every group also sums l; group 0
+    // stores it.
+    float* o = part + (((size_t)i * nh + hq) * nchunk_max + c) * (HD + 2);
+    float e[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) e[k] = S[s + 16 * k];
+    float l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; k++)
+        if (s + 16 * k < cnt) l = l + e[k];
+    l = tree16(l);
+    if (tid == 0) {
+        o[0] = m;
+        o[1] = l;
     }
-    // o_d = R16 over the chunk of e_j * V_jd: lane s of group q owns slot s of
-    // columns q, q + 16, ... (HD/16 of them).
-    {
-        const int s = tid & 15, q = tid >> 4;
-        constexpr int NC = HD / 16;
-        float vv[NC][16];
+    constexpr int NB = (HD + 63) / 64;  // column blocks of 64 (16 groups x 4 columns)
 #pragma unroll
-        for (int m = 0; m < 16; m++) {
-            const int p = s + 16 * m;
+    for (int b = 0; b < NB; b++) {
+        const int d0 = 64 * b + 4 * q;
+        if (d0 >= HD) break;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int k = 0; k < NC; k++) vv[k][m] = p < cnt ? f16_to_f32(Vs[p * VS + q + 16 * k]) : 0.0f;
-        }
-        for (int hh = 0; hh < hpg; hh++) {
-            float e[16];
-#pragma unroll
-            for (int m = 0; m < 16; m++) e[m] = S[hh * kAttnChunk + s + 16 * m];
-#pragma unroll
-            for (int k = 0; k < NC; k++) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int m = 0; m < 16; m++)
-                    if (s + 16 * m < cnt) acc = acc + e[m] * vv[k][m];
-                acc = tree16(acc);
-                if (s == 0) out[(((size_t)i * nh + g * hpg + hh) * nchunk_max + c) * stride + 2 + q + 16 * k] = acc;
+        for (int k = 0; k < 16; k++) {
+            const int p = s + 16 * k;
+            if (p < cnt) {
+                const uint2 w = *reinterpret_cast<const uint2*>(Vs + p * VS + d0);
+                acc[0] = acc[0] + e[k] * f16_to_f32((uint16_t)(w.x & 0xffff));
+                acc[1] = acc[1] + e[k] * f16_to_f32((uint16_t)(w.x >> 16));
+                acc[2] = acc[2] + e[k] * f16_to_f32((uint16_t)(w.y & 0xffff));
+                acc[3] = acc[3] + e[k] * f16_to_f32((uint16_t)(w.y >> 16));
             }
         }
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[r] = tree16(acc[r]);
+        if (s == 0)
+#pragma unroll
+            for (int r = 0; r < 4; r++) o[2 + d0 + r] = acc[r];  // rows of HD + 2 floats: no vector store
     }
 }
 
@@ -469,11 +506,10 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
 // the output projection. The chunk weights are computed once per
 // (head, chunk) by 16 lanes per head and shared through LDS.
 __global__ __launch_bounds__(kRowThreads) void attn_merge_quant_kernel(
-    const float* __restrict__ part, const int32_t* __restrict__ parent, int nh, int hd, int nchunk_max,
+    const float* __restrict__ part, const int32_t* __restrict__ tinfo, int nh, int hd, int nchunk_max,
     int8_t* __restrict__ xq, float* __restrict__ xs, const specv_ctrl* ctrl) {
     extern __shared__ float wts[];  // [nh][nchunk_max] chunk weights, then l[nh]
     __shared__ float red[kRowThreads / 64];
-    __shared__ int s_par[kMaxNodes];
     const int i = blockIdx.x, tid = threadIdx.x;
     const int K = nh * hd;
     if (ctrl->done) return;
@@ -482,9 +518,7 @@ __global__ __launch_bounds__(kRowThreads) void attn_merge_quant_kernel(
         return;
     }
     float* lsum = wts + (size_t)nh * nchunk_max;
-    if (tid <= i) s_par[tid] = parent[tid];
-    __syncthreads();
-    const int len = ctrl->committed_len + lds_depth(s_par, i) + 1;
+    const int len = ctrl->committed_len + min(max(tinfo[i], 0), i) + 1;
     const int nch_len = (len + kAttnChunk - 1) / kAttnChunk;
     const int nch = nch_len < nchunk_max ? nch_len : nchunk_max;
     const int stride = hd + 2;
@@ -493,7 +527,7 @@ __global__ __launch_bounds__(kRowThreads) void attn_merge_quant_kernel(
         const float* ph = part + ((size_t)i * nh + hh) * nchunk_max * stride;
         float m = -__builtin_inff();
         for (int c = s; c < nch; c += 16) m = fmaxf(m, ph[(size_t)c * stride]);
-        for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+        m = max16(m);
         float acc = 0.0f;
         for (int c = s; c < nch; c += 16) {
             const float wc = det_exp(ph[(size_t)c * stride] - m);
@@ -558,6 +592,7 @@ StepLayout step_layout(const specv_model* m, int n) {
     s.logits = take(4 * n * V);
     s.argmax_part = take(tree_argmax_accept_workspace(V, n));
     s.tree = take(4 * 16 * 4);  // parent, token, argmax, path for up to 16 nodes
+    s.tinfo = take(4 * kTreeInfoInts);  // depths and ancestor lists of the step's tree
     s.wcounter = take(4);
     size_t lin = 0;
     for (size_t Nk : {QKV, H, 2 * I}) lin = std::max(lin, w4a8_linear_workspace(n, (int)Nk, (int)H));
@@ -576,7 +611,7 @@ int validate_model(const specv_model* m) {
         m->n_heads % m->n_kv_heads || m->n_heads / m->n_kv_heads > kMaxGroup || m->head_dim < 16 ||
         m->head_dim % 16 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
         m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || !(m->eps >= 0.0f) ||
-        attn_lds_bytes(m->n_heads / m->n_kv_heads, m->head_dim) > 64 * 1024 ||
+        attn_lds_bytes(m->n_heads / m->n_kv_heads, m->head_dim) > 150 * 1024 ||
         (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024 ||
         (size_t)m->n_heads * m->head_dim > (size_t)kMergeRegs * kRowThreads ||
         merge_lds_bytes(m->n_heads, (m->kv_capacity + kAttnChunk - 1) / kAttnChunk) > 64 * 1024)
@@ -598,14 +633,24 @@ int validate_model(const specv_model* m) {
     } while (0)
 
 static int launch_attn_chunk(int hd, dim3 grid, size_t lds, hipStream_t s, const float* qrot,
-                             const uint16_t* kc, const uint16_t* vc, const int32_t* parent, int layer, int cap,
+                             const uint16_t* kc, const uint16_t* vc, const int32_t* tinfo, int layer, int cap,
                              int nh, int nkv, float scale, float* part, int nchunk_max, const specv_ctrl* ctrl) {
     switch (hd) {
 #define SPECV_ATTN(HDV)                                                                                   \
-    case HDV:                                                                                             \
-        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), lds, s, qrot, kc, vc, parent, \
+    case HDV: {                                                                                           \
+        static size_t enabled = 64 * 1024; /* dynamic LDS above 64 KB is enabled per kernel */          \
+        if (lds > enabled) {                                                                              \
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_chunk_kernel<HDV>),               \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) { \
+                (void)hipGetLastError();                                                                  \
+                return SPECV_E_HIP;                                                                       \
+            }                                                                                             \
+            enabled = lds;                                                                                \
+        }                                                                                                 \
+        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), lds, s, qrot, kc, vc, tinfo, \
                            layer, cap, nh, nkv, scale, part, nchunk_max, ctrl);                         \
-        return launch_status();
+        return launch_status();                                                                           \
+    }
         SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
         SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
 #undef SPECV_ATTN
@@ -625,11 +670,13 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     float* qrot = reinterpret_cast<float*>(ws + lay.qrot);
     float* attn = reinterpret_cast<float*>(ws + lay.attn);
     float* gu = reinterpret_cast<float*>(ws + lay.gu);
+    int32_t* tinfo = reinterpret_cast<int32_t*>(ws + lay.tinfo);
     void* lin = lay.linear_bytes ? ws + lay.linear : nullptr;
     const size_t linb = lay.linear_bytes;
     const float scale = (float)(1.0 / std::sqrt((double)hd));
 
-    hipLaunchKernelGGL(embed_kernel, dim3(n), dim3(kFwdThreads), 0, s, token, m->w_lm, m->s_lm, H, V, h, ctrl);
+    hipLaunchKernelGGL(embed_kernel, dim3(n), dim3(kFwdThreads), 0, s, token, parent, m->w_lm, m->s_lm, H, V, h,
+                       tinfo, ctrl);
     SPECV_TRY(launch_status());
     for (int l = 0; l < m->n_layers; l++) {
         const uint8_t* wqkv = m->w_qkv + (size_t)l * QKV * (H / 2);
@@ -645,14 +692,14 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
                            l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, H, m->eps, xq, xs, ctrl);
         SPECV_TRY(launch_status());
         SPECV_TRY(w4a8_linear_T(wqkv, sqkv, xq, xs, qkv, n, QKV, H, lin, linb, s));
-        hipLaunchKernelGGL(rope_kv_kernel, dim3(n, nh + nkv), dim3(64), 0, s, qkv, parent, m->rope_cos,
+        hipLaunchKernelGGL(rope_kv_kernel, dim3(n, nh + nkv), dim3(64), 0, s, qkv, tinfo, m->rope_cos,
                            m->rope_sin, m->max_pos, hd, nh, nkv, qrot, m->k_cache, m->v_cache, l, cap, ctrl);
         SPECV_TRY(launch_status());
-        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nkv, n), attn_lds_bytes(nh / nkv, hd), s, qrot,
-                                    m->k_cache, m->v_cache, parent, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
+        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nh, n), attn_lds_bytes(nh / nkv, hd), s, qrot,
+                                    m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
                                     ctrl));
         hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kRowThreads),
-                           merge_lds_bytes(nh, lay.nchunk_max), s, attn, parent, nh, hd, lay.nchunk_max, xq, xs,
+                           merge_lds_bytes(nh, lay.nchunk_max), s, attn, tinfo, nh, hd, lay.nchunk_max, xq, xs,
                            ctrl);
         SPECV_TRY(launch_status());
         SPECV_TRY(w4a8_linear_T(wo, so, xq, xs, delta, n, H, A, lin, linb, s));
