@@ -8,7 +8,8 @@ a Llama-3-8B-shaped model and then accepts on the GPU:
   model fuses this quantisation into the kernel producing the activations);
   per layer (32): qkv (6144x4096, q/k/v rows concatenated), o (4096x4096),
   gate_up (28672x4096, gate/up rows concatenated), down (4096x14336);
-  then lm_head (128256x4096), argmax + tree acceptance, and KV compaction of
+  then lm_head (128256x4096) with the fused argmax epilogue (the logits are
+  not written), tree acceptance, and KV compaction of
   the accepted rows (32 layers x 8 KV heads x head_dim 128).
 Weights are int4 in groups of 32 with fp16 scales U(0.005, 0.02). The
 weights of 4 distinct generated layer sets are copied into 32 separate layer
@@ -18,7 +19,7 @@ once as a HIP graph and replayed.
 
 Prints one JSON line (rank 0). `value` is the algorithmic bytes of the step
 (weights, activation codes and scales, linear outputs, quantisation traffic,
-logits read by the argmax, compaction moves) divided by the step time, in
+argmax pairs, compaction moves) divided by the step time, in
 GB/s, at T = 8.
 """
 from __future__ import annotations
@@ -40,8 +41,8 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "62f1122edbe63826659b1ead0da95cb96827db2d43d11e3f2ce1b0144c591ffe",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33739484}
+LINEAR_TRAFFIC = {"source_sha256": "1cd82c1ec6fcfc12fe9fed9e35a2b208bbe1b6a278716c4e8fa564640c99edae",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33718697}
 
 
 def linear_traffic(T, workload):
@@ -74,6 +75,13 @@ def weight_bytes(N, K):
 def linear_bytes(T, N, K):
     """Algorithmic bytes of one W4A8 linear launch."""
     return weight_bytes(N, K) + T * K + 4 * T + 4 * T * N
+
+
+def argmax_linear_bytes(T, N, K, chunks):
+    """Algorithmic bytes of the fused lm_head + argmax launch: weights,
+    activation codes and scales, and one (value, index) pair per token and
+    workgroup (the logits are not written)."""
+    return weight_bytes(N, K) + T * K + 4 * T + 8 * T * chunks
 
 
 def quant_bytes(T, K):
@@ -134,7 +142,6 @@ class Model:
         self.act_T = None
         self.y = {nm: torch.empty((Tmax * N,), dtype=torch.float32, device=dev)
                   for nm, N, _ in layer_linears(m)}
-        self.logits = torch.empty((Tmax * m["vocab"],), dtype=torch.float32, device=dev)
         # size the shared split-K workspace once, before any graph capture
         for T in range(1, Tmax + 1):
             for _, N, K in layer_linears(m) + [("lm_head", m["vocab"], m["hidden"])]:
@@ -144,7 +151,8 @@ class Model:
         self.cap = self.L0 + 4096
         self.kc = torch.zeros((m["layers"], m["kv_heads"], self.cap, m["head_dim"]), dtype=torch.int16, device=dev)
         self.vc = torch.zeros_like(self.kc)
-        self.ws_acc = torch.empty(sv.argmax_accept_workspace_bytes(m["vocab"], 16), dtype=torch.uint8, device=dev)
+        self.ws_lmarg = torch.empty(int(sv.LIB.w4a8_linear_argmax_workspace(Tmax, m["vocab"], m["hidden"])),
+                                    dtype=torch.uint8, device=dev)
         self.argmax = torch.empty(16, dtype=torch.int32, device=dev)
         self.path = torch.zeros(16, dtype=torch.int32, device=dev)
         self.stats = torch.zeros(3, dtype=torch.int32, device=dev)
@@ -199,26 +207,35 @@ class Model:
             if events is not None:   # kernel begin/end timestamps of this launch
                 e0, e1 = timing_events(torch)
                 sv.check("specv_time_next_linear", sv.LIB.specv_time_next_linear(e0.cuda_event, e1.cuda_event))
-            sv.linear(wpair[0], wpair[1], xq, xs, y[: T * N].view(T, N))
+            if y is None:            # lm_head: fused argmax epilogue, logits not written
+                sv.linear_argmax(wpair[0], wpair[1], xq, xs, argmax=self.argmax[:T], workspace=self.ws_lmarg)
+                nb = argmax_linear_bytes(T, N, K, self.lm_chunks(T))
+            else:
+                sv.linear(wpair[0], wpair[1], xq, xs, y[: T * N].view(T, N))
+                nb = linear_bytes(T, N, K)
             if events is not None:
-                events.append((e0, e1, linear_bytes(T, N, K), name))
+                events.append((e0, e1, nb, name))
 
         for l, lay in enumerate(layers):
             for nm, N, K in layer_linears(m):
                 lin(nm, lay[nm], K, N, self.y[nm], self.in_index[l][nm])
-        lin("lm_head", lm, m["hidden"], m["vocab"], self.logits, self.lm_index)
-        sv.tree_argmax_accept(self.logits[: T * m["vocab"]].view(T, m["vocab"]), self.parent, self.token,
-                              self.ctrl, argmax=self.argmax, path=self.path, stats=self.stats,
-                              ring=self.ring, workspace=self.ws_acc)
+        lin("lm_head", lm, m["hidden"], m["vocab"], None, self.lm_index)
+        sv.tree_accept(self.argmax[:T], self.parent, self.token, self.ctrl, path=self.path, stats=self.stats,
+                       ring=self.ring)
         sv.kv_compact(self.kc, self.vc, self.path, self.ctrl)
+
+    def lm_chunks(self, T):
+        """(value, index) pairs per token of the fused lm_head: one per workgroup."""
+        m = self.m
+        return int(self.sv.LIB.w4a8_linear_argmax_workspace(T, m["vocab"], m["hidden"])) // (8 * T)
 
     def step_bytes(self, T, m_acc):
         m = self.m
         b = 0
         for _, N, K in layer_linears(m):
             b += m["layers"] * (linear_bytes(T, N, K) + quant_bytes(T, K))
-        b += linear_bytes(T, m["vocab"], m["hidden"]) + quant_bytes(T, m["hidden"])
-        b += 4 * T * m["vocab"]                                         # argmax reads the logits
+        b += argmax_linear_bytes(T, m["vocab"], m["hidden"], self.lm_chunks(T)) + quant_bytes(T, m["hidden"])
+        b += 8 * T * self.lm_chunks(T)                                  # the argmax finishing pass reads the pairs
         b += 2 * 2 * m_acc * m["layers"] * m["kv_heads"] * m["head_dim"] * 2  # K and V rows read + written
         return b
 
@@ -230,7 +247,7 @@ class Model:
 
 def run_T(model, T, steps, warmup, torch):
     """Graph-captured steps at T nodes: returns ms per step, accepted m,
-    and whether graph replays reproduce the eager logits bit for bit."""
+    and whether graph replays reproduce the eager outputs bit for bit."""
     copies = len(model.copies)
     model.prepare_acts(T)
     model.set_tree(T)
@@ -241,7 +258,10 @@ def run_T(model, T, steps, warmup, torch):
     model.reset_ctrl(T)
     model.step(T)
     torch.cuda.synchronize()
-    eager_logits = model.logits[: T * model.m["vocab"]].clone()
+    def snapshot():   # every output the replays must reproduce bit for bit
+        return torch.cat([model.argmax[:T].view(torch.float32)] +
+                         [model.y[nm][: T * N] for nm, N, _ in layer_linears(model.m)])
+    eager_out = snapshot().clone()
     m_acc = int(model.ctrl[4].item())
 
     graphs = []
@@ -261,7 +281,7 @@ def run_T(model, T, steps, warmup, torch):
     for i in range(warmup):
         graphs[i % copies].replay()
     torch.cuda.synchronize()
-    replay_ok = bool(torch.equal(model.logits[: T * model.m["vocab"]], eager_logits))
+    replay_ok = snapshot().view(torch.int32).equal(eager_out.view(torch.int32))
     model.reset_ctrl(T)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -271,7 +291,7 @@ def run_T(model, T, steps, warmup, torch):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    replay_ok = replay_ok and bool(torch.equal(model.logits[: T * model.m["vocab"]], eager_logits))
+    replay_ok = replay_ok and snapshot().view(torch.int32).equal(eager_out.view(torch.int32))
     del graphs
     return ms, m_acc, replay_ok
 
@@ -452,7 +472,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{args.workload}-shaped verify step: {MODELS[args.workload]['layers']} x (qkv, o, "
-                         f"gate_up, down) + lm_head W4A8 g32, argmax + tree accept + KV compaction, "
+                         f"gate_up, down) + lm_head W4A8 g32 with fused argmax, tree accept + KV compaction, "
                          f"T={args.T} tree nodes, HIP-graph replay"),
             "T": args.T,
             "weight_bytes": model.weight_bytes_total(),

@@ -130,6 +130,27 @@ int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const
                   size_t workspace_bytes, void* stream);
 
 /*
+ * W4A8 linear with a fused argmax epilogue ([P1], GPU-Resident Speculation
+ * Loop: the greedy prediction of each tree node; here fused into the lm_head
+ * as the ranked next step of the hot path). Computes the same y as
+ * w4a8_linear_T and argmax[t] = the lowest n with y[t][n] = max_n y[t][n]
+ * (IEEE comparison, -0 == +0; NaN outputs are a precondition violation).
+ * Each workgroup reduces its rows to one (value, index) pair per token, so
+ * the outputs need not be written:
+ *   y        nullable fp32 [T][N]: written only when non-NULL.
+ *   argmax   int32 [T] out.
+ *   workspace  w4a8_linear_argmax_workspace(T, N, K) bytes, 8-byte aligned,
+ *              no initialisation needed (the per-workgroup pairs).
+ * Shapes as w4a8_linear_T with N >= 1, limited to those whose staged
+ * activations fit one workgroup (w4a8_linear_argmax_workspace returns 0 and
+ * the call SPECV_E_SHAPE otherwise; T * K <= 37888 always fits).
+ */
+size_t w4a8_linear_argmax_workspace(int32_t T, int32_t N, int32_t K);
+int w4a8_linear_argmax_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
+                         float* y, int32_t* argmax, int32_t T, int32_t N, int32_t K, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * Timing diagnostic (not part of the computation): the next w4a8_linear_T
  * launch made by the calling host thread records `start_event` and
  * `stop_event` (hipEvent_t created with timing) at the beginning and end of
@@ -171,6 +192,16 @@ int tree_argmax_accept(const float* logits, int64_t V, int32_t n_max,
                        int32_t* argmax, int32_t* path, specv_ctrl* ctrl,
                        specv_step_stats* stats, int32_t* ring, int32_t ring_cap,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Tree acceptance from the greedy prediction of each node (for example from
+ * w4a8_linear_argmax_T): the same acceptance, commit, ring and statistics as
+ * tree_argmax_accept, reading argmax int32 [n_max] instead of logits.
+ * n_max in [1, 16].
+ */
+int tree_accept(const int32_t* argmax, int32_t n_max, const int32_t* parent, const int32_t* token,
+                int32_t* path, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* ring,
+                int32_t ring_cap, void* stream);
 
 /*
  * KV-cache compaction of the accepted path ([P1], GPU-Resident Speculation

@@ -89,6 +89,47 @@ def linear(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tenso
     return y
 
 
+def linear_argmax(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
+                  y: torch.Tensor | None = None, argmax: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """argmax int32 [T] of the W4A8 linear's outputs (w4a8_linear_argmax_T);
+    the outputs are written to y only when y is given."""
+    N = wq.shape[0]
+    T, K = xq.shape
+    if wq.shape != (N, K // 2) or ws.shape != (K // 32, N) or xs.shape != (T,):
+        raise ValueError("shape mismatch between wq, ws (group-major), xq and xs")
+    if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
+        raise TypeError("ws must hold fp16 bit patterns")
+    need = int(LIB.w4a8_linear_argmax_workspace(T, N, K))
+    if need == 0:
+        raise ValueError("shape not supported by the fused argmax linear")
+    dev = xq.device
+    argmax = torch.empty(T, dtype=torch.int32, device=dev) if argmax is None else argmax
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    yp = _dev(y, "y", torch.float32) if y is not None else None
+    check("w4a8_linear_argmax_T", LIB.w4a8_linear_argmax_T(
+        _dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype), _dev(xq, "xq", torch.int8),
+        _dev(xs, "xs", torch.float32), yp, _dev(argmax, "argmax", torch.int32), T, N, K,
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream()))
+    return argmax
+
+
+def tree_accept(argmax: torch.Tensor, parent: torch.Tensor, token: torch.Tensor, ctrl: torch.Tensor,
+                path: torch.Tensor | None = None, stats: torch.Tensor | None = None,
+                ring: torch.Tensor | None = None) -> torch.Tensor:
+    """Acceptance from each node's greedy prediction (tree_accept); returns path."""
+    n_max = argmax.numel()
+    path = torch.zeros(n_max, dtype=torch.int32, device=argmax.device) if path is None else path
+    st = _dev(stats, "stats", torch.int32) if stats is not None else None
+    rp = _dev(ring, "ring", torch.int32) if ring is not None else None
+    check("tree_accept", LIB.tree_accept(
+        _dev(argmax, "argmax", torch.int32), n_max, _dev(parent, "parent", torch.int32),
+        _dev(token, "token", torch.int32), _dev(path, "path", torch.int32), _dev(ctrl, "ctrl", torch.int32),
+        st, rp, ring.numel() if ring is not None else 0, _stream()))
+    return path
+
+
 def argmax_accept_workspace_bytes(V: int, n_max: int) -> int:
     return int(LIB.tree_argmax_accept_workspace(V, n_max))
 

@@ -23,15 +23,6 @@ constexpr int kArgThreads = 256;
 constexpr int kArgChunk = 4096;  // logits per partial workgroup
 constexpr int kMaxNodes = 16;
 
-struct Best {
-    float v;
-    int i;
-};
-
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-    return v > bv || (v == bv && i < bi);
-}
-
 __device__ __forceinline__ void wave_best(float& v, int& i, int width) {
     for (int off = width / 2; off >= 1; off >>= 1) {
         const float ov = __shfl_xor(v, off, width);
@@ -76,7 +67,8 @@ __global__ __launch_bounds__(kArgThreads) void argmax_partial_kernel(
 }
 
 __global__ __launch_bounds__(kArgThreads) void accept_kernel(
-    const Best* __restrict__ part, int chunks, int n_max, const int32_t* __restrict__ parent,
+    const Best* __restrict__ part, int chunks, const int32_t* __restrict__ amax_in, int n_max,
+    const int32_t* __restrict__ parent,
     const int32_t* __restrict__ token, int32_t* __restrict__ argmax_out, int32_t* __restrict__ path,
     specv_ctrl* __restrict__ ctrl, specv_step_stats* __restrict__ stats_base, int32_t* __restrict__ wcounter,
     int32_t* __restrict__ ring, int ring_cap) {
@@ -100,23 +92,28 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
         }
         return;
     }
-    // 16 threads per node finish the argmax over the node's partials.
+    // 16 threads per node finish the argmax over the node's partials (or
+    // take the given argmax).
     const int node = threadIdx.x >> 4;
     const int sub = threadIdx.x & 15;
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
-    if (node < n)
-        for (int c = sub; c < chunks; c += 16) {
-            const Best b = part[(int64_t)node * chunks + c];
-            if (better(b.v, b.i, bv, bi)) {
-                bv = b.v;
-                bi = b.i;
+    if (amax_in) {
+        if (node < n && sub == 0) s_amax[node] = amax_in[node];
+    } else {
+        float bv = -__builtin_inff();
+        int bi = 0x7fffffff;
+        if (node < n)
+            for (int c = sub; c < chunks; c += 16) {
+                const Best b = part[(int64_t)node * chunks + c];
+                if (better(b.v, b.i, bv, bi)) {
+                    bv = b.v;
+                    bi = b.i;
+                }
             }
+        best16(bv, bi);
+        if (node < n && sub == 0) {
+            s_amax[node] = bi;
+            if (argmax_out) argmax_out[node] = bi;
         }
-    wave_best(bv, bi, 16);
-    if (node < n && sub == 0) {
-        s_amax[node] = bi;
-        argmax_out[node] = bi;
     }
     __syncthreads();
     if (threadIdx.x != 0) return;
@@ -180,8 +177,15 @@ int enqueue_argmax_accept(const float* logits, int64_t V, int n_max, const int32
                        part, chunks);
     const int rc = launch_status();
     if (rc != SPECV_OK) return rc;
-    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kArgThreads), 0, s, part, chunks, n_max, parent, token,
-                       argmax, path, ctrl, stats, wcounter, ring, ring_cap);
+    return enqueue_accept(part, chunks, nullptr, n_max, parent, token, argmax, path, ctrl, stats, wcounter, ring,
+                          ring_cap, s);
+}
+
+int enqueue_accept(const Best* part, int chunks, const int32_t* amax_in, int n_max, const int32_t* parent,
+                   const int32_t* token, int32_t* argmax_out, int32_t* path, specv_ctrl* ctrl,
+                   specv_step_stats* stats, int32_t* wcounter, int32_t* ring, int32_t ring_cap, hipStream_t s) {
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kArgThreads), 0, s, part, chunks, amax_in, n_max, parent, token,
+                       argmax_out, path, ctrl, stats, wcounter, ring, ring_cap);
     return launch_status();
 }
 
@@ -204,4 +208,18 @@ extern "C" int tree_argmax_accept(const float* logits, int64_t V, int32_t n_max,
     if (!aligned(workspace, 4)) return SPECV_E_ALIGN;
     return enqueue_argmax_accept(logits, V, n_max, parent, token, argmax, path, ctrl, stats, nullptr, ring,
                                  ring_cap, workspace, (hipStream_t)stream);
+}
+
+extern "C" int tree_accept(const int32_t* argmax, int32_t n_max, const int32_t* parent, const int32_t* token,
+                           int32_t* path, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* ring,
+                           int32_t ring_cap, void* stream) {
+    using namespace specv;
+    if (n_max < 1 || n_max > kMaxNodes) return SPECV_E_SHAPE;
+    if (!argmax || !parent || !token || !path || !ctrl) return SPECV_E_INVAL;
+    if (ring && ring_cap < 1) return SPECV_E_INVAL;
+    if (!aligned(argmax, 4) || !aligned(parent, 4) || !aligned(token, 4) || !aligned(path, 4) ||
+        !aligned(ctrl, 4) || !aligned(stats, 4) || !aligned(ring, 4))
+        return SPECV_E_ALIGN;
+    return enqueue_accept(nullptr, 0, argmax, n_max, parent, token, nullptr, path, ctrl, stats, nullptr, ring,
+                          ring_cap, (hipStream_t)stream);
 }

@@ -37,6 +37,40 @@ __device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
+// (value, index) pair of an argmax reduction. "Better" is the larger value,
+// or an equal value at a lower index: a total order on (value, -index) with
+// -0 == +0, so every reduction shape yields the lowest index of the maximum.
+struct Best {
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// Best of 16 aligned lanes (order-free), exchanged with DPP: quad permutes
+// of lane ^ 1 and lane ^ 2, then the half-row and row mirrors.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+    const float ov = __builtin_bit_cast(float, dpp_i32<CTRL>(__builtin_bit_cast(int, v)));
+    const int oi = dpp_i32<CTRL>(i);
+    if (better(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+__device__ __forceinline__ void best16(float& v, int& i) {
+    best_step<0xB1>(v, i);
+    best_step<0x4E>(v, i);
+    best_step<0x141>(v, i);
+    best_step<0x140>(v, i);
+}
+
 // Reinterpret one 32-bit lane of a loaded vector as fp32. The element is
 // taken by value first: clang lowers __builtin_bit_cast applied directly to
 // an ext-vector element expression as a cast of element 0.

@@ -590,7 +590,7 @@ StepLayout step_layout(const specv_model* m, int n) {
     s.attn = take(4 * (size_t)n * m->n_heads * nch * (m->head_dim + 2));
     s.gu = take(4 * n * 2 * I);
     s.logits = take(4 * n * V);
-    s.argmax_part = take(tree_argmax_accept_workspace(V, n));
+    s.argmax_part = take(std::max(tree_argmax_accept_workspace(V, n), (size_t)n * ((V + 15) / 16) * sizeof(Best)));
     s.tree = take(4 * 16 * 4);  // parent, token, argmax, path for up to 16 nodes
     s.tinfo = take(4 * kTreeInfoInts);  // depths and ancestor lists of the step's tree
     s.wcounter = take(4);
@@ -659,7 +659,7 @@ static int launch_attn_chunk(int hd, dim3 grid, size_t lds, hipStream_t s, const
 }
 
 int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const int32_t* token, float* logits,
-                    specv_ctrl* ctrl, char* ws, const StepLayout& lay, hipStream_t s) {
+                    Best* amax, specv_ctrl* ctrl, char* ws, const StepLayout& lay, hipStream_t s) {
     const int H = m->hidden, I = m->inter, V = m->vocab, nh = m->n_heads, nkv = m->n_kv_heads, hd = m->head_dim;
     const int QKV = (nh + 2 * nkv) * hd, A = nh * hd, cap = m->kv_capacity;
     float* h = reinterpret_cast<float*>(ws + lay.h);
@@ -714,15 +714,27 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, h, delta,
                        m->norm_final, H, m->eps, xq, xs, ctrl);
     SPECV_TRY(launch_status());
+    if (amax) return linear_enqueue(m->w_lm, m->s_lm, xq, xs, logits, amax, n, V, H, lin, s);
     return w4a8_linear_T(m->w_lm, m->s_lm, xq, xs, logits, n, V, H, lin, linb, s);
 }
 
 int enqueue_step(const specv_model* m, int n, const int32_t* parent, const int32_t* token, float* logits,
                  int32_t* argmax, int32_t* path, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* wcounter,
                  int32_t* ring, int32_t ring_cap, char* ws, const StepLayout& lay, hipStream_t s) {
-    SPECV_TRY(enqueue_forward(m, n, parent, token, logits, ctrl, ws, lay, s));
-    SPECV_TRY(enqueue_argmax_accept(logits, m->vocab, n, parent, token, argmax, path, ctrl, stats, wcounter, ring,
-                                    ring_cap, ws + lay.argmax_part, s));
+    // The lm_head's argmax epilogue reduces each workgroup's rows to one
+    // (max, lowest index) pair per node, so the logits are written only when
+    // the caller asks for them; acceptance finishes from the pairs.
+    if (linear_argmax_supported(n, m->vocab, m->hidden)) {
+        Best* part = reinterpret_cast<Best*>(ws + lay.argmax_part);
+        SPECV_TRY(enqueue_forward(m, n, parent, token, logits, part, ctrl, ws, lay, s));
+        SPECV_TRY(enqueue_accept(part, linear_argmax_chunks(n, m->vocab, m->hidden), nullptr, n, parent, token,
+                                 argmax, path, ctrl, stats, wcounter, ring, ring_cap, s));
+    } else {
+        float* lg = logits ? logits : reinterpret_cast<float*>(ws + lay.logits);
+        SPECV_TRY(enqueue_forward(m, n, parent, token, lg, nullptr, ctrl, ws, lay, s));
+        SPECV_TRY(enqueue_argmax_accept(lg, m->vocab, n, parent, token, argmax, path, ctrl, stats, wcounter, ring,
+                                        ring_cap, ws + lay.argmax_part, s));
+    }
     return kv_compact(m->k_cache, m->v_cache, m->n_layers, m->n_kv_heads, m->kv_capacity, m->head_dim, path, ctrl,
                       s);
 }

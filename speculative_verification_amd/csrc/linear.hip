@@ -91,8 +91,8 @@ constexpr int kZeroBytes = 512;    // zero area after the staged activations
 template <int T, int MODE>
 __global__ __launch_bounds__(256) void w4a8_linear_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq,
-    const float* __restrict__ xs, float* __restrict__ y, float* __restrict__ part, int* __restrict__ cnt,
-    int N, int K) {
+    const float* __restrict__ xs, float* __restrict__ y, Best* __restrict__ amax, int write_y,
+    float* __restrict__ part, int* __restrict__ cnt, int N, int K) {
     constexpr int S = MODE == kNarrow || MODE == kWide ? 1 : MODE;  // K-slices
     constexpr int QS = 4 / S;                        // slot quads staged per workgroup
     constexpr int Q = MODE == kNarrow ? 1 : QS;      // slot quads per wave
@@ -334,26 +334,54 @@ __global__ __launch_bounds__(256) void w4a8_linear_kernel(
             val[qq][t] = v;
         }
 
+    // Optional argmax epilogue (amax != null): per token, the best
+    // (value, lowest row) of the workgroup's rows goes to amax[t][rg]; the
+    // outputs are written only when write_y is set.
     if (MODE == kNarrow) {  // levels w = 4, 8 across the four waves, in LDS
         __shared__ float red[4][T][16];
         if (q == 0)
 #pragma unroll
             for (int t = 0; t < T; t++) red[wave][t][r] = val[0][t];
         __syncthreads();
-        if (tid < 16 * T) {
+        if (tid < 16 * T) {  // 16-lane groups: token t = tid / 16, row rr of the group
             const int t = tid >> 4, rr = tid & 15;
             const int orow = rg * ROWS + rr;
-            if (orow < N)
-                y[(int64_t)t * N + orow] = xs[t] * ((red[0][t][rr] + red[1][t][rr]) + (red[2][t][rr] + red[3][t][rr]));
+            const float v = xs[t] * ((red[0][t][rr] + red[1][t][rr]) + (red[2][t][rr] + red[3][t][rr]));
+            if (orow < N && write_y) y[(int64_t)t * N + orow] = v;
+            if (amax) {
+                float bv = orow < N ? v : -__builtin_inff();
+                int bi = orow < N ? orow : 0x7fffffff;
+                best16(bv, bi);
+                if (rr == 0) amax[(int64_t)t * NG + rg] = Best{bv, bi};
+            }
         }
         return;
     }
     if (MODE == kWide) {  // levels w = 4, 8 inside the lane, then the token scale
-        if (q == 0 && row_ok)
+        float vt[T];
 #pragma unroll
-            for (int t = 0; t < T; t++)
-                y[(int64_t)t * N + row] =
-                    xs[t] * ((val[0][t] + val[1 % Q][t]) + (val[2 % Q][t] + val[3 % Q][t]));
+        for (int t = 0; t < T; t++) vt[t] = xs[t] * ((val[0][t] + val[1 % Q][t]) + (val[2 % Q][t] + val[3 % Q][t]));
+        if (q == 0 && row_ok && write_y)
+#pragma unroll
+            for (int t = 0; t < T; t++) y[(int64_t)t * N + row] = vt[t];
+        if (amax) {  // lanes 0..15 of a wave hold its 16 rows (every quarter holds the same)
+            __shared__ Best wb[4][T];
+#pragma unroll
+            for (int t = 0; t < T; t++) {
+                float bv = row_ok ? vt[t] : -__builtin_inff();
+                int bi = row_ok ? row : 0x7fffffff;
+                best16(bv, bi);
+                if (lane == 0) wb[wave][t] = Best{bv, bi};
+            }
+            __syncthreads();
+            if (tid < T) {
+                Best b = wb[0][tid];
+#pragma unroll
+                for (int w = 1; w < 4; w++)
+                    if (better(wb[w][tid].v, wb[w][tid].i, b.v, b.i)) b = wb[w][tid];
+                amax[(int64_t)tid * NG + rg] = b;
+            }
+        }
         return;
     }
 
@@ -430,7 +458,8 @@ static thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
 
 template <int T, int MODE>
 static int launch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                  float* part, int* cnt, int N, int K, hipStream_t s) {
+                  Best* amax, float* part, int* cnt, int N, int K, hipStream_t s) {
+    const int write_y = y != nullptr;
     // Dynamic LDS above 64 KB must be enabled per kernel, up to what the
     // launch needs (the static LDS of the kernel counts towards the limit).
     static size_t lds_enabled = 64 * 1024;
@@ -449,23 +478,75 @@ static int launch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const
                                      : MODE * linear_row_groups_padded(N);
     if (g_time_start) {
         hipExtLaunchKernelGGL((w4a8_linear_kernel<T, MODE>), dim3(grid), dim3(256), lds, s, g_time_start,
-                              g_time_stop, 0, wq, ws, xq, xs, y, part, cnt, N, K);
+                              g_time_stop, 0, wq, ws, xq, xs, y, amax, write_y, part, cnt, N, K);
         g_time_start = g_time_stop = nullptr;
     } else {
-        hipLaunchKernelGGL((w4a8_linear_kernel<T, MODE>), dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, part,
-                           cnt, N, K);
+        hipLaunchKernelGGL((w4a8_linear_kernel<T, MODE>), dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, amax,
+                           write_y, part, cnt, N, K);
     }
     return launch_status();
 }
 
 template <int T>
 static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                    float* part, int* cnt, int N, int K, hipStream_t s) {
+                    Best* amax, float* part, int* cnt, int N, int K, hipStream_t s) {
     switch (linear_mode(T, N, K)) {
-        case kNarrow: return launch<T, kNarrow>(wq, ws, xq, xs, y, part, cnt, N, K, s);
-        case kWide: return launch<T, kWide>(wq, ws, xq, xs, y, part, cnt, N, K, s);
-        case 2: return launch<T, 2>(wq, ws, xq, xs, y, part, cnt, N, K, s);
-        default: return launch<T, 4>(wq, ws, xq, xs, y, part, cnt, N, K, s);
+        case kNarrow: return launch<T, kNarrow>(wq, ws, xq, xs, y, amax, part, cnt, N, K, s);
+        case kWide: return launch<T, kWide>(wq, ws, xq, xs, y, amax, part, cnt, N, K, s);
+        case 2: return launch<T, 2>(wq, ws, xq, xs, y, nullptr, part, cnt, N, K, s);
+        default: return launch<T, 4>(wq, ws, xq, xs, y, nullptr, part, cnt, N, K, s);
+    }
+}
+
+// Finishes the argmax of each token from its row groups' partials.
+__global__ __launch_bounds__(256) void argmax_finish_kernel(const Best* __restrict__ part, int chunks,
+                                                            int32_t* __restrict__ argmax) {
+    const int t = blockIdx.x;
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+        const Best b = part[(int64_t)t * chunks + c];
+        if (better(b.v, b.i, bv, bi)) {
+            bv = b.v;
+            bi = b.i;
+        }
+    }
+    best16(bv, bi);
+    __shared__ Best wb[16];
+    if ((threadIdx.x & 15) == 0) wb[threadIdx.x >> 4] = Best{bv, bi};
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Best b = wb[0];
+        for (int w = 1; w < 16; w++)
+            if (better(wb[w].v, wb[w].i, b.v, b.i)) b = wb[w];
+        argmax[t] = b.i;
+    }
+}
+
+bool linear_argmax_supported(int T, int N, int K) {
+    const int mode = linear_mode(T, N, K);
+    return mode == kNarrow || mode == kWide;
+}
+
+int linear_argmax_chunks(int T, int N, int K) {
+    return linear_mode(T, N, K) == kNarrow ? (N + 15) / 16 : (N + 63) / 64;
+}
+
+// Validated arguments. y may be null when amax is set; the argmax epilogue
+// needs the narrow or wide layout (linear_argmax_supported).
+int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
+                   int T, int N, int K, void* workspace, hipStream_t s) {
+    int* cnt = static_cast<int*>(workspace);
+    const size_t need = w4a8_linear_workspace(T, N, K);
+    float* part = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+    switch (T) {
+#define SPECV_CASE(n) \
+    case n: return launch_T<n>(wq, ws, xq, xs, y, amax, part, cnt, N, K, s);
+        SPECV_CASE(1) SPECV_CASE(2) SPECV_CASE(3) SPECV_CASE(4) SPECV_CASE(5) SPECV_CASE(6)
+        SPECV_CASE(7) SPECV_CASE(8) SPECV_CASE(9) SPECV_CASE(10) SPECV_CASE(11) SPECV_CASE(12)
+        SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
+#undef SPECV_CASE
+        default: return SPECV_E_SHAPE;
     }
 }
 
@@ -500,16 +581,33 @@ extern "C" int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t
     const size_t need = w4a8_linear_workspace(T, N, K);
     if (need && (!workspace || workspace_bytes < need)) return SPECV_E_WORKSPACE;
     if (need && !aligned(workspace, 256)) return SPECV_E_ALIGN;
-    int* cnt = static_cast<int*>(workspace);
-    float* part = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+    return linear_enqueue(wq, ws, xq, xs, y, nullptr, T, N, K, workspace, (hipStream_t)stream);
+}
+
+extern "C" size_t w4a8_linear_argmax_workspace(int32_t T, int32_t N, int32_t K) {
+    using namespace specv;
+    if (T < 1 || T > 16 || N < 1 || K < 32 || K % 32 || !linear_argmax_supported(T, N, K)) return 0;
+    return (size_t)T * linear_argmax_chunks(T, N, K) * sizeof(Best);
+}
+
+extern "C" int w4a8_linear_argmax_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
+                                    float* y, int32_t* argmax, int32_t T, int32_t N, int32_t K, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    using namespace specv;
+    if (T < 1 || T > 16 || N < 1 || N > (1 << 24) || K < 32 || K > (1 << 20) || K % 32) return SPECV_E_SHAPE;
+    if ((int64_t)N * (K / 2) >= (int64_t)1 << 31) return SPECV_E_SHAPE;
+    if (!linear_argmax_supported(T, N, K)) return SPECV_E_SHAPE;
+    if (!wq || !ws || !xq || !xs || !argmax) return SPECV_E_INVAL;
+    if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(ws, 2) || !aligned(xs, 4) || !aligned(y, 4) ||
+        !aligned(argmax, 4))
+        return SPECV_E_ALIGN;
+    const size_t need = w4a8_linear_argmax_workspace(T, N, K);
+    if (!workspace || workspace_bytes < need) return SPECV_E_WORKSPACE;
+    if (!aligned(workspace, 8)) return SPECV_E_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    switch (T) {
-#define SPECV_CASE(n) \
-    case n: return launch_T<n>(wq, ws, xq, xs, y, part, cnt, N, K, s);
-        SPECV_CASE(1) SPECV_CASE(2) SPECV_CASE(3) SPECV_CASE(4) SPECV_CASE(5) SPECV_CASE(6)
-        SPECV_CASE(7) SPECV_CASE(8) SPECV_CASE(9) SPECV_CASE(10) SPECV_CASE(11) SPECV_CASE(12)
-        SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
-#undef SPECV_CASE
-        default: return SPECV_E_SHAPE;
-    }
+    Best* part = static_cast<Best*>(workspace);
+    const int rc = linear_enqueue(wq, ws, xq, xs, y, part, T, N, K, nullptr, s);
+    if (rc != SPECV_OK) return rc;
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(T), dim3(256), 0, s, part, linear_argmax_chunks(T, N, K), argmax);
+    return launch_status();
 }

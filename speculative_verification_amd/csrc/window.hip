@@ -103,7 +103,7 @@ static int enqueue_window_step(const WindowKey& k, const StepLayout& lay, hipStr
     int32_t* tree = reinterpret_cast<int32_t*>(ws + lay.tree);
     int32_t *parent = tree, *token = tree + 16, *argmax = tree + 32, *path = tree + 48;
     int32_t* wcounter = reinterpret_cast<int32_t*>(ws + lay.wcounter);
-    float* logits = reinterpret_cast<float*>(ws + lay.logits);
+    float* logits = nullptr;  // not wanted: acceptance reads the lm_head's argmax pairs
     if (k.has_drafter)
         hipLaunchKernelGGL(draft_kernel, dim3(1), dim3(64), 0, s, k.ctrl, k.width, k.drafter.reference,
                            k.drafter.reference_len, k.drafter.draws, k.drafter.draw_rows,

@@ -192,3 +192,31 @@ def test_window_rejects_bad_arguments(lib):
     assert f(ctypes.addressof(m1), A, A, None, 0, None, 1, 0, A, need, None, None) == OK
     m2 = fake_model(head_dim=15)
     assert f(ctypes.addressof(m2), A, A, None, 0, dp, 8, 4, A, need, None, None) == E_SHAPE
+
+
+def test_linear_argmax_rejects_bad_arguments(lib):
+    f = lib.w4a8_linear_argmax_T
+    need = lib.w4a8_linear_argmax_workspace(8, 151936, 896)
+    assert need == 8 * ((151936 + 63) // 64) * 8                      # 64-row layout: one pair per 64 rows
+    assert lib.w4a8_linear_argmax_workspace(8, 896, 896) == 8 * 56 * 8  # 16-row layout
+    assert lib.w4a8_linear_argmax_workspace(16, 4096, 14336) == 0     # staged rows exceed LDS: unsupported
+    assert f(A, A, A, A, None, A, 16, 4096, 14336, A, 1 << 20, None) == E_SHAPE
+    assert f(A, A, A, A, None, A, 8, 0, 896, A, need, None) == E_SHAPE   # no rows
+    assert f(A, A, A, A, None, A, 0, 896, 896, A, need, None) == E_SHAPE
+    assert f(A, A, A, A, None, None, 8, 151936, 896, A, need, None) == E_INVAL
+    assert f(None, A, A, A, None, A, 8, 151936, 896, A, need, None) == E_INVAL
+    assert f(A, A, A, A, None, A, 8, 151936, 896, A, need - 1, None) == E_WORKSPACE
+    assert f(A, A, A, A, None, A, 8, 151936, 896, None, need, None) == E_WORKSPACE
+    assert f(A, A, A, A, A + 2, A, 8, 151936, 896, A, need, None) == E_ALIGN
+    assert f(A, A, A, A, None, A + 2, 8, 151936, 896, A, need, None) == E_ALIGN
+    assert f(A + 8, A, A, A, None, A, 8, 151936, 896, A, need, None) == E_ALIGN
+
+
+def test_tree_accept_rejects_bad_arguments(lib):
+    f = lib.tree_accept
+    assert f(A, 0, A, A, A, A, None, None, 0, None) == E_SHAPE
+    assert f(A, 17, A, A, A, A, None, None, 0, None) == E_SHAPE
+    assert f(None, 8, A, A, A, A, None, None, 0, None) == E_INVAL
+    assert f(A, 8, A, A, A, None, None, None, 0, None) == E_INVAL
+    assert f(A, 8, A, A, A, A, None, A, 0, None) == E_INVAL       # ring without capacity
+    assert f(A + 2, 8, A, A, A, A, None, None, 0, None) == E_ALIGN

@@ -1,0 +1,125 @@
+"""GPU parity of the fused lm_head argmax (w4a8_linear_argmax_T) and of
+acceptance from given predictions (tree_accept), against the CPU oracle.
+
+The argmax is an index, so it must match exactly: the oracle's argmax of the
+oracle's linear, on the same int8 codes, with exact ties planted by copying
+the winning row into an earlier row (the lowest index must win). When the
+outputs are requested they must equal the oracle's bit for bit. At the full
+Llama-3-8B lm_head size the index is checked against the argmax of the
+library's own w4a8_linear_T outputs (whose values are checked against the
+oracle on sampled rows elsewhere).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthgen as sg
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_verification_amd as m
+    return m
+
+
+def case(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def plant_ties(wq, ws, y):
+    """Copy each token's winning row into a lower row: that row's output
+    becomes an exact tie with the maximum, at a lower index."""
+    wq, ws = wq.copy(), ws.copy()
+    for t in range(y.shape[0]):
+        r = int(np.argmax(y[t]))
+        if r > 0:
+            lo = r // 2
+            wq[lo] = wq[r]
+            ws[lo] = ws[r]
+    return wq, ws
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 16, 32), (3, 17, 64), (8, 100, 896), (16, 300, 64), (5, 2048, 896),
+                                   (8, 1000, 4096), (2, 16385, 128), (8, 151936, 896), (16, 151936, 896),
+                                   (1, 1, 32)])
+def test_linear_argmax_parity(sv, T, N, K):
+    case(f"linear argmax T={T} N={N} K={K}")
+    wq, ws, x = sg.linear_case(70 + T, T, N, K)
+    xq, xs = oracle.quantize_act(x)
+    y0 = oracle.w4a8_linear(wq, ws, xq, xs)
+    if T > 1:
+        wq, ws = plant_ties(wq, ws, y0)
+    y_o = oracle.w4a8_linear(wq, ws, xq, xs)
+    a_o = oracle.argmax(y_o)
+    wq_d, ws_d = to_dev(wq), to_dev(np.ascontiguousarray(ws.T))
+    xq_d, xs_d = to_dev(xq), to_dev(xs)
+    y = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+    a = sv.linear_argmax(wq_d, ws_d, xq_d, xs_d, y=y)
+    a2 = sv.linear_argmax(wq_d, ws_d, xq_d, xs_d)          # outputs not written
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy(), a_o), (a.cpu().numpy(), a_o)
+    assert np.array_equal(a2.cpu().numpy(), a_o)
+    assert y.cpu().numpy().tobytes() == y_o.tobytes()
+    if T > 1 and N > 1:  # the planted ties are real ties at the maximum
+        for t in range(T):
+            assert np.count_nonzero(y_o[t] == y_o[t].max()) >= 1
+
+
+@pytest.mark.parametrize("T", [1, 8, 16])
+def test_linear_argmax_llama_lm_head(sv, T):
+    """128256 x 4096: the fused index equals the lowest index of the maximum of
+    w4a8_linear_T's outputs on the same inputs, with a tie planted on device."""
+    case(f"linear argmax llama lm_head T={T}")
+    N, K = 128256, 4096
+    wq, ws, x = sg.linear_case(90 + T, T, N, K)
+    xq, xs = oracle.quantize_act(x)
+    wq_d, ws_d = to_dev(wq), to_dev(np.ascontiguousarray(ws.T))
+    xq_d, xs_d = to_dev(xq), to_dev(xs)
+    y = sv.linear(wq_d, ws_d, xq_d, xs_d)
+    torch.cuda.synchronize()
+    r = int(torch.argmax(y[0]).item())
+    if r > 0:      # tie for token 0: copy the winning row into row r // 2 (rows and scale columns)
+        wq_d[r // 2] = wq_d[r]
+        ws_d[:, r // 2] = ws_d[:, r]
+        y = sv.linear(wq_d, ws_d, xq_d, xs_d)
+    a = sv.linear_argmax(wq_d, ws_d, xq_d, xs_d)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert a.cpu().numpy().tolist() == [int(np.argmax(yh[t])) for t in range(T)]
+    if r > 0:
+        assert int(a[0].item()) == r // 2
+
+
+def test_tree_accept_parity(sv):
+    case("tree_accept vs oracle")
+    for seed in range(6):
+        n = [1, 2, 5, 8, 13, 16][seed]
+        parent = sg.random_tree_parents(sg.stream_key(seed, sg.TID_PARENT), n)
+        amax = sg.tokens(sg.stream_key(seed, sg.TID_TOKEN), n, 50)
+        token = sg.tokens(sg.stream_key(seed + 100, sg.TID_TOKEN), n, 50)
+        for i in range(1, n):                     # accept some children
+            if (i + seed) % 3 != 0:
+                token[i] = amax[parent[i]]
+        m_o, path_o, bonus_o = oracle.tree_accept(parent, token, amax)
+        L0 = 40
+        ctrl = sv.new_ctrl(L0, n, 1000)
+        stats = torch.zeros(3, dtype=torch.int32, device="cuda")
+        ring = torch.zeros(32, dtype=torch.int32, device="cuda")
+        path = sv.tree_accept(to_dev(amax), to_dev(parent), to_dev(token), ctrl, stats=stats, ring=ring)
+        torch.cuda.synchronize()
+        c = ctrl.cpu().numpy()
+        assert (c[0], c[4], c[5], c[6], c[7]) == (L0 + m_o + 1, m_o, bonus_o, 1, m_o + 1)
+        assert np.array_equal(path.cpu().numpy()[: m_o + 1], path_o)
+        assert stats.cpu().numpy().tolist() == [m_o, 0, n]
+        emitted = [int(token[p]) for p in path_o[1:]] + [bonus_o]
+        assert ring.cpu().numpy()[: m_o + 1].tolist() == emitted
