@@ -590,7 +590,7 @@ StepLayout step_layout(const specv_model* m, int n) {
     s.attn = take(4 * (size_t)n * m->n_heads * nch * (m->head_dim + 2));
     s.gu = take(4 * n * 2 * I);
     s.logits = take(4 * n * V);
-    s.argmax_part = take(std::max(tree_argmax_accept_workspace(V, n), (size_t)n * ((V + 15) / 16) * sizeof(Best)));
+    s.argmax_part = take(std::max(tree_argmax_accept_workspace(V, n), (size_t)n * (((V + 15) / 16 + 31) / 32 * 32) * sizeof(Best)));
     s.tree = take(4 * 16 * 4);  // parent, token, argmax, path for up to 16 nodes
     s.tinfo = take(4 * kTreeInfoInts);  // depths and ancestor lists of the step's tree
     s.wcounter = take(4);

@@ -197,8 +197,11 @@ def test_window_rejects_bad_arguments(lib):
 def test_linear_argmax_rejects_bad_arguments(lib):
     f = lib.w4a8_linear_argmax_T
     need = lib.w4a8_linear_argmax_workspace(8, 151936, 896)
-    assert need == 8 * ((151936 + 63) // 64) * 8                      # 64-row layout: one pair per 64 rows
-    assert lib.w4a8_linear_argmax_workspace(8, 896, 896) == 8 * 56 * 8  # 16-row layout
+    # one (value, row) pair per token per workgroup: a multiple of 32 workgroups,
+    # no more than the 16-row tiles need, capped near two per CU
+    chunks = need // (8 * 8)
+    assert need == 8 * chunks * 8 and chunks % 32 == 0 and 32 <= chunks <= (151936 // 16 + 31) // 32 * 32
+    assert lib.w4a8_linear_argmax_workspace(8, 896, 896) == 8 * 64 * 8   # 56 tiles: 64 workgroups
     assert lib.w4a8_linear_argmax_workspace(16, 4096, 14336) == 0     # staged rows exceed LDS: unsupported
     assert f(A, A, A, A, None, A, 16, 4096, 14336, A, 1 << 20, None) == E_SHAPE
     assert f(A, A, A, A, None, A, 8, 0, 896, A, need, None) == E_SHAPE   # no rows

@@ -108,7 +108,9 @@ def test_quantize_misaligned_rows(sv):
                                    (16, 50, 4864), (4, 1, 4096), (2, 15, 14336), (9, 31, 512),
                                    (12, 64, 1024), (6, 48, 160), (16, 130, 14336),
                                    # K split in 2 (>= 256 row groups) and unsplit (>= 1024)
-                                   (3, 16400, 96), (8, 16385, 544), (5, 65601, 64), (16, 65600, 160)])
+                                   (3, 16400, 96), (8, 16385, 544), (5, 65601, 64), (16, 65600, 160),
+                                   # several 16-row tiles per workgroup, ragged rows and groups
+                                   (8, 4100, 4864), (16, 4097, 8192), (1, 4111, 96), (2, 8211, 1056)])
 def test_linear_parity_ragged(sv, T, N, K):
     case(f"linear ragged T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(50 + T, T, N, K)
