@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "1cd82c1ec6fcfc12fe9fed9e35a2b208bbe1b6a278716c4e8fa564640c99edae",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33718697}
+LINEAR_TRAFFIC = {"source_sha256": "cefaeac7b345e1448a8a0af7eb43d63fea0b33a034f32f925f6dcef8c15df15d",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33622780}
 
 
 def linear_traffic(T, workload):
@@ -487,7 +487,8 @@ def main():
                   for T, v in per_T.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": linear_traffic(args.T, args.workload),
-                     "kernel": f"w4a8_linear_kernel<{args.T},S> (all K-split variants)",
+                     "kernel": f"w4a8_linear_stream_kernel<{args.T},4,*> (the lm_head runs the argmax specialisation)",
+                     "lm_head_chunks": model.lm_chunks(args.T),
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
                      "by_shape": by_shape},

@@ -119,7 +119,7 @@ struct SStage {
     v4i x[(T + 7) / 8]; // first tile only: 16 bytes of this wave's activation quarter per 8 tokens
 };
 
-template <int T, int P>
+template <int T, int P, bool AMAX>
 __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq,
     const float* __restrict__ xs, float* __restrict__ y, Best* __restrict__ amax, int write_y, int N, int K) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
     if (ntiles == 0) {
-        if (amax && fin && fr == 0) amax[(int64_t)ft * nwg + b] = Best{bv, bi};
+        if (AMAX && fin && fr == 0) amax[(int64_t)ft * nwg + b] = Best{bv, bi};
         return;
     }
     const float fxs = fin ? xs[ft] : 0.0f;
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
             const float val = fxs * ((red[buf][0][ft][fr] + red[buf][1][ft][fr]) +
                                      (red[buf][2][ft][fr] + red[buf][3][ft][fr]));
             if (row < N) {
-                if (write_y) y[(int64_t)ft * N + row] = val;
-                if (better(val, row, bv, bi)) {
+                if (!AMAX || write_y) y[(int64_t)ft * N + row] = val;
+                if (AMAX && better(val, row, bv, bi)) {
                     bv = val;
                     bi = row;
                 }
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
         run_tile(std::false_type{}, k, acc);
         finish_tile(k, acc, k & 1);
     }
-    if (amax && fin) {
+    if (AMAX && fin) {
         best16(bv, bi);
         if (fr == 0) amax[(int64_t)ft * nwg + b] = Best{bv, bi};
     }
@@ -622,18 +622,22 @@ static int launch_stream(const uint8_t* wq, const uint16_t* ws, const int8_t* xq
     static size_t lds_enabled = 64 * 1024;
     const size_t lds = stream_lds_bytes(T, K);
     if (!stream_fits(T, K)) return SPECV_E_SHAPE;
-    const int rc = enable_lds(reinterpret_cast<const void*>(&w4a8_linear_stream_kernel<T, P>), lds, lds_enabled);
-    if (rc != SPECV_OK) return rc;
     const int grid = stream_grid(N);
-    if (g_time_start) {
-        hipExtLaunchKernelGGL((w4a8_linear_stream_kernel<T, P>), dim3(grid), dim3(256), lds, s, g_time_start,
-                              g_time_stop, 0, wq, ws, xq, xs, y, amax, write_y, N, K);
-        g_time_start = g_time_stop = nullptr;
-    } else {
-        hipLaunchKernelGGL((w4a8_linear_stream_kernel<T, P>), dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y,
-                           amax, write_y, N, K);
-    }
-    return launch_status();
+    auto go = [&](auto kernel, size_t& enabled) {
+        const int rc = enable_lds(reinterpret_cast<const void*>(kernel), lds, enabled);
+        if (rc != SPECV_OK) return rc;
+        if (g_time_start) {
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, g_time_start, g_time_stop, 0, wq, ws, xq, xs,
+                                  y, amax, write_y, N, K);
+            g_time_start = g_time_stop = nullptr;
+        } else {
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, amax, write_y, N, K);
+        }
+        return launch_status();
+    };
+    static size_t lds_enabled_amax = 64 * 1024;
+    return amax ? go(&w4a8_linear_stream_kernel<T, P, true>, lds_enabled_amax)
+                : go(&w4a8_linear_stream_kernel<T, P, false>, lds_enabled);
 }
 
 template <int T, int S>

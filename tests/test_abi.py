@@ -82,7 +82,7 @@ def test_linear_rejects_bad_arguments(lib):
     assert f(A, A, A, A, A, 16, 4096, 14336, A + 16, need, None) == E_ALIGN
     assert lib.w4a8_linear_workspace(16, 16400, 10240) == (1 << 20) + 2 * 16 * 16400 * 4  # 2 slices
     for T, N, K in ((8, 4096, 4096), (8, 4096, 14336), (8, 28672, 4096), (8, 128256, 4096), (16, 896, 4864)):
-        assert lib.w4a8_linear_workspace(T, N, K) == 0              # narrow or wide: none
+        assert lib.w4a8_linear_workspace(T, N, K) == 0              # streaming layout: none
     assert lib.w4a8_linear_workspace(0, 16, 64) == 0
 
 

@@ -197,7 +197,7 @@ def test_linear_run_to_run_identical(sv):
 @pytest.mark.parametrize("T,N,K", [(16, 16400, 10240), (16, 4096, 14336), (8, 4096, 14336), (8, 28672, 4096)])
 def test_linear_layouts_sampled(sv, T, N, K):
     """Two-slice and four-slice K splits (activations too large for LDS) and
-    the narrow and wide layouts at full size, on sampled rows."""
+    the streaming layout at full size, on sampled rows."""
     case(f"linear layout T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(11, T, N, K)
     xq_o, xs_o = oracle.quantize_act(x)
