@@ -25,6 +25,9 @@ FLAGS = [
     # matrix-core results in ordinary VGPRs: the linear scales every group
     # dot right away, so accumulator registers would only add copies
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the first kernel arguments arrive in SGPRs with the wave, so a
+    # kernel's first loads do not wait for an argument fetch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 

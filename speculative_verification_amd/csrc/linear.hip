@@ -119,10 +119,13 @@ struct SStage {
     v4i x[(T + 7) / 8]; // first tile only: 16 bytes of this wave's activation quarter per 8 tokens
 };
 
+// The arguments the first loads need come first: with kernel-argument
+// preloading the first 14 dwords arrive in SGPRs, and the rest (the argmax
+// output, used last) is fetched while the stream starts.
 template <int T, int P, bool AMAX>
 __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
-    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq,
-    const float* __restrict__ xs, float* __restrict__ y, Best* __restrict__ amax, int write_y, int N, int K) {
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq, int N, int K,
+    int nwg, const float* __restrict__ xs, float* __restrict__ y, int write_y, Best* __restrict__ amax) {
     constexpr int TT = (T + 3) / 4;
     constexpr int TX = (T + 7) / 8;
     extern __shared__ __attribute__((aligned(16))) int8_t act[];
@@ -139,7 +142,6 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     const int J = (G + 15) >> 4;
     const int JP = (J + P - 1) / P * P;  // iterations per tile, padded to whole blocks of P
     const int NT = (N + 15) >> 4;
-    const int nwg = gridDim.x;
     // The four 16-row tiles of a 64-row block share the 128-byte lines of
     // their group-major scales: they go to workgroups that the hardware's
     // round-robin placement (workgroup b on XCD b mod 8) puts on one XCD,
@@ -627,11 +629,11 @@ static int launch_stream(const uint8_t* wq, const uint16_t* ws, const int8_t* xq
         const int rc = enable_lds(reinterpret_cast<const void*>(kernel), lds, enabled);
         if (rc != SPECV_OK) return rc;
         if (g_time_start) {
-            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, g_time_start, g_time_stop, 0, wq, ws, xq, xs,
-                                  y, amax, write_y, N, K);
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, g_time_start, g_time_stop, 0, wq, ws, xq, N,
+                                  K, grid, xs, y, write_y, amax);
             g_time_start = g_time_stop = nullptr;
         } else {
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, amax, write_y, N, K);
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, wq, ws, xq, N, K, grid, xs, y, write_y, amax);
         }
         return launch_status();
     };
