@@ -346,6 +346,74 @@ int spec_window_run(const specv_model* m, specv_ctrl* ctrl, specv_step_stats* st
                     int32_t W, void* workspace, size_t workspace_bytes, void* host_readback,
                     void* stream);
 
+/*
+ * Context-mixing drafter ([P1], Draft-Free Drafting From Web Context: every
+ * position of the token history computes the length of its match with the
+ * current suffix, at orders up to 8; the best positions' continuations are
+ * blended into a weighted trie, weighted by a fixed function of the match
+ * length; the most probable prefix-closed node set is the next tree).
+ * The stream s[0..n) is the committed tokens followed by the pending root
+ * s[n-1]. Position p <= n-2 matches with length l(p), the largest
+ * l <= min(max_order, p + 1) with s[p-i] == s[n-1-i] for i < l. The
+ * candidates are the `candidates` positions with l >= 1 largest by (l, p);
+ * candidate p continues with s[p+1 .. min(p + depth, n - 1)]. A trie node is
+ * a prefix of some continuation, weighing the sum of weight[l(p)] over the
+ * candidates that continue with it. The tree keeps the width - 1 nodes
+ * largest by (weight, smaller depth, earlier first candidate), which is
+ * prefix-closed; node 0 is the root (parent -1), then the kept nodes by
+ * depth and rank. The step's best match is the first candidate's l (0 if
+ * none). Everything is integer, so results are exact.
+ * 48 bytes.
+ */
+typedef struct {
+    int32_t max_order;   /* match orders up to this, in [1, 8] */
+    int32_t candidates;  /* positions kept, in [1, 32] */
+    int32_t depth;       /* continuation tokens per candidate, in [1, 8] */
+    uint32_t weight[9];  /* weight[l], l = 1..8, in [1, 2^24]; weight[0] ignored */
+} specv_cm_params;
+
+/* Workspace bytes of cm_draft for a stream of n tokens (0 if invalid). */
+size_t cm_draft_workspace(int32_t n, const specv_cm_params* p);
+
+/*
+ * One tree from a token stream ([P1], Draft-Free Drafting From Web Context).
+ *   stream      int32 [n] device, n >= 1: committed tokens, then the root.
+ *   p           host parameters, validated as documented above.
+ *   width       tree size limit, in [1, 16].
+ *   parent, token  int32 [width] device: the tree's first nodes.
+ *   out         int32 [2] device: node count (1..width), best match length.
+ *   workspace   cm_draft_workspace(n, p) bytes, 4-byte aligned (any content).
+ * Returns SPECV_E_SHAPE, SPECV_E_INVAL, SPECV_E_ALIGN or SPECV_E_WORKSPACE
+ * without enqueueing anything on bad arguments.
+ */
+int cm_draft(const int32_t* stream, int32_t n, const specv_cm_params* p, int32_t width, int32_t* parent,
+             int32_t* token, int32_t* out, void* workspace, size_t workspace_bytes, void* stream_handle);
+
+/* Workspace bytes of a context-mixing window (0 if invalid). */
+size_t spec_window_cm_workspace(const specv_model* m, int32_t width, int32_t ring_cap, const specv_cm_params* p);
+
+/*
+ * Speculation window drafted by the context-mixing drafter: as
+ * spec_window_run, with each step's tree drafted from the token history by
+ * the drafter above (ctrl->n_nodes becomes the tree's size, at most width;
+ * the step's best_match record is the drafter's). The history is the ring:
+ * ring[i] holds the token at position i of the stream, so the caller fills
+ * ring[0..L] with the committed tokens and the root (L = committed_len) and
+ * sets ring_head = L + 1; ring_cap must exceed the context limit so the
+ * ring never wraps. A step whose ring does not hold the stream (ring_head !=
+ * committed_len + 1, or ring[committed_len] != root_token) drafts the root
+ * alone.
+ *   ring       int32 [ring_cap] device, required.
+ *   p          host drafter parameters.
+ *   workspace  spec_window_cm_workspace(m, width, ring_cap, p) bytes,
+ *              256-byte aligned, zero-filled before its first use.
+ * Other arguments, the graph cache and the readback are as in
+ * spec_window_run.
+ */
+int spec_window_run_cm(const specv_model* m, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* ring,
+                       int32_t ring_cap, const specv_cm_params* p, int32_t width, int32_t W, void* workspace,
+                       size_t workspace_bytes, void* host_readback, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

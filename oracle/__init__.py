@@ -13,7 +13,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SO = os.path.join(HERE, "liboracle.so")
-SOURCES = ["oracle.c", "forward.c"]
+SOURCES = ["oracle.c", "forward.c", "drafter.c"]
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
           "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
@@ -64,9 +64,10 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_forward.argtypes = [P, P, P, I, I, I, P, P, P]
     L.orc_tree_step.argtypes = [P, P, P, I, P, I, P, P, P, P, P, P]
     L.orc_draft_tree.argtypes = [I, I, ctypes.c_int32, P, I, P, ctypes.c_uint32, I, P, P, P]
+    L.orc_cm_draft.argtypes = [P, I, I, I, I, P, I, P, P, P]
     for f in ("orc_quantize_act", "orc_group_dots", "orc_w4a8_linear", "orc_w4a8_linear_rows",
               "orc_argmax", "orc_tree_accept", "orc_kv_compact", "orc_rope_table", "orc_attention",
-              "orc_forward", "orc_tree_step", "orc_draft_tree"):
+              "orc_forward", "orc_tree_step", "orc_draft_tree", "orc_cm_draft"):
         getattr(L, f).restype = I
 
 
@@ -269,6 +270,26 @@ def draft_tree(width, L, root_token, greedy, draws, threshold, vocab):
     return parent, token, bm.value
 
 
+def cm_draft(stream, width: int, max_order: int = 8, cands: int = 16, depth: int = 8, weight=None):
+    """Context-mixing drafter: (parent, token, n_nodes, best_match) of the
+    next tree from the token stream (committed tokens + pending root)."""
+    s = np.ascontiguousarray(stream, np.int32)
+    w = np.ascontiguousarray(CM_WEIGHT if weight is None else weight, np.uint32)
+    assert w.size == 9
+    parent = np.zeros(width, np.int32)
+    token = np.zeros(width, np.int32)
+    bm = ctypes.c_int32(0)
+    n = lib().orc_cm_draft(_p(s), s.size, max_order, cands, depth, _p(w), width, _p(parent), _p(token),
+                           ctypes.byref(bm))
+    _check(n, "cm_draft")
+    return parent[:n].copy(), token[:n].copy(), n, bm.value
+
+
+# Default candidate weight by match length l = 0..8: 2^(l-1), so one match
+# one token longer counts as much as two shorter ones.
+CM_WEIGHT = [0, 1, 2, 4, 8, 16, 32, 64, 128]
+
+
 def window(model: Model, kc, vc, ctrl: dict, width: int, W: int, greedy, draws_table, threshold):
     """W speculation steps of the device-resident window, driven by the
     control state (committed_len, root_token, step, done, ctx_len, ring):
@@ -293,4 +314,32 @@ def window(model: Model, kc, vc, ctrl: dict, width: int, W: int, greedy, draws_t
         if r["L"] + width > ctrl["ctx_len"]:
             ctrl["done"] = 1
         stats.append((m, bm, width))
+    return stats, emitted
+
+
+def window_cm(model: Model, kc, vc, ctrl: dict, width: int, W: int, history, max_order: int = 8,
+              cands: int = 16, depth: int = 8, weight=None):
+    """W speculation steps drafted by the context-mixing drafter. `history`
+    (a list, extended in place) holds the token stream: history[i] is the
+    token at position i, history[committed_len] the pending root. Returns the
+    per-step statistics (m, best match, nodes) and the emitted tokens."""
+    stats, emitted = [], []
+    for _ in range(W):
+        if ctrl["done"]:
+            stats.append((-1, 0, ctrl["n_nodes"]))
+            ctrl["accept_len"] = 0
+            continue
+        L = ctrl["committed_len"]
+        assert len(history) == L + 1 and history[L] == ctrl["root_token"]
+        parent, token, n, bm = cm_draft(history, width, max_order, cands, depth, weight)
+        r = tree_step(model, kc, vc, L, parent, token)
+        m = r["m"]
+        out = [int(token[p]) for p in r["path"][1:]] + [r["bonus"]]
+        emitted.extend(out)
+        history.extend(out)
+        ctrl.update(committed_len=r["L"], n_nodes=n, accept_len=m, root_token=r["bonus"], step=ctrl["step"] + 1,
+                    ring_head=ctrl["ring_head"] + m + 1)
+        if r["L"] + n > ctrl["ctx_len"]:   # the step's own node count, as the acceptance rule states
+            ctrl["done"] = 1
+        stats.append((m, bm, n))
     return stats, emitted

@@ -57,6 +57,13 @@ int orc_tree_accept(const int32_t* parent, const int32_t* token, const int32_t* 
 int orc_kv_compact(uint16_t* cache, int layers, int heads, int cap, int hd,
                    int L, const int32_t* path, int m);
 
+/* Context-mixing drafter (drafter.c): the next tree from the token stream
+ * s[0..n) whose last token is the pending root. weight[l] (l = 1..8, in
+ * [1, 2^24]) is the weight of a candidate with match length l. Returns the node
+ * count (1..width) and fills parent/token [width] and *best_match, or -1. */
+int orc_cm_draft(const int32_t* s, int n, int max_order, int cands, int depth, const uint32_t* weight,
+                 int width, int32_t* parent, int32_t* token, int32_t* best_match);
+
 #ifdef __cplusplus
 }
 #endif

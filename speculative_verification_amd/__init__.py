@@ -7,13 +7,15 @@ in the library's HIP kernels.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
-from ._lib import LIB, SpecvError, check
+from ._lib import CM_WEIGHT, LIB, SpecvError, check, cm_params
 from .model import DeviceModel
 
 __all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
-           "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace"]
+           "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace", "cm_params", "cm_draft", "CM_WEIGHT"]
 
 CTRL_FIELDS = ("committed_len", "n_nodes", "ctx_len", "done", "accept_len", "root_token", "step",
                "ring_head")
@@ -167,3 +169,23 @@ def kv_compact(k_cache: torch.Tensor, v_cache: torch.Tensor, path: torch.Tensor,
                                        _dev(v_cache, "v_cache", v_cache.dtype), layers, heads, cap, hd,
                                        _dev(path, "path", torch.int32), _dev(ctrl, "ctrl", torch.int32),
                                        _stream()))
+
+
+def cm_draft(stream: torch.Tensor, width: int, params=None, workspace: torch.Tensor | None = None):
+    """Context-mixing drafter on a token stream (committed tokens, then the
+    root): returns (parent, token) int32 [width] device tensors, of which the
+    first n are the tree, and an int32 [2] device tensor (n, best match)."""
+    p = params if params is not None else cm_params()
+    n = stream.numel()
+    need = int(LIB.cm_draft_workspace(n, ctypes.byref(p)))
+    if need == 0:
+        raise ValueError("cm_draft_workspace rejected its arguments")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=stream.device)
+    parent = torch.empty(width, dtype=torch.int32, device=stream.device)
+    token = torch.empty(width, dtype=torch.int32, device=stream.device)
+    out = torch.empty(2, dtype=torch.int32, device=stream.device)
+    check("cm_draft", LIB.cm_draft(_dev(stream, "stream", torch.int32), n, ctypes.byref(p), width, parent.data_ptr(),
+                                   token.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream()))
+    return parent, token, out

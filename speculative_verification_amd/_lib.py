@@ -33,6 +33,10 @@ SIGNATURES = {
     "spec_tree_step": (ctypes.c_int, [P, P, P, P, I32, P, P, P, P, P, I32, P, SZ, P]),
     "spec_window_workspace": (SZ, [P, I32]),
     "spec_window_run": (ctypes.c_int, [P, P, P, P, I32, P, I32, I32, P, SZ, P, P]),
+    "cm_draft_workspace": (SZ, [I32, P]),
+    "cm_draft": (ctypes.c_int, [P, I32, P, I32, P, P, P, P, SZ, P]),
+    "spec_window_cm_workspace": (SZ, [P, I32, I32, P]),
+    "spec_window_run_cm": (ctypes.c_int, [P, P, P, P, I32, P, I32, I32, P, SZ, P, P]),
 }
 
 
@@ -50,6 +54,24 @@ class SpecvDrafter(ctypes.Structure):
     """Mirror of specv_drafter."""
     _fields_ = [("reference", ctypes.c_void_p), ("reference_len", ctypes.c_int32), ("draw_rows", ctypes.c_int32),
                 ("draws", ctypes.c_void_p), ("accept_threshold", ctypes.c_uint32), ("reserved", ctypes.c_int32)]
+
+
+class SpecvCmParams(ctypes.Structure):
+    """Mirror of specv_cm_params."""
+    _fields_ = [("max_order", ctypes.c_int32), ("candidates", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("weight", ctypes.c_uint32 * 9)]
+
+
+# Default candidate weight by match length l = 0..8: 2^(l - 1), so a match
+# one token longer counts as much as two shorter ones.
+CM_WEIGHT = (0, 1, 2, 4, 8, 16, 32, 64, 128)
+
+
+def cm_params(max_order: int = 8, candidates: int = 16, depth: int = 8, weight=CM_WEIGHT) -> SpecvCmParams:
+    p = SpecvCmParams(max_order, candidates, depth)
+    for i, w in enumerate(weight):
+        p.weight[i] = int(w)
+    return p
 
 
 class SpecvError(RuntimeError):

@@ -46,4 +46,14 @@ int enqueue_step(const specv_model* m, int n, const int32_t* parent, const int32
                  int32_t* argmax, int32_t* path, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* wcounter,
                  int32_t* ring, int32_t ring_cap, char* ws, const StepLayout& lay, hipStream_t s);
 
+// Context-mixing drafter. With ctrl set, the stream is the ring (length
+// committed_len + 1) and the tree's size and best match go to ctrl and
+// stats[*wcounter]; otherwise the stream has n_given tokens and they go to
+// n_nodes_out and best_match_out. cap: stream capacity (scan grid size).
+bool cm_params_ok(const specv_cm_params* p);
+size_t cm_workspace_bytes(int cap, const specv_cm_params* p);
+int enqueue_cm_draft(const int32_t* s, int n_given, int cap, specv_ctrl* ctrl, const specv_cm_params* p, int width,
+                     int32_t* parent, int32_t* token, int32_t* n_nodes_out, int32_t* best_match_out,
+                     specv_step_stats* stats, const int32_t* wcounter, void* workspace, hipStream_t st);
+
 }  // namespace specv

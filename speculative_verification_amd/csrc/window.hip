@@ -74,6 +74,8 @@ __global__ void window_begin_kernel(int32_t* wcounter) {
     if (threadIdx.x == 0) *wcounter = 0;
 }
 
+enum { kRootOnly = 0, kSynthetic = 1, kContextMixing = 2 };
+
 struct WindowKey {
     specv_model model;
     specv_ctrl* ctrl;
@@ -81,8 +83,9 @@ struct WindowKey {
     int32_t* ring;
     int32_t ring_cap;
     int32_t width;
+    int32_t drafter_kind;  // kRootOnly, kSynthetic or kContextMixing
     specv_drafter drafter;
-    int32_t has_drafter;
+    specv_cm_params cm;
     void* workspace;
     bool operator<(const WindowKey& o) const { return std::memcmp(this, &o, sizeof(WindowKey)) < 0; }
 };
@@ -104,13 +107,19 @@ static int enqueue_window_step(const WindowKey& k, const StepLayout& lay, hipStr
     int32_t *parent = tree, *token = tree + 16, *argmax = tree + 32, *path = tree + 48;
     int32_t* wcounter = reinterpret_cast<int32_t*>(ws + lay.wcounter);
     float* logits = nullptr;  // not wanted: acceptance reads the lm_head's argmax pairs
-    if (k.has_drafter)
+    int rc = SPECV_OK;
+    if (k.drafter_kind == kSynthetic) {
         hipLaunchKernelGGL(draft_kernel, dim3(1), dim3(64), 0, s, k.ctrl, k.width, k.drafter.reference,
                            k.drafter.reference_len, k.drafter.draws, k.drafter.draw_rows,
                            k.drafter.accept_threshold, k.model.vocab, parent, token, k.stats, wcounter);
-    else
+        rc = launch_status();
+    } else if (k.drafter_kind == kContextMixing) {
+        rc = enqueue_cm_draft(k.ring, 0, k.ring_cap, k.ctrl, &k.cm, k.width, parent, token, nullptr, nullptr, k.stats,
+                              wcounter, ws + lay.total, s);
+    } else {
         hipLaunchKernelGGL(root_only_kernel, dim3(1), dim3(64), 0, s, k.ctrl, parent, token, k.stats, wcounter);
-    const int rc = launch_status();
+        rc = launch_status();
+    }
     if (rc != SPECV_OK) return rc;
     return enqueue_step(&k.model, k.width, parent, token, logits, argmax, path, k.ctrl, k.stats, wcounter, k.ring,
                         k.ring_cap, ws, lay, s);
@@ -151,6 +160,31 @@ static int window_graph(const WindowKey& k, const StepLayout& lay, hipGraphExec_
     return SPECV_OK;
 }
 
+// The window itself: the cached step graph replayed W times, then the
+// readback of the control block and the statistics.
+static int run_window(const WindowKey& k, const StepLayout& lay, int W, void* host_readback, hipStream_t s) {
+    specv_ctrl* ctrl = k.ctrl;
+    specv_step_stats* stats = k.stats;
+    void* workspace = k.workspace;
+    hipGraphExec_t exec = nullptr;
+    int rc = window_graph(k, lay, &exec);
+    if (rc != SPECV_OK) return rc;
+    int32_t* wcounter = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.wcounter);
+    hipLaunchKernelGGL(window_begin_kernel, dim3(1), dim3(64), 0, s, wcounter);
+    rc = launch_status();
+    if (rc != SPECV_OK) return rc;
+    for (int i = 0; i < W; i++)
+        if (hipGraphLaunch(exec, s) != hipSuccess) return SPECV_E_HIP;
+    if (host_readback) {
+        char* hb = static_cast<char*>(host_readback);
+        if (hipMemcpyAsync(hb, ctrl, sizeof(specv_ctrl), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipMemcpyAsync(hb + sizeof(specv_ctrl), stats, sizeof(specv_step_stats) * (size_t)W,
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            return SPECV_E_HIP;
+    }
+    return SPECV_OK;
+}
+
 }  // namespace specv
 
 extern "C" size_t spec_window_workspace(const specv_model* m, int32_t width) {
@@ -183,29 +217,49 @@ extern "C" int spec_window_run(const specv_model* m, specv_ctrl* ctrl, specv_ste
     k.ring = ring;
     k.ring_cap = ring ? ring_cap : 0;
     k.width = width;
-    k.has_drafter = width > 1;
-    if (k.has_drafter) {
+    k.drafter_kind = width > 1 ? kSynthetic : kRootOnly;
+    if (k.drafter_kind == kSynthetic) {
         k.drafter = *d;
         k.drafter.reserved = 0;
     }
     k.workspace = workspace;
-
-    hipGraphExec_t exec = nullptr;
-    int rc = window_graph(k, lay, &exec);
-    if (rc != SPECV_OK) return rc;
-    hipStream_t s = (hipStream_t)stream;
-    int32_t* wcounter = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.wcounter);
-    hipLaunchKernelGGL(window_begin_kernel, dim3(1), dim3(64), 0, s, wcounter);
-    rc = launch_status();
-    if (rc != SPECV_OK) return rc;
-    for (int i = 0; i < W; i++)
-        if (hipGraphLaunch(exec, s) != hipSuccess) return SPECV_E_HIP;
-    if (host_readback) {
-        char* hb = static_cast<char*>(host_readback);
-        if (hipMemcpyAsync(hb, ctrl, sizeof(specv_ctrl), hipMemcpyDeviceToHost, s) != hipSuccess ||
-            hipMemcpyAsync(hb + sizeof(specv_ctrl), stats, sizeof(specv_step_stats) * (size_t)W,
-                           hipMemcpyDeviceToHost, s) != hipSuccess)
-            return SPECV_E_HIP;
-    }
-    return SPECV_OK;
+    return run_window(k, lay, W, host_readback, (hipStream_t)stream);
 }
+
+extern "C" size_t spec_window_cm_workspace(const specv_model* m, int32_t width, int32_t ring_cap,
+                                           const specv_cm_params* p) {
+    using namespace specv;
+    if (validate_model(m) != SPECV_OK || width < 1 || width > 16 || ring_cap < 1 || ring_cap > (1 << 24) ||
+        !cm_params_ok(p))
+        return 0;
+    return step_layout(m, width).total + cm_workspace_bytes(ring_cap, p);
+}
+
+extern "C" int spec_window_run_cm(const specv_model* m, specv_ctrl* ctrl, specv_step_stats* stats, int32_t* ring,
+                                  int32_t ring_cap, const specv_cm_params* p, int32_t width, int32_t W,
+                                  void* workspace, size_t workspace_bytes, void* host_readback, void* stream) {
+    using namespace specv;
+    const int vrc = validate_model(m);
+    if (vrc != SPECV_OK) return vrc;
+    if (width < 1 || width > 16 || W < 0 || W > 4096 || ring_cap > (1 << 24)) return SPECV_E_SHAPE;
+    if (!ctrl || !stats || !ring || ring_cap < 1 || !p || !cm_params_ok(p)) return SPECV_E_INVAL;
+    if (!aligned(ctrl, 4) || !aligned(stats, 4) || !aligned(ring, 4)) return SPECV_E_ALIGN;
+    const StepLayout lay = step_layout(m, width);
+    if (!workspace || workspace_bytes < lay.total + cm_workspace_bytes(ring_cap, p)) return SPECV_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return SPECV_E_ALIGN;
+    if (W == 0) return SPECV_OK;
+
+    WindowKey k;
+    std::memset(&k, 0, sizeof(k));
+    k.model = *m;
+    k.ctrl = ctrl;
+    k.stats = stats;
+    k.ring = ring;
+    k.ring_cap = ring_cap;
+    k.width = width;
+    k.drafter_kind = kContextMixing;
+    k.cm = *p;
+    k.workspace = workspace;
+    return run_window(k, lay, W, host_readback, (hipStream_t)stream);
+}
+

@@ -13,7 +13,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import LIB, SpecvDrafter, SpecvModel, check
+from ._lib import LIB, SpecvDrafter, SpecvModel, check, cm_params
 
 CFG_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab", "max_pos")
 
@@ -101,6 +101,29 @@ class DeviceModel:
             ring.data_ptr() if ring is not None else None, ring.numel() if ring is not None else 0,
             ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
         return logits, argmax, path
+
+    def window_cm(self, ctrl: torch.Tensor, stats: torch.Tensor, width: int, W: int, ring: torch.Tensor,
+                  params=None, readback: torch.Tensor | None = None):
+        """W speculation steps drafted by the context-mixing drafter
+        (spec_window_run_cm). `ring` int32 holds the token stream: ring[i] is
+        the token at position i (committed tokens, then the root), with
+        ctrl's ring_head = committed_len + 1."""
+        p = params if params is not None else cm_params()
+        assert ring.dtype == torch.int32 and stats.dtype == torch.int32 and stats.numel() >= 3 * W
+        if readback is not None:
+            assert readback.device.type == "cpu" and readback.numel() * readback.element_size() >= 32 + 12 * W
+        need = int(LIB.spec_window_cm_workspace(self.ptr(), width, ring.numel(), ctypes.byref(p)))
+        if need == 0:
+            raise ValueError("spec_window_cm_workspace rejected its arguments")
+        key = ("cm", width, ring.numel())
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(need, dtype=torch.uint8, device=self.k_cache.device)
+            self._ws[key] = ws
+        check("spec_window_run_cm", LIB.spec_window_run_cm(
+            self.ptr(), ctrl.data_ptr(), stats.data_ptr(), ring.data_ptr(), ring.numel(), ctypes.byref(p), width, W,
+            ws.data_ptr(), ws.numel(), readback.data_ptr() if readback is not None else None,
+            torch.cuda.current_stream().cuda_stream))
 
     def window(self, ctrl: torch.Tensor, stats: torch.Tensor, width: int, W: int,
                reference: torch.Tensor | None = None, draws: torch.Tensor | None = None, threshold: int = 0,

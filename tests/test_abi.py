@@ -223,3 +223,64 @@ def test_tree_accept_rejects_bad_arguments(lib):
     assert f(A, 8, A, A, A, None, None, None, 0, None) == E_INVAL
     assert f(A, 8, A, A, A, A, None, A, 0, None) == E_INVAL       # ring without capacity
     assert f(A + 2, 8, A, A, A, A, None, None, 0, None) == E_ALIGN
+
+
+def test_cm_params_layout(tmp_path):
+    src = tmp_path / "cm.c"
+    src.write_text('#include "specv.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   'int main(void){printf("%zu %zu\\n", sizeof(specv_cm_params), offsetof(specv_cm_params, weight));'
+                   ' return 0;}\n')
+    exe = tmp_path / "cm"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    from speculative_verification_amd._lib import SpecvCmParams
+    assert out == ["48", "12"] == [str(ctypes.sizeof(SpecvCmParams)), str(SpecvCmParams.weight.offset)]
+
+
+def test_cm_draft_rejects_bad_arguments(lib):
+    from speculative_verification_amd._lib import cm_params
+    p = cm_params()
+    pp = ctypes.byref(p)
+    need = lib.cm_draft_workspace(4097, pp)
+    assert need == 17 * 16 * 4                     # 17 scan workgroups of 256 positions, 16 keys each
+    assert lib.cm_draft_workspace(0, pp) == 0
+    for bad in (cm_params(max_order=0), cm_params(max_order=9), cm_params(candidates=33), cm_params(depth=0),
+                cm_params(depth=9), cm_params(weight=(0, 0, 1, 1, 1, 1, 1, 1, 1)),
+                cm_params(weight=(0, 1, 1, 1, 1, 1, 1, 1, (1 << 24) + 1))):
+        assert lib.cm_draft_workspace(100, ctypes.byref(bad)) == 0
+        assert lib.cm_draft(A, 100, ctypes.byref(bad), 8, A, A, A, A, 1 << 20, None) == E_INVAL
+    f = lib.cm_draft
+    assert f(A, 0, pp, 8, A, A, A, A, need, None) == E_SHAPE
+    assert f(A, 4097, pp, 0, A, A, A, A, need, None) == E_SHAPE
+    assert f(A, 4097, pp, 17, A, A, A, A, need, None) == E_SHAPE
+    assert f(None, 4097, pp, 8, A, A, A, A, need, None) == E_INVAL
+    assert f(A, 4097, None, 8, A, A, A, A, need, None) == E_INVAL
+    assert f(A, 4097, pp, 8, None, A, A, A, need, None) == E_INVAL
+    assert f(A, 4097, pp, 8, A, A, None, A, need, None) == E_INVAL
+    assert f(A + 2, 4097, pp, 8, A, A, A, A, need, None) == E_ALIGN
+    assert f(A, 4097, pp, 8, A, A, A, A, need - 1, None) == E_WORKSPACE
+    assert f(A, 4097, pp, 8, A, A, A, None, need, None) == E_WORKSPACE
+
+
+def test_cm_window_rejects_bad_arguments(lib):
+    from speculative_verification_amd._lib import cm_params
+    m = fake_model()
+    mp = ctypes.addressof(m)
+    p = cm_params()
+    pp = ctypes.byref(p)
+    need = lib.spec_window_cm_workspace(mp, 8, 1024, pp)
+    assert need == lib.spec_step_workspace(mp, 8) + 4 * 16 * 4
+    assert lib.spec_window_cm_workspace(mp, 8, 0, pp) == 0
+    assert lib.spec_window_cm_workspace(mp, 17, 1024, pp) == 0
+    f = lib.spec_window_run_cm
+    assert f(mp, A, A, A, 1024, pp, 0, 4, A, need, None, None) == E_SHAPE
+    assert f(mp, A, A, A, 1024, pp, 8, 4097, A, need, None, None) == E_SHAPE
+    assert f(mp, A, A, None, 1024, pp, 8, 4, A, need, None, None) == E_INVAL     # the ring is the history
+    assert f(mp, A, A, A, 0, pp, 8, 4, A, need, None, None) == E_INVAL
+    assert f(mp, A, A, A, 1024, None, 8, 4, A, need, None, None) == E_INVAL
+    assert f(mp, A, A, A, 1024, ctypes.byref(cm_params(depth=9)), 8, 4, A, need, None, None) == E_INVAL
+    assert f(mp, None, A, A, 1024, pp, 8, 4, A, need, None, None) == E_INVAL
+    assert f(mp, A, A, A + 2, 1024, pp, 8, 4, A, need, None, None) == E_ALIGN
+    assert f(mp, A, A, A, 1024, pp, 8, 4, A, need - 1, None, None) == E_WORKSPACE
+    assert f(mp, A, A, A, 1024, pp, 8, 4, A + 16, need, None, None) == E_ALIGN
+    assert f(mp, A, A, A, 1024, pp, 8, 0, A, need, None, None) == OK
