@@ -400,9 +400,81 @@ def window_bench(torch, sv, sg, widths, W=16, max_windows=400):
     t1 = out["1"]["us_per_step"]
     for v in out.values():
         v["step_cost_vs_width1"] = round(v["us_per_step"] / t1, 3)
+    cm = cm_window_bench(torch, sv, dm, ref, widths, L0, ctx, root, cfg["vocab"], W, max_windows)
     return {"workload": f"qwen2.5-0.5b-shaped decoder, {W}-step windows from 1024 to 4096 context, "
                         f"synthetic drafter at acceptance 0.6, pinned readback of {32 + 12 * W} B per window",
-            "W": W, "by_width": out}
+            "W": W, "by_width": out, "context_mixing": cm}
+
+
+def cm_window_bench(torch, sv, dm, ref, widths, L0, ctx, root, vocab, W, max_windows, echo=512):
+    """Windows drafted by the context-mixing drafter from the token history
+    in the ring, on a synthetic history: 1024 committed tokens of a seeded
+    random page in which the root and the next `echo` tokens of the greedy
+    reply appear once, as a passage the reply repeats; after the passage the
+    history no longer predicts the reply. Fixed widths first, then the width
+    controller (its load-time costs are the fixed-width step costs), two
+    windows in flight."""
+    from speculative_verification_amd.controller import WidthController, run_controlled
+    page = np.random.default_rng(5).integers(0, vocab, size=L0).astype(np.int32)
+    page[199] = root
+    page[200:200 + echo] = ref[L0 + 1:L0 + 1 + echo].cpu().numpy()
+    hist = torch.from_numpy(np.concatenate([page, [root]]).astype(np.int32)).cuda()
+    ring = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    stats = torch.zeros((W, 3), dtype=torch.int32, device="cuda")
+    rb = torch.zeros(32 + 12 * W, dtype=torch.uint8, pin_memory=True)
+
+    def reset():
+        ring.zero_()
+        ring[:L0 + 1] = hist
+        c = sv.new_ctrl(L0, 1, ctx, root_token=root)
+        c[7] = L0 + 1   # ring_head: the ring holds the whole stream
+        return c
+
+    out = {}
+    for width in [1] + [w for w in widths if w != 1]:
+        ctrl = reset()
+        dm.window_cm(ctrl, stats, width, W, ring, readback=rb)      # capture + warm
+        torch.cuda.synchronize()
+        ctrl = reset()
+        t_us, steps, tokens = 0.0, 0, 0
+        for _ in range(max_windows):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dm.window_cm(ctrl, stats, width, W, ring, readback=rb)
+            e1.record()
+            e1.synchronize()
+            st = rb[32:].numpy().view(np.int32).reshape(W, 3)
+            if (st[:, 0] < 0).any():
+                break
+            t_us += e0.elapsed_time(e1) * 1e3
+            steps += W
+            tokens += int(st[:, 0].sum()) + W
+        out[str(width)] = {"us_per_step": round(t_us / max(steps, 1), 2),
+                           "tokens_per_step": round(tokens / max(steps, 1), 3),
+                           "tokens_per_s": round(tokens / (t_us * 1e-6), 1) if t_us else None,
+                           "windows": steps // W}
+        print(f"[bench] cm window width={width}: {out[str(width)]}", file=sys.stderr, flush=True)
+    ctl = WidthController({int(w): v["us_per_step"] for w, v in out.items()})
+    first = ctl.width
+    ctrl = reset()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    log = run_controlled(dm, ctrl, ring, ctl, W, max_windows)
+    e1.record()
+    torch.cuda.synchronize()
+    tokens = int(ctrl[0].item()) - L0
+    us = e0.elapsed_time(e1) * 1e3
+    hist_w = {}
+    for w, _, _ in log:
+        hist_w[str(w)] = hist_w.get(str(w), 0) + 1
+    ctl_out = {"first_width": first, "windows_by_width": hist_w, "tokens": tokens,
+               "tokens_per_s": round(tokens / (us * 1e-6), 1),
+               "note": "wall time from the first enqueue to the last completion, host decisions included"}
+    print(f"[bench] cm controller: {ctl_out}", file=sys.stderr, flush=True)
+    return {"workload": f"context-mixing drafter on a 1024-token synthetic page echoing {echo} tokens of the "
+                        f"reply; {W}-step windows to the 4096 context",
+            "by_width": out, "controller": ctl_out}
 
 
 def main():
