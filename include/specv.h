@@ -97,7 +97,22 @@ int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* x
                       void* stream);
 
 /*
- * W4A8 linear for T = 1..16 tokens ([P1], Small-Batch Verification Kernels
+ * Per-block int8 activation quantisation ([P1], Small-Batch Verification
+ * Kernels: each token's activations are quantised per block of 32 values):
+ * as w4a8_quantize_act, with one absmax scale per token and 32-input block.
+ *   x   fp32 [T][K]      input activations (finite values).
+ *   xq  int8 [T][K]      codes: round-to-nearest-even of x * (127/absmax of
+ *                        the block), in [-127, 127].
+ *   xs  fp32 [T][K/32]   scale absmax/127 per block (0 for an all-zero block,
+ *                        whose codes are 0).
+ * T in [0, 2^20], K a multiple of 32 in [32, 2^24], T*K < 2^31. T == 0
+ * enqueues nothing.
+ * Alignment: x 16 bytes, xq and xs 4.
+ */
+int w4a8_quantize_act_blocks(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs, void* stream);
+
+/*
+ * W4A8 linear for T = 1..32 tokens ([P1], Small-Batch Verification Kernels
  * and Implementation; packing of [P2]):
  *   y[t][n] = xs[t] * R16_g( f32(ws[g][n]) * f32(d[t][n][g]) ),
  *   d[t][n][g] = sum_{k in group g} (u(n,k) - 8) * xq[t][k]   (exact int32),
@@ -113,21 +128,30 @@ int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* x
  *                        contiguous).
  *   xq  int8 [T][K], xs fp32 [T]   from w4a8_quantize_act.
  *   y   fp32 [T][N]
- *   workspace  device buffer of w4a8_linear_workspace(T, N, K) bytes
- *              (may be 0, then NULL is accepted), 256-byte aligned: a 1 MiB
- *              region of split-K counters followed by partial sums. It must
- *              be zero-filled before its first use; every call returns the
- *              counters it used to zero, so one buffer, sized for the
- *              largest shape, serves any sequence of calls on one stream.
- *              Calls that run concurrently need separate workspaces.
- * T in [1, 16], N in [0, 2^24], K a multiple of 32 in [32, 2^20],
- * N*K/2 < 2^31 bytes. N == 0 enqueues nothing.
+ *   workspace  unused (w4a8_linear_workspace returns 0 for every shape);
+ *              any value, NULL included, is accepted.
+ * T in [1, 32] (the buckets of [P1] are 1, 2, 4, 8, 16 and 32 tokens; 17..31
+ * run in the 32-token kernel), N in [0, 2^24], K a multiple of 32 in
+ * [32, 2^20], N*K/2 < 2^31 bytes. N == 0 enqueues nothing.
  * Alignment: wq and xq 16 bytes, ws 2, xs and y 4.
  */
 size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K);
 int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
                   float* y, int32_t T, int32_t N, int32_t K, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * W4A8 linear with per-block activation scales ([P1], Small-Batch
+ * Verification Kernels: activations quantised per block of 32 values, each
+ * block meeting one weight group), in the same fixed order:
+ *   y[t][n] = R16_g( ( f32(ws[g][n]) * xs[t][g] ) * f32(d[t][n][g]) ),
+ * each product rounded once, the two scales combined first; d and R16 as in
+ * w4a8_linear_T. Row t of a T-token call equals a 1-token call on token t.
+ *   xq  int8 [T][K], xs fp32 [T][K/32]   from w4a8_quantize_act_blocks.
+ * Other arguments, ranges and alignments as w4a8_linear_T (no workspace).
+ */
+int w4a8_linear_blocks_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
+                         float* y, int32_t T, int32_t N, int32_t K, void* stream);
 
 /*
  * W4A8 linear with a fused argmax epilogue ([P1], GPU-Resident Speculation

@@ -53,6 +53,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_group_dots.argtypes = [P, P, I, I, I, P]
     L.orc_w4a8_linear.argtypes = [P, P, P, P, P, I, I, I]
     L.orc_w4a8_linear_rows.argtypes = [P, P, P, P, P, I, I, I, P, I]
+    L.orc_quantize_act_blocks.argtypes = [P, I, I, P, P]
+    L.orc_w4a8_linear_blocks.argtypes = [P, P, P, P, P, I, I, I]
     L.orc_argmax.argtypes = [P, I, I64, P]
     L.orc_tree_accept.argtypes = [P, P, P, I, P, P]
     L.orc_kv_compact.argtypes = [P, I, I, I, I, I, P, I]
@@ -65,7 +67,7 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_tree_step.argtypes = [P, P, P, I, P, I, P, P, P, P, P, P]
     L.orc_draft_tree.argtypes = [I, I, ctypes.c_int32, P, I, P, ctypes.c_uint32, I, P, P, P]
     L.orc_cm_draft.argtypes = [P, I, I, I, I, P, I, P, P, P]
-    for f in ("orc_quantize_act", "orc_group_dots", "orc_w4a8_linear", "orc_w4a8_linear_rows",
+    for f in ("orc_quantize_act_blocks", "orc_w4a8_linear_blocks", "orc_quantize_act", "orc_group_dots", "orc_w4a8_linear", "orc_w4a8_linear_rows",
               "orc_argmax", "orc_tree_accept", "orc_kv_compact", "orc_rope_table", "orc_attention",
               "orc_forward", "orc_tree_step", "orc_draft_tree", "orc_cm_draft"):
         getattr(L, f).restype = I
@@ -119,6 +121,26 @@ def w4a8_linear(wq: np.ndarray, ws: np.ndarray, xq: np.ndarray, xs: np.ndarray) 
     T, K = xq.shape
     y = np.empty((T, N), np.float32)
     _check(lib().orc_w4a8_linear(_p(wq), _p(ws), _p(xq), _p(xs), _p(y), T, N, K), "w4a8_linear")
+    return y
+
+
+def quantize_act_blocks(x: np.ndarray):
+    """Per-block (32 inputs) int8 codes and scales [T][K/32]."""
+    x = np.ascontiguousarray(x, np.float32)
+    T, K = x.shape
+    xq = np.zeros((T, K), np.int8)
+    xs = np.zeros((T, K // 32), np.float32)
+    _check(lib().orc_quantize_act_blocks(_p(x), T, K, _p(xq), _p(xs)), "quantize_act_blocks")
+    return xq, xs
+
+
+def w4a8_linear_blocks(wq: np.ndarray, ws: np.ndarray, xq: np.ndarray, xs: np.ndarray) -> np.ndarray:
+    """W4A8 linear with per-block activation scales xs [T][K/32]."""
+    wq, ws = np.ascontiguousarray(wq, np.uint8), np.ascontiguousarray(ws, np.uint16)
+    xq, xs = np.ascontiguousarray(xq, np.int8), np.ascontiguousarray(xs, np.float32)
+    N, T, K = wq.shape[0], xq.shape[0], xq.shape[1]
+    y = np.zeros((T, N), np.float32)
+    _check(lib().orc_w4a8_linear_blocks(_p(wq), _p(ws), _p(xq), _p(xs), _p(y), T, N, K), "w4a8_linear_blocks")
     return y
 
 

@@ -190,6 +190,54 @@ int orc_w4a8_linear(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
     return 0;
 }
 
+/*
+ * Per-block activation scales, the format of [P1, Small-Batch Verification
+ * Kernels] (activations quantised to 8-bit integers per block of 32 values).
+ * Readings: the block is a weight group (inputs 32g..32g+31); its scale is
+ * absmax/127 and its codes round(x * (127/absmax)) to nearest-even, as for a
+ * token above; an all-zero block has scale 0 and codes 0. xs is [T][K/32].
+ */
+int orc_quantize_act_blocks(const float* x, int T, int K, int8_t* xq, float* xs) {
+    if (T < 0 || K < 0 || K % 32 || (T > 0 && K > 0 && (!x || !xq || !xs))) return -1;
+    const int G = K / 32;
+    for (int t = 0; t < T; t++)
+        for (int g = 0; g < G; g++)
+            if (orc_quantize_act(x + (int64_t)t * K + 32 * g, 1, 32, xq + (int64_t)t * K + 32 * g,
+                                 xs + (int64_t)t * G + g) != 0)
+                return -1;
+    return 0;
+}
+
+/*
+ * W4A8 linear with per-block activation scales. Reading: each group's two
+ * scales combine first, then meet the exact integer dot, and the products
+ * are summed in the fixed order with no trailing scale:
+ *   s_g = f32(scale_g) * xs[t][g],  one rounding;
+ *   p_g = s_g * f32(d_g),            one rounding;
+ *   y   = R16(p_0 .. p_{G-1}).
+ */
+int orc_w4a8_linear_blocks(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
+                           const float* xs, float* y, int T, int N, int K) {
+    if (T < 0 || N < 0 || K < 32 || K % 32) return -1;
+    const int G = K / 32;
+    float* p = (float*)malloc(sizeof(float) * (size_t)G);
+    if (!p) return -1;
+    for (int t = 0; t < T; t++)
+        for (int n = 0; n < N; n++) {
+            const uint8_t* row = wq + (int64_t)n * (K / 2);
+            const int8_t* xr = xq + (int64_t)t * K;
+            for (int g = 0; g < G; g++) {
+                int32_t d = 0;
+                for (int kk = 0; kk < 32; kk++) d += weight_code(row, 32 * g + kk) * (int32_t)xr[32 * g + kk];
+                const float s = orc_f16_to_f32(ws[(int64_t)n * G + g]) * xs[(int64_t)t * G + g];
+                p[g] = s * (float)d;
+            }
+            y[(int64_t)t * N + n] = orc_r16(p, G);
+        }
+    free(p);
+    return 0;
+}
+
 int orc_w4a8_linear_rows(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
                          const float* xs, float* y, int T, int N, int K,
                          const int32_t* rows, int nrows) {

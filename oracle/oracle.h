@@ -44,6 +44,12 @@ int orc_w4a8_linear_rows(const uint8_t* wq, const uint16_t* ws, const int8_t* xq
                          const float* xs, float* y, int T, int N, int K,
                          const int32_t* rows, int nrows);
 
+/* Per-block variants: one activation scale per token and 32-input block,
+ * xs [T][K/32]; the linear sums fl(fl(scale * xs) * d) in the fixed order. */
+int orc_quantize_act_blocks(const float* x, int T, int K, int8_t* xq, float* xs);
+int orc_w4a8_linear_blocks(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
+                           const float* xs, float* y, int T, int N, int K);
+
 /* Lowest index of the maximum of each row of logits [N][V]. */
 int orc_argmax(const float* logits, int N, int64_t V, int32_t* out);
 

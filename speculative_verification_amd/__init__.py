@@ -15,7 +15,7 @@ from ._lib import CM_WEIGHT, LIB, SpecvError, check, cm_params
 from .model import DeviceModel
 
 __all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
-           "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace", "cm_params", "cm_draft", "CM_WEIGHT"]
+           "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace", "cm_params", "cm_draft", "CM_WEIGHT", "quantize_act_blocks", "linear_blocks"]
 
 CTRL_FIELDS = ("committed_len", "n_nodes", "ctx_len", "done", "accept_len", "root_token", "step",
                "ring_head")
@@ -88,6 +88,34 @@ def linear(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tenso
     check("w4a8_linear_T", LIB.w4a8_linear_T(_dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype),
                                              _dev(xq, "xq", torch.int8), _dev(xs, "xs", torch.float32),
                                              _dev(y, "y", torch.float32), T, N, K, wsp, wsb, _stream()))
+    return y
+
+
+def quantize_act_blocks(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tensor | None = None):
+    """Per-block codes int8 [T][K] and scales fp32 [T][K/32]."""
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device=x.device) if xq is None else xq
+    xs = torch.empty((T, K // 32), dtype=torch.float32, device=x.device) if xs is None else xs
+    check("w4a8_quantize_act_blocks", LIB.w4a8_quantize_act_blocks(_dev(x, "x", torch.float32), T, K,
+                                                                   _dev(xq, "xq", torch.int8),
+                                                                   _dev(xs, "xs", torch.float32), _stream()))
+    return xq, xs
+
+
+def linear_blocks(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
+                  y: torch.Tensor | None = None) -> torch.Tensor:
+    """As linear, with per-block activation scales xs [T][K/32]."""
+    N = wq.shape[0]
+    T, K = xq.shape
+    if wq.shape != (N, K // 2) or ws.shape != (K // 32, N) or xs.shape != (T, K // 32):
+        raise ValueError("shape mismatch between wq, ws (group-major), xq and xs")
+    if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
+        raise TypeError("ws must hold fp16 bit patterns")
+    y = torch.empty((T, N), dtype=torch.float32, device=xq.device) if y is None else y
+    check("w4a8_linear_blocks_T", LIB.w4a8_linear_blocks_T(_dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype),
+                                                           _dev(xq, "xq", torch.int8),
+                                                           _dev(xs, "xs", torch.float32),
+                                                           _dev(y, "y", torch.float32), T, N, K, _stream()))
     return y
 
 

@@ -19,6 +19,8 @@ SZ = ctypes.c_size_t
 SIGNATURES = {
     "specv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w4a8_quantize_act": (ctypes.c_int, [P, I32, I32, P, P, P]),
+    "w4a8_quantize_act_blocks": (ctypes.c_int, [P, I32, I32, P, P, P]),
+    "w4a8_linear_blocks_T": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P]),
     "w4a8_linear_workspace": (SZ, [I32, I32, I32]),
     "w4a8_linear_T": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P, SZ, P]),
     "specv_time_next_linear": (ctypes.c_int, [P, P]),

@@ -1,27 +1,27 @@
-// W4A8 linear for T = 1..16 tokens on CDNA4 matrix cores.
+// W4A8 linear for T = 1..32 tokens on CDNA4 matrix cores.
 //
 // Operation (GPU-Resident Speculative Decoding for In-Browser LLM Inference
 // with WebGPU, Small-Batch Verification Kernels and Implementation):
 //   d[t][n][g] = sum_{k in group g} q(n,k) * xq[t][k]   exact int32
+// per-token activation scales xs[t]:
 //   p_g        = f32(scale[g][n]) * f32(d)               one rounding
 //   y[t][n]    = xs[t] * R16(p_0 .. p_{G-1})             fixed order
+// per-block activation scales xs[t][g] (one per 32 inputs):
+//   p_g        = (f32(scale[g][n]) * xs[t][g]) * f32(d)  two roundings
+//   y[t][n]    = R16(p_0 .. p_{G-1})
 // R16: slot s in 0..15 accumulates the groups g = s, s+16, s+32, ... in
 // increasing g from +0; the 16 slots are then added as a binary tree in
 // index order (slot s += slot s+w for s divisible by 2w, w = 1, 2, 4, 8).
 // An iteration j covers the 16 groups 16j .. 16j+15, one per slot; the 16
 // slots form four quads of four.
 //
-// Work decomposition, two layouts chosen per shape:
-//  stream: the default. About two workgroups per CU, each walking a list of
-//          16-row tiles; its four waves take the four slot quads of every
-//          tile (wave w: groups 16j + 4w + 0..3, 64 contiguous bytes per row
-//          per iteration). A wave keeps its quarter of the activation codes
-//          in LDS after loading it with its first tile, and its weight loads
-//          run a fixed number of iterations ahead, across tile boundaries.
-//  split:  for shapes whose activations do not fit in LDS (T x K large): 64
-//          rows and one of S = 2 or 4 K-slices per workgroup; each slice
-//          reduces its own slots and the last workgroup of a row group to
-//          finish adds the S partials in tree order.
+// Work decomposition. About two workgroups per CU, each walking a list of
+// 16-row tiles; its four waves take the four slot quads of every tile (wave
+// w: groups 16j + 4w + 0..3, 64 contiguous bytes per row per iteration), and
+// its weight loads run a fixed number of iterations ahead, across tile
+// boundaries. A wave keeps its quarter of the activation codes in LDS after
+// loading it with its first tile; when T x K is too large for LDS, the
+// reload variant loads the quarter again with every tile instead.
 //
 // Integer dots. One v_mfma_i32_16x16x64_i8 computes, for 16 rows, the dots
 // of 16 inputs of each group of a slot quad against up to four tokens: B
@@ -41,9 +41,10 @@
 // low nibbles, the odd inputs out of its high nibbles, with no byte permute,
 // because the staged activations of each 8-input chunk are stored in the same
 // even-then-odd order. The dots therefore come out as 16d (exact,
-// |16d| < 2^20), and the scale is pre-divided by 16 (exact: a power of two on
-// a widened fp16 value), so f32(scale/16) * f32(16d) is the same real product
-// as f32(scale) * f32(d) and rounds identically.
+// |16d| < 2^20). With per-token scales the weight scale is pre-divided by 16
+// (exact: a power of two on a widened fp16 value), so f32(scale/16) *
+// f32(16d) is the same real product as f32(scale) * f32(d) and rounds
+// identically; with per-block scales d itself is recovered as 16d >> 4.
 //
 // Ragged shapes. All global loads go through buffer resources, whose range
 // check returns zeros. Rows past N lie past the end of the weights; groups
@@ -57,15 +58,12 @@
 
 namespace specv {
 
-// Weight iterations in flight per wave, and streaming workgroups per CU.
+// Weight iterations in flight per wave, and workgroups per CU.
 #ifndef SPECV_STREAM_STAGES
 #define SPECV_STREAM_STAGES 4
 #endif
 #ifndef SPECV_STREAM_WGS_PER_CU
 #define SPECV_STREAM_WGS_PER_CU 2
-#endif
-#ifndef SPECV_SPLIT_STAGES
-#define SPECV_SPLIT_STAGES 2
 #endif
 
 // Integer dots of one group per slot of a quad (see the header): w is the
@@ -94,42 +92,41 @@ __device__ __forceinline__ v4i even_odd(const v4i a) {
                (int)__builtin_amdgcn_perm(a[3], a[2], 0x06040200u), (int)__builtin_amdgcn_perm(a[3], a[2], 0x07050301u)};
 }
 
-// ---------------------------------------------------------------- stream
-
-// Streaming layout. The grid is a multiple of 32 workgroups; workgroup b
-// walks the 16-row tiles v, v + nwg, v + 2 nwg, ... Its four waves take the
-// four slot quads of every tile, so a wave only ever uses its own quarter of
-// each token's activation codes: it loads that quarter together with the
-// first tile's weights, iteration by iteration, stores it in LDS in the MFMA
-// operand order, and reads it back from there for every later tile (the
-// activations cross the CU once per workgroup instead of once per 16 rows).
-// Slot pp of the load pipeline holds iterations pp, pp + P, ... of a tile,
-// and in the tile's last block it is refilled with iteration pp of the next
-// tile, so the stream does not drain between tiles. At the end of a tile the
-// four quad sums of each row meet in LDS (tree levels w = 4, 8) and 16T
-// threads scale and store them. With an argmax, each of those threads keeps
-// the best of its rows over the tiles, and the workgroup writes one (value,
-// lowest row) pair per token.
+// The grid is a multiple of 32 workgroups; workgroup b walks the 16-row
+// tiles v, v + nwg, v + 2 nwg, ... Its four waves take the four slot quads of
+// every tile, so a wave only ever uses its own quarter of each token's
+// activation codes: it loads that quarter together with a tile's weights,
+// iteration by iteration, stores it in LDS in the MFMA operand order, and
+// reads it back from there (for every later tile too, unless RELOAD). Slot pp
+// of the load pipeline holds iterations pp, pp + P, ... of a tile, and in the
+// tile's last block it is refilled with iteration pp of the next tile, so the
+// stream does not drain between tiles. At the end of a tile the four quad
+// sums of each row meet in LDS (tree levels w = 4, 8), and threads scale and
+// store them, 16 rows per token. With an argmax (T <= 16), each finishing
+// thread keeps the best of its rows over the tiles, and the workgroup writes
+// one (value, lowest row) pair per token. T is the compiled token capacity;
+// the call's token count Tr <= T (the 32-token bucket serves 17..32).
 constexpr int kStreamZero = 64;  // zero bytes after the staged activations
 
-template <int T>
+template <int T, bool BS>
 struct SStage {
-    v4i w;              // 16 bytes of nibbles: one group of one row
-    uint16_t s;         // its fp16 scale
-    v4i x[(T + 7) / 8]; // first tile only: 16 bytes of this wave's activation quarter per 8 tokens
+    v4i w;                                 // 16 bytes of nibbles: one group of one row
+    uint16_t s;                            // its fp16 scale
+    v4i x[(T + 7) / 8];                    // activation quarter: 16 bytes per 8 tokens
+    float xb[BS ? (4 * T + 63) / 64 : 1];  // block scales of the quarter's 4 groups, per token
 };
 
-// The arguments the first loads need come first: with kernel-argument
-// preloading the first 14 dwords arrive in SGPRs, and the rest (the argmax
-// output, used last) is fetched while the stream starts.
-template <int T, int P, bool AMAX>
+template <int T, int P, bool AMAX, bool BS, bool RELOAD>
 __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq, int N, int K,
-    int nwg, const float* __restrict__ xs, float* __restrict__ y, int write_y, Best* __restrict__ amax) {
+    int nwg, int Tr, const float* __restrict__ xs, float* __restrict__ y, int write_y, Best* __restrict__ amax) {
     constexpr int TT = (T + 3) / 4;
     constexpr int TX = (T + 7) / 8;
+    constexpr int XB = (4 * T + 63) / 64;  // block-scale loads per lane and iteration
+    constexpr int FP = (16 * T + 255) / 256;  // finishing passes: 16 rows per token, 256 threads
     extern __shared__ __attribute__((aligned(16))) int8_t act[];
     __shared__ float red[2][4][T][16];
+    static_assert(!AMAX || T <= 16, "the argmax keeps one token per finishing thread");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -141,6 +138,7 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     const int G = K >> 5;
     const int J = (G + 15) >> 4;
     const int JP = (J + P - 1) / P * P;  // iterations per tile, padded to whole blocks of P
+    const int JA = RELOAD ? 1 : JP;      // iterations kept in LDS
     const int NT = (N + 15) >> 4;
     // The four 16-row tiles of a 64-row block share the 128-byte lines of
     // their group-major scales: they go to workgroups that the hardware's
@@ -151,32 +149,38 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     const int v = 4 * ((ib >> 2) * 8 + (b & 7)) + (ib & 3);
     const int ntiles = v < NT ? (NT - v + nwg - 1) / nwg : 0;
 
-    // finishing thread of a tile: token ft, row fr
+    // With the argmax, thread (ft, fr) finishes row fr of token ft.
     const int ft = tid >> 4, fr = tid & 15;
-    const bool fin = tid < 16 * T;
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
     if (ntiles == 0) {
-        if (AMAX && fin && fr == 0) amax[(int64_t)ft * nwg + b] = Best{bv, bi};
+        if (AMAX && ft < Tr && fr == 0) amax[(int64_t)ft * nwg + b] = Best{bv, bi};
         return;
     }
-    const float fxs = fin ? xs[ft] : 0.0f;
+    float fxs[FP];
+#pragma unroll
+    for (int k = 0; k < FP; k++) {
+        const int t = (tid + 256 * k) >> 4;
+        fxs[k] = !BS && t < Tr ? xs[t] : 0.0f;
+    }
 
     const auto rw = make_rsrc(wq, (uint32_t)((int64_t)N * (K / 2)));
     const auto rs = make_rsrc(wsg, (uint32_t)((int64_t)G * N * 2));
-    const auto rx = make_rsrc(xq, (uint32_t)(T * K));
+    const auto rx = make_rsrc(xq, (uint32_t)(Tr * K));
+    const auto rb = make_rsrc(xs, BS ? (uint32_t)(Tr * G * 4) : 0u);
     const uint32_t lq = 4u * wave + q;  // group of this lane within an iteration
     const int xc = lane & 7;            // 16-byte chunk of the quarter this lane loads
     const uint32_t xlane = 32u * (4u * wave + (xc >> 1)) + 16u * (xc & 1);
 
-    // One iteration j of a tile: the lane's 16 bytes of nibbles and scale, and
-    // on the first tile 16 bytes of activation codes per 8 tokens. Every load
-    // is issued unconditionally, so the compiler counts them statically: a
-    // row past N lies past the weights, a group past G (a ragged or padding
-    // iteration) and a tile past the list take the out-of-range bit, and all
-    // of these read zeros. Offsets stay below 2^32: the weights and scales are
-    // each under 2^31 bytes.
-    auto load = [&](SStage<T>& st, int tile, int j, bool with_act, uint32_t past) {
+    // One iteration j of a tile: the lane's 16 bytes of nibbles and scale,
+    // and with the activations, 16 bytes of codes per 8 tokens (and with block
+    // scales, one scale per lane for up to 64 (token, group) pairs). Every
+    // load is issued unconditionally, so the compiler counts them statically:
+    // a row past N lies past the weights, a group past G (a ragged or padding
+    // iteration), a token past Tr and a tile past the list take the
+    // out-of-range bit, and all of these read zeros. Offsets stay below 2^32:
+    // the weights and scales are each under 2^31 bytes.
+    auto load = [&](SStage<T, BS>& st, int tile, int j, bool with_act, uint32_t past) {
         const uint32_t bad = ((16 * j + (int)lq >= G) ? kOOB : 0u) | past;
         const uint32_t row = 16u * (uint32_t)tile + (uint32_t)r;
         st.w = load16(rw, (row * (uint32_t)(K / 2) + 16u * lq + 256u * (uint32_t)j) | bad);
@@ -185,34 +189,55 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
 #pragma unroll
             for (int x = 0; x < TX; x++) {
                 const int xt = (lane >> 3) + 8 * x;
-                const bool ok = xt < T && 16 * j + 4 * wave + (xc >> 1) < G;
+                const bool ok = xt < Tr && 16 * j + 4 * wave + (xc >> 1) < G;
                 st.x[x] = load16(rx, ((uint32_t)(xt * K + 512 * j) + xlane) | (ok ? 0u : kOOB));
+            }
+            if constexpr (BS) {
+#pragma unroll
+                for (int x = 0; x < XB; x++) {
+                    const int e = lane + 64 * x;  // (token e >> 2, group 16j + 4 wave + (e & 3))
+                    const int g = 16 * j + 4 * wave + (e & 3);
+                    const bool ok = (e >> 2) < Tr && g < G;
+                    st.xb[x] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(
+                                   rb, ((uint32_t)((e >> 2) * G + g) * 4u) | (ok ? 0u : kOOB), 0, 0));
+                }
             }
         }
     };
-    // Activation chunks go to LDS as [t][j][wave][128 bytes] (padding
-    // iterations store zeros). Only this wave reads its quarter, and a wave's
-    // LDS accesses complete in order, so no barrier is needed.
-    auto put_act = [&](const SStage<T>& st, int j) {
+    // LDS: activation chunks as [t][ja][wave][128 bytes] (ja = j, or 0 when
+    // reloading), the zero bytes, then with block scales [ja][wave][slot][T]
+    // floats. Only this wave reads what it stores, and a wave's LDS accesses
+    // complete in order, so no barrier is needed.
+    const int zero_off = T * JA * 512;
+    float* xbl = reinterpret_cast<float*>(act + zero_off + kStreamZero);
+    auto put_act = [&](const SStage<T, BS>& st, int j) {
+        const int ja = RELOAD ? 0 : j;
 #pragma unroll
         for (int x = 0; x < TX; x++) {
             const int xt = (lane >> 3) + 8 * x;
-            if (xt < T) *reinterpret_cast<v4i*>(act + ((xt * JP + j) * 4 + wave) * 128 + 16 * xc) = even_odd(st.x[x]);
+            if (xt < T) *reinterpret_cast<v4i*>(act + ((xt * JA + ja) * 4 + wave) * 128 + 16 * xc) = even_odd(st.x[x]);
+        }
+        if constexpr (BS) {
+#pragma unroll
+            for (int x = 0; x < XB; x++) {
+                const int e = lane + 64 * x;
+                if ((e >> 2) < T) xbl[((ja * 4 + wave) * 4 + (e & 3)) * T + (e >> 2)] = st.xb[x];
+            }
         }
     };
 
     // A operand addresses: token t = 4tt + tp of slot h, advanced by one
     // iteration per j; lanes whose A row is zero stay on the zero bytes.
-    const int zero_off = T * JP * 512;
     int abase[TT], astep[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; tt++) {
         const int t = 4 * tt + tp;
         const bool ok = q == h && t < T;
-        abase[tt] = ok ? (t * JP * 4 + wave) * 128 + h * 32 : zero_off;
-        astep[tt] = ok ? 512 : 0;
+        abase[tt] = ok ? (t * JA * 4 + wave) * 128 + h * 32 : zero_off;
+        astep[tt] = ok && !RELOAD ? 512 : 0;
     }
-    auto compute = [&](const SStage<T>& st, int j, float (&acc)[T]) {
+    auto compute = [&](const SStage<T, BS>& st, int j, float (&acc)[T]) {
         v4i a0[TT], a1[TT], d[TT];
 #pragma unroll
         for (int tt = 0; tt < TT; tt++) {
@@ -221,15 +246,28 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
             a1[tt] = *reinterpret_cast<const v4i*>(act + off + 16);
         }
         quad_dots<TT>(st.w, a0, a1, d);
-        const float s16 = (float)__builtin_bit_cast(_Float16, st.s) * 0.0625f;
+        if constexpr (BS) {
+            // s = f32(scale) * xs[t][g], then s * f32(d), with d = 16d >> 4 exactly
+            const float ws32 = (float)__builtin_bit_cast(_Float16, st.s);
+            const float* xb = xbl + (((RELOAD ? 0 : j) * 4 + wave) * 4 + q) * T;
 #pragma unroll
-        for (int tt = 0; tt < TT; tt++)
+            for (int tt = 0; tt < TT; tt++)
 #pragma unroll
-            for (int u = 0; u < 4; u++)
-                if (4 * tt + u < T) acc[4 * tt + u] = acc[4 * tt + u] + s16 * (float)d[tt][u];
+                for (int u = 0; u < 4; u++) {
+                    const int t = 4 * tt + u;
+                    if (t < T) acc[t] = acc[t] + (ws32 * xb[t]) * (float)(d[tt][u] >> 4);
+                }
+        } else {
+            const float s16 = (float)__builtin_bit_cast(_Float16, st.s) * 0.0625f;
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++)
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    if (4 * tt + u < T) acc[4 * tt + u] = acc[4 * tt + u] + s16 * (float)d[tt][u];
+        }
     };
 
-    SStage<T> st[P];
+    SStage<T, BS> st[P];
 #pragma unroll
     for (int pp = 0; pp < P; pp++) {
         load(st[pp], v, pp, true, 0u);
@@ -239,26 +277,26 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     __syncthreads();
 
     auto run_tile = [&](auto first_tag, int k, float (&acc)[T]) {
-        constexpr bool FIRST = decltype(first_tag)::value;
+        constexpr bool WITH_ACT = decltype(first_tag)::value || RELOAD;  // this tile brings its activations
         const int tile = v + k * nwg;
         int j0 = 0;
         for (; j0 + P < JP; j0 += P) {
 #pragma unroll
             for (int pp = 0; pp < P; pp++) {
-                if (FIRST) put_act(st[pp], j0 + pp);
+                if (WITH_ACT) put_act(st[pp], j0 + pp);
                 compute(st[pp], j0 + pp, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                load(st[pp], tile, j0 + pp + P, FIRST, 0u);
+                load(st[pp], tile, j0 + pp + P, WITH_ACT, 0u);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         const uint32_t past = k + 1 < ntiles ? 0u : kOOB;
 #pragma unroll
         for (int pp = 0; pp < P; pp++) {
-            if (FIRST) put_act(st[pp], j0 + pp);
+            if (WITH_ACT) put_act(st[pp], j0 + pp);
             compute(st[pp], j0 + pp, acc);
             __builtin_amdgcn_sched_barrier(0);
-            load(st[pp], tile + nwg, pp, false, past);
+            load(st[pp], tile + nwg, pp, RELOAD, past);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -276,12 +314,16 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
             if (q == 0) red[buf][wave][t][r] = s;
         }
         __syncthreads();
-        if (fin) {
-            const int row = 16 * tile + fr;
-            const float val = fxs * ((red[buf][0][ft][fr] + red[buf][1][ft][fr]) +
-                                     (red[buf][2][ft][fr] + red[buf][3][ft][fr]));
-            if (row < N) {
-                if (!AMAX || write_y) y[(int64_t)ft * N + row] = val;
+#pragma unroll
+        for (int kk = 0; kk < FP; kk++) {
+            const int idx = tid + 256 * kk;
+            const int t = idx >> 4, rr = idx & 15;
+            const int row = 16 * tile + rr;
+            if (t < Tr && row < N) {
+                const float sum =
+                    (red[buf][0][t][rr] + red[buf][1][t][rr]) + (red[buf][2][t][rr] + red[buf][3][t][rr]);
+                const float val = BS ? sum : fxs[kk] * sum;
+                if (!AMAX || write_y) y[(int64_t)t * N + row] = val;
                 if (AMAX && better(val, row, bv, bi)) {
                     bv = val;
                     bi = row;
@@ -303,262 +345,27 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
         run_tile(std::false_type{}, k, acc);
         finish_tile(k, acc, k & 1);
     }
-    if (AMAX && fin) {
+    if (AMAX && ft < Tr) {
         best16(bv, bi);
         if (fr == 0) amax[(int64_t)ft * nwg + b] = Best{bv, bi};
     }
 }
 
-// ---------------------------------------------------------------- split
-
-// Split-K layout: a workgroup owns 64 rows (4 waves x 16) and one of S
-// K-slices, the Q = 4/S slot quads pQ .. pQ+Q-1 of every iteration. The S
-// workgroups of a row group are numbered so that the round-robin placement
-// puts them on one XCD, whose L2 serves the lines they share. A workgroup
-// stages its slice's activations in LDS as [t][j][Q*128 bytes] (j below J
-// rounded up to whole blocks of P, zeros past the last group), followed by
-// kSplitZero zero bytes that lanes whose A operand must be zero read.
-constexpr int kSplitZero = 512;
-
-template <int Q>
-struct WStage {
-    v4i w[Q];       // per slot quad: 16 bytes of nibbles (one group of one row)
-    uint16_t s[Q];  // and its fp16 scale
-};
-
-template <int T, int S>
-__global__ __launch_bounds__(256) void w4a8_linear_split_kernel(
-    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq,
-    const float* __restrict__ xs, float* __restrict__ y, float* __restrict__ part, int* __restrict__ cnt, int N,
-    int K) {
-    constexpr int Q = 4 / S;  // slot quads of the slice
-    constexpr int ROWS = 64;
-    constexpr int TT = (T + 3) / 4;
-    constexpr int P = SPECV_SPLIT_STAGES;
-    extern __shared__ __attribute__((aligned(16))) int8_t act[];
-    __shared__ int s_last;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int r = lane & 15;
-    const int q = lane >> 4;
-    const int h = (lane & 15) >> 2;
-    const int tp = lane & 3;
-    const int G = K >> 5;
-    const int J = (G + 15) >> 4;
-    const int JP = (J + P - 1) / P * P;
-    const int NG = (N + ROWS - 1) / ROWS;
-
-    const int b = blockIdx.x, ib = b >> 3;
-    const int p = ib % S;
-    const int rg = (ib / S) * 8 + (b & 7);
-    if (rg >= NG) return;
-    const int row = rg * ROWS + wave * 16 + r;
-    const bool row_ok = row < N;
-    const int quad0 = p * Q;
-
-    const auto rw = make_rsrc(wq, (uint32_t)((int64_t)N * (K / 2)));
-    const auto rs = make_rsrc(wsg, (uint32_t)((int64_t)G * N * 2));
-    const auto rx = make_rsrc(xq, (uint32_t)(T * K));
-
-    // The steady loop's loads are plain (in range, not a ragged last
-    // iteration); the last block or two take checked loads, where iterations
-    // past J, and in a ragged last iteration the lanes past G, take the
-    // out-of-range bit and read zeros.
-    const uint32_t wlane = (uint32_t)row * (uint32_t)(K / 2) + 16u * (uint32_t)(4 * quad0 + q);
-    const uint32_t slane = ((uint32_t)(4 * quad0 + q) * (uint32_t)N + (uint32_t)row) * 2u;
-    const bool ragged = (G & 15) != 0;
-    auto load_fast = [&](WStage<Q>& st, int j) {
-        const uint32_t wo = wlane + 256u * (uint32_t)j;
-        const uint32_t so = slane + 32u * (uint32_t)N * (uint32_t)j;
-#pragma unroll
-        for (int qq = 0; qq < Q; qq++) {
-            st.w[qq] = load16(rw, wo + 64u * (uint32_t)qq);
-            st.s[qq] = load2(rs, so + 8u * (uint32_t)N * (uint32_t)qq);
-        }
-    };
-    auto load_stage = [&](WStage<Q>& st, int j) {
-        const uint32_t wo = wlane + 256u * (uint32_t)j;
-        const uint32_t so = slane + 32u * (uint32_t)N * (uint32_t)j;
-        const uint32_t past = j >= J ? kOOB : 0u;
-#pragma unroll
-        for (int qq = 0; qq < Q; qq++) {
-            const uint32_t bad = past | ((uint32_t)(16 * j + 4 * (quad0 + qq) + q >= G) << 31);
-            st.w[qq] = load16(rw, (wo + 64u * (uint32_t)qq) | bad);
-            st.s[qq] = load2(rs, (so + 8u * (uint32_t)N * (uint32_t)qq) | bad);
-        }
-    };
-
-    WStage<Q> st[P];
-#pragma unroll
-    for (int pp = 0; pp < P; pp++) {
-        load_stage(st[pp], pp);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // Stage the slice's activations in rounds of U chunks per thread; the
-    // loads of round r + 1 are issued before the LDS writes of round r, so
-    // the rounds' L2 round trips overlap.
-    const int nchunks = T * JP * Q * 8;  // 16-byte chunks
-    constexpr int U = 8;
-    auto stage_load = [&](v4i (&vv)[U], int base) {
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            if (base + u * 256 >= nchunks) break;
-            const int i = base + u * 256 + tid;
-            const int c = i % (Q * 8);
-            const int tj = i / (Q * 8);
-            const int j = tj % JP;
-            const int t = tj / JP;
-            const int g = 16 * j + 4 * quad0 + (c >> 1);
-            const bool ok = i < nchunks && g < G;
-            vv[u] = load16(rx, ((uint32_t)(t * K + 32 * g + 16 * (c & 1))) | ((uint32_t)!ok << 31));
-        }
-    };
-    auto stage_store = [&](const v4i (&vv)[U], int base) {
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            if (base + u * 256 >= nchunks) break;
-            const int i = base + u * 256 + tid;
-            if (i < nchunks) *reinterpret_cast<v4i*>(act + 16 * i) = even_odd(vv[u]);
-        }
-    };
-    {
-        v4i va[U], vb[U];
-        stage_load(va, 0);
-        for (int base = 0; base < nchunks; base += 512 * U) {
-            const bool more = base + 256 * U < nchunks;
-            if (more) stage_load(vb, base + 256 * U);
-            stage_store(va, base);
-            if (!more) break;
-            if (base + 512 * U < nchunks) stage_load(va, base + 512 * U);
-            stage_store(vb, base + 256 * U);
-        }
-    }
-    const int zero_off = nchunks * 16;
-    if (tid < kSplitZero / 16) *reinterpret_cast<v4i*>(act + zero_off + 16 * tid) = v4i{0, 0, 0, 0};
-    __syncthreads();
-
-    float acc[Q][T];
-#pragma unroll
-    for (int qq = 0; qq < Q; qq++)
-#pragma unroll
-        for (int t = 0; t < T; t++) acc[qq][t] = 0.0f;
-
-    int abase[TT], astep[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; tt++) {
-        const int t = 4 * tt + tp;
-        const bool ok = q == h && t < T;
-        abase[tt] = ok ? (t * JP * Q) * 128 + h * 32 : zero_off;
-        astep[tt] = ok ? Q * 128 : 0;
-    }
-    auto compute = [&](const WStage<Q>& stg, int j) {
-#pragma unroll
-        for (int qq = 0; qq < Q; qq++) {
-            v4i a0[TT], a1[TT], d[TT];
-#pragma unroll
-            for (int tt = 0; tt < TT; tt++) {
-                const int off = abase[tt] + j * astep[tt] + qq * 128;  // zero lanes: within the zero bytes
-                a0[tt] = *reinterpret_cast<const v4i*>(act + off);
-                a1[tt] = *reinterpret_cast<const v4i*>(act + off + 16);
-            }
-            quad_dots<TT>(stg.w[qq], a0, a1, d);
-            const float s16 = (float)__builtin_bit_cast(_Float16, stg.s[qq]) * 0.0625f;
-#pragma unroll
-            for (int tt = 0; tt < TT; tt++)
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    if (4 * tt + u < T) acc[qq][4 * tt + u] = acc[qq][4 * tt + u] + s16 * (float)d[tt][u];
-        }
-    };
-
-    const int Jsafe = ragged ? J - 1 : J;
-    int j0 = 0;
-    for (; j0 + 2 * P <= Jsafe; j0 += P) {
-#pragma unroll
-        for (int pp = 0; pp < P; pp++) {
-            compute(st[pp], j0 + pp);
-            __builtin_amdgcn_sched_barrier(0);
-            load_fast(st[pp], j0 + pp + P);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    for (; j0 < J; j0 += P) {
-#pragma unroll
-        for (int pp = 0; pp < P; pp++) {
-            compute(st[pp], j0 + pp);
-            __builtin_amdgcn_sched_barrier(0);
-            load_stage(st[pp], j0 + pp + P);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // Tree levels w = 1, 2 pair the four slots of a quad (lanes q ^ 1, q ^ 2);
-    // with two quads, level w = 4 adds them inside the lane.
-    float val[Q][T];
-#pragma unroll
-    for (int qq = 0; qq < Q; qq++)
-#pragma unroll
-        for (int t = 0; t < T; t++) {
-            float v = acc[qq][t];
-            v = v + __shfl_xor(v, 16, 64);
-            v = v + __shfl_xor(v, 32, 64);
-            val[qq][t] = v;
-        }
-
-    // Partials and counters use device-scope relaxed atomic accesses: they
-    // are coherent across the XCDs' separate L2 caches without a device-scope
-    // fence (which would write back the whole L2). All partial stores of the
-    // workgroup complete (s_waitcnt, then the barrier) before its counter
-    // increment, so the workgroup that observes the final count reads every
-    // partial.
-    if (q == 0 && row_ok)
-#pragma unroll
-        for (int t = 0; t < T; t++)
-            __hip_atomic_store(&part[((int64_t)p * T + t) * N + row], (Q == 2) ? (val[0][t] + val[1 % Q][t]) : val[0][t],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0)
-        s_last = (__hip_atomic_fetch_add(&cnt[rg], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1);
-    __syncthreads();
-    if (!s_last) return;
-    const int64_t ps = (int64_t)T * N;
-    for (int idx = tid; idx < ROWS * T; idx += 256) {
-        const int t = idx / ROWS;
-        const int orow = rg * ROWS + idx % ROWS;
-        if (orow >= N) continue;
-        float* pp = part + (int64_t)t * N + orow;
-        float v[S];
-#pragma unroll
-        for (int k = 0; k < S; k++) v[k] = __hip_atomic_load(pp + k * ps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float tot = (S == 2) ? v[0] + v[1 % S] : (v[0] + v[1 % S]) + (v[2 % S] + v[3 % S]);
-        y[(int64_t)t * N + orow] = xs[t] * tot;
-    }
-    if (tid == 0) __hip_atomic_store(&cnt[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ---------------------------------------------------------------- host
 
 constexpr size_t kLdsBudget = 150 * 1024;
-enum { kStream = 1 };  // layout; a split layout is its slice count S in {2, 4}
 
-// Dynamic LDS of a streaming workgroup (its tile reduction buffer, 512T
-// bytes, is static).
-inline size_t stream_lds_bytes(int T, int K) {
+// Dynamic LDS of a workgroup (its tile reduction buffer, 512T bytes, is
+// static): the activation quarters of JA iterations, the zero bytes, and the
+// block scales.
+inline size_t stream_lds_bytes(int T, int K, bool bs, bool reload) {
     const int J = (K / 32 + 15) / 16;
-    const int JP = (J + SPECV_STREAM_STAGES - 1) / SPECV_STREAM_STAGES * SPECV_STREAM_STAGES;
-    return (size_t)T * JP * 512 + kStreamZero;
+    const int JA = reload ? 1 : (J + SPECV_STREAM_STAGES - 1) / SPECV_STREAM_STAGES * SPECV_STREAM_STAGES;
+    return (size_t)T * JA * 512 + kStreamZero + (bs ? (size_t)JA * 64 * T : 0);
 }
-inline bool stream_fits(int T, int K) { return stream_lds_bytes(T, K) + (size_t)T * 512 <= kLdsBudget; }
-
-// Staged activation bytes of a split workgroup with S slices.
-inline size_t split_lds_bytes(int T, int K, int S) {
-    const int J = (K / 32 + 15) / 16;
-    const int JP = (J + SPECV_SPLIT_STAGES - 1) / SPECV_SPLIT_STAGES * SPECV_SPLIT_STAGES;
-    return (size_t)T * JP * (4 / S) * 128 + kSplitZero;
+// Whether the activations of every iteration fit beside the reduction buffer.
+inline bool stream_keeps(int T, int K, bool bs) {
+    return stream_lds_bytes(T, K, bs, false) + (size_t)T * 512 <= kLdsBudget;
 }
 
 // Compute units of the current device (cached per device).
@@ -574,32 +381,14 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Workgroups of a streaming launch: a multiple of 32 (the tile numbering
-// needs it), no more than the tiles need, about WGS_PER_CU per CU.
+// Workgroups of a launch: a multiple of 32 (the tile numbering needs it), no
+// more than the tiles need, about WGS_PER_CU per CU.
 inline int stream_grid(int N) {
     const int NT = (N + 15) / 16;
     const int cap = (device_cus() * SPECV_STREAM_WGS_PER_CU + 31) / 32 * 32;
     const int need = (NT + 31) / 32 * 32;
     return need < cap ? need : cap;
 }
-
-// Layout for a shape: streaming when a wave's activation quarter of every
-// token fits in LDS; otherwise K split in 2 slices (many rows) or 4.
-inline int linear_mode(int T, int N, int K) {
-    if (stream_fits(T, K)) return kStream;
-    return split_lds_bytes(T, K, 2) <= kLdsBudget && (N + 63) / 64 >= 256 ? 2 : 4;
-}
-
-inline int linear_row_groups_padded(int N) {
-    const int NG = (N + 63) / 64;
-    return (NG + 7) / 8 * 8;
-}
-
-// Split-K workspace: one counter per row group in a fixed region sized for
-// the largest N (so its location never depends on the call), then the
-// partials. Only the counters must start at zero; every call returns the
-// counters it used to zero, and partials are written before they are read.
-constexpr size_t kCounterBytes = (size_t)((1 << 24) / 64) * 4;
 
 // Events for the next linear launch of this host thread (timing diagnostics).
 static thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
@@ -616,60 +405,41 @@ static int enable_lds(const void* kernel, size_t lds, size_t& enabled) {
     return SPECV_OK;
 }
 
-template <int T>
-static int launch_stream(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                         Best* amax, int N, int K, hipStream_t s) {
+template <int T, bool AMAX, bool BS, bool RELOAD>
+static int launch_one(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
+                      Best* amax, int Tr, int N, int K, hipStream_t s) {
     constexpr int P = SPECV_STREAM_STAGES;
-    const int write_y = y != nullptr;
     static size_t lds_enabled = 64 * 1024;
-    const size_t lds = stream_lds_bytes(T, K);
-    if (!stream_fits(T, K)) return SPECV_E_SHAPE;
-    const int grid = stream_grid(N);
-    auto go = [&](auto kernel, size_t& enabled) {
-        const int rc = enable_lds(reinterpret_cast<const void*>(kernel), lds, enabled);
-        if (rc != SPECV_OK) return rc;
-        if (g_time_start) {
-            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, g_time_start, g_time_stop, 0, wq, ws, xq, N,
-                                  K, grid, xs, y, write_y, amax);
-            g_time_start = g_time_stop = nullptr;
-        } else {
-            hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, wq, ws, xq, N, K, grid, xs, y, write_y, amax);
-        }
-        return launch_status();
-    };
-    static size_t lds_enabled_amax = 64 * 1024;
-    return amax ? go(&w4a8_linear_stream_kernel<T, P, true>, lds_enabled_amax)
-                : go(&w4a8_linear_stream_kernel<T, P, false>, lds_enabled);
-}
-
-template <int T, int S>
-static int launch_split(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                        float* part, int* cnt, int N, int K, hipStream_t s) {
-    static size_t lds_enabled = 64 * 1024;
-    const size_t lds = split_lds_bytes(T, K, S);
-    if (lds > kLdsBudget) return SPECV_E_SHAPE;
-    const int rc = enable_lds(reinterpret_cast<const void*>(&w4a8_linear_split_kernel<T, S>), lds, lds_enabled);
+    const size_t lds = stream_lds_bytes(T, K, BS, RELOAD);
+    if (lds + (size_t)T * 512 > kLdsBudget) return SPECV_E_SHAPE;
+    auto kernel = &w4a8_linear_stream_kernel<T, P, AMAX, BS, RELOAD>;
+    const int rc = enable_lds(reinterpret_cast<const void*>(kernel), lds, lds_enabled);
     if (rc != SPECV_OK) return rc;
-    const int grid = S * linear_row_groups_padded(N);
+    const int grid = stream_grid(N);
+    const int write_y = y != nullptr;
     if (g_time_start) {
-        hipExtLaunchKernelGGL((w4a8_linear_split_kernel<T, S>), dim3(grid), dim3(256), lds, s, g_time_start,
-                              g_time_stop, 0, wq, ws, xq, xs, y, part, cnt, N, K);
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, g_time_start, g_time_stop, 0, wq, ws, xq, N, K,
+                              grid, Tr, xs, y, write_y, amax);
         g_time_start = g_time_stop = nullptr;
     } else {
-        hipLaunchKernelGGL((w4a8_linear_split_kernel<T, S>), dim3(grid), dim3(256), lds, s, wq, ws, xq, xs, y, part,
-                           cnt, N, K);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, wq, ws, xq, N, K, grid, Tr, xs, y, write_y, amax);
     }
     return launch_status();
 }
 
-template <int T>
-static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                    Best* amax, float* part, int* cnt, int N, int K, hipStream_t s) {
-    switch (linear_mode(T, N, K)) {
-        case kStream: return launch_stream<T>(wq, ws, xq, xs, y, amax, N, K, s);
-        case 2: return amax ? SPECV_E_SHAPE : launch_split<T, 2>(wq, ws, xq, xs, y, part, cnt, N, K, s);
-        default: return amax ? SPECV_E_SHAPE : launch_split<T, 4>(wq, ws, xq, xs, y, part, cnt, N, K, s);
+template <int T, bool BS>
+static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
+                    int Tr, int N, int K, hipStream_t s) {
+    const bool keep = stream_keeps(T, K, BS);
+    if constexpr (T <= 16 && !BS) {
+        if (amax)
+            return keep ? launch_one<T, true, false, false>(wq, ws, xq, xs, y, amax, Tr, N, K, s)
+                        : launch_one<T, true, false, true>(wq, ws, xq, xs, y, amax, Tr, N, K, s);
+    } else {
+        if (amax) return SPECV_E_SHAPE;
     }
+    return keep ? launch_one<T, false, BS, false>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s)
+                : launch_one<T, false, BS, true>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s);
 }
 
 // Finishes the argmax of each token from its workgroups' (value, row) pairs.
@@ -697,26 +467,48 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const Best* __restri
     }
 }
 
-bool linear_argmax_supported(int T, int N, int K) { return linear_mode(T, N, K) == kStream; }
+bool linear_argmax_supported(int T, int N, int K) { return T >= 1 && T <= 16 && N >= 1 && K >= 32; }
 
 int linear_argmax_chunks(int T, int N, int K) { return linear_argmax_supported(T, N, K) ? stream_grid(N) : 0; }
 
-// Validated arguments. y may be null when amax is set; the argmax epilogue
-// needs the streaming layout (linear_argmax_supported).
-int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
-                   int T, int N, int K, void* workspace, hipStream_t s) {
-    int* cnt = static_cast<int*>(workspace);
-    const size_t need = w4a8_linear_workspace(T, N, K);
-    float* part = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+// Validated arguments. y may be null when amax is set (T <= 16, per-token
+// scales). bs: xs holds per-block scales [T][K/32].
+static int linear_dispatch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
+                           Best* amax, int T, int N, int K, bool bs, hipStream_t s) {
     switch (T) {
-#define SPECV_CASE(n) \
-    case n: return launch_T<n>(wq, ws, xq, xs, y, amax, part, cnt, N, K, s);
+#define SPECV_CASE(n)                                                  \
+    case n:                                                            \
+        return bs ? launch_T<n, true>(wq, ws, xq, xs, y, amax, n, N, K, s) \
+                  : launch_T<n, false>(wq, ws, xq, xs, y, amax, n, N, K, s);
         SPECV_CASE(1) SPECV_CASE(2) SPECV_CASE(3) SPECV_CASE(4) SPECV_CASE(5) SPECV_CASE(6)
         SPECV_CASE(7) SPECV_CASE(8) SPECV_CASE(9) SPECV_CASE(10) SPECV_CASE(11) SPECV_CASE(12)
         SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
 #undef SPECV_CASE
-        default: return SPECV_E_SHAPE;
+        default:
+            if (T > 16 && T <= 32)  // the 32-token bucket
+                return bs ? launch_T<32, true>(wq, ws, xq, xs, y, amax, T, N, K, s)
+                          : launch_T<32, false>(wq, ws, xq, xs, y, amax, T, N, K, s);
+            return SPECV_E_SHAPE;
     }
+}
+
+int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
+                   int T, int N, int K, void* /*workspace*/, hipStream_t s) {
+    return linear_dispatch(wq, ws, xq, xs, y, amax, T, N, K, false, s);
+}
+
+// Shape and pointer checks shared by the linear entry points (N >= 1).
+static int linear_args(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, int32_t T,
+                       int32_t N, int32_t K) {
+    if (T < 1 || T > 32 || N < 1 || N > (1 << 24) || K < 32 || K > (1 << 20) || K % 32) return SPECV_E_SHAPE;
+    if ((int64_t)N * (K / 2) >= (int64_t)1 << 31) return SPECV_E_SHAPE;
+    if (!wq || !ws || !xq || !xs) return SPECV_E_INVAL;
+    if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(ws, 2) || !aligned(xs, 4)) return SPECV_E_ALIGN;
+    return SPECV_OK;
+}
+
+static bool empty_call(int32_t T, int32_t N, int32_t K) {
+    return T >= 1 && T <= 32 && N == 0 && K >= 32 && K <= (1 << 20) && K % 32 == 0;
 }
 
 }  // namespace specv
@@ -728,29 +520,31 @@ extern "C" int specv_time_next_linear(void* start_event, void* stop_event) {
     return SPECV_OK;
 }
 
-extern "C" size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K) {
-    using namespace specv;
-    if (T < 1 || T > 16 || N < 1 || K < 32 || K % 32) return 0;
-    const int mode = linear_mode(T, N, K);
-    if (mode == kStream) return 0;
-    return kCounterBytes + (size_t)mode * T * N * 4;
-}
+extern "C" size_t w4a8_linear_workspace(int32_t, int32_t, int32_t) { return 0; }
 
 extern "C" int w4a8_linear_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
                              float* y, int32_t T, int32_t N, int32_t K, void* workspace,
                              size_t workspace_bytes, void* stream) {
     using namespace specv;
-    if (T < 1 || T > 16 || N < 0 || N > (1 << 24) || K < 32 || K > (1 << 20) || K % 32)
-        return SPECV_E_SHAPE;
-    if ((int64_t)N * (K / 2) >= (int64_t)1 << 31) return SPECV_E_SHAPE;
-    if (N == 0) return SPECV_OK;
-    if (!wq || !ws || !xq || !xs || !y) return SPECV_E_INVAL;
-    if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(ws, 2) || !aligned(xs, 4) || !aligned(y, 4))
-        return SPECV_E_ALIGN;
-    const size_t need = w4a8_linear_workspace(T, N, K);
-    if (need && (!workspace || workspace_bytes < need)) return SPECV_E_WORKSPACE;
-    if (need && !aligned(workspace, 256)) return SPECV_E_ALIGN;
-    return linear_enqueue(wq, ws, xq, xs, y, nullptr, T, N, K, workspace, (hipStream_t)stream);
+    (void)workspace;
+    (void)workspace_bytes;
+    if (empty_call(T, N, K)) return SPECV_OK;
+    const int rc = linear_args(wq, ws, xq, xs, T, N, K);
+    if (rc != SPECV_OK) return rc;
+    if (!y) return SPECV_E_INVAL;
+    if (!aligned(y, 4)) return SPECV_E_ALIGN;
+    return linear_dispatch(wq, ws, xq, xs, y, nullptr, T, N, K, false, (hipStream_t)stream);
+}
+
+extern "C" int w4a8_linear_blocks_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
+                                    float* y, int32_t T, int32_t N, int32_t K, void* stream) {
+    using namespace specv;
+    if (empty_call(T, N, K)) return SPECV_OK;
+    const int rc = linear_args(wq, ws, xq, xs, T, N, K);
+    if (rc != SPECV_OK) return rc;
+    if (!y) return SPECV_E_INVAL;
+    if (!aligned(y, 4)) return SPECV_E_ALIGN;
+    return linear_dispatch(wq, ws, xq, xs, y, nullptr, T, N, K, true, (hipStream_t)stream);
 }
 
 extern "C" size_t w4a8_linear_argmax_workspace(int32_t T, int32_t N, int32_t K) {
@@ -763,20 +557,18 @@ extern "C" int w4a8_linear_argmax_T(const uint8_t* wq, const uint16_t* ws, const
                                     float* y, int32_t* argmax, int32_t T, int32_t N, int32_t K, void* workspace,
                                     size_t workspace_bytes, void* stream) {
     using namespace specv;
-    if (T < 1 || T > 16 || N < 1 || N > (1 << 24) || K < 32 || K > (1 << 20) || K % 32) return SPECV_E_SHAPE;
-    if ((int64_t)N * (K / 2) >= (int64_t)1 << 31) return SPECV_E_SHAPE;
-    if (!linear_argmax_supported(T, N, K)) return SPECV_E_SHAPE;
-    if (!wq || !ws || !xq || !xs || !argmax) return SPECV_E_INVAL;
-    if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(ws, 2) || !aligned(xs, 4) || !aligned(y, 4) ||
-        !aligned(argmax, 4))
-        return SPECV_E_ALIGN;
+    if (T < 1 || T > 16) return SPECV_E_SHAPE;
+    const int rc = linear_args(wq, ws, xq, xs, T, N, K);
+    if (rc != SPECV_OK) return rc;
+    if (!argmax) return SPECV_E_INVAL;
+    if (!aligned(y, 4) || !aligned(argmax, 4)) return SPECV_E_ALIGN;
     const size_t need = w4a8_linear_argmax_workspace(T, N, K);
     if (!workspace || workspace_bytes < need) return SPECV_E_WORKSPACE;
     if (!aligned(workspace, 8)) return SPECV_E_ALIGN;
     hipStream_t s = (hipStream_t)stream;
     Best* part = static_cast<Best*>(workspace);
-    const int rc = linear_enqueue(wq, ws, xq, xs, y, part, T, N, K, nullptr, s);
-    if (rc != SPECV_OK) return rc;
+    const int lrc = linear_dispatch(wq, ws, xq, xs, y, part, T, N, K, false, s);
+    if (lrc != SPECV_OK) return lrc;
     hipLaunchKernelGGL(argmax_finish_kernel, dim3(T), dim3(256), 0, s, part, linear_argmax_chunks(T, N, K), argmax);
     return launch_status();
 }

@@ -87,7 +87,53 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_reg_kernel(
     }
 }
 
+// Per-block variant (one scale per token and 32 inputs): eight lanes own a
+// block, four values each; the block's max is taken over the eight lanes
+// (exact in any order), and the scale and reciprocal are single IEEE
+// divisions as above. Blocks are consecutive 128-byte runs of x, since
+// K % 32 == 0, and xs[t][g] is the block's index in that run.
+__global__ __launch_bounds__(kQuantThreads) void quantize_act_blocks_kernel(
+    const float* __restrict__ x, int64_t nblocks, int8_t* __restrict__ xq, float* __restrict__ xs) {
+    const int64_t gi = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    const int64_t blk = gi >> 3;
+    const int part = (int)(gi & 7);
+    const bool ok = blk < nblocks;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (ok) v = *reinterpret_cast<const float4*>(x + 32 * blk + 4 * part);
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    a = fmaxf(a, __shfl_xor(a, 4, 64));
+    const bool zero = (a == 0.0f);
+    const float inv = zero ? 0.0f : 127.0f / a;
+    if (!ok) return;
+    if (part == 0) xs[blk] = zero ? 0.0f : a / 127.0f;
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float r = __builtin_rintf(e[i] * inv);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        packed |= ((uint32_t)(int)r & 0xffu) << (8 * i);
+    }
+    *reinterpret_cast<uint32_t*>(xq + 32 * blk + 4 * part) = packed;
+}
+
 }  // namespace specv
+
+extern "C" int w4a8_quantize_act_blocks(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs, void* stream) {
+    using namespace specv;
+    if (T < 0 || T > (1 << 20) || K < 32 || K > (1 << 24) || K % 32) return SPECV_E_SHAPE;
+    if ((int64_t)T * K >= (int64_t)1 << 31) return SPECV_E_SHAPE;
+    if (T == 0) return SPECV_OK;
+    if (!x || !xq || !xs) return SPECV_E_INVAL;
+    if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xs, 4)) return SPECV_E_ALIGN;
+    const int64_t nblocks = (int64_t)T * (K / 32);
+    const int64_t grid = (nblocks * 8 + kQuantThreads - 1) / kQuantThreads;
+    hipLaunchKernelGGL(quantize_act_blocks_kernel, dim3((unsigned)grid), dim3(kQuantThreads), 0, (hipStream_t)stream,
+                       x, nblocks, xq, xs);
+    return launch_status();
+}
 
 extern "C" int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs,
                                  void* stream) {

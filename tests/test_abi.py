@@ -61,29 +61,35 @@ A = 0x10000  # a fake, 64 KiB-aligned address: validation never dereferences it
 
 
 def test_linear_rejects_bad_arguments(lib):
-    f = lib.w4a8_linear_T
-    W = 1 << 30  # workspace bytes: larger than any shape below needs
-    assert f(A, A, A, A, A, 1, 16, 33, A, W, None) == E_SHAPE      # K not a multiple of 32
-    assert f(A, A, A, A, A, 0, 16, 64, A, W, None) == E_SHAPE      # T < 1
-    assert f(A, A, A, A, A, 17, 16, 64, A, W, None) == E_SHAPE     # T > 16
-    assert f(A, A, A, A, A, 1, -1, 64, A, W, None) == E_SHAPE
-    assert f(A, A, A, A, A, 1, 1 << 22, 1024, A, W, None) == E_SHAPE  # weights >= 2 GiB
-    assert f(None, A, A, A, A, 1, 16, 64, A, W, None) == E_INVAL
-    assert f(A, A, A, A, None, 1, 16, 64, A, W, None) == E_INVAL
-    assert f(A + 8, A, A, A, A, 1, 16, 64, A, W, None) == E_ALIGN   # wq not 16-byte aligned
-    assert f(A, A, A + 4, A, A, 1, 16, 64, A, W, None) == E_ALIGN   # xq not 16-byte aligned
-    assert f(A, A + 1, A, A, A, 1, 16, 64, A, W, None) == E_ALIGN
-    assert f(None, None, None, None, None, 1, 0, 64, None, 0, None) == OK  # N == 0: nothing to do
-    # workspace: only shapes whose staged activations overflow LDS split K
-    need = lib.w4a8_linear_workspace(16, 4096, 14336)
-    assert need == (1 << 20) + 4 * 16 * 4096 * 4                     # 4 slices
-    assert f(A, A, A, A, A, 16, 4096, 14336, None, 0, None) == E_WORKSPACE
-    assert f(A, A, A, A, A, 16, 4096, 14336, A, need - 1, None) == E_WORKSPACE
-    assert f(A, A, A, A, A, 16, 4096, 14336, A + 16, need, None) == E_ALIGN
-    assert lib.w4a8_linear_workspace(16, 16400, 10240) == (1 << 20) + 2 * 16 * 16400 * 4  # 2 slices
-    for T, N, K in ((8, 4096, 4096), (8, 4096, 14336), (8, 28672, 4096), (8, 128256, 4096), (16, 896, 4864)):
-        assert lib.w4a8_linear_workspace(T, N, K) == 0              # streaming layout: none
-    assert lib.w4a8_linear_workspace(0, 16, 64) == 0
+    for f, args in ((lib.w4a8_linear_T, lambda *a: a + (A, 1 << 30, None)),
+                    (lib.w4a8_linear_blocks_T, lambda *a: a + (None,))):
+        assert f(*args(A, A, A, A, A, 1, 16, 33)) == E_SHAPE        # K not a multiple of 32
+        assert f(*args(A, A, A, A, A, 0, 16, 64)) == E_SHAPE        # T < 1
+        assert f(*args(A, A, A, A, A, 33, 16, 64)) == E_SHAPE       # T > 32
+        assert f(*args(A, A, A, A, A, 1, -1, 64)) == E_SHAPE
+        assert f(*args(A, A, A, A, A, 1, 1 << 22, 1024)) == E_SHAPE  # weights >= 2 GiB
+        assert f(*args(None, A, A, A, A, 1, 16, 64)) == E_INVAL
+        assert f(*args(A, A, A, A, None, 1, 16, 64)) == E_INVAL
+        assert f(*args(A + 8, A, A, A, A, 1, 16, 64)) == E_ALIGN     # wq not 16-byte aligned
+        assert f(*args(A, A, A + 4, A, A, 1, 16, 64)) == E_ALIGN     # xq not 16-byte aligned
+        assert f(*args(A, A + 1, A, A, A, 1, 16, 64)) == E_ALIGN
+        assert f(*args(None, None, None, None, None, 1, 0, 64)) == OK  # N == 0: nothing to do
+        assert f(*args(None, None, None, None, None, 32, 0, 64)) == OK
+    # no layout needs a workspace
+    for T, N, K in ((8, 4096, 4096), (16, 4096, 14336), (32, 28672, 4096), (1, 16, 64)):
+        assert lib.w4a8_linear_workspace(T, N, K) == 0
+
+
+def test_quantize_blocks_rejects_bad_arguments(lib):
+    f = lib.w4a8_quantize_act_blocks
+    assert f(A, 2, 48, A, A, None) == E_SHAPE                     # K not a multiple of 32
+    assert f(A, -1, 64, A, A, None) == E_SHAPE
+    assert f(A, 1 << 20, 1 << 12, A, A, None) == E_SHAPE          # T*K >= 2^31
+    assert f(None, 2, 64, A, A, None) == E_INVAL
+    assert f(A, 2, 64, A, None, None) == E_INVAL
+    assert f(A + 4, 2, 64, A, A, None) == E_ALIGN                 # x not 16-byte aligned
+    assert f(A, 2, 64, A + 2, A, None) == E_ALIGN
+    assert f(None, 0, 64, None, None, None) == OK
 
 
 def test_time_next_linear_arguments(lib):
@@ -202,8 +208,9 @@ def test_linear_argmax_rejects_bad_arguments(lib):
     chunks = need // (8 * 8)
     assert need == 8 * chunks * 8 and chunks % 32 == 0 and 32 <= chunks <= (151936 // 16 + 31) // 32 * 32
     assert lib.w4a8_linear_argmax_workspace(8, 896, 896) == 8 * 64 * 8   # 56 tiles: 64 workgroups
-    assert lib.w4a8_linear_argmax_workspace(16, 4096, 14336) == 0     # staged rows exceed LDS: unsupported
-    assert f(A, A, A, A, None, A, 16, 4096, 14336, A, 1 << 20, None) == E_SHAPE
+    assert lib.w4a8_linear_argmax_workspace(16, 4096, 14336) == 16 * 256 * 8   # reloading layout: 256 tiles
+    assert lib.w4a8_linear_argmax_workspace(17, 4096, 4096) == 0     # argmax only up to 16 tokens
+    assert f(A, A, A, A, None, A, 17, 4096, 4096, A, 1 << 20, None) == E_SHAPE
     assert f(A, A, A, A, None, A, 8, 0, 896, A, need, None) == E_SHAPE   # no rows
     assert f(A, A, A, A, None, A, 0, 896, 896, A, need, None) == E_SHAPE
     assert f(A, A, A, A, None, None, 8, 151936, 896, A, need, None) == E_INVAL

@@ -110,7 +110,9 @@ def test_quantize_misaligned_rows(sv):
                                    # K split in 2 (>= 256 row groups) and unsplit (>= 1024)
                                    (3, 16400, 96), (8, 16385, 544), (5, 65601, 64), (16, 65600, 160),
                                    # several 16-row tiles per workgroup, ragged rows and groups
-                                   (8, 4100, 4864), (16, 4097, 8192), (1, 4111, 96), (2, 8211, 1056)])
+                                   (8, 4100, 4864), (16, 4097, 8192), (1, 4111, 96), (2, 8211, 1056),
+                                   # the 32-token bucket (17..32 tokens)
+                                   (20, 33, 896), (32, 100, 544), (25, 4100, 96), (17, 16, 32)])
 def test_linear_parity_ragged(sv, T, N, K):
     case(f"linear ragged T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(50 + T, T, N, K)
@@ -194,10 +196,12 @@ def test_linear_run_to_run_identical(sv):
     assert a.tobytes() == b.tobytes()
 
 
-@pytest.mark.parametrize("T,N,K", [(16, 16400, 10240), (16, 4096, 14336), (8, 4096, 14336), (8, 28672, 4096)])
+@pytest.mark.parametrize("T,N,K", [(16, 16400, 10240), (16, 4096, 14336), (8, 4096, 14336), (8, 28672, 4096),
+                                   (32, 4096, 14336), (24, 9728, 4864), (32, 28672, 4096), (17, 5000, 896)])
 def test_linear_layouts_sampled(sv, T, N, K):
-    """Two-slice and four-slice K splits (activations too large for LDS) and
-    the streaming layout at full size, on sampled rows."""
+    """Activations kept in LDS across a workgroup's tiles, and reloaded with
+    every tile when T x K does not fit (T = 16 at K = 14336 or 10240, and
+    the 32-token bucket at K = 4864 and 14336), on sampled rows."""
     case(f"linear layout T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(11, T, N, K)
     xq_o, xs_o = oracle.quantize_act(x)
@@ -206,23 +210,82 @@ def test_linear_layouts_sampled(sv, T, N, K):
     assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), f"T={T} N={N} K={K}")
 
 
-@pytest.mark.parametrize("T,N,K", [(16, 4096, 14336), (16, 16400, 10240), (8, 128256, 896)])
-def test_linear_workspace_reuse(sv, T, N, K):
-    """One zeroed workspace serves repeated calls and calls of other shapes:
-    the split-K counters are left at zero by every call."""
-    case(f"workspace reuse T={T} N={N} K={K}")
+@pytest.mark.parametrize("T,N,K", [(16, 4096, 14336), (16, 16400, 10240), (8, 128256, 896), (32, 8000, 4096)])
+def test_linear_repeated_and_interleaved_calls(sv, T, N, K):
+    """Calls of other shapes in between leave a shape's result unchanged."""
+    case(f"repeated calls T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(10, T, N, K)
     wq_d, ws_d = to_dev(wq), ws_dev(ws)
     xq, xs = sv.quantize_act(to_dev(x))
     first = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
-    for T2 in (1, 5, 16):
+    for T2 in (1, 5, 16, 27):
+        T2 = min(T2, T)
         sv.linear(wq_d[: N // 2].contiguous(), ws_d[:, : N // 2].contiguous(), xq[:T2].contiguous(),
                   xs[:T2].contiguous())
         again = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
         assert again.tobytes() == first.tobytes()
     rows = _sample_rows(N, 10, n=32)
     xq_o, xs_o = oracle.quantize_act(x)
-    assert_bits(first[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), "reuse sampled")
+    assert_bits(first[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), "repeat sampled")
+
+
+def test_linear_32_bucket_rows_equal_single_token(sv):
+    """Tokens 17..32 run in the 32-token kernel: every row still equals the
+    1-token call on its token (8B-shaped q projection)."""
+    N, K = LLAMA["q"]
+    wq, ws, x = sg.linear_case(12, 32, N, K)
+    wq_d, ws_d = to_dev(wq), ws_dev(ws)
+    xq, xs = sv.quantize_act(to_dev(x))
+    single = torch.cat([sv.linear(wq_d, ws_d, xq[t:t + 1].contiguous(), xs[t:t + 1].contiguous())
+                        for t in range(32)], 0).cpu().numpy()
+    for T in (17, 20, 31, 32):
+        case(f"32-token bucket T={T}")
+        yT = sv.linear(wq_d, ws_d, xq[:T].contiguous(), xs[:T].contiguous()).cpu().numpy()
+        assert_bits(yT, single[:T].copy(), f"T={T} vs single-token")
+
+
+# ------------------------------------------------------------------ per-block activation scales
+
+@pytest.mark.parametrize("T,K", [(1, 32), (3, 896), (8, 4096), (16, 14336), (32, 4864), (5, 96)])
+def test_quantize_blocks_parity(sv, T, K):
+    case(f"quantize blocks T={T} K={K}")
+    x = sg.normal_f32(sg.stream_key(60 + T, sg.TID_X), T * K).reshape(T, K)
+    x[0, :32] = 0.0                                  # an all-zero block
+    if K >= 96:
+        x[-1, 64:96] *= np.float32(1e-30)            # a block of tiny values
+    xq, xs = sv.quantize_act_blocks(to_dev(x))
+    torch.cuda.synchronize()
+    xq_o, xs_o = oracle.quantize_act_blocks(x)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert_bits(xs.cpu().numpy(), xs_o, "xs blocks")
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 16, 32), (3, 17, 64), (8, 100, 896), (16, 50, 4864), (2, 15, 14336),
+                                   (7, 4111, 96), (12, 64, 1024), (32, 40, 544), (20, 33, 896),
+                                   (16, 130, 14336), (32, 50, 4864)])
+def test_linear_blocks_parity(sv, T, N, K):
+    case(f"linear blocks T={T} N={N} K={K}")
+    wq, ws, x = sg.linear_case(80 + T, T, N, K)
+    xq, xs = sv.quantize_act_blocks(to_dev(x))
+    y = sv.linear_blocks(to_dev(wq), ws_dev(ws), xq, xs)
+    torch.cuda.synchronize()
+    xq_o, xs_o = oracle.quantize_act_blocks(x)
+    assert np.array_equal(xq.cpu().numpy(), xq_o)
+    assert_bits(y.cpu().numpy(), oracle.w4a8_linear_blocks(wq, ws, xq_o, xs_o), f"blocks T={T} N={N} K={K}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 16, 32])
+@pytest.mark.parametrize("name", ["q", "gate", "down", "lm_head"])
+def test_linear_blocks_llama_sampled(sv, name, T):
+    N, K = LLAMA[name]
+    case(f"linear blocks llama {name} N={N} K={K} T={T}")
+    wq, ws, wq_d, ws_d = _weights(0, N, K, 100 + list(LLAMA).index(name))
+    _, _, x = sg.linear_case(0, T, 1, K, layer=200 + list(LLAMA).index(name))
+    xq, xs = sv.quantize_act_blocks(to_dev(x))
+    y = sv.linear_blocks(wq_d, ws_d, xq, xs).cpu().numpy()
+    xq_o, xs_o = oracle.quantize_act_blocks(x)
+    rows = _sample_rows(N, 3, n=32)
+    assert_bits(y[:, rows].copy(), oracle.w4a8_linear_blocks(wq[rows], ws[rows], xq_o, xs_o), f"{name} T={T}")
 
 
 def test_linear_degenerate_values(sv):
