@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "cefaeac7b345e1448a8a0af7eb43d63fea0b33a034f32f925f6dcef8c15df15d",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33622780}
+LINEAR_TRAFFIC = {"source_sha256": "e1bba93002f29c9abe30855a3443469f6f310ab0c5db2f16cab908836ecbe4de",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33608300}
 
 
 def linear_traffic(T, workload):
@@ -559,7 +559,7 @@ def main():
                   for T, v in per_T.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": linear_traffic(args.T, args.workload),
-                     "kernel": f"w4a8_linear_stream_kernel<{args.T},4,*> (the lm_head runs the argmax specialisation)",
+                     "kernel": f"w4a8_linear_stream_kernel<{args.T},4,*,false,false> (the lm_head runs the argmax specialisation)",
                      "lm_head_chunks": model.lm_chunks(args.T),
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
