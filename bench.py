@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "e1bba93002f29c9abe30855a3443469f6f310ab0c5db2f16cab908836ecbe4de",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33608300}
+LINEAR_TRAFFIC = {"source_sha256": "c728c11a4cb18cea600e3effdc0ef34292a860c113272bf8741bd3cf8428f7d6",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33621583}
 
 
 def linear_traffic(T, workload):

@@ -76,6 +76,32 @@ __device__ __forceinline__ void best16(float& v, int& i) {
 // an ext-vector element expression as a cast of element 0.
 __device__ __forceinline__ float lane_f32(int v) { return __builtin_bit_cast(float, v); }
 
+// Deterministic exp: Cody-Waite reduction x = n*ln2 + r with ln2 split in
+// C1 (9 significant bits, n*C1 exact for |n| <= 128) and C2 = fl(ln2 - C1),
+// a degree-7 Taylor polynomial in r by Horner's rule (separate multiply and
+// add), and 2^n assembled from its exponent bits.
+__device__ __forceinline__ float det_exp(float x) {
+    if (x > 88.0f) return __builtin_inff();
+    if (x < -87.0f) return 0.0f;
+    const float inv_ln2 = 0x1.715476p+0f;
+    const float C1 = 0x1.63p-1f;
+    const float C2 = -0x1.bd0106p-13f;
+    const float n = __builtin_rintf(x * inv_ln2);
+    const float r = (x - n * C1) - n * C2;
+    float p = 0x1.a01a02p-13f;         // 1/7!
+    p = p * r + 0x1.6c16c2p-10f;       // 1/6!
+    p = p * r + 0x1.111112p-7f;        // 1/5!
+    p = p * r + 0x1.555556p-5f;        // 1/4!
+    p = p * r + 0x1.555556p-3f;        // 1/3!
+    p = p * r + 0x1.0p-1f;             // 1/2!
+    p = p * r + 1.0f;                  // 1/1!
+    p = p * r + 1.0f;                  // 1/0!
+    const int ni = (int)n;
+    return p * __builtin_bit_cast(float, (uint32_t)(ni + 127) << 23);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + det_exp(-g)); }
+
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? SPECV_OK : SPECV_E_HIP;
 }

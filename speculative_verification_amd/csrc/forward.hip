@@ -22,33 +22,6 @@
 
 namespace specv {
 
-// ---------------------------------------------------------------- exp
-
-// Deterministic exp: Cody-Waite reduction x = n*ln2 + r with ln2 split in
-// C1 (9 significant bits, n*C1 exact for |n| <= 128) and C2 = fl(ln2 - C1),
-// a degree-7 Taylor polynomial in r by Horner's rule (separate multiply and
-// add), and 2^n assembled from its exponent bits.
-__device__ __forceinline__ float det_exp(float x) {
-    if (x > 88.0f) return __builtin_inff();
-    if (x < -87.0f) return 0.0f;
-    const float inv_ln2 = 0x1.715476p+0f;
-    const float C1 = 0x1.63p-1f;
-    const float C2 = -0x1.bd0106p-13f;
-    const float n = __builtin_rintf(x * inv_ln2);
-    const float r = (x - n * C1) - n * C2;
-    float p = 0x1.a01a02p-13f;         // 1/7!
-    p = p * r + 0x1.6c16c2p-10f;       // 1/6!
-    p = p * r + 0x1.111112p-7f;        // 1/5!
-    p = p * r + 0x1.555556p-5f;        // 1/4!
-    p = p * r + 0x1.555556p-3f;        // 1/3!
-    p = p * r + 0x1.0p-1f;             // 1/2!
-    p = p * r + 1.0f;                  // 1/1!
-    p = p * r + 1.0f;                  // 1/0!
-    const int ni = (int)n;
-    return p * __builtin_bit_cast(float, (uint32_t)(ni + 127) << 23);
-}
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + det_exp(-g)); }
 
 // Value of another lane of the same 16-lane row, by a DPP control: 0xB1 and
 // 0x4E are the quad permutes of lane ^ 1 and lane ^ 2, 0x141 mirrors each
@@ -90,6 +63,13 @@ __device__ __forceinline__ uint16_t f32_to_f16(float x) {
 
 constexpr int kFwdThreads = 256;   // embedding and attention-chunk workgroups
 constexpr int kRowThreads = 1024;  // row kernels: norms, SiLU, attention merge
+// SiLU rows are produced by the down linear itself up to this many values
+// (tokens x intermediate): every workgroup recomputes them all, so the fused
+// prologue grows with the step and a separate row kernel wins past it.
+constexpr int64_t kSiluFuseMax = 6144;
+// Likewise RMSNorm rows up to this many tokens (one per wave): with two or
+// more per wave the redundant rows cost more than the row kernel's launch.
+constexpr int kNormFuseMaxT = 4;
 constexpr int kRowRegs = 4;        // float4 chunks per thread: rows up to 16384 values
 constexpr int kMergeRegs = 8;      // values per thread in the merge: rows up to 8192
 constexpr int kMaxNodes = 16;
@@ -582,6 +562,7 @@ StepLayout step_layout(const specv_model* m, int n) {
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     s.nchunk_max = nch;
     s.h = take(4 * n * H);
+    s.h2 = take(4 * n * H);  // the residual ping-pongs between h and h2 when the norms are fused
     s.delta = take(4 * n * H);
     s.xq = take(n * xq_cols);
     s.xs = take(4 * n);
@@ -663,6 +644,7 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     const int H = m->hidden, I = m->inter, V = m->vocab, nh = m->n_heads, nkv = m->n_kv_heads, hd = m->head_dim;
     const int QKV = (nh + 2 * nkv) * hd, A = nh * hd, cap = m->kv_capacity;
     float* h = reinterpret_cast<float*>(ws + lay.h);
+    float* h2 = reinterpret_cast<float*>(ws + lay.h2);
     float* delta = reinterpret_cast<float*>(ws + lay.delta);
     int8_t* xq = reinterpret_cast<int8_t*>(ws + lay.xq);
     float* xs = reinterpret_cast<float*>(ws + lay.xs);
@@ -678,6 +660,27 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     hipLaunchKernelGGL(embed_kernel, dim3(n), dim3(kFwdThreads), 0, s, token, parent, m->w_lm, m->s_lm, H, V, h,
                        tinfo, ctrl);
     SPECV_TRY(launch_status());
+    // RMSNorm (of h, or of h + resid with the sum kept as the new residual)
+    // and the linear that consumes it: one fused launch when the linear can
+    // produce its rows, else the row kernel and the linear. Fused, the
+    // residual alternates between h and h2.
+    float* hcur = h;
+    auto norm_linear = [&](const float* resid, const float* w, const uint8_t* wq, const uint16_t* ws_,
+                           float* y, Best* am, int N, bool keep) -> int {
+        if (n <= kNormFuseMaxT && linear_fused_supported(kProdNorm, n, H)) {
+            float* hnext = !resid || !keep ? nullptr : (hcur == h ? h2 : h);
+            ProdArgs pa{hcur, resid, w, hnext, m->eps, 0, ctrl};
+            const int rc = linear_enqueue_fused(kProdNorm, pa, wq, ws_, y, am, n, N, H, s);
+            if (hnext) hcur = hnext;
+            return rc;
+        }
+        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, hcur, resid, w,
+                           H, m->eps, xq, xs, ctrl);
+        SPECV_TRY(launch_status());
+        if (am) return linear_enqueue(wq, ws_, xq, xs, y, am, n, N, H, lin, s);
+        return w4a8_linear_T(wq, ws_, xq, xs, y, n, N, H, lin, linb, s);
+    };
+    const bool fuse_silu = (int64_t)n * I <= kSiluFuseMax && linear_fused_supported(kProdSilu, n, I);
     for (int l = 0; l < m->n_layers; l++) {
         const uint8_t* wqkv = m->w_qkv + (size_t)l * QKV * (H / 2);
         const uint16_t* sqkv = m->s_qkv + (size_t)l * (H / 32) * QKV;
@@ -688,10 +691,8 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
         const uint8_t* wd = m->w_down + (size_t)l * H * (I / 2);
         const uint16_t* sd = m->s_down + (size_t)l * (I / 32) * H;
 
-        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, h,
-                           l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, H, m->eps, xq, xs, ctrl);
-        SPECV_TRY(launch_status());
-        SPECV_TRY(w4a8_linear_T(wqkv, sqkv, xq, xs, qkv, n, QKV, H, lin, linb, s));
+        SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
+                              true));
         hipLaunchKernelGGL(rope_kv_kernel, dim3(n, nh + nkv), dim3(64), 0, s, qkv, tinfo, m->rope_cos,
                            m->rope_sin, m->max_pos, hd, nh, nkv, qrot, m->k_cache, m->v_cache, l, cap, ctrl);
         SPECV_TRY(launch_status());
@@ -703,19 +704,18 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
                            ctrl);
         SPECV_TRY(launch_status());
         SPECV_TRY(w4a8_linear_T(wo, so, xq, xs, delta, n, H, A, lin, linb, s));
-        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, h, delta,
-                           m->norm_mlp + (size_t)l * H, H, m->eps, xq, xs, ctrl);
-        SPECV_TRY(launch_status());
-        SPECV_TRY(w4a8_linear_T(wgu, sgu, xq, xs, gu, n, 2 * I, H, lin, linb, s));
-        hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(n), dim3(kRowThreads), 0, s, gu, I, xq, xs, ctrl);
-        SPECV_TRY(launch_status());
-        SPECV_TRY(w4a8_linear_T(wd, sd, xq, xs, delta, n, H, I, lin, linb, s));
+        SPECV_TRY(norm_linear(delta, m->norm_mlp + (size_t)l * H, wgu, sgu, gu, nullptr, 2 * I, true));
+        if (fuse_silu) {
+            ProdArgs pa{gu, nullptr, nullptr, nullptr, 0.0f, 0, ctrl};
+            SPECV_TRY(linear_enqueue_fused(kProdSilu, pa, wd, sd, delta, nullptr, n, H, I, s));
+        } else {
+            hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(n), dim3(kRowThreads), 0, s, gu, I, xq, xs, ctrl);
+            SPECV_TRY(launch_status());
+            SPECV_TRY(w4a8_linear_T(wd, sd, xq, xs, delta, n, H, I, lin, linb, s));
+        }
     }
-    hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, h, delta,
-                       m->norm_final, H, m->eps, xq, xs, ctrl);
-    SPECV_TRY(launch_status());
-    if (amax) return linear_enqueue(m->w_lm, m->s_lm, xq, xs, logits, amax, n, V, H, lin, s);
-    return w4a8_linear_T(m->w_lm, m->s_lm, xq, xs, logits, n, V, H, lin, linb, s);
+    // the residual is not needed after the final norm
+    return norm_linear(delta, m->norm_final, m->w_lm, m->s_lm, logits, amax, V, false);
 }
 
 int enqueue_step(const specv_model* m, int n, const int32_t* parent, const int32_t* token, float* logits,

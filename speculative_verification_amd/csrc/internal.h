@@ -9,12 +9,38 @@ namespace specv {
 
 // Byte offsets of one step's buffers inside the caller's workspace.
 struct StepLayout {
-    size_t h, delta, xq, xs, qkv, qrot, attn, gu, logits, argmax_part, tree, tinfo, wcounter, linear;
+    size_t h, h2, delta, xq, xs, qkv, qrot, attn, gu, logits, argmax_part, tree, tinfo, wcounter, linear;
     size_t linear_bytes, total;
     int nchunk_max;
 };
 
 StepLayout step_layout(const specv_model* m, int n_max);
+
+// Activation rows a linear can produce itself, in its prologue, instead of
+// reading codes a row kernel wrote: every workgroup computes the rows of all
+// tokens with the row kernel's arithmetic (so the codes are the same bits).
+//   kProdNorm: x = a (+ b), written to h_out by workgroup 0 when h_out is
+//              set; RMSNorm with weight w and eps; per-token quantisation.
+//   kProdSilu: z = silu(a[t][k]) * a[t][K + k]; per-token quantisation.
+// Tokens at or past ctrl->n_nodes, or all tokens once ctrl->done is set,
+// quantise to zero.
+enum { kProdNone = 0, kProdNorm = 1, kProdSilu = 2 };
+struct ProdArgs {
+    const float* a;
+    const float* b;
+    const float* w;
+    float* h_out;
+    float eps;
+    int pad;
+    const specv_ctrl* ctrl;
+};
+
+// W4A8 linear whose activations the kernel produces (T <= 16, per-token
+// scales, activations kept in LDS). Returns SPECV_E_SHAPE, enqueueing
+// nothing, when the shape does not allow it.
+int linear_enqueue_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const uint16_t* ws, float* y, Best* amax,
+                         int T, int N, int K, hipStream_t s);
+bool linear_fused_supported(int prod, int T, int K);
 int validate_model(const specv_model* m);
 
 // W4A8 linear on validated arguments; y may be null when amax is set. The

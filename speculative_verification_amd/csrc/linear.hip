@@ -55,6 +55,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "internal.h"
 
 namespace specv {
 
@@ -116,17 +117,307 @@ struct SStage {
     float xb[BS ? (4 * T + 63) / 64 : 1];  // block scales of the quarter's 4 groups, per token
 };
 
-template <int T, int P, bool AMAX, bool BS, bool RELOAD>
+// The activation rows of a fused linear (see ProdArgs), written as int8
+// codes in the layout [t][j][quarter][128 bytes] (each 8-input chunk in
+// even-then-odd order) with the token's scale in s_xs[t]. The arithmetic is
+// the row kernels': RMSNorm takes ss = R16 over the squares x*x (16 lanes,
+// each summing its slot in increasing k, then the lane tree), ms = ss / K,
+// rs = 1 / sqrt(ms + eps), y = (x * rs) * w; SiLU rows are
+// z = silu(gate) * up; both quantise with scale absmax / 127 and codes
+// rint(v * 127 / absmax) clamped to +-127. Every row load of a token is
+// issued before its first use, so a token costs about one memory round trip.
+constexpr int kProdRegs = 4;       // float4 chunks per lane of a RMSNorm row kept in registers (K <= 1024)
+constexpr int kSiluRegs = 6;       // float4 chunks per thread of a SiLU row (K <= 6144)
+constexpr int kSiluTokens = 2;     // SiLU rows a fused linear produces at most
+
+__device__ __forceinline__ float tree16_lanes(float v) {
+#define SPECV_DPP_ADD(ctrl) \
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false))
+    SPECV_DPP_ADD(0xB1);
+    SPECV_DPP_ADD(0x4E);
+    SPECV_DPP_ADD(0x141);
+    SPECV_DPP_ADD(0x140);
+#undef SPECV_DPP_ADD
+    return v;
+}
+
+// Lane l reads lane l ^ 1 (quad permutation 1, 0, 3, 2).
+__device__ __forceinline__ int swap_pair(int v) { return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); }
+
+// Maximum over the wave, uniform: each row of 16 lanes by DPP, then the four
+// rows' values read as scalars. Every lane must be active.
+__device__ __forceinline__ float wave_max(float v) {
+#define SPECV_DPP_MAX(ctrl) \
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false)))
+    SPECV_DPP_MAX(0xB1);
+    SPECV_DPP_MAX(0x4E);
+    SPECV_DPP_MAX(0x141);
+    SPECV_DPP_MAX(0x140);
+#undef SPECV_DPP_MAX
+    const int b = __builtin_bit_cast(int, v);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+
+__device__ __forceinline__ float max4(const float4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// Codes of inputs 4c .. 4c+3 (c = the calling lane's chunk). An 8-input
+// chunk is stored evens first, so chunk 2m holds bytes 0, 4, 1, 5 of its
+// 8-byte slot and chunk 2m + 1 bytes 2, 6, 3, 7: the even lane of a pair
+// (c even, its neighbour lane holding c + 1) writes all 8 bytes. Both lanes
+// of a pair must call this together, with chunks in range or not together.
+__device__ __forceinline__ uint32_t code_of(float v, float inv) {
+    float q = __builtin_rintf(v * inv);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (uint32_t)(uint8_t)(int8_t)(int)q;
+}
+
+__device__ __forceinline__ void put_codes(int8_t* rowb, int c, const float4 y, float inv) {
+    // this lane's evens (inputs 0, 2 of the chunk) and odds (1, 3), as byte pairs
+    const uint32_t ev = code_of(y.x, inv) | code_of(y.z, inv) << 8;
+    const uint32_t od = code_of(y.y, inv) | code_of(y.w, inv) << 8;
+    const uint32_t ev2 = (uint32_t)swap_pair((int)ev);
+    const uint32_t od2 = (uint32_t)swap_pair((int)od);
+    if ((c & 1) == 0) {
+        const int k0 = 4 * c;  // first input of the 8-input chunk
+        const int gi = k0 >> 5;
+        const int off = ((gi >> 4) * 4 + ((gi >> 2) & 3)) * 128 + (gi & 3) * 32 + (k0 & 31);
+        *reinterpret_cast<uint2*>(rowb + off) = make_uint2(ev | ev2 << 16, od | od2 << 16);
+    }
+}
+
+// Floats of a wave's RMSNorm buffer: the row (long rows), or its squares as
+// 16 slots of a stride rounded up to whole float4s.
+__host__ __device__ inline int norm_row_floats(int K) { return 16 * (((K >> 4) + 3) & ~3); }
+
+// Zero the staged row of token t (by one wave, or by the workgroup).
+__device__ __forceinline__ void zero_row_lds(int8_t* act, int t, int JP, int first, int step) {
+    v4i* row = reinterpret_cast<v4i*>(act + (size_t)t * JP * 512);
+    for (int c = first; c < JP * 32; c += step) row[c] = v4i{0, 0, 0, 0};
+}
+
+// The 16 slot sums of a row's squares in the R16 order: slot s adds
+// sq[s], sq[s + 16], ... in increasing k, then the lane tree. The squares
+// sit transposed in the wave's LDS buffer (slot s at sq[s * stride ...]), so
+// a slot lane reads its values as float4s, all issued before the adds.
+constexpr int kSlotRegs = 16;  // float4s per slot lane: rows up to 1024 values
+
+__device__ __forceinline__ float slot_sum_t(const float* sq, int K, int stride, int lane) {
+    float acc = 0.0f;
+    if (lane < 16) {
+        const int n16 = K >> 4;
+        float4 v[kSlotRegs];
+#pragma unroll
+        for (int i = 0; i < kSlotRegs; i++)
+            if (4 * i < n16) v[i] = *reinterpret_cast<const float4*>(sq + lane * stride + 4 * i);
+#pragma unroll
+        for (int i = 0; i < kSlotRegs; i++) {
+            const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                if (4 * i + u < n16) acc = acc + e[u];
+        }
+    }
+    acc = tree16_lanes(acc);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, acc)));
+}
+
+// RMSNorm rows: wave w takes tokens w, w + 4, ... Rows of up to 1024 values
+// live in registers, every load of the wave's tokens issued up front; longer
+// rows go through the wave's LDS row and read the weight twice.
+template <int T>
+__device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
+                             float* scratch) {
+    constexpr int TPW = (T + 3) / 4;  // tokens per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K4 = K >> 2;
+    const bool wb = pa.h_out && pa.b && blockIdx.x == 0;
+    float* xr = scratch + (size_t)wave * norm_row_floats(K);
+    if (K4 <= 64 * kProdRegs) {
+        float4 x[TPW][kProdRegs], d[TPW][kProdRegs], wv[kProdRegs];
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            const int t = wave + 4 * u;
+            if (t < T && t < Tr) {
+#pragma unroll
+                for (int i = 0; i < kProdRegs; i++) {
+                    const int c = lane + 64 * i;
+                    if (c < K4) {
+                        x[u][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * K + 4 * c);
+                        if (pa.b) d[u][i] = *reinterpret_cast<const float4*>(pa.b + (size_t)t * K + 4 * c);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kProdRegs; i++)
+            if (lane + 64 * i < K4) wv[i] = *reinterpret_cast<const float4*>(pa.w + 4 * (lane + 64 * i));
+        for (int t = wave; t < T; t += 4) {
+            zero_row_lds(act, t, JP, lane, 64);
+            if (lane == 0) s_xs[t] = 0.0f;
+        }
+        const int stride = ((K >> 4) + 3) & ~3;
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            const int t = wave + 4 * u;
+            if (t >= T || t >= Tr || t >= live) continue;
+            int8_t* rowb = act + (size_t)t * JP * 512;
+#pragma unroll
+            for (int i = 0; i < kProdRegs; i++) {
+                const int c = lane + 64 * i;
+                if (c >= K4) continue;
+                float4& v = x[u][i];
+                if (pa.b) v = make_float4(v.x + d[u][i].x, v.y + d[u][i].y, v.z + d[u][i].z, v.w + d[u][i].w);
+                if (wb) *reinterpret_cast<float4*>(pa.h_out + (size_t)t * K + 4 * c) = v;
+                // inputs 4c .. 4c+3: slots (4c & 15) + e, position 4c >> 4 within the slot
+                float* q = xr + (4 * c & 15) * stride + (c >> 2);
+                q[0] = v.x * v.x;
+                q[stride] = v.y * v.y;
+                q[2 * stride] = v.z * v.z;
+                q[3 * stride] = v.w * v.w;
+            }
+            const float ss = slot_sum_t(xr, K, stride, lane);
+            const float rs = 1.0f / sqrtf(ss / (float)K + pa.eps);
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kProdRegs; i++)
+                if (lane + 64 * i < K4) {
+                    float4& v = x[u][i];
+                    v = make_float4((v.x * rs) * wv[i].x, (v.y * rs) * wv[i].y, (v.z * rs) * wv[i].z,
+                                    (v.w * rs) * wv[i].w);
+                    amax = fmaxf(amax, max4(v));
+                }
+            amax = wave_max(amax);
+            const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+            if (lane == 0) s_xs[t] = amax == 0.0f ? 0.0f : amax / 127.0f;
+#pragma unroll
+            for (int i = 0; i < kProdRegs; i++)
+                if (lane + 64 * i < K4) put_codes(rowb, lane + 64 * i, x[u][i], inv);
+        }
+        return;
+    }
+    for (int t = wave; t < T; t += 4) {
+        zero_row_lds(act, t, JP, lane, 64);
+        if (lane == 0) s_xs[t] = 0.0f;
+    }
+    for (int t = wave; t < T && t < Tr && t < live; t += 4) {
+        const float* ar = pa.a + (size_t)t * K;
+        const float* br = pa.b ? pa.b + (size_t)t * K : nullptr;
+        int8_t* rowb = act + (size_t)t * JP * 512;
+        for (int c = lane; c < K4; c += 64) {
+            float4 v = *reinterpret_cast<const float4*>(ar + 4 * c);
+            if (br) {
+                const float4 d = *reinterpret_cast<const float4*>(br + 4 * c);
+                v = make_float4(v.x + d.x, v.y + d.y, v.z + d.z, v.w + d.w);
+                if (wb) *reinterpret_cast<float4*>(pa.h_out + (size_t)t * K + 4 * c) = v;
+            }
+            *reinterpret_cast<float4*>(xr + 4 * c) = v;
+        }
+        float acc = 0.0f;
+        if (lane < 16)
+            for (int k = lane; k < K; k += 16) acc = acc + xr[k] * xr[k];
+        acc = tree16_lanes(acc);
+        const float ss = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, acc)));
+        const float rs = 1.0f / sqrtf(ss / (float)K + pa.eps);
+        auto value4 = [&](int c) {
+            const float4 x = *reinterpret_cast<const float4*>(xr + 4 * c);
+            const float4 wv = *reinterpret_cast<const float4*>(pa.w + 4 * c);
+            return make_float4((x.x * rs) * wv.x, (x.y * rs) * wv.y, (x.z * rs) * wv.z, (x.w * rs) * wv.w);
+        };
+        float amax = 0.0f;
+        for (int c = lane; c < K4; c += 64) amax = fmaxf(amax, max4(value4(c)));
+        amax = wave_max(amax);
+        const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+        if (lane == 0) s_xs[t] = amax == 0.0f ? 0.0f : amax / 127.0f;
+        for (int c = lane; c < K4; c += 64) put_codes(rowb, c, value4(c), inv);
+    }
+}
+
+// SiLU rows (at most kSiluTokens): the whole workgroup, every load issued up
+// front, values in registers, each token's absmax met in LDS.
+template <int T>
+__device__ void produce_silu(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
+                             float* part) {
+    constexpr int TS = T < kSiluTokens ? T : kSiluTokens;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K4 = K >> 2;
+    float4 gv[TS][kSiluRegs], uv[TS][kSiluRegs];
+#pragma unroll
+    for (int t = 0; t < TS; t++)
+        if (t < Tr) {
+#pragma unroll
+            for (int i = 0; i < kSiluRegs; i++) {
+                const int c = tid + 256 * i;
+                if (c < K4) {
+                    gv[t][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * 2 * K + 4 * c);
+                    uv[t][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * 2 * K + K + 4 * c);
+                }
+            }
+        }
+    for (int t = 0; t < T; t++) zero_row_lds(act, t, JP, tid, 256);
+    if (tid < T) s_xs[tid] = 0.0f;
+    float amax[TS];
+#pragma unroll
+    for (int t = 0; t < TS; t++) {
+        amax[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kSiluRegs; i++)
+            if (t < Tr && t < live && tid + 256 * i < K4) {
+                float4& z = gv[t][i];
+                z = make_float4(silu(z.x) * uv[t][i].x, silu(z.y) * uv[t][i].y, silu(z.z) * uv[t][i].z,
+                                silu(z.w) * uv[t][i].w);
+                amax[t] = fmaxf(amax[t], max4(z));
+            }
+        amax[t] = wave_max(amax[t]);
+        if (lane == 0) part[4 * t + wave] = amax[t];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TS; t++) {
+        if (t >= Tr || t >= live) continue;
+        const float m = fmaxf(fmaxf(part[4 * t], part[4 * t + 1]), fmaxf(part[4 * t + 2], part[4 * t + 3]));
+        const float inv = m == 0.0f ? 0.0f : 127.0f / m;
+        if (tid == 0) s_xs[t] = m == 0.0f ? 0.0f : m / 127.0f;
+        int8_t* rowb = act + (size_t)t * JP * 512;
+#pragma unroll
+        for (int i = 0; i < kSiluRegs; i++)
+            if (tid + 256 * i < K4) put_codes(rowb, tid + 256 * i, gv[t][i], inv);
+    }
+}
+
+// All rows of the step: zero the staged rows (padding groups, and tokens
+// past Tr or the live count, stay zero), then the producer.
+// All rows of the step; tokens past Tr or the live count, and padding
+// groups, stay zero. Each producer issues its row loads before it zeroes the
+// staged rows, so the two overlap.
+template <int T, int PROD>
+__device__ void produce_rows(const ProdArgs& pa, int Tr, int K, int JP, int8_t* act, float* s_xs, float* scratch) {
+    const bool done = pa.ctrl->done != 0;
+    const int live = done ? 0 : pa.ctrl->n_nodes;
+    if constexpr (PROD == kProdNorm)
+        produce_norm<T>(pa, Tr, live, K, JP, act, s_xs, scratch);
+    else
+        produce_silu<T>(pa, Tr, live, K, JP, act, s_xs, scratch);
+}
+
+template <int T, int P, bool AMAX, bool BS, bool RELOAD, int PROD>
 __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq, int N, int K,
-    int nwg, int Tr, const float* __restrict__ xs, float* __restrict__ y, int write_y, Best* __restrict__ amax) {
+    int nwg, int Tr, const float* __restrict__ xs, float* __restrict__ y, int write_y, Best* __restrict__ amax,
+    const ProdArgs pa) {
     constexpr int TT = (T + 3) / 4;
     constexpr int TX = (T + 7) / 8;
     constexpr int XB = (4 * T + 63) / 64;  // block-scale loads per lane and iteration
     constexpr int FP = (16 * T + 255) / 256;  // finishing passes: 16 rows per token, 256 threads
     extern __shared__ __attribute__((aligned(16))) int8_t act[];
     __shared__ float red[2][4][T][16];
+    __shared__ float s_xs[PROD != kProdNone ? T : 1];  // token scales of produced rows
     static_assert(!AMAX || T <= 16, "the argmax keeps one token per finishing thread");
+    static_assert(PROD == kProdNone || (!BS && !RELOAD), "produced rows are kept in LDS, per-token scales");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -161,7 +452,7 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
 #pragma unroll
     for (int k = 0; k < FP; k++) {
         const int t = (tid + 256 * k) >> 4;
-        fxs[k] = !BS && t < Tr ? xs[t] : 0.0f;
+        fxs[k] = !BS && PROD == kProdNone && t < Tr ? xs[t] : 0.0f;
     }
 
     const auto rw = make_rsrc(wq, (uint32_t)((int64_t)N * (K / 2)));
@@ -270,10 +561,13 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     SStage<T, BS> st[P];
 #pragma unroll
     for (int pp = 0; pp < P; pp++) {
-        load(st[pp], v, pp, true, 0u);
+        load(st[pp], v, pp, PROD == kProdNone, 0u);
         __builtin_amdgcn_sched_barrier(0);
     }
     if (tid < kStreamZero / 16) *reinterpret_cast<v4i*>(act + zero_off + 16 * tid) = v4i{0, 0, 0, 0};
+    if constexpr (PROD != kProdNone)  // the rows, while the first weights are in flight
+        produce_rows<T, PROD>(pa, Tr, K, JP, act, s_xs,
+                              reinterpret_cast<float*>(act + zero_off + kStreamZero + (BS ? JA * 64 * T : 0)));
     __syncthreads();
 
     auto run_tile = [&](auto first_tag, int k, float (&acc)[T]) {
@@ -322,7 +616,7 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
             if (t < Tr && row < N) {
                 const float sum =
                     (red[buf][0][t][rr] + red[buf][1][t][rr]) + (red[buf][2][t][rr] + red[buf][3][t][rr]);
-                const float val = BS ? sum : fxs[kk] * sum;
+                const float val = BS ? sum : (PROD != kProdNone ? s_xs[t] : fxs[kk]) * sum;
                 if (!AMAX || write_y) y[(int64_t)t * N + row] = val;
                 if (AMAX && better(val, row, bv, bi)) {
                     bv = val;
@@ -331,14 +625,14 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
             }
         }
     };
-    {
+    if constexpr (PROD == kProdNone) {  // the first tile brings the activations
         float acc[T];
 #pragma unroll
         for (int t = 0; t < T; t++) acc[t] = 0.0f;
         run_tile(std::true_type{}, 0, acc);
         finish_tile(0, acc, 0);
     }
-    for (int k = 1; k < ntiles; k++) {
+    for (int k = PROD == kProdNone ? 1 : 0; k < ntiles; k++) {
         float acc[T];
 #pragma unroll
         for (int t = 0; t < T; t++) acc[t] = 0.0f;
@@ -362,6 +656,10 @@ inline size_t stream_lds_bytes(int T, int K, bool bs, bool reload) {
     const int J = (K / 32 + 15) / 16;
     const int JA = reload ? 1 : (J + SPECV_STREAM_STAGES - 1) / SPECV_STREAM_STAGES * SPECV_STREAM_STAGES;
     return (size_t)T * JA * 512 + kStreamZero + (bs ? (size_t)JA * 64 * T : 0);
+}
+// LDS of a producer: one row per wave (RMSNorm), the absmax exchange (SiLU).
+inline size_t prod_scratch_bytes(int prod, int K) {
+    return prod == kProdNorm ? (size_t)16 * norm_row_floats(K) : prod == kProdSilu ? 16 * kSiluTokens : 0;
 }
 // Whether the activations of every iteration fit beside the reduction buffer.
 inline bool stream_keeps(int T, int K, bool bs) {
@@ -405,24 +703,25 @@ static int enable_lds(const void* kernel, size_t lds, size_t& enabled) {
     return SPECV_OK;
 }
 
-template <int T, bool AMAX, bool BS, bool RELOAD>
+template <int T, bool AMAX, bool BS, bool RELOAD, int PROD = kProdNone>
 static int launch_one(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                      Best* amax, int Tr, int N, int K, hipStream_t s) {
+                      Best* amax, int Tr, int N, int K, hipStream_t s, const ProdArgs& pa = ProdArgs{}) {
     constexpr int P = SPECV_STREAM_STAGES;
     static size_t lds_enabled = 64 * 1024;
-    const size_t lds = stream_lds_bytes(T, K, BS, RELOAD);
+    const size_t lds = stream_lds_bytes(T, K, BS, RELOAD) + prod_scratch_bytes(PROD, K);
     if (lds + (size_t)T * 512 > kLdsBudget) return SPECV_E_SHAPE;
-    auto kernel = &w4a8_linear_stream_kernel<T, P, AMAX, BS, RELOAD>;
+    auto kernel = &w4a8_linear_stream_kernel<T, P, AMAX, BS, RELOAD, PROD>;
     const int rc = enable_lds(reinterpret_cast<const void*>(kernel), lds, lds_enabled);
     if (rc != SPECV_OK) return rc;
     const int grid = stream_grid(N);
     const int write_y = y != nullptr;
     if (g_time_start) {
         hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, g_time_start, g_time_stop, 0, wq, ws, xq, N, K,
-                              grid, Tr, xs, y, write_y, amax);
+                              grid, Tr, xs, y, write_y, amax, pa);
         g_time_start = g_time_stop = nullptr;
     } else {
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, wq, ws, xq, N, K, grid, Tr, xs, y, write_y, amax);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, s, wq, ws, xq, N, K, grid, Tr, xs, y, write_y, amax,
+                           pa);
     }
     return launch_status();
 }
@@ -440,6 +739,39 @@ static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, con
     }
     return keep ? launch_one<T, false, BS, false>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s)
                 : launch_one<T, false, BS, true>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s);
+}
+
+// Fused producers: T <= 16, per-token scales, every iteration's activations
+// (and, for RMSNorm, one row per wave) kept in LDS.
+bool linear_fused_supported(int prod, int T, int K) {
+    if (T < 1 || T > 16 || K < 32 || K % 32 || (prod != kProdNorm && prod != kProdSilu)) return false;
+    if (prod == kProdSilu && (K > 256 * 4 * kSiluRegs || T > kSiluTokens)) return false;
+    return stream_lds_bytes(T, K, false, false) + prod_scratch_bytes(prod, K) + (size_t)T * 512 <= kLdsBudget;
+}
+
+template <int T>
+static int launch_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const uint16_t* ws, float* y, Best* amax,
+                        int N, int K, hipStream_t s) {
+    if (prod == kProdNorm)
+        return amax ? launch_one<T, true, false, false, kProdNorm>(wq, ws, nullptr, nullptr, y, amax, T, N, K, s, pa)
+                    : launch_one<T, false, false, false, kProdNorm>(wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s,
+                                                                     pa);
+    if (amax) return SPECV_E_SHAPE;
+    return launch_one<T, false, false, false, kProdSilu>(wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
+}
+
+int linear_enqueue_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const uint16_t* ws, float* y, Best* amax,
+                         int T, int N, int K, hipStream_t s) {
+    if (!linear_fused_supported(prod, T, K)) return SPECV_E_SHAPE;
+    switch (T) {
+#define SPECV_CASE(n) \
+    case n: return launch_fused<n>(prod, pa, wq, ws, y, amax, N, K, s);
+        SPECV_CASE(1) SPECV_CASE(2) SPECV_CASE(3) SPECV_CASE(4) SPECV_CASE(5) SPECV_CASE(6)
+        SPECV_CASE(7) SPECV_CASE(8) SPECV_CASE(9) SPECV_CASE(10) SPECV_CASE(11) SPECV_CASE(12)
+        SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
+#undef SPECV_CASE
+        default: return SPECV_E_SHAPE;
+    }
 }
 
 // Finishes the argmax of each token from its workgroups' (value, row) pairs.

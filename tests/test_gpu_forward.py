@@ -27,10 +27,16 @@ def sv():
     return m
 
 
+# Rows longer than 1024 values take the fused RMSNorm's LDS-row path, and an
+# intermediate of 2176 the fused SiLU up to 4 tokens.
+WIDE = dict(n_layers=2, hidden=1280, n_heads=10, n_kv_heads=2, head_dim=128, inter=2176, vocab=1000,
+            eps=1e-6, max_pos=640)
+
+
 @functools.lru_cache(maxsize=2)
 def model_pair(name):
-    cfg = sg.TINY if name == "tiny" else sg.QWEN05
-    arrays = sg.model_case(7 if name == "tiny" else 3, cfg)
+    cfg = {"tiny": sg.TINY, "wide": WIDE}.get(name, sg.QWEN05)
+    arrays = sg.model_case({"tiny": 7, "wide": 11}.get(name, 3), cfg)
     c, s = oracle.rope_table(cfg["max_pos"], cfg["head_dim"], 1e6)
     arrays = dict(arrays, rope_cos=c, rope_sin=s)
     return cfg, arrays, oracle.Model(arrays, cfg)
@@ -98,6 +104,12 @@ def compare_step(sv, name, seed, N, L, plant=True):
 def test_tiny_tree_step_parity(sv, seed, N, L):
     case(f"tiny tree step seed={seed} N={N} L={L}")
     compare_step(sv, "tiny", seed, N, L)
+
+
+@pytest.mark.parametrize("seed,N,L", [(41, 1, 100), (42, 4, 257), (43, 8, 64), (44, 16, 300)])
+def test_wide_tree_step_parity(sv, seed, N, L):
+    case(f"wide (hidden 1280) tree step seed={seed} N={N} L={L}")
+    compare_step(sv, "wide", seed, N, L)
 
 
 def test_tiny_unplanted_tree(sv):
