@@ -114,16 +114,19 @@ class Model:
         wq, ws, _ = sg.linear_case(99, 1, m["vocab"], m["hidden"], layer=1000)
         host_lm = (wq, ws)
         self.host_sets, self.gen_s = host_sets, time.time() - t0
-        def gm(b):  # scales [N][K/32] -> the library's group-major [K/32][N]
-            return torch.from_numpy(np.ascontiguousarray(b.T).view(np.int16)).to(dev)
-        dev_sets = [{nm: (torch.from_numpy(a).to(dev), gm(b)) for nm, (a, b) in s.items()} for s in host_sets]
+        def pack(a, b):  # interchange nibbles and scales -> the library's packed tile layout
+            return sv.pack_weights(torch.from_numpy(a).to(dev), torch.from_numpy(b.view(np.int16)).to(dev))
+
+        def clone(p):
+            return sv.Packed(p.wp.clone(), p.sp.clone(), p.N, p.K)
+        dev_sets = [{nm: pack(a, b) for nm, (a, b) in s.items()} for s in host_sets]
         for c in range(m["copies"]):
             layers = []
             for l in range(m["layers"]):
                 src = dev_sets[(l + c) % m["distinct"]]
-                layers.append({nm: (a.clone(), b.clone()) for nm, (a, b) in src.items()})
-            lm = (torch.from_numpy(host_lm[0]).to(dev), gm(host_lm[1]))
-            self.copies.append((layers, lm if c == 0 else (lm[0].clone(), lm[1].clone())))
+                layers.append({nm: clone(p) for nm, p in src.items()})
+            lm = pack(*host_lm)
+            self.copies.append((layers, lm if c == 0 else clone(lm)))
         del dev_sets
         # activations: every linear of the step has its own fp32 input rows,
         # generated once per K as [inputs][Tmax][K]
@@ -202,16 +205,16 @@ class Model:
             n = x.shape[0]
             sv.quantize_act(x.view(n * T, K), self.xqa[K].view(n * T, K), self.xsa[K].view(n * T))
 
-        def lin(name, wpair, K, N, y, i):
+        def lin(name, w, K, N, y, i):
             xq, xs = self.xqa[K][i], self.xsa[K][i]
             if events is not None:   # kernel begin/end timestamps of this launch
                 e0, e1 = timing_events(torch)
                 sv.check("specv_time_next_linear", sv.LIB.specv_time_next_linear(e0.cuda_event, e1.cuda_event))
             if y is None:            # lm_head: fused argmax epilogue, logits not written
-                sv.linear_argmax(wpair[0], wpair[1], xq, xs, argmax=self.argmax[:T], workspace=self.ws_lmarg)
+                sv.linear_argmax(w, xq, xs, argmax=self.argmax[:T], workspace=self.ws_lmarg)
                 nb = argmax_linear_bytes(T, N, K, self.lm_chunks(T))
             else:
-                sv.linear(wpair[0], wpair[1], xq, xs, y[: T * N].view(T, N))
+                sv.linear(w, xq, xs, y[: T * N].view(T, N))
                 nb = linear_bytes(T, N, K)
             if events is not None:
                 events.append((e0, e1, nb, name))

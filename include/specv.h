@@ -112,6 +112,31 @@ int w4a8_quantize_act(const float* x, int32_t T, int32_t K, int8_t* xq, float* x
 int w4a8_quantize_act_blocks(const float* x, int32_t T, int32_t K, int8_t* xq, float* xs, void* stream);
 
 /*
+ * Packed tile layout of the W4A8 weights, made once when a model is loaded.
+ * The interchange format is the one [P2] (A quantised matrix-vector kernel
+ * in WGSL) packs: nibbles row-major, byte b of row n holding input 2b in the
+ * low nibble and input 2b+1 in the high nibble, each stored as u = q + 8,
+ * and one fp16 scale per row and group of 32 inputs. The linear kernels
+ * read 16-row tiles group by group, so the packed layout stores each tile's
+ * bytes in that order and every wavefront load is one contiguous kilobyte:
+ *   wq  uint8 [N][K/2]    interchange nibbles (device memory).
+ *   ws  uint16 [N][K/32]  interchange fp16 scale bits (device memory).
+ *   wp  uint8,  w4a8_packed_weight_bytes(N, K) bytes: the 16 bytes of row
+ *       16t + r, group g (inputs 32g .. 32g + 31) at byte offset
+ *       ((t*G + g)*16 + r)*16, with G = K/32 and t < ceil(N/16).
+ *   sp  uint16, w4a8_packed_scale_bytes(N, K) bytes: the scale of row
+ *       16t + r, group g at element (t*G + g)*16 + r.
+ * Rows from N up to the next multiple of 16 are written as zeros. The call
+ * only moves bytes; it enqueues one kernel on `stream`.
+ * N in [1, 2^24], K a multiple of 32 in [32, 2^20], packed weights
+ * < 2^31 bytes. Alignment: wq, wp 16 bytes; ws, sp 2.
+ */
+size_t w4a8_packed_weight_bytes(int32_t N, int32_t K);
+size_t w4a8_packed_scale_bytes(int32_t N, int32_t K);
+int w4a8_pack_weights(const uint8_t* wq, const uint16_t* ws, int32_t N, int32_t K, uint8_t* wp, uint16_t* sp,
+                      void* stream);
+
+/*
  * W4A8 linear for T = 1..32 tokens ([P1], Small-Batch Verification Kernels
  * and Implementation; packing of [P2]):
  *   y[t][n] = xs[t] * R16_g( f32(ws[g][n]) * f32(d[t][n][g]) ),
@@ -121,18 +146,17 @@ int w4a8_quantize_act_blocks(const float* x, int32_t T, int32_t K, int8_t* xq, f
  * added as a binary tree in index order (slot s += slot s+w for s divisible
  * by 2w, w = 1, 2, 4, 8). The order does not depend on T, so row t of a
  * T-token call equals a 1-token call on token t bit for bit.
- *   wq  uint8 [N][K/2]   byte b of row n: input 2b in the low nibble, input
- *                        2b+1 in the high nibble, each stored as u = q + 8.
- *   ws  uint16 [K/32][N] fp16 bit patterns, one scale per 32 inputs, stored
- *                        group-major (the scales of group g for all rows are
- *                        contiguous).
+ *   wq, ws  the weights and scales in the packed tile layout of
+ *           w4a8_pack_weights (codes u(n,k) = q + 8, one fp16 scale per 32
+ *           inputs).
  *   xq  int8 [T][K], xs fp32 [T]   from w4a8_quantize_act.
  *   y   fp32 [T][N]
  *   workspace  unused (w4a8_linear_workspace returns 0 for every shape);
  *              any value, NULL included, is accepted.
  * T in [1, 32] (the buckets of [P1] are 1, 2, 4, 8, 16 and 32 tokens; 17..31
  * run in the 32-token kernel), N in [0, 2^24], K a multiple of 32 in
- * [32, 2^20], N*K/2 < 2^31 bytes. N == 0 enqueues nothing.
+ * [32, 2^20], w4a8_packed_weight_bytes(N, K) < 2^31. N == 0 enqueues
+ * nothing.
  * Alignment: wq and xq 16 bytes, ws 2, xs and y 4.
  */
 size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K);
@@ -255,15 +279,18 @@ int kv_compact(uint16_t* k_cache, uint16_t* v_cache, int32_t n_layers, int32_t n
  * each key and value once). Host struct of device pointers; per-layer
  * tensors are stacked along a leading layer axis. With
  * QKV = (n_heads + 2*n_kv_heads)*head_dim, A = n_heads*head_dim,
- * H = hidden, I = inter, V = vocab:
- *   w_qkv  uint8 [layers][QKV][H/2]   q rows, then k rows, then v rows
- *   s_qkv  uint16 [layers][H/32][QKV] (group-major scales, as w4a8_linear_T)
- *   w_o    [layers][H][A/2],  s_o    [layers][A/32][H]
- *   w_gu   [layers][2I][H/2], s_gu   [layers][H/32][2I]  gate rows, then up
- *   w_down [layers][H][I/2],  s_down [layers][I/32][H]
+ * H = hidden, I = inter, V = vocab. Every matrix is in the packed tile
+ * layout of w4a8_pack_weights; a layer's matrix starts
+ * w4a8_packed_weight_bytes(rows, K) bytes (and w4a8_packed_scale_bytes
+ * bytes for its scales) after the previous layer's:
+ *   w_qkv, s_qkv    [layers] x packed (QKV rows, K = H): q rows, then k
+ *                   rows, then v rows
+ *   w_o, s_o        [layers] x packed (H rows, K = A)
+ *   w_gu, s_gu      [layers] x packed (2I rows, K = H): gate rows, then up
+ *   w_down, s_down  [layers] x packed (H rows, K = I)
  *   norm_attn, norm_mlp  fp32 [layers][H]; norm_final fp32 [H]
- *   w_lm   [V][H/2], s_lm [H/32][V]; the embedding of a token is its
- *          dequantised lm_head row (tied weights)
+ *   w_lm, s_lm      packed (V rows, K = H); the embedding of a token is its
+ *                   dequantised lm_head row (tied weights)
  *   rope_cos, rope_sin  fp32 [max_pos][head_dim/2] (specv_rope_table)
  *   k_cache, v_cache    fp16 bits [layers][n_kv_heads][kv_capacity][head_dim]
  * A step with committed length L and n nodes writes the K/V rows of node i

@@ -15,7 +15,8 @@ from ._lib import CM_WEIGHT, LIB, SpecvError, check, cm_params
 from .model import DeviceModel
 
 __all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
-           "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace", "cm_params", "cm_draft", "CM_WEIGHT", "quantize_act_blocks", "linear_blocks"]
+           "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace", "cm_params", "cm_draft", "CM_WEIGHT",
+           "quantize_act_blocks", "linear_blocks", "Packed", "pack_weights"]
 
 CTRL_FIELDS = ("committed_len", "n_nodes", "ctx_len", "done", "accept_len", "root_token", "step",
                "ring_head")
@@ -52,6 +53,50 @@ def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tens
     return xq, xs
 
 
+class Packed:
+    """A W4A8 matrix of N rows and K inputs in the library's packed tile
+    layout (w4a8_pack_weights): flat uint8 nibbles and int16 fp16-bit scales."""
+
+    def __init__(self, wp: torch.Tensor, sp: torch.Tensor, N: int, K: int):
+        self.wp, self.sp, self.N, self.K = wp, sp, int(N), int(K)
+
+    def rows(self, n: int) -> "Packed":
+        """The first n rows (n a multiple of 16): a prefix of both buffers."""
+        if n % 16 or not 0 < n <= self.N:
+            raise ValueError("a row prefix must be a positive multiple of 16 within the matrix")
+        return Packed(self.wp[: n * self.K // 2], self.sp[: n * self.K // 32], n, self.K)
+
+
+def packed_sizes(N: int, K: int) -> tuple[int, int]:
+    """(weight bytes, scale elements) of an N x K matrix in the packed layout."""
+    wb, sb = int(LIB.w4a8_packed_weight_bytes(N, K)), int(LIB.w4a8_packed_scale_bytes(N, K))
+    if wb == 0 or sb == 0:
+        raise ValueError(f"no packed layout for N={N}, K={K}")
+    return wb, sb // 2
+
+
+def pack_weights(wq: torch.Tensor, ws: torch.Tensor, wp: torch.Tensor | None = None,
+                 sp: torch.Tensor | None = None) -> Packed:
+    """Packs interchange nibbles wq uint8 [N][K/2] and fp16 scale bits ws
+    [N][K/32] (device tensors) into the packed tile layout; wp / sp may be
+    given (flat, at least the packed sizes) to pack in place."""
+    N, half = wq.shape
+    K = 2 * half
+    if ws.shape != (N, K // 32):
+        raise ValueError("ws must be [N][K/32]")
+    if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
+        raise TypeError("ws must hold fp16 bit patterns")
+    wb, se = packed_sizes(N, K)
+    wp = torch.empty(wb, dtype=torch.uint8, device=wq.device) if wp is None else wp
+    sp = torch.empty(se, dtype=torch.int16, device=wq.device) if sp is None else sp
+    if wp.numel() < wb or sp.numel() < se:
+        raise ValueError("packed buffers too small")
+    check("w4a8_pack_weights", LIB.w4a8_pack_weights(_dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype), N, K,
+                                                     _dev(wp, "wp", torch.uint8), _dev(sp, "sp", sp.dtype),
+                                                     _stream()))
+    return Packed(wp, sp, N, K)
+
+
 _WORKSPACES: dict = {}
 
 
@@ -69,17 +114,23 @@ def linear_workspace(T: int, N: int, K: int, device) -> torch.Tensor | None:
     return ws
 
 
-def linear(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
-           y: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y [T][N] fp32 from nibbles wq uint8 [N][K/2], group-major fp16 scale
-    bits ws (int16/uint16/float16 storage) [K/32][N], codes xq int8 [T][K]
-    and token scales xs [T]."""
-    N = wq.shape[0]
+def _check_packed(w: Packed, xq: torch.Tensor, xs_shape: tuple) -> tuple[int, int, int]:
+    if not isinstance(w, Packed):
+        raise TypeError("weights must be a Packed matrix (pack_weights)")
     T, K = xq.shape
-    if wq.shape != (N, K // 2) or ws.shape != (K // 32, N) or xs.shape != (T,):
-        raise ValueError("shape mismatch between wq, ws (group-major), xq and xs")
-    if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
-        raise TypeError("ws must hold fp16 bit patterns")
+    if w.K != K or xs_shape[0] != T:
+        raise ValueError("shape mismatch between the packed weights, xq and xs")
+    return T, w.N, K
+
+
+def linear(w: Packed, xq: torch.Tensor, xs: torch.Tensor, y: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y [T][N] fp32 from a packed matrix, codes xq int8 [T][K] and token
+    scales xs [T]."""
+    T, N, K = _check_packed(w, xq, tuple(xs.shape))
+    if xs.shape != (T,):
+        raise ValueError("xs must be [T]")
+    wq, ws = w.wp, w.sp
     y = torch.empty((T, N), dtype=torch.float32, device=xq.device) if y is None else y
     if workspace is None:
         workspace = linear_workspace(T, N, K, xq.device)
@@ -102,15 +153,12 @@ def quantize_act_blocks(x: torch.Tensor, xq: torch.Tensor | None = None, xs: tor
     return xq, xs
 
 
-def linear_blocks(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
-                  y: torch.Tensor | None = None) -> torch.Tensor:
+def linear_blocks(w: Packed, xq: torch.Tensor, xs: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
     """As linear, with per-block activation scales xs [T][K/32]."""
-    N = wq.shape[0]
-    T, K = xq.shape
-    if wq.shape != (N, K // 2) or ws.shape != (K // 32, N) or xs.shape != (T, K // 32):
-        raise ValueError("shape mismatch between wq, ws (group-major), xq and xs")
-    if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
-        raise TypeError("ws must hold fp16 bit patterns")
+    T, N, K = _check_packed(w, xq, tuple(xs.shape))
+    if xs.shape != (T, K // 32):
+        raise ValueError("xs must be [T][K/32]")
+    wq, ws = w.wp, w.sp
     y = torch.empty((T, N), dtype=torch.float32, device=xq.device) if y is None else y
     check("w4a8_linear_blocks_T", LIB.w4a8_linear_blocks_T(_dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype),
                                                            _dev(xq, "xq", torch.int8),
@@ -119,17 +167,14 @@ def linear_blocks(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torc
     return y
 
 
-def linear_argmax(wq: torch.Tensor, ws: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
-                  y: torch.Tensor | None = None, argmax: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+def linear_argmax(w: Packed, xq: torch.Tensor, xs: torch.Tensor, y: torch.Tensor | None = None,
+                  argmax: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """argmax int32 [T] of the W4A8 linear's outputs (w4a8_linear_argmax_T);
     the outputs are written to y only when y is given."""
-    N = wq.shape[0]
-    T, K = xq.shape
-    if wq.shape != (N, K // 2) or ws.shape != (K // 32, N) or xs.shape != (T,):
-        raise ValueError("shape mismatch between wq, ws (group-major), xq and xs")
-    if ws.dtype not in (torch.int16, torch.uint16, torch.float16):
-        raise TypeError("ws must hold fp16 bit patterns")
+    T, N, K = _check_packed(w, xq, tuple(xs.shape))
+    if xs.shape != (T,):
+        raise ValueError("xs must be [T]")
+    wq, ws = w.wp, w.sp
     need = int(LIB.w4a8_linear_argmax_workspace(T, N, K))
     if need == 0:
         raise ValueError("shape not supported by the fused argmax linear")

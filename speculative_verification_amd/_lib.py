@@ -21,6 +21,9 @@ SIGNATURES = {
     "w4a8_quantize_act": (ctypes.c_int, [P, I32, I32, P, P, P]),
     "w4a8_quantize_act_blocks": (ctypes.c_int, [P, I32, I32, P, P, P]),
     "w4a8_linear_blocks_T": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P]),
+    "w4a8_packed_weight_bytes": (SZ, [I32, I32]),
+    "w4a8_packed_scale_bytes": (SZ, [I32, I32]),
+    "w4a8_pack_weights": (ctypes.c_int, [P, P, I32, I32, P, P, P]),
     "w4a8_linear_workspace": (SZ, [I32, I32, I32]),
     "w4a8_linear_T": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P, SZ, P]),
     "specv_time_next_linear": (ctypes.c_int, [P, P]),

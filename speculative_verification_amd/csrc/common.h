@@ -108,4 +108,11 @@ inline int launch_status() {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Sizes of a matrix of N rows and K inputs in the packed tile layout: rows
+// padded to whole 16-row tiles, 16 bytes of nibbles and one fp16 scale per
+// row and 32-input group.
+__host__ __device__ inline int64_t packed_rows(int64_t N) { return (N + 15) / 16 * 16; }
+__host__ __device__ inline int64_t packed_weight_bytes(int64_t N, int64_t K) { return packed_rows(N) * (K / 2); }
+__host__ __device__ inline int64_t packed_scale_bytes(int64_t N, int64_t K) { return packed_rows(N) * (K / 32) * 2; }
+
 }  // namespace specv

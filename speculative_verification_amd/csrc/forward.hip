@@ -155,11 +155,15 @@ __global__ __launch_bounds__(kFwdThreads) void embed_kernel(const int32_t* __res
     if (threadIdx.x <= i) s_par[threadIdx.x] = parent[threadIdx.x];
     int tok = token[i];
     tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
-    const uint8_t* wr = wlm + (size_t)tok * (H / 2);
+    // row tok of the packed lm_head: tile tok / 16, row tok % 16 of each
+    // group's 16-row chunk
+    const size_t G = (size_t)(H >> 5);
+    const size_t tbase = (size_t)(tok >> 4) * G * 16 + (size_t)(tok & 15);
     for (int k = threadIdx.x; k < H; k += kFwdThreads) {
-        const uint8_t b = wr[k >> 1];
+        const size_t c = tbase + (size_t)(k >> 5) * 16;
+        const uint8_t b = wlm[c * 16 + ((k & 31) >> 1)];
         const int code = ((k & 1) ? (b >> 4) : (b & 15)) - 8;
-        h[(size_t)i * H + k] = f16_to_f32(slm[(size_t)(k >> 5) * V + tok]) * (float)code;
+        h[(size_t)i * H + k] = f16_to_f32(slm[c]) * (float)code;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -682,14 +686,15 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     };
     const bool fuse_silu = (int64_t)n * I <= kSiluFuseMax && linear_fused_supported(kProdSilu, n, I);
     for (int l = 0; l < m->n_layers; l++) {
-        const uint8_t* wqkv = m->w_qkv + (size_t)l * QKV * (H / 2);
-        const uint16_t* sqkv = m->s_qkv + (size_t)l * (H / 32) * QKV;
-        const uint8_t* wo = m->w_o + (size_t)l * H * (A / 2);
-        const uint16_t* so = m->s_o + (size_t)l * (A / 32) * H;
-        const uint8_t* wgu = m->w_gu + (size_t)l * 2 * I * (H / 2);
-        const uint16_t* sgu = m->s_gu + (size_t)l * (H / 32) * 2 * I;
-        const uint8_t* wd = m->w_down + (size_t)l * H * (I / 2);
-        const uint16_t* sd = m->s_down + (size_t)l * (I / 32) * H;
+        // each layer's matrices in the packed tile layout, one after another
+        const uint8_t* wqkv = m->w_qkv + (size_t)l * packed_weight_bytes(QKV, H);
+        const uint16_t* sqkv = m->s_qkv + (size_t)l * packed_scale_bytes(QKV, H) / 2;
+        const uint8_t* wo = m->w_o + (size_t)l * packed_weight_bytes(H, A);
+        const uint16_t* so = m->s_o + (size_t)l * packed_scale_bytes(H, A) / 2;
+        const uint8_t* wgu = m->w_gu + (size_t)l * packed_weight_bytes(2 * I, H);
+        const uint16_t* sgu = m->s_gu + (size_t)l * packed_scale_bytes(2 * I, H) / 2;
+        const uint8_t* wd = m->w_down + (size_t)l * packed_weight_bytes(H, I);
+        const uint16_t* sd = m->s_down + (size_t)l * packed_scale_bytes(H, I) / 2;
 
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
                               true));

@@ -46,10 +46,16 @@
 // f32(16d) is the same real product as f32(scale) * f32(d) and rounds
 // identically; with per-block scales d itself is recovered as 16d >> 4.
 //
+// Weights are read in the packed tile layout (pack.hip): the 16-byte group
+// chunks of a 16-row tile follow each other group by group, so the load of
+// one iteration by one wave (16 rows x 4 groups) is one contiguous kilobyte
+// and a tile is one contiguous stream; the scales follow the same order.
+//
 // Ragged shapes. All global loads go through buffer resources, whose range
-// check returns zeros. Rows past N lie past the end of the weights; groups
-// past G read zeros (an out-of-range offset) against zero activations, so
-// they add +0, which never changes a slot (a slot is never -0).
+// check returns zeros. Rows past N are the zero rows that pad the last tile;
+// groups past G read zeros (an out-of-range offset) against zero
+// activations, so they add +0, which never changes a slot (a slot is never
+// -0).
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -93,8 +99,8 @@ __device__ __forceinline__ v4i even_odd(const v4i a) {
                (int)__builtin_amdgcn_perm(a[3], a[2], 0x06040200u), (int)__builtin_amdgcn_perm(a[3], a[2], 0x07050301u)};
 }
 
-// The grid is a multiple of 32 workgroups; workgroup b walks the 16-row
-// tiles v, v + nwg, v + 2 nwg, ... Its four waves take the four slot quads of
+// Workgroup b of nwg walks the 16-row tiles b, b + nwg, b + 2 nwg, ... Its
+// four waves take the four slot quads of
 // every tile, so a wave only ever uses its own quarter of each token's
 // activation codes: it loads that quarter together with a tile's weights,
 // iteration by iteration, stores it in LDS in the MFMA operand order, and
@@ -431,13 +437,10 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     const int JP = (J + P - 1) / P * P;  // iterations per tile, padded to whole blocks of P
     const int JA = RELOAD ? 1 : JP;      // iterations kept in LDS
     const int NT = (N + 15) >> 4;
-    // The four 16-row tiles of a 64-row block share the 128-byte lines of
-    // their group-major scales: they go to workgroups that the hardware's
-    // round-robin placement (workgroup b on XCD b mod 8) puts on one XCD,
-    // whose L2 then fetches each line once. nwg being a multiple of 32 keeps
-    // that true for every tile of the lists.
-    const int b = blockIdx.x, ib = b >> 3;
-    const int v = 4 * ((ib >> 2) * 8 + (b & 7)) + (ib & 3);
+    // Workgroup b takes tiles b, b + nwg, ...: the workgroups in flight
+    // read neighbouring stretches of the packed matrix, front to back.
+    const int b = blockIdx.x;
+    const int v = b;
     const int ntiles = v < NT ? (NT - v + nwg - 1) / nwg : 0;
 
     // With the argmax, thread (ft, fr) finishes row fr of token ft.
@@ -455,8 +458,8 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
         fxs[k] = !BS && PROD == kProdNone && t < Tr ? xs[t] : 0.0f;
     }
 
-    const auto rw = make_rsrc(wq, (uint32_t)((int64_t)N * (K / 2)));
-    const auto rs = make_rsrc(wsg, (uint32_t)((int64_t)G * N * 2));
+    const auto rw = make_rsrc(wq, (uint32_t)packed_weight_bytes(N, K));
+    const auto rs = make_rsrc(wsg, (uint32_t)packed_scale_bytes(N, K));
     const auto rx = make_rsrc(xq, (uint32_t)(Tr * K));
     const auto rb = make_rsrc(xs, BS ? (uint32_t)(Tr * G * 4) : 0u);
     const uint32_t lq = 4u * wave + q;  // group of this lane within an iteration
@@ -467,15 +470,16 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     // and with the activations, 16 bytes of codes per 8 tokens (and with block
     // scales, one scale per lane for up to 64 (token, group) pairs). Every
     // load is issued unconditionally, so the compiler counts them statically:
-    // a row past N lies past the weights, a group past G (a ragged or padding
-    // iteration), a token past Tr and a tile past the list take the
-    // out-of-range bit, and all of these read zeros. Offsets stay below 2^32:
-    // the weights and scales are each under 2^31 bytes.
+    // a group past G (a ragged or padding iteration), a token past Tr and a
+    // tile past the list take the out-of-range bit, and all of these read
+    // zeros (rows past N are zero rows of the packed layout). Offsets stay
+    // below 2^32 (the packed weights and scales are each under 2^31 bytes),
+    // or have the out-of-range bit set.
     auto load = [&](SStage<T, BS>& st, int tile, int j, bool with_act, uint32_t past) {
         const uint32_t bad = ((16 * j + (int)lq >= G) ? kOOB : 0u) | past;
-        const uint32_t row = 16u * (uint32_t)tile + (uint32_t)r;
-        st.w = load16(rw, (row * (uint32_t)(K / 2) + 16u * lq + 256u * (uint32_t)j) | bad);
-        st.s = load2(rs, ((((uint32_t)(16 * j) + lq) * (uint32_t)N + row) * 2u) | bad);
+        const uint32_t chunk = ((uint32_t)tile * (uint32_t)G + 16u * (uint32_t)j + lq) * 16u + (uint32_t)r;
+        st.w = load16(rw, (chunk * 16u) | bad);
+        st.s = load2(rs, (chunk * 2u) | bad);
         if (with_act) {
 #pragma unroll
             for (int x = 0; x < TX; x++) {
@@ -652,9 +656,9 @@ constexpr size_t kLdsBudget = 150 * 1024;
 // Dynamic LDS of a workgroup (its tile reduction buffer, 512T bytes, is
 // static): the activation quarters of JA iterations, the zero bytes, and the
 // block scales.
-inline size_t stream_lds_bytes(int T, int K, bool bs, bool reload) {
+inline size_t stream_lds_bytes(int T, int K, bool bs, bool reload, int P = SPECV_STREAM_STAGES) {
     const int J = (K / 32 + 15) / 16;
-    const int JA = reload ? 1 : (J + SPECV_STREAM_STAGES - 1) / SPECV_STREAM_STAGES * SPECV_STREAM_STAGES;
+    const int JA = reload ? 1 : (J + P - 1) / P * P;
     return (size_t)T * JA * 512 + kStreamZero + (bs ? (size_t)JA * 64 * T : 0);
 }
 // LDS of a producer: one row per wave (RMSNorm), the absmax exchange (SiLU).
@@ -679,13 +683,11 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Workgroups of a launch: a multiple of 32 (the tile numbering needs it), no
-// more than the tiles need, about WGS_PER_CU per CU.
+// Workgroups of a launch: one per tile, at most about WGS_PER_CU per CU.
 inline int stream_grid(int N) {
     const int NT = (N + 15) / 16;
-    const int cap = (device_cus() * SPECV_STREAM_WGS_PER_CU + 31) / 32 * 32;
-    const int need = (NT + 31) / 32 * 32;
-    return need < cap ? need : cap;
+    const int cap = device_cus() * SPECV_STREAM_WGS_PER_CU;
+    return NT < cap ? NT : cap;
 }
 
 // Events for the next linear launch of this host thread (timing diagnostics).
@@ -703,12 +705,11 @@ static int enable_lds(const void* kernel, size_t lds, size_t& enabled) {
     return SPECV_OK;
 }
 
-template <int T, bool AMAX, bool BS, bool RELOAD, int PROD = kProdNone>
+template <int T, bool AMAX, bool BS, bool RELOAD, int PROD = kProdNone, int P = SPECV_STREAM_STAGES>
 static int launch_one(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
                       Best* amax, int Tr, int N, int K, hipStream_t s, const ProdArgs& pa = ProdArgs{}) {
-    constexpr int P = SPECV_STREAM_STAGES;
     static size_t lds_enabled = 64 * 1024;
-    const size_t lds = stream_lds_bytes(T, K, BS, RELOAD) + prod_scratch_bytes(PROD, K);
+    const size_t lds = stream_lds_bytes(T, K, BS, RELOAD, P) + prod_scratch_bytes(PROD, K);
     if (lds + (size_t)T * 512 > kLdsBudget) return SPECV_E_SHAPE;
     auto kernel = &w4a8_linear_stream_kernel<T, P, AMAX, BS, RELOAD, PROD>;
     const int rc = enable_lds(reinterpret_cast<const void*>(kernel), lds, lds_enabled);
@@ -730,6 +731,16 @@ template <int T, bool BS>
 static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
                     int Tr, int N, int K, hipStream_t s) {
     const bool keep = stream_keeps(T, K, BS);
+#ifdef SPECV_PDEEP
+    if constexpr (T <= 16 && !BS) {
+        const int J = (K / 32 + 15) / 16;
+        if (keep && J % SPECV_PDEEP == 0 &&
+            stream_lds_bytes(T, K, false, false, SPECV_PDEEP) + (size_t)T * 512 <= kLdsBudget)
+            return amax ? launch_one<T, true, false, false, kProdNone, SPECV_PDEEP>(wq, ws, xq, xs, y, amax, Tr, N, K, s)
+                        : launch_one<T, false, false, false, kProdNone, SPECV_PDEEP>(wq, ws, xq, xs, y, nullptr, Tr,
+                                                                                      N, K, s);
+    }
+#endif
     if constexpr (T <= 16 && !BS) {
         if (amax)
             return keep ? launch_one<T, true, false, false>(wq, ws, xq, xs, y, amax, Tr, N, K, s)
@@ -833,7 +844,7 @@ int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, cons
 static int linear_args(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, int32_t T,
                        int32_t N, int32_t K) {
     if (T < 1 || T > 32 || N < 1 || N > (1 << 24) || K < 32 || K > (1 << 20) || K % 32) return SPECV_E_SHAPE;
-    if ((int64_t)N * (K / 2) >= (int64_t)1 << 31) return SPECV_E_SHAPE;
+    if (packed_weight_bytes(N, K) >= (int64_t)1 << 31) return SPECV_E_SHAPE;
     if (!wq || !ws || !xq || !xs) return SPECV_E_INVAL;
     if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(ws, 2) || !aligned(xs, 4)) return SPECV_E_ALIGN;
     return SPECV_OK;

@@ -2,9 +2,10 @@
 
 Packs a decoder given in the interchange layout (per layer: nibbles
 [rows][K/2] and scales [rows][K/32] for q, k, v, o, gate, up, down; norms;
-lm_head) into the library's device layout (layers stacked, q/k/v and
-gate/up rows concatenated, scales group-major), and exposes the step.
-Layout conversion only: all arithmetic runs in libspecv.so.
+lm_head) into the library's device layout (q/k/v and gate/up rows
+concatenated, each matrix in the packed tile layout of w4a8_pack_weights,
+layers one after another), and exposes the step. Layout conversion only:
+all arithmetic runs in libspecv.so.
 """
 from __future__ import annotations
 
@@ -18,9 +19,21 @@ from ._lib import LIB, SpecvDrafter, SpecvModel, check, cm_params
 CFG_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab", "max_pos")
 
 
-def _gm(s: np.ndarray) -> np.ndarray:
-    """Scales [rows][K/32] -> group-major [K/32][rows]."""
-    return np.ascontiguousarray(s.T)
+def _pack_layers(nl: int, wfn, sfn, dev) -> tuple[torch.Tensor, torch.Tensor]:
+    """Layers' interchange matrices (wfn(l): nibbles [rows][K/2], sfn(l):
+    scales [rows][K/32]) packed one after another into flat device buffers."""
+    from . import pack_weights, packed_sizes
+    w0 = wfn(0)
+    rows, K = w0.shape[0], 2 * w0.shape[1]
+    wb, se = packed_sizes(rows, K)
+    wp = torch.empty(nl * wb, dtype=torch.uint8, device=dev)
+    sp = torch.empty(nl * se, dtype=torch.int16, device=dev)
+    for l in range(nl):
+        wq = torch.from_numpy(np.ascontiguousarray(wfn(l))).to(dev)
+        ws = torch.from_numpy(np.ascontiguousarray(sfn(l)).view(np.int16)).to(dev)
+        pack_weights(wq, ws, wp[l * wb:(l + 1) * wb], sp[l * se:(l + 1) * se])
+    torch.cuda.synchronize(dev)
+    return wp, sp
 
 
 class DeviceModel:
@@ -33,22 +46,17 @@ class DeviceModel:
         def stack(fn):
             return torch.from_numpy(np.ascontiguousarray(np.stack([fn(l) for l in range(nl)]))).to(dev)
 
-        def as_i16(a):
-            return a.view(np.int16)
-
-        self.w_qkv = stack(lambda l: np.concatenate([arrays["wq"][l], arrays["wk"][l], arrays["wv"][l]]))
-        self.s_qkv = stack(lambda l: as_i16(_gm(np.concatenate([arrays["sq"][l], arrays["sk"][l], arrays["sv"][l]]))))
-        self.w_o = stack(lambda l: arrays["wo"][l])
-        self.s_o = stack(lambda l: as_i16(_gm(arrays["so"][l])))
-        self.w_gu = stack(lambda l: np.concatenate([arrays["wg"][l], arrays["wu"][l]]))
-        self.s_gu = stack(lambda l: as_i16(_gm(np.concatenate([arrays["sg"][l], arrays["su"][l]]))))
-        self.w_down = stack(lambda l: arrays["wd"][l])
-        self.s_down = stack(lambda l: as_i16(_gm(arrays["sd"][l])))
+        a = arrays
+        self.w_qkv, self.s_qkv = _pack_layers(nl, lambda l: np.concatenate([a["wq"][l], a["wk"][l], a["wv"][l]]),
+                                              lambda l: np.concatenate([a["sq"][l], a["sk"][l], a["sv"][l]]), dev)
+        self.w_o, self.s_o = _pack_layers(nl, lambda l: a["wo"][l], lambda l: a["so"][l], dev)
+        self.w_gu, self.s_gu = _pack_layers(nl, lambda l: np.concatenate([a["wg"][l], a["wu"][l]]),
+                                            lambda l: np.concatenate([a["sg"][l], a["su"][l]]), dev)
+        self.w_down, self.s_down = _pack_layers(nl, lambda l: a["wd"][l], lambda l: a["sd"][l], dev)
         self.norm_attn = stack(lambda l: arrays["norm_attn"][l])
         self.norm_mlp = stack(lambda l: arrays["norm_mlp"][l])
         self.norm_final = torch.from_numpy(arrays["norm_final"]).to(dev)
-        self.w_lm = torch.from_numpy(arrays["wlm"]).to(dev)
-        self.s_lm = torch.from_numpy(as_i16(_gm(arrays["slm"]))).to(dev)
+        self.w_lm, self.s_lm = _pack_layers(1, lambda l: a["wlm"], lambda l: a["slm"], dev)
         half = cfg["head_dim"] // 2
         c = np.empty((cfg["max_pos"], half), np.float32)
         s = np.empty((cfg["max_pos"], half), np.float32)

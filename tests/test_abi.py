@@ -80,6 +80,25 @@ def test_linear_rejects_bad_arguments(lib):
         assert lib.w4a8_linear_workspace(T, N, K) == 0
 
 
+def test_pack_sizes_and_bad_arguments(lib):
+    # rows padded to whole 16-row tiles; 16 bytes and one fp16 scale per row and group
+    for N, K in ((1, 32), (16, 64), (17, 896), (151936, 896), (128256, 4096), (4096, 14336)):
+        rows = (N + 15) // 16 * 16
+        assert lib.w4a8_packed_weight_bytes(N, K) == rows * K // 2
+        assert lib.w4a8_packed_scale_bytes(N, K) == rows * (K // 32) * 2
+    for N, K in ((0, 64), (16, 48), (16, 0), (1 << 22, 1024), (-1, 64)):
+        assert lib.w4a8_packed_weight_bytes(N, K) == 0 and lib.w4a8_packed_scale_bytes(N, K) == 0
+    f = lib.w4a8_pack_weights
+    assert f(A, A, 16, 48, A, A, None) == E_SHAPE
+    assert f(A, A, 0, 64, A, A, None) == E_SHAPE
+    assert f(A, A, 1 << 22, 1024, A, A, None) == E_SHAPE         # packed weights >= 2 GiB
+    assert f(None, A, 16, 64, A, A, None) == E_INVAL
+    assert f(A, A, 16, 64, A, None, None) == E_INVAL
+    assert f(A + 8, A, 16, 64, A, A, None) == E_ALIGN
+    assert f(A, A, 16, 64, A + 8, A, None) == E_ALIGN
+    assert f(A, A + 1, 16, 64, A, A, None) == E_ALIGN
+
+
 def test_quantize_blocks_rejects_bad_arguments(lib):
     f = lib.w4a8_quantize_act_blocks
     assert f(A, 2, 48, A, A, None) == E_SHAPE                     # K not a multiple of 32
@@ -203,11 +222,11 @@ def test_window_rejects_bad_arguments(lib):
 def test_linear_argmax_rejects_bad_arguments(lib):
     f = lib.w4a8_linear_argmax_T
     need = lib.w4a8_linear_argmax_workspace(8, 151936, 896)
-    # one (value, row) pair per token per workgroup: a multiple of 32 workgroups,
-    # no more than the 16-row tiles need, capped near two per CU
+    # one (value, row) pair per token per workgroup: one workgroup per 16-row
+    # tile, capped near two per CU
     chunks = need // (8 * 8)
-    assert need == 8 * chunks * 8 and chunks % 32 == 0 and 32 <= chunks <= (151936 // 16 + 31) // 32 * 32
-    assert lib.w4a8_linear_argmax_workspace(8, 896, 896) == 8 * 64 * 8   # 56 tiles: 64 workgroups
+    assert need == 8 * chunks * 8 and 32 <= chunks <= 151936 // 16
+    assert lib.w4a8_linear_argmax_workspace(8, 896, 896) == 8 * 56 * 8   # 56 tiles: 56 workgroups
     assert lib.w4a8_linear_argmax_workspace(16, 4096, 14336) == 16 * 256 * 8   # reloading layout: 256 tiles
     assert lib.w4a8_linear_argmax_workspace(17, 4096, 4096) == 0     # argmax only up to 16 tokens
     assert f(A, A, A, A, None, A, 17, 4096, 4096, A, 1 << 20, None) == E_SHAPE

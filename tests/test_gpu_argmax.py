@@ -61,11 +61,11 @@ def test_linear_argmax_parity(sv, T, N, K):
         wq, ws = plant_ties(wq, ws, y0)
     y_o = oracle.w4a8_linear(wq, ws, xq, xs)
     a_o = oracle.argmax(y_o)
-    wq_d, ws_d = to_dev(wq), to_dev(np.ascontiguousarray(ws.T))
+    w = sv.pack_weights(to_dev(wq), to_dev(ws))
     xq_d, xs_d = to_dev(xq), to_dev(xs)
     y = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
-    a = sv.linear_argmax(wq_d, ws_d, xq_d, xs_d, y=y)
-    a2 = sv.linear_argmax(wq_d, ws_d, xq_d, xs_d)          # outputs not written
+    a = sv.linear_argmax(w, xq_d, xs_d, y=y)
+    a2 = sv.linear_argmax(w, xq_d, xs_d)          # outputs not written
     torch.cuda.synchronize()
     assert np.array_equal(a.cpu().numpy(), a_o), (a.cpu().numpy(), a_o)
     assert np.array_equal(a2.cpu().numpy(), a_o)
@@ -83,16 +83,18 @@ def test_linear_argmax_llama_lm_head(sv, T):
     N, K = 128256, 4096
     wq, ws, x = sg.linear_case(90 + T, T, N, K)
     xq, xs = oracle.quantize_act(x)
-    wq_d, ws_d = to_dev(wq), to_dev(np.ascontiguousarray(ws.T))
+    wq_d, ws_d = to_dev(wq), to_dev(ws)
     xq_d, xs_d = to_dev(xq), to_dev(xs)
-    y = sv.linear(wq_d, ws_d, xq_d, xs_d)
+    w = sv.pack_weights(wq_d, ws_d)
+    y = sv.linear(w, xq_d, xs_d)
     torch.cuda.synchronize()
     r = int(torch.argmax(y[0]).item())
-    if r > 0:      # tie for token 0: copy the winning row into row r // 2 (rows and scale columns)
+    if r > 0:      # tie for token 0: copy the winning row into row r // 2 (nibbles and scales), repack
         wq_d[r // 2] = wq_d[r]
-        ws_d[:, r // 2] = ws_d[:, r]
-        y = sv.linear(wq_d, ws_d, xq_d, xs_d)
-    a = sv.linear_argmax(wq_d, ws_d, xq_d, xs_d)
+        ws_d[r // 2] = ws_d[r]
+        w = sv.pack_weights(wq_d, ws_d)
+        y = sv.linear(w, xq_d, xs_d)
+    a = sv.linear_argmax(w, xq_d, xs_d)
     torch.cuda.synchronize()
     yh = y.cpu().numpy()
     assert a.cpu().numpy().tolist() == [int(np.argmax(yh[t])) for t in range(T)]

@@ -41,20 +41,22 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def ws_dev(ws: np.ndarray) -> torch.Tensor:
-    """Scales [N][K/32] as generated -> the library's group-major [K/32][N]."""
-    return to_dev(np.ascontiguousarray(ws.T))
+def packed(wq: np.ndarray, ws: np.ndarray):
+    """Interchange nibbles and scales as generated -> the library's packed
+    tile layout (w4a8_pack_weights, on the device)."""
+    import speculative_verification_amd as m
+    return m.pack_weights(to_dev(wq), to_dev(ws))
 
 
 @functools.lru_cache(maxsize=2)
 def _weights(seed, N, K, layer):
     wq, ws, _ = sg.linear_case(seed, 1, N, K, layer=layer)
-    return wq, ws, to_dev(wq), ws_dev(ws)
+    return wq, ws, packed(wq, ws)
 
 
-def gpu_quant_linear(sv, wq, ws, x, wq_d=None, ws_d=None):
+def gpu_quant_linear(sv, wq, ws, x, w=None):
     xq, xs = sv.quantize_act(to_dev(x))
-    y = sv.linear(to_dev(wq) if wq_d is None else wq_d, ws_dev(ws) if ws_d is None else ws_d, xq, xs)
+    y = sv.linear(packed(wq, ws) if w is None else w, xq, xs)
     torch.cuda.synchronize()
     return xq.cpu().numpy(), xs.cpu().numpy(), y.cpu().numpy()
 
@@ -70,6 +72,24 @@ def assert_bits(a: np.ndarray, b: np.ndarray, what: str):
 
 
 # ------------------------------------------------------------------ quantisation
+
+@pytest.mark.parametrize("N,K", [(1, 32), (17, 64), (300, 896), (4096, 14336), (151936, 896)])
+def test_pack_layout(sv, N, K):
+    """w4a8_pack_weights moves every byte where the packed tile layout puts
+    it: row 16t + r, group g at chunk (t*G + g)*16 + r, zero padding rows."""
+    case(f"pack N={N} K={K}")
+    wq, ws, _ = sg.linear_case(3, 1, N, K)
+    w = packed(wq, ws)
+    rows, G = (N + 15) // 16 * 16, K // 32
+    wpad = np.zeros((rows, K // 2), np.uint8)
+    wpad[:N] = wq
+    spad = np.zeros((rows, G), np.uint16)
+    spad[:N] = ws
+    want_w = wpad.reshape(rows // 16, 16, G, 16).transpose(0, 2, 1, 3).reshape(-1)
+    want_s = spad.reshape(rows // 16, 16, G).transpose(0, 2, 1).reshape(-1)
+    assert np.array_equal(w.wp.cpu().numpy(), want_w)
+    assert np.array_equal(w.sp.cpu().numpy().view(np.uint16), want_s)
+
 
 @pytest.mark.parametrize("T,K", [(1, 896), (8, 896), (3, 4864), (16, 4096), (8, 14336), (2, 33), (5, 1),
                                  (64, 96), (3, 16388), (4, 1024), (2, 2048)])
@@ -144,10 +164,10 @@ def test_linear_qwen_shapes(sv, name, T):
     N, K = QWEN[name]
     for seed in ((0, 1, 2, 3) if T == 8 else (0,)):
         case(f"linear qwen {name} N={N} K={K} T={T} seed={seed}")
-        wq, ws, wq_d, ws_d = _weights(seed, N, K, list(QWEN).index(name))
+        wq, ws, w = _weights(seed, N, K, list(QWEN).index(name))
         _, _, x = sg.linear_case(seed, T, 1, K, layer=list(QWEN).index(name))
         xq_o, xs_o = oracle.quantize_act(x)
-        _, _, y = gpu_quant_linear(sv, wq, ws, x, wq_d, ws_d)
+        _, _, y = gpu_quant_linear(sv, wq, ws, x, w)
         if N * K <= 896 * 4864:
             assert_bits(y, oracle.w4a8_linear(wq, ws, xq_o, xs_o), f"{name} T={T} seed={seed}")
         else:
@@ -162,10 +182,10 @@ def test_linear_llama_shapes_sampled(sv, name, T):
     N, K = LLAMA[name]
     seed = 0
     case(f"linear llama {name} N={N} K={K} T={T}")
-    wq, ws, wq_d, ws_d = _weights(seed, N, K, 100 + list(LLAMA).index(name))
+    wq, ws, w = _weights(seed, N, K, 100 + list(LLAMA).index(name))
     _, _, x = sg.linear_case(seed, T, 1, K, layer=100 + list(LLAMA).index(name))
     xq_o, xs_o = oracle.quantize_act(x)
-    _, _, y = gpu_quant_linear(sv, wq, ws, x, wq_d, ws_d)
+    _, _, y = gpu_quant_linear(sv, wq, ws, x, w)
     rows = _sample_rows(N, seed, n=48)
     assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), f"{name} T={T}")
 
@@ -175,13 +195,13 @@ def test_linear_rows_of_T_equal_single_token(sv):
     on token t, for every T bucket, on the 8B-shaped q projection."""
     N, K = LLAMA["q"]
     wq, ws, x = sg.linear_case(7, 16, N, K)
-    wq_d, ws_d = to_dev(wq), ws_dev(ws)
+    w = packed(wq, ws)
     xq, xs = sv.quantize_act(to_dev(x))
-    singles = [sv.linear(wq_d, ws_d, xq[t:t + 1].contiguous(), xs[t:t + 1].contiguous()) for t in range(16)]
+    singles = [sv.linear(w, xq[t:t + 1].contiguous(), xs[t:t + 1].contiguous()) for t in range(16)]
     single = torch.cat(singles, 0).cpu().numpy()
     for T in range(1, 17):
         case(f"rows-of-T T={T}")
-        yT = sv.linear(wq_d, ws_d, xq[:T].contiguous(), xs[:T].contiguous()).cpu().numpy()
+        yT = sv.linear(w, xq[:T].contiguous(), xs[:T].contiguous()).cpu().numpy()
         assert_bits(yT, single[:T].copy(), f"T={T} vs single-token")
 
 
@@ -189,10 +209,10 @@ def test_linear_run_to_run_identical(sv):
     case("determinism lm_head qwen T=8")
     N, K = QWEN["lm_head"]
     wq, ws, x = sg.linear_case(8, 8, N, K)
-    wq_d, ws_d = to_dev(wq), ws_dev(ws)
+    w = packed(wq, ws)
     xq, xs = sv.quantize_act(to_dev(x))
-    a = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
-    b = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
+    a = sv.linear(w, xq, xs).cpu().numpy()
+    b = sv.linear(w, xq, xs).cpu().numpy()
     assert a.tobytes() == b.tobytes()
 
 
@@ -215,14 +235,14 @@ def test_linear_repeated_and_interleaved_calls(sv, T, N, K):
     """Calls of other shapes in between leave a shape's result unchanged."""
     case(f"repeated calls T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(10, T, N, K)
-    wq_d, ws_d = to_dev(wq), ws_dev(ws)
+    w = packed(wq, ws)
     xq, xs = sv.quantize_act(to_dev(x))
-    first = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
+    first = sv.linear(w, xq, xs).cpu().numpy()
     for T2 in (1, 5, 16, 27):
         T2 = min(T2, T)
-        sv.linear(wq_d[: N // 2].contiguous(), ws_d[:, : N // 2].contiguous(), xq[:T2].contiguous(),
+        sv.linear(w.rows(N // 32 * 16), xq[:T2].contiguous(),
                   xs[:T2].contiguous())
-        again = sv.linear(wq_d, ws_d, xq, xs).cpu().numpy()
+        again = sv.linear(w, xq, xs).cpu().numpy()
         assert again.tobytes() == first.tobytes()
     rows = _sample_rows(N, 10, n=32)
     xq_o, xs_o = oracle.quantize_act(x)
@@ -234,13 +254,13 @@ def test_linear_32_bucket_rows_equal_single_token(sv):
     1-token call on its token (8B-shaped q projection)."""
     N, K = LLAMA["q"]
     wq, ws, x = sg.linear_case(12, 32, N, K)
-    wq_d, ws_d = to_dev(wq), ws_dev(ws)
+    w = packed(wq, ws)
     xq, xs = sv.quantize_act(to_dev(x))
-    single = torch.cat([sv.linear(wq_d, ws_d, xq[t:t + 1].contiguous(), xs[t:t + 1].contiguous())
+    single = torch.cat([sv.linear(w, xq[t:t + 1].contiguous(), xs[t:t + 1].contiguous())
                         for t in range(32)], 0).cpu().numpy()
     for T in (17, 20, 31, 32):
         case(f"32-token bucket T={T}")
-        yT = sv.linear(wq_d, ws_d, xq[:T].contiguous(), xs[:T].contiguous()).cpu().numpy()
+        yT = sv.linear(w, xq[:T].contiguous(), xs[:T].contiguous()).cpu().numpy()
         assert_bits(yT, single[:T].copy(), f"T={T} vs single-token")
 
 
@@ -267,7 +287,7 @@ def test_linear_blocks_parity(sv, T, N, K):
     case(f"linear blocks T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(80 + T, T, N, K)
     xq, xs = sv.quantize_act_blocks(to_dev(x))
-    y = sv.linear_blocks(to_dev(wq), ws_dev(ws), xq, xs)
+    y = sv.linear_blocks(packed(wq, ws), xq, xs)
     torch.cuda.synchronize()
     xq_o, xs_o = oracle.quantize_act_blocks(x)
     assert np.array_equal(xq.cpu().numpy(), xq_o)
@@ -279,10 +299,10 @@ def test_linear_blocks_parity(sv, T, N, K):
 def test_linear_blocks_llama_sampled(sv, name, T):
     N, K = LLAMA[name]
     case(f"linear blocks llama {name} N={N} K={K} T={T}")
-    wq, ws, wq_d, ws_d = _weights(0, N, K, 100 + list(LLAMA).index(name))
+    wq, ws, w = _weights(0, N, K, 100 + list(LLAMA).index(name))
     _, _, x = sg.linear_case(0, T, 1, K, layer=200 + list(LLAMA).index(name))
     xq, xs = sv.quantize_act_blocks(to_dev(x))
-    y = sv.linear_blocks(wq_d, ws_d, xq, xs).cpu().numpy()
+    y = sv.linear_blocks(w, xq, xs).cpu().numpy()
     xq_o, xs_o = oracle.quantize_act_blocks(x)
     rows = _sample_rows(N, 3, n=32)
     assert_bits(y[:, rows].copy(), oracle.w4a8_linear_blocks(wq[rows], ws[rows], xq_o, xs_o), f"{name} T={T}")
@@ -304,10 +324,9 @@ def test_linear_degenerate_values(sv):
     y_o = oracle.w4a8_linear(wq, ws, xq_o, xs_o)
     _, _, y = gpu_quant_linear(sv, wq, ws, x)
     assert_bits(y, y_o, "degenerate")
-    empty = sv.linear(torch.zeros((0, 16), dtype=torch.uint8, device="cuda"),
-                      torch.zeros((1, 0), dtype=torch.int16, device="cuda"),
-                      torch.zeros((1, 32), dtype=torch.int8, device="cuda"),
-                      torch.ones(1, device="cuda"))
+    no_rows = sv.Packed(torch.zeros(16, dtype=torch.uint8, device="cuda"),
+                        torch.zeros(1, dtype=torch.int16, device="cuda"), 0, 32)
+    empty = sv.linear(no_rows, torch.zeros((1, 32), dtype=torch.int8, device="cuda"), torch.ones(1, device="cuda"))
     assert empty.shape == (1, 0)
 
 
