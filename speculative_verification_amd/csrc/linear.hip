@@ -92,6 +92,32 @@ __device__ __forceinline__ void quad_dots(const v4i w, const v4i (&a0)[TT], cons
     for (int tt = 0; tt < TT; tt++) d[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[tt], b[1], d[tt], 0, 0, 0);
 }
 
+// Tree levels w = 1, 2 of the four slots of a quad, which sit in the four
+// 16-lane rows of a wave (slot q of the quad in row q): row q meets row
+// q ^ 1, then row q ^ 2. A permlane swap of a value with itself returns, in
+// a lane of the lower row (half) of a pair, its own value and the upper
+// partner's, and in the upper row the lower partner's value and its own;
+// each lane adds the partner's value to its own, so both lanes of a pair
+// hold the same fp32 sum (a + b and b + a round alike). The exchanges of
+// all tokens are issued together, in VALU registers, without LDS.
+template <int T>
+__device__ __forceinline__ void pair_rows(float (&s)[T]) {
+    const int lane = threadIdx.x & 63;
+    const bool odd_row = (lane >> 4) & 1, upper_half = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        const unsigned u = __builtin_bit_cast(unsigned, s[t]);
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        s[t] = s[t] + __builtin_bit_cast(float, odd_row ? p[0] : p[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        const unsigned u = __builtin_bit_cast(unsigned, s[t]);
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        s[t] = s[t] + __builtin_bit_cast(float, upper_half ? p[0] : p[1]);
+    }
+}
+
 // Activation codes of one 16-byte chunk (two 8-input chunks) in the
 // even-then-odd order of the nibble decode: inputs 0, 2, 4, 6, 1, 3, 5, 7.
 __device__ __forceinline__ v4i even_odd(const v4i a) {
@@ -604,12 +630,13 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     // before any thread passes the next tile's barrier.
     auto finish_tile = [&](int k, const float (&acc)[T], int buf) {
         const int tile = v + k * nwg;
+        float s[T];
 #pragma unroll
-        for (int t = 0; t < T; t++) {
-            float s = acc[t];
-            s = s + __shfl_xor(s, 16, 64);
-            s = s + __shfl_xor(s, 32, 64);
-            if (q == 0) red[buf][wave][t][r] = s;
+        for (int t = 0; t < T; t++) s[t] = acc[t];
+        pair_rows<T>(s);
+        if (q == 0) {
+#pragma unroll
+            for (int t = 0; t < T; t++) red[buf][wave][t][r] = s[t];
         }
         __syncthreads();
 #pragma unroll
@@ -705,6 +732,21 @@ static int enable_lds(const void* kernel, size_t lds, size_t& enabled) {
     return SPECV_OK;
 }
 
+// A deeper load pipeline for matrices whose tiles give each CU at most one
+// workgroup and whose waves walk many iterations (the long-K down projection
+// of the 8B shape: K = 14336, 256 tiles): with four waves per CU, seven
+// iterations in flight per wave hide more of the memory latency. Shapes with
+// two workgroups per CU stream best with four (measured on MI355X: deeper
+// pipelines there were slower). The depth must divide the iteration count,
+// so no padding iterations are added.
+constexpr int kDeepStages = 7;
+inline bool deep_stream(int T, int N, int K) {
+    const int J = (K / 32 + 15) / 16;
+    const int NT = (N + 15) / 16;
+    return J % kDeepStages == 0 && J >= 2 * kDeepStages && NT <= device_cus() &&
+           stream_lds_bytes(T, K, false, false, kDeepStages) + (size_t)T * 512 <= kLdsBudget;
+}
+
 template <int T, bool AMAX, bool BS, bool RELOAD, int PROD = kProdNone, int P = SPECV_STREAM_STAGES>
 static int launch_one(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
                       Best* amax, int Tr, int N, int K, hipStream_t s, const ProdArgs& pa = ProdArgs{}) {
@@ -731,16 +773,13 @@ template <int T, bool BS>
 static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
                     int Tr, int N, int K, hipStream_t s) {
     const bool keep = stream_keeps(T, K, BS);
-#ifdef SPECV_PDEEP
     if constexpr (T <= 16 && !BS) {
-        const int J = (K / 32 + 15) / 16;
-        if (keep && J % SPECV_PDEEP == 0 &&
-            stream_lds_bytes(T, K, false, false, SPECV_PDEEP) + (size_t)T * 512 <= kLdsBudget)
-            return amax ? launch_one<T, true, false, false, kProdNone, SPECV_PDEEP>(wq, ws, xq, xs, y, amax, Tr, N, K, s)
-                        : launch_one<T, false, false, false, kProdNone, SPECV_PDEEP>(wq, ws, xq, xs, y, nullptr, Tr,
-                                                                                      N, K, s);
+        if (deep_stream(T, N, K))
+            return amax ? launch_one<T, true, false, false, kProdNone, kDeepStages>(wq, ws, xq, xs, y, amax, Tr, N,
+                                                                                    K, s)
+                        : launch_one<T, false, false, false, kProdNone, kDeepStages>(wq, ws, xq, xs, y, nullptr, Tr,
+                                                                                     N, K, s);
     }
-#endif
     if constexpr (T <= 16 && !BS) {
         if (amax)
             return keep ? launch_one<T, true, false, false>(wq, ws, xq, xs, y, amax, Tr, N, K, s)
