@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "c728c11a4cb18cea600e3effdc0ef34292a860c113272bf8741bd3cf8428f7d6",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33621583}
+LINEAR_TRAFFIC = {"source_sha256": "934d322b4551ce67ccc51f86daeafa5c53e2454671e960d8de112f51898a0019",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33630615}
 
 
 def linear_traffic(T, workload):
@@ -562,7 +562,8 @@ def main():
                   for T, v in per_T.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": linear_traffic(args.T, args.workload),
-                     "kernel": f"w4a8_linear_stream_kernel<{args.T},4,*,false,false> (the lm_head runs the argmax specialisation)",
+                     "kernel": f"w4a8_linear_stream_kernel<{args.T},P,*,false,false> (P = 7 for down, 4 otherwise; "
+                               f"the lm_head runs the argmax specialisation)",
                      "lm_head_chunks": model.lm_chunks(args.T),
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
