@@ -327,28 +327,97 @@ def roofline_linear(model, T, reps, torch):
     return avg_b / avg_s / 1e9, avg_s, avg_b, len(durs) // reps, by_shape
 
 
-def cpu_baseline(model, T, min_seconds=10.0):
+def ceilings(model, T, torch, sv):
+    """Rates of plain streaming reads (specv_stream_read: no arithmetic) on
+    the same device, as ceilings for the step: one read of all the step's
+    weight bytes; an empty launch per graph node; and a dependent chain of
+    129 reads, one per linear launch of the step, of the same byte counts
+    from distinct regions (cold), in graph replays."""
+    m = model.m
+    sizes = []
+    for _ in range(m["layers"]):
+        sizes += [weight_bytes(N, K) for _, N, K in layer_linears(m)]
+    sizes.append(weight_bytes(m["vocab"], m["hidden"]))
+    offs, tot = [], 0
+    for b in sizes:
+        offs.append(tot)
+        tot += (b + 4095) // 4096 * 4096
+    buf = torch.ones(tot // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    base, sp = buf.data_ptr(), sink.data_ptr()
+
+    def graph_us(fn, n, reps=5):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(s.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn(s.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        del g
+        return float(np.median(ts)) / n
+
+    def read(ptr, nb, grid, st):
+        sv.check("specv_stream_read", sv.LIB.specv_stream_read(ptr, nb, sp, grid, st))
+
+    empty = graph_us(lambda st: [read(base, 0, 512, st) for _ in range(200)], 200)
+    whole = min(graph_us(lambda st: read(base, tot, g, st), 1) for g in (512, 1024, 2048))
+    chain = graph_us(lambda st: [read(base + o, b, 512, st) for o, b in zip(offs, sizes)], 1)
+    del buf
+    return {"read_all_weights_GBs": round(tot / whole / 1e3, 1), "empty_launch_us": round(empty, 3),
+            "read_chain_us": round(chain, 2), "read_chain_GBs": round(sum(sizes) / chain / 1e3, 1),
+            "note": "plain streaming reads with no arithmetic (specv_stream_read), graph replays, cold: one read "
+                    "of the step's weight bytes; an empty launch; a dependent chain of 129 reads with the byte "
+                    "counts of the step's linear launches"}
+
+
+def cpu_baseline(model, T, seconds=(6.0, 6.0)):
     """The oracle, as it stands, on a bounded sample: quantize + W4A8 linear
     over the generated layer sets (qkv, o, gate_up, down) at T tokens, one
-    linear after another until at least `min_seconds` have passed, single
-    thread."""
+    linear after another, first on one host thread for at least seconds[0],
+    then with the linear's output rows split over every host thread (the C
+    oracle releases the interpreter lock; rows are independent, so results
+    are identical) for at least seconds[1]. `value` is the all-threads rate."""
     import oracle
     sg = model.sg
-    t0 = time.perf_counter()
-    nbytes, n = 0, 0
     lins = [(s, nm, N, K) for s in model.host_sets for nm, N, K in layer_linears(model.m)]
-    while n == 0 or time.perf_counter() - t0 < min_seconds:
-        lay, nm, N, K = lins[n % len(lins)]
-        x = sg.normal_f32(sg.stream_key(5, 3 + K), T * K).reshape(T, K)
-        xq, xs = oracle.quantize_act(x)
-        oracle.w4a8_linear(lay[nm][0], lay[nm][1], xq, xs)
-        nbytes += linear_bytes(T, N, K) + quant_bytes(T, K)
-        n += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"quantize + W4A8 linear, {n} linears of the {model.m['hidden']}-hidden layer sets "
-                      f"(qkv, o, gate_up, down) at T={T}: {nbytes/1e6:.1f} MB algorithmic in {dt:.2f} s, "
-                      f"single thread on {platform.machine()} ({os.cpu_count()} host cpus visible)"}
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def run(nthreads, min_s):
+        t0 = time.perf_counter()
+        nbytes, n = 0, 0
+        while n == 0 or time.perf_counter() - t0 < min_s:
+            lay, nm, N, K = lins[n % len(lins)]
+            x = sg.normal_f32(sg.stream_key(5, 3 + K), T * K).reshape(T, K)
+            xq, xs = oracle.quantize_act(x)
+            if nthreads == 1:
+                oracle.w4a8_linear(lay[nm][0], lay[nm][1], xq, xs)
+            else:
+                oracle.w4a8_linear_threads(lay[nm][0], lay[nm][1], xq, xs, nthreads)
+            nbytes += linear_bytes(T, N, K) + quant_bytes(T, K)
+            n += 1
+        return nbytes, n, time.perf_counter() - t0
+
+    b1, n1, t1 = run(1, seconds[0])
+    bt, nt, tt = run(threads, seconds[1])
+    return {"value": round(bt / tt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": round(b1 / t1 / 1e9, 4),
+            "sample": f"quantize + W4A8 linear over the {model.m['hidden']}-hidden layer sets (qkv, o, gate_up, "
+                      f"down) at T={T}, one linear after another: {n1} linears ({b1/1e6:.1f} MB algorithmic) in "
+                      f"{t1:.2f} s on one thread, then {nt} linears ({bt/1e6:.1f} MB) in {tt:.2f} s with output "
+                      f"rows split over {threads} threads, on {platform.machine()} ({os.cpu_count()} host cpus "
+                      f"visible)"}
 
 
 def window_bench(torch, sv, sg, widths, W=16, max_windows=400):
@@ -492,6 +561,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window-widths", default="1,2,4,8,16",
                     help="tree widths of the speculation-window measurement (empty: skip)")
+    ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
+                    help="skip the plain streaming-read ceilings")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -529,6 +600,11 @@ def main():
               f"replay exact={ok}", file=sys.stderr, flush=True)
 
     ach, avg_s, avg_b, nlaunch, by_shape = roofline_linear(model, args.T, args.roofline_reps, torch)
+    ceil = ceilings(model, args.T, torch, sv) if args.ceilings else None
+    if ceil:
+        ceil["step_pct_of_read_all"] = round(100 * per_T[args.T]["GB/s"] / ceil["read_all_weights_GBs"], 1)
+        ceil["step_over_read_chain"] = round(per_T[args.T]["ms"] * 1e3 / ceil["read_chain_us"], 3)
+        print(f"[bench] ceilings: {ceil}", file=sys.stderr, flush=True)
     widths = [int(w) for w in args.window_widths.split(",") if w]
     window = window_bench(torch, sv, sg, widths) if widths else None
     main_T = per_T[args.T]
@@ -568,6 +644,7 @@ def main():
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
                      "by_shape": by_shape},
+        "ceilings": ceil,
         "window": window,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(model, args.T),
     }

@@ -210,6 +210,19 @@ int w4a8_linear_argmax_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq
 int specv_time_next_linear(void* start_event, void* stop_event);
 
 /*
+ * Measurement diagnostic (not part of the computation): reads `bytes` bytes
+ * at p (device memory, 16-byte aligned, bytes a multiple of 16) with `grid`
+ * workgroups of 256 threads, each thread keeping four 16-byte loads in
+ * flight, and does nothing with them (sink, 4 bytes of device memory, is
+ * written only if the folded bytes equal a fixed sentinel). It gives the
+ * rate at which the same bytes stream with no arithmetic; bytes == 0 is an
+ * empty launch, for the per-launch cost of the queue. grid in [1, 65536].
+ * Returns SPECV_E_INVAL or SPECV_E_ALIGN on bad arguments, enqueueing
+ * nothing.
+ */
+int specv_stream_read(const void* p, size_t bytes, uint32_t* sink, int32_t grid, void* stream);
+
+/*
  * Greedy argmax per tree node and tree acceptance ([P1], GPU-Resident
  * Speculation Loop: the acceptance kernel walks the tree from the root and
  * follows the child whose token equals the greedy prediction of its parent;

@@ -124,6 +124,27 @@ def w4a8_linear(wq: np.ndarray, ws: np.ndarray, xq: np.ndarray, xs: np.ndarray) 
     return y
 
 
+def w4a8_linear_threads(wq: np.ndarray, ws: np.ndarray, xq: np.ndarray, xs: np.ndarray,
+                        threads: int) -> np.ndarray:
+    """w4a8_linear over blocks of output rows on `threads` host threads (the
+    C call releases the interpreter lock). Every row is computed by the same
+    code on the same inputs, so the result equals w4a8_linear bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+    wq, ws = np.ascontiguousarray(wq), np.ascontiguousarray(ws)
+    N = wq.shape[0]
+    T = xq.shape[0]
+    bounds = np.linspace(0, N, max(1, min(threads, N)) + 1).astype(int)
+    y = np.empty((T, N), np.float32)
+
+    def block(i):
+        r0, r1 = bounds[i], bounds[i + 1]
+        y[:, r0:r1] = w4a8_linear(wq[r0:r1], ws[r0:r1], xq, xs)
+
+    with ThreadPoolExecutor(max_workers=len(bounds) - 1) as ex:
+        list(ex.map(block, range(len(bounds) - 1)))
+    return y
+
+
 def quantize_act_blocks(x: np.ndarray):
     """Per-block (32 inputs) int8 codes and scales [T][K/32]."""
     x = np.ascontiguousarray(x, np.float32)

@@ -27,6 +27,7 @@ SIGNATURES = {
     "w4a8_linear_workspace": (SZ, [I32, I32, I32]),
     "w4a8_linear_T": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, P, SZ, P]),
     "specv_time_next_linear": (ctypes.c_int, [P, P]),
+    "specv_stream_read": (ctypes.c_int, [P, SZ, P, I32, P]),
     "w4a8_linear_argmax_workspace": (SZ, [I32, I32, I32]),
     "w4a8_linear_argmax_T": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, P, SZ, P]),
     "tree_accept": (ctypes.c_int, [P, I32, P, P, P, P, P, P, I32, P]),

@@ -117,6 +117,17 @@ def test_time_next_linear_arguments(lib):
     assert lib.specv_time_next_linear(None, None) == OK
 
 
+def test_stream_read_arguments(lib):
+    f = lib.specv_stream_read
+    assert f(A, 1 << 20, A, 0, None) == E_INVAL            # grid < 1
+    assert f(A, 1 << 20, A, 65537, None) == E_INVAL
+    assert f(A, 24, A, 512, None) == E_INVAL                # not a multiple of 16
+    assert f(None, 32, A, 512, None) == E_INVAL
+    assert f(A, 32, None, 512, None) == E_INVAL
+    assert f(A + 8, 32, A, 512, None) == E_ALIGN
+    assert f(A, 32, A + 2, 512, None) == E_ALIGN
+
+
 def test_quantize_rejects_bad_arguments(lib):
     f = lib.w4a8_quantize_act
     assert f(A, 0, 64, A, A, None) == OK                      # T == 0: nothing to do

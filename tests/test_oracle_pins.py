@@ -246,6 +246,15 @@ def test_linear_rows_subset_matches_full(orc):
     assert orc.w4a8_linear_rows(wq, ws, xq, xs, rows).tobytes() == y[:, rows].copy().tobytes()
 
 
+def test_linear_threads_equal_single_thread(orc):
+    """The row-block threaded oracle (the all-cores CPU baseline) computes
+    every row with the same code, so it equals the one-call result."""
+    for T, N, K, th in ((8, 300, 896, 7), (1, 17, 64, 16), (3, 5, 128, 8)):
+        wq, ws, x = sg.linear_case(21, T, N, K)
+        xq, xs = orc.quantize_act(x)
+        assert orc.w4a8_linear_threads(wq, ws, xq, xs, th).tobytes() == orc.w4a8_linear(wq, ws, xq, xs).tobytes()
+
+
 def test_linear_sequential_order_differs(orc):
     """Summing the scaled group terms sequentially instead of in R16 order
     changes some output bits, so the parity tests would see a wrong order."""
