@@ -314,6 +314,7 @@ int kv_compact(uint16_t* k_cache, uint16_t* v_cache, int32_t n_layers, int32_t n
  * are bit-reproducible. Limits: n_heads/n_kv_heads <= 16; head_dim a
  * multiple of 16 in [16, 128]; hidden, inter and n_heads*head_dim multiples
  * of 32; hidden, inter <= 16384; n_heads*head_dim <= 8192;
+ * max_pos >= kv_capacity (a rotary row for every position a step reaches);
  * 4*n_heads*(ceil(kv_capacity/256)+1) <= 64 KiB. The norm weights are
  * 16-byte aligned.
  */

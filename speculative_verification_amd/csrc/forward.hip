@@ -284,42 +284,6 @@ __global__ __launch_bounds__(kRowThreads) void silu_mul_quant_kernel(const float
     quantize_regs(z, I, xq + (size_t)i * I, xs + i, red);
 }
 
-// Rotary positions at L + depth(i) on the q and k heads of node i; k and v
-// go to the fp16 caches at physical row L + i of this layer.
-// Rotate-half: x'_d = x_d c - x_{d+h} s, x'_{d+h} = x_{d+h} c + x_d s.
-__global__ __launch_bounds__(64) void rope_kv_kernel(const float* __restrict__ qkv, const int32_t* __restrict__ tinfo,
-                                                     const float* __restrict__ cos_t, const float* __restrict__ sin_t,
-                                                     int max_pos, int hd, int nh, int nkv, float* __restrict__ qrot,
-                                                     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int layer,
-                                                     int cap, const specv_ctrl* ctrl) {
-    const int i = blockIdx.x, head = blockIdx.y;
-    if (ctrl->done || i >= ctrl->n_nodes) return;
-    const int L = ctrl->committed_len;
-    const int pos = L + min(max(tinfo[i], 0), i);
-    const int half = hd / 2, d = threadIdx.x;
-    const int QKV = (nh + 2 * nkv) * hd;
-    if (d >= half || pos >= max_pos || L + i >= cap) return;
-    const float c = cos_t[(size_t)pos * half + d], s = sin_t[(size_t)pos * half + d];
-    const float* src = qkv + (size_t)i * QKV + head * hd;
-    const float a = src[d], b = src[d + half];
-    const float ra = a * c - b * s;
-    const float rb = b * c + a * s;
-    if (head < nh) {
-        float* dst = qrot + ((size_t)i * nh + head) * hd;
-        dst[d] = ra;
-        dst[d + half] = rb;
-    } else {
-        const int g = head - nh;
-        const size_t row = (((size_t)layer * nkv + g) * cap + (L + i)) * hd;
-        const float* vs = qkv + (size_t)i * QKV + (nh + nkv) * hd + g * hd;
-        const float va = vs[d], vb = vs[d + half];
-        kc[row + d] = f32_to_f16(ra);
-        kc[row + d + half] = f32_to_f16(rb);
-        vc[row + d] = f32_to_f16(va);
-        vc[row + d + half] = f32_to_f16(vb);
-    }
-}
-
 constexpr int kAttnChunk = 256;   // logical positions per chunk
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;     // query heads per KV head
@@ -335,9 +299,22 @@ inline size_t attn_lds_bytes(int hpg, int hd) {  // dynamic part: the staged val
 
 inline size_t merge_lds_bytes(int nh, int nchunk_max) { return (size_t)4 * nh * (nchunk_max + 1); }
 
+// Rotate-half rotary position p of one head's pair (x_d, x_{d+h}), h = HD/2:
+// x'_d = x_d c - x_{d+h} s, x'_{d+h} = x_{d+h} c + x_d s, with c, s the
+// table's fp32 values for (p, d).
+__device__ __forceinline__ void rope_pair(float a, float b, float c, float s, float& ra, float& rb) {
+    ra = a * c - b * s;
+    rb = b * c + a * s;
+}
+
 // One chunk of the visible sequence of one node for one query head. Logical
-// position j < L is cache row j; position L + t is the physical row of the
-// node's ancestor at depth t (the node itself last). For the head:
+// position j < L is cache row j; position L + t is the node's ancestor at
+// depth t (the node itself last), whose key and value this step makes: the
+// key rotated at position L + t and both rounded to fp16, exactly the row
+// the step writes to the cache at physical row L + ancestor. The query of
+// the node is rotated at position L + depth(i). The workgroup of chunk 0 and
+// the first query head of each KV group writes node i's key and value rows
+// to the caches (no workgroup of this launch reads them). For the head:
 // s_j = R16_d(q_d * K_jd) * scale, m = max s_j, e_j = E(s_j - m),
 // l = R16_j(e_j), o_d = R16_j(e_j * V_jd), sums over the chunk's positions
 // in logical order. Output per (node, head, chunk): m, l, o[hd].
@@ -354,10 +331,11 @@ inline size_t merge_lds_bytes(int nh, int nchunk_max) { return (size_t)4 * nh * 
 // index-order tree.
 template <int HD>
 __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
-    const float* __restrict__ qrot, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ tinfo, int layer, int cap, int nh, int nkv, float scale,
-    float* __restrict__ part, int nchunk_max, const specv_ctrl* ctrl) {
+    const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
+    int nh, int nkv, float scale, float* __restrict__ part, int nchunk_max, const specv_ctrl* ctrl) {
     constexpr int VS = HD + 8;
+    constexpr int HALF = HD / 2;
     const int c = blockIdx.x, hq = blockIdx.y, i = blockIdx.z, tid = threadIdx.x;
     const int depth_raw = tinfo[i];  // issued with the control loads (i < 16)
     if (ctrl->done || i >= ctrl->n_nodes) return;
@@ -368,16 +346,36 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     const int j0 = c * kAttnChunk;
     if (j0 >= len) return;
     const int cnt = len - j0 < kAttnChunk ? len - j0 : kAttnChunk;
-    const int g = hq / (nh / nkv);
+    const int grp = nh / nkv, g = hq / grp;
+    const int QKV = (nh + 2 * nkv) * HD;
     __shared__ int anc[kMaxNodes];
+    __shared__ int apos[kMaxNodes];  // rotary position of each ancestor of the node
+    __shared__ __attribute__((aligned(16))) uint16_t tk[kMaxNodes][HD];  // the ancestors' fp16 key rows
+    __shared__ __attribute__((aligned(16))) uint16_t tv[kMaxNodes][HD];  // and value rows
     __shared__ float qs[HD];
     __shared__ float S[kAttnChunk];
     __shared__ float s_m;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][VS]
 
-    if (tid < HD / 4) *reinterpret_cast<float4*>(qs + 4 * tid) = ld4(qrot + ((size_t)i * nh + hq) * HD + 4 * tid);
     const size_t plane = (((size_t)layer * nkv + g) * cap) * HD;
+    if (tid < HALF) {  // the node's rotated query
+        const size_t tp = (size_t)(L + depth) * HALF + tid;
+        const float* src = qkv + (size_t)i * QKV + hq * HD;
+        rope_pair(src[tid], src[tid + HALF], cos_t[tp], sin_t[tp], qs[tid], qs[tid + HALF]);
+    } else if (c == 0 && hq % grp == 0 && tid < 2 * HALF) {  // the node's key and value rows to the caches
+        const int d = tid - HALF;
+        const size_t tp = (size_t)(L + depth) * HALF + d;
+        const float* ks = qkv + (size_t)i * QKV + (nh + g) * HD;
+        const float* vs = qkv + (size_t)i * QKV + (nh + nkv + g) * HD;
+        float ra, rb;
+        rope_pair(ks[d], ks[d + HALF], cos_t[tp], sin_t[tp], ra, rb);
+        const size_t row = plane + (size_t)(L + i) * HD;
+        kc[row + d] = f32_to_f16(ra);
+        kc[row + d + HALF] = f32_to_f16(rb);
+        vc[row + d] = f32_to_f16(vs[d]);
+        vc[row + d + HALF] = f32_to_f16(vs[d + HALF]);
+    }
     const bool live = tid < cnt;
     const int j = j0 + tid;
     v4i kr[HD / 8], vr[HD / 8];
@@ -391,16 +389,35 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
             vr[t] = vsrc[t];
         }
     }
-    if (tid <= depth) anc[tid] = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
+    if (tid <= depth) {
+        const int a = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
+        anc[tid] = a;
+        apos[tid] = L + min(max(tinfo[a], 0), a);
+    }
     __syncthreads();
-    if (live && !early) {
-        const int row = L + anc[j - L];
-        const v4i* ksrc = reinterpret_cast<const v4i*>(kc + plane + (size_t)row * HD);
-        const v4i* vsrc = reinterpret_cast<const v4i*>(vc + plane + (size_t)row * HD);
+    if (j0 + cnt > L) {  // the chunk holds tree positions: their rows, made once into LDS
+        for (int w = tid; w < (depth + 1) * HALF; w += kFwdThreads) {
+            const int t = w / HALF, d = w - t * HALF;
+            const int a = anc[t];
+            const float* ks = qkv + (size_t)a * QKV + (nh + g) * HD;
+            const float* vs = qkv + (size_t)a * QKV + (nh + nkv + g) * HD;
+            const size_t tp = (size_t)apos[t] * HALF + d;
+            float ra, rb;
+            rope_pair(ks[d], ks[d + HALF], cos_t[tp], sin_t[tp], ra, rb);
+            tk[t][d] = f32_to_f16(ra);
+            tk[t][d + HALF] = f32_to_f16(rb);
+            tv[t][d] = f32_to_f16(vs[d]);
+            tv[t][d + HALF] = f32_to_f16(vs[d + HALF]);
+        }
+        __syncthreads();
+        if (live && !early) {
+            const v4i* ksrc = reinterpret_cast<const v4i*>(&tk[j - L][0]);
+            const v4i* vsrc = reinterpret_cast<const v4i*>(&tv[j - L][0]);
 #pragma unroll
-        for (int t = 0; t < HD / 8; t++) {
-            kr[t] = ksrc[t];
-            vr[t] = vsrc[t];
+            for (int t = 0; t < HD / 8; t++) {
+                kr[t] = ksrc[t];
+                vr[t] = vsrc[t];
+            }
         }
     }
     // score of this thread's position
@@ -571,7 +588,6 @@ StepLayout step_layout(const specv_model* m, int n) {
     s.xq = take(n * xq_cols);
     s.xs = take(4 * n);
     s.qkv = take(4 * n * QKV);
-    s.qrot = take(4 * n * A);
     s.attn = take(4 * (size_t)n * m->n_heads * nch * (m->head_dim + 2));
     s.gu = take(4 * n * 2 * I);
     s.logits = take(4 * n * V);
@@ -595,7 +611,8 @@ int validate_model(const specv_model* m) {
     if (m->n_layers < 1 || m->hidden < 32 || m->hidden % 32 || m->n_heads < 1 || m->n_kv_heads < 1 ||
         m->n_heads % m->n_kv_heads || m->n_heads / m->n_kv_heads > kMaxGroup || m->head_dim < 16 ||
         m->head_dim % 16 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
-        m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || !(m->eps >= 0.0f) ||
+        m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || m->max_pos < m->kv_capacity ||
+        !(m->eps >= 0.0f) ||
         attn_lds_bytes(m->n_heads / m->n_kv_heads, m->head_dim) > 150 * 1024 ||
         (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024 ||
         (size_t)m->n_heads * m->head_dim > (size_t)kMergeRegs * kRowThreads ||
@@ -617,9 +634,10 @@ int validate_model(const specv_model* m) {
         if (rc_ != SPECV_OK) return rc_; \
     } while (0)
 
-static int launch_attn_chunk(int hd, dim3 grid, size_t lds, hipStream_t s, const float* qrot,
-                             const uint16_t* kc, const uint16_t* vc, const int32_t* tinfo, int layer, int cap,
-                             int nh, int nkv, float scale, float* part, int nchunk_max, const specv_ctrl* ctrl) {
+static int launch_attn_chunk(int hd, dim3 grid, size_t lds, hipStream_t s, const float* qkv, const float* cos_t,
+                             const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
+                             int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
+                             const specv_ctrl* ctrl) {
     switch (hd) {
 #define SPECV_ATTN(HDV)                                                                                   \
     case HDV: {                                                                                           \
@@ -632,8 +650,8 @@ static int launch_attn_chunk(int hd, dim3 grid, size_t lds, hipStream_t s, const
             }                                                                                             \
             enabled = lds;                                                                                \
         }                                                                                                 \
-        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), lds, s, qrot, kc, vc, tinfo, \
-                           layer, cap, nh, nkv, scale, part, nchunk_max, ctrl);                         \
+        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), lds, s, qkv, cos_t, sin_t, kc, vc, \
+                           tinfo, layer, cap, nh, nkv, scale, part, nchunk_max, ctrl);                  \
         return launch_status();                                                                           \
     }
         SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
@@ -653,7 +671,6 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     int8_t* xq = reinterpret_cast<int8_t*>(ws + lay.xq);
     float* xs = reinterpret_cast<float*>(ws + lay.xs);
     float* qkv = reinterpret_cast<float*>(ws + lay.qkv);
-    float* qrot = reinterpret_cast<float*>(ws + lay.qrot);
     float* attn = reinterpret_cast<float*>(ws + lay.attn);
     float* gu = reinterpret_cast<float*>(ws + lay.gu);
     int32_t* tinfo = reinterpret_cast<int32_t*>(ws + lay.tinfo);
@@ -698,12 +715,9 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
 
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
                               true));
-        hipLaunchKernelGGL(rope_kv_kernel, dim3(n, nh + nkv), dim3(64), 0, s, qkv, tinfo, m->rope_cos,
-                           m->rope_sin, m->max_pos, hd, nh, nkv, qrot, m->k_cache, m->v_cache, l, cap, ctrl);
-        SPECV_TRY(launch_status());
-        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nh, n), attn_lds_bytes(nh / nkv, hd), s, qrot,
-                                    m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
-                                    ctrl));
+        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nh, n), attn_lds_bytes(nh / nkv, hd), s, qkv,
+                                    m->rope_cos, m->rope_sin, m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale,
+                                    attn, lay.nchunk_max, ctrl));
         hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kRowThreads),
                            merge_lds_bytes(nh, lay.nchunk_max), s, attn, tinfo, nh, hd, lay.nchunk_max, xq, xs,
                            ctrl);

@@ -189,10 +189,18 @@ def fake_model(**over):
     cfg.update(over)
     for k, v in cfg.items():
         setattr(m, k, v)
-    m.eps, m.kv_capacity = 1e-6, 700
+    m.eps, m.kv_capacity = 1e-6, 600
     for k, _ in SpecvModel._fields_[10:]:
         setattr(m, k, A)
     return m
+
+
+def test_model_needs_rotary_rows_for_every_position(lib):
+    """Every position a step can reach (below kv_capacity) has a rotary table
+    row: a model whose max_pos is below its capacity is rejected."""
+    ok, short = fake_model(max_pos=600), fake_model(max_pos=599)
+    assert lib.spec_step_workspace(ctypes.addressof(ok), 8) > 0
+    assert lib.spec_step_workspace(ctypes.addressof(short), 8) == 0
 
 
 def test_window_rejects_bad_arguments(lib):
