@@ -92,27 +92,53 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
         }
         return;
     }
-    // 16 threads per node finish the argmax over the node's partials (or
-    // take the given argmax).
-    const int node = threadIdx.x >> 4;
-    const int sub = threadIdx.x & 15;
+    // The tree goes to LDS while the argmax partials are read.
+    __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_path[kMaxNodes];
+    __shared__ Best s_grp[kArgThreads / 16];
+    if (threadIdx.x < n) {
+        s_par[threadIdx.x] = parent[threadIdx.x];
+        s_tok[threadIdx.x] = token[threadIdx.x];
+    }
     if (amax_in) {
-        if (node < n && sub == 0) s_amax[node] = amax_in[node];
+        if (threadIdx.x < n) s_amax[threadIdx.x] = amax_in[threadIdx.x];
     } else {
+        // tpn = 256 / (n rounded up to a power of two) threads per node, each
+        // taking every tpn-th partial, four loads in flight; the best of each
+        // 16-lane group, then of the node's groups (order-free).
+        int np = 1;
+        while (np < n) np <<= 1;
+        const int tpn = kArgThreads / np;
+        const int node = threadIdx.x / tpn, sub = threadIdx.x - node * tpn;
         float bv = -__builtin_inff();
         int bi = 0x7fffffff;
-        if (node < n)
-            for (int c = sub; c < chunks; c += 16) {
-                const Best b = part[(int64_t)node * chunks + c];
+        if (node < n) {
+            const Best* pn = part + (int64_t)node * chunks;
+            int c = sub;
+            for (; c + 3 * tpn < chunks; c += 4 * tpn) {
+                const Best b0 = pn[c], b1 = pn[c + tpn], b2 = pn[c + 2 * tpn], b3 = pn[c + 3 * tpn];
+                if (better(b0.v, b0.i, bv, bi)) { bv = b0.v; bi = b0.i; }
+                if (better(b1.v, b1.i, bv, bi)) { bv = b1.v; bi = b1.i; }
+                if (better(b2.v, b2.i, bv, bi)) { bv = b2.v; bi = b2.i; }
+                if (better(b3.v, b3.i, bv, bi)) { bv = b3.v; bi = b3.i; }
+            }
+            for (; c < chunks; c += tpn) {
+                const Best b = pn[c];
                 if (better(b.v, b.i, bv, bi)) {
                     bv = b.v;
                     bi = b.i;
                 }
             }
+        }
         best16(bv, bi);
-        if (node < n && sub == 0) {
-            s_amax[node] = bi;
-            if (argmax_out) argmax_out[node] = bi;
+        if ((threadIdx.x & 15) == 0) s_grp[threadIdx.x >> 4] = Best{bv, bi};
+        __syncthreads();
+        if (threadIdx.x < n) {
+            const int g0 = threadIdx.x * (tpn / 16), ng = tpn / 16;
+            Best b = s_grp[g0];
+            for (int k = 1; k < ng; k++)
+                if (better(s_grp[g0 + k].v, s_grp[g0 + k].i, b.v, b.i)) b = s_grp[g0 + k];
+            s_amax[threadIdx.x] = b.i;
+            if (argmax_out) argmax_out[threadIdx.x] = b.i;
         }
     }
     __syncthreads();
@@ -121,12 +147,12 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
     s_acc[0] = 1;
     s_depth[0] = 0;
     for (int i = 1; i < n; i++) {
-        const int p = parent[i];
+        const int p = s_par[i];
         if (p < 0 || p >= i) {
             s_acc[i] = 0;
             s_depth[i] = 0;
         } else {
-            s_acc[i] = s_acc[p] && token[i] == s_amax[p];
+            s_acc[i] = s_acc[p] && s_tok[i] == s_amax[p];
             s_depth[i] = s_depth[p] + 1;
         }
     }
@@ -135,13 +161,14 @@ __global__ __launch_bounds__(kArgThreads) void accept_kernel(
         if (s_acc[i] && s_depth[i] > s_depth[w]) w = i;
     const int m = s_depth[w];
     for (int i = w, j = m; j >= 0; j--) {
+        s_path[j] = i;
         path[j] = i;
-        i = j > 0 ? parent[i] : i;
+        i = j > 0 ? s_par[i] : i;
     }
     const int bonus = s_amax[w];
     const int head = ctrl->ring_head;
     if (ring && ring_cap > 0)
-        for (int j = 0; j <= m; j++) ring[(uint32_t)(head + j) % (uint32_t)ring_cap] = j < m ? token[path[j + 1]] : bonus;
+        for (int j = 0; j <= m; j++) ring[(uint32_t)(head + j) % (uint32_t)ring_cap] = j < m ? s_tok[s_path[j + 1]] : bonus;
     const int L = ctrl->committed_len + m + 1;
     ctrl->accept_len = m;
     ctrl->committed_len = L;

@@ -349,7 +349,6 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     const int grp = nh / nkv, g = hq / grp;
     const int QKV = (nh + 2 * nkv) * HD;
     __shared__ int anc[kMaxNodes];
-    __shared__ int apos[kMaxNodes];  // rotary position of each ancestor of the node
     __shared__ __attribute__((aligned(16))) uint16_t tk[kMaxNodes][HD];  // the ancestors' fp16 key rows
     __shared__ __attribute__((aligned(16))) uint16_t tv[kMaxNodes][HD];  // and value rows
     __shared__ float qs[HD];
@@ -389,19 +388,17 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
             vr[t] = vsrc[t];
         }
     }
-    if (tid <= depth) {
-        const int a = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
-        anc[tid] = a;
-        apos[tid] = L + min(max(tinfo[a], 0), a);
-    }
+    if (tid <= depth) anc[tid] = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
     __syncthreads();
     if (j0 + cnt > L) {  // the chunk holds tree positions: their rows, made once into LDS
+        // The ancestor at depth t has depth t itself (its own walk to the root
+        // is the tail of the node's), so its rotary position is L + t.
         for (int w = tid; w < (depth + 1) * HALF; w += kFwdThreads) {
             const int t = w / HALF, d = w - t * HALF;
             const int a = anc[t];
             const float* ks = qkv + (size_t)a * QKV + (nh + g) * HD;
             const float* vs = qkv + (size_t)a * QKV + (nh + nkv + g) * HD;
-            const size_t tp = (size_t)apos[t] * HALF + d;
+            const size_t tp = (size_t)(L + t) * HALF + d;
             float ra, rb;
             rope_pair(ks[d], ks[d + HALF], cos_t[tp], sin_t[tp], ra, rb);
             tk[t][d] = f32_to_f16(ra);
@@ -523,6 +520,16 @@ __global__ __launch_bounds__(kRowThreads) void attn_merge_quant_kernel(
     const int nch_len = (len + kAttnChunk - 1) / kAttnChunk;
     const int nch = nch_len < nchunk_max ? nch_len : nchunk_max;
     const int stride = hd + 2;
+    // the first 16 chunks of this thread's first column, loaded before the
+    // chunk weights are known (columns past the first kRowThreads load theirs
+    // after them)
+    float ov0[16];
+    {
+        const int hh = tid / hd, d = tid - hh * hd;
+        const float* ph = part + ((size_t)i * nh + hh) * nchunk_max * stride + 2 + d;
+#pragma unroll
+        for (int c = 0; c < 16; c++) ov0[c] = tid < K && c < nch ? ph[(size_t)c * stride] : 0.0f;
+    }
     for (int hh = tid >> 4; hh < nh; hh += kRowThreads / 16) {
         const int s = tid & 15;
         const float* ph = part + ((size_t)i * nh + hh) * nchunk_max * stride;
@@ -554,7 +561,8 @@ __global__ __launch_bounds__(kRowThreads) void attn_merge_quant_kernel(
         for (int c0 = 0; c0 < nch; c0 += 16) {
             float ov[16];
 #pragma unroll
-            for (int s = 0; s < 16; s++) ov[s] = c0 + s < nch ? ph[(size_t)(c0 + s) * stride] : 0.0f;
+            for (int s = 0; s < 16; s++)
+                ov[s] = r == 0 && c0 == 0 ? ov0[s] : c0 + s < nch ? ph[(size_t)(c0 + s) * stride] : 0.0f;
 #pragma unroll
             for (int s = 0; s < 16; s++)
                 if (c0 + s < nch) slot[s] = slot[s] + wh[c0 + s] * ov[s];
