@@ -94,18 +94,20 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
     __shared__ int32_t cont[32][8];
     __shared__ int clen[32];
     __shared__ uint32_t cw[32];
-    __shared__ uint32_t wt[32][8];
-    __shared__ int rankv[32][8];
+    __shared__ __attribute__((aligned(16))) uint32_t wt[32][8];
+    __shared__ __attribute__((aligned(16))) int rankv[32][8];
     __shared__ int outi[32][8];
-    __shared__ int nsel_s;
+    __shared__ int wcount[4];
     const int tid = threadIdx.x;
     const int cands = prm.candidates, depth = prm.depth;
     const int n = cm_stream_len(ctrl, n_given, cap, s);
 
-    // running best `cands` keys over all parts: [0, cands) holds them, the
-    // next chunk of parts follows, and the whole is sorted at the smallest
-    // power of two that holds it
-    const int total = nparts * cands;
+    // running best `cands` keys over the parts that hold stream positions
+    // (later parts hold only the zero keys of positions without a match):
+    // [0, cands) holds them, the next chunk of parts follows, and the whole
+    // is sorted at the smallest power of two that holds it
+    const int used = min(nparts, (n + kScanThreads - 1) / kScanThreads);
+    const int total = used * cands;
     for (int i = tid; i < cands; i += 256) keys[i] = 0u;
     for (int base = 0; base < total; base += kMergeChunk) {
         const int m = min(kMergeChunk, total - base);
@@ -148,15 +150,22 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
     const bool is_node = valid && rep == k;
     wt[k][d] = is_node ? w : 0u;
     __syncthreads();
+    // rank among the nodes, reading the weight table 16 bytes at a time
+    // (every node weighs at least 1, so a zero entry is not a node)
     int rank = 1 << 20;
     if (is_node) {
         rank = 0;
-        for (int j = 0; j < 32; j++)
+#pragma unroll 4
+        for (int j = 0; j < 32; j++) {
+            const uint4 a = *reinterpret_cast<const uint4*>(&wt[j][0]);
+            const uint4 b = *reinterpret_cast<const uint4*>(&wt[j][4]);
+            const uint32_t row[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
             for (int e = 0; e < 8; e++) {
-                const uint32_t w2 = wt[j][e];
-                if (w2 == 0u) continue;  // not a node (every node weighs at least 1)
-                if (w2 > w || (w2 == w && (e < d || (e == d && j < k)))) rank++;
+                const uint32_t w2 = row[e];
+                rank += w2 != 0u && (w2 > w || (w2 == w && (e < d || (e == d && j < k))));
             }
+        }
     }
     const bool keep = is_node && rank < width - 1;
     rankv[k][d] = keep ? rank : -1;
@@ -164,18 +173,20 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
     // output position: by depth, then rank
     if (keep) {
         int pos = 1;
-        for (int j = 0; j < 32; j++)
-            for (int e = 0; e < 8; e++) {
-                const int r2 = rankv[j][e];
-                if (r2 >= 0 && (e < d || (e == d && r2 < rank))) pos++;
-            }
+#pragma unroll 4
+        for (int j = 0; j < 32; j++) {
+            const int4 a = *reinterpret_cast<const int4*>(&rankv[j][0]);
+            const int4 b = *reinterpret_cast<const int4*>(&rankv[j][4]);
+            const int row[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) pos += row[e] >= 0 && (e < d || (e == d && row[e] < rank));
+        }
         outi[k][d] = pos;
     }
-    if (tid == 0) {
-        int c = 0;
-        for (int j = 0; j < 32; j++)
-            for (int e = 0; e < 8; e++) c += rankv[j][e] >= 0;
-        nsel_s = c;
+    // the number of kept nodes: one per thread, summed over the workgroup
+    {
+        const unsigned long long b = __ballot(keep);
+        if ((tid & 63) == 0) wcount[tid >> 6] = __popcll(b);
     }
     __syncthreads();
     if (keep) {
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
         token[pos] = cont[k][d];
     }
     if (tid == 0) {
-        const int nodes = n > 0 ? 1 + nsel_s : 1;
+        const int nodes = n > 0 ? 1 + wcount[0] + wcount[1] + wcount[2] + wcount[3] : 1;
         const int bm = (n > 0 && keys[0]) ? (int)(keys[0] >> 24) : 0;
         parent[0] = -1;
         if (ctrl) {
