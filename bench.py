@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
 LINEAR_TRAFFIC = {"source_sha256": "934d322b4551ce67ccc51f86daeafa5c53e2454671e960d8de112f51898a0019",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33630615}
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33629748}
 
 
 def linear_traffic(T, workload):
