@@ -37,6 +37,17 @@ __device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
+// The same loads with the non-temporal cache policy (the `nt` bit), for data
+// read once per pass, such as the weights of a linear: the caches need not
+// keep them for a reuse that does not come.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ v4i load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT));
+}
+__device__ __forceinline__ uint16_t load2_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kCachePolicyNT);
+}
+
 // (value, index) pair of an argmax reduction. "Better" is the larger value,
 // or an equal value at a lower index: a total order on (value, -index) with
 // -0 == +0, so every reduction shape yields the lowest index of the maximum.

@@ -504,8 +504,8 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     auto load = [&](SStage<T, BS>& st, int tile, int j, bool with_act, uint32_t past) {
         const uint32_t bad = ((16 * j + (int)lq >= G) ? kOOB : 0u) | past;
         const uint32_t chunk = ((uint32_t)tile * (uint32_t)G + 16u * (uint32_t)j + lq) * 16u + (uint32_t)r;
-        st.w = load16(rw, (chunk * 16u) | bad);
-        st.s = load2(rs, (chunk * 2u) | bad);
+        st.w = load16_stream(rw, (chunk * 16u) | bad);
+        st.s = load2_stream(rs, (chunk * 2u) | bad);
         if (with_act) {
 #pragma unroll
             for (int x = 0; x < TX; x++) {
