@@ -74,11 +74,16 @@ constexpr int kRowRegs = 4;        // float4 chunks per thread: rows up to 16384
 constexpr int kMergeRegs = 8;      // values per thread in the merge: rows up to 8192
 constexpr int kMaxNodes = 16;
 
-// Block-wide max of non-negative values over kRowThreads threads (order-free).
+// Block-wide max of non-negative values over kRowThreads threads (order-free):
+// each 16-lane row by DPP, the wave's four rows read as scalars, then the
+// waves' maxima through LDS.
 __device__ __forceinline__ float block_max(float a, float* red) {
     a = max16(a);
-    a = fmaxf(a, __shfl_xor(a, 16, 64));
-    a = fmaxf(a, __shfl_xor(a, 32, 64));
+    const int b = __builtin_bit_cast(int, a);
+    a = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+              fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
     float r = red[0];
@@ -120,6 +125,10 @@ __device__ void quantize_regs(const float (&y)[R][V], int K, int8_t* __restrict_
             xrow[c0] = (int8_t)(packed & 0xff);
     }
 }
+
+// Floats per slot row of the RMSNorm kernel's transposed squares: H/16
+// rounded up to whole float4s.
+inline __host__ __device__ int norm_slot_stride(int H) { return ((H >> 4) + 3) & ~3; }
 
 // Rows of nodes past the live count quantise to zero, so the linears that
 // follow produce exact zeros for them. K is a multiple of 4.
@@ -194,10 +203,11 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_quant_kernel(float* __res
                                                                     float eps, int8_t* __restrict__ xq,
                                                                     float* __restrict__ xs,
                                                                     const specv_ctrl* ctrl) {
-    extern __shared__ float sq[];  // H squares, summed by 16 lanes in slot order
+    extern __shared__ __attribute__((aligned(16))) float sq[];  // squares transposed: 16 slot rows
     __shared__ float red[kRowThreads / 64];
     __shared__ float s_ss;
     const int i = blockIdx.x, tid = threadIdx.x, H4 = H / 4;
+    const int sstride = norm_slot_stride(H);
     if (ctrl->done) return;
     if (i >= ctrl->n_nodes) {
         zero_row(xq + (size_t)i * H, xs + i, H);
@@ -226,13 +236,32 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_quant_kernel(float* __res
             x[r][2] = x[r][2] + rv[r].z, x[r][3] = x[r][3] + rv[r].w;
             *reinterpret_cast<float4*>(hr + 4 * c) = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
         }
-        *reinterpret_cast<float4*>(sq + 4 * c) =
-            make_float4(x[r][0] * x[r][0], x[r][1] * x[r][1], x[r][2] * x[r][2], x[r][3] * x[r][3]);
+        // input k = 4c + e sits at slot k mod 16, position k / 16 of the
+        // slot's row of the transposed copy
+        float* q = sq + (4 * c & 15) * sstride + (c >> 2);
+        q[0] = x[r][0] * x[r][0];
+        q[sstride] = x[r][1] * x[r][1];
+        q[2 * sstride] = x[r][2] * x[r][2];
+        q[3 * sstride] = x[r][3] * x[r][3];
     }
     __syncthreads();
-    if (tid < 16) {
+    if (tid < 16) {  // slot tid: its row in increasing k, read 16 float4s at a time
+        const int n16 = H >> 4;
+        const float* row = sq + tid * sstride;
         float acc = 0.0f;
-        for (int k = tid; k < H; k += 16) acc = acc + sq[k];
+        for (int b0 = 0; b0 < n16; b0 += 64) {
+            float4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++)
+                if (b0 + 4 * u < n16) v[u] = *reinterpret_cast<const float4*>(row + b0 + 4 * u);
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int z = 0; z < 4; z++)
+                    if (b0 + 4 * u + z < n16) acc = acc + e[z];
+            }
+        }
         acc = tree16(acc);
         if (tid == 0) s_ss = acc;
     }
@@ -703,7 +732,8 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
             if (hnext) hcur = hnext;
             return rc;
         }
-        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads), H * sizeof(float), s, hcur, resid, w,
+        hipLaunchKernelGGL(rmsnorm_quant_kernel, dim3(n), dim3(kRowThreads),
+                           (size_t)16 * norm_slot_stride(H) * sizeof(float), s, hcur, resid, w,
                            H, m->eps, xq, xs, ctrl);
         SPECV_TRY(launch_status());
         if (am) return linear_enqueue(wq, ws_, xq, xs, y, am, n, N, H, lin, s);
