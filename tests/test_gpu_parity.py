@@ -217,7 +217,8 @@ def test_linear_run_to_run_identical(sv):
 
 
 @pytest.mark.parametrize("T,N,K", [(16, 16400, 10240), (16, 4096, 14336), (8, 4096, 14336), (8, 28672, 4096),
-                                   (32, 4096, 14336), (24, 9728, 4864), (32, 28672, 4096), (17, 5000, 896)])
+                                   (8, 6144, 4096), (32, 4096, 14336), (24, 9728, 4864), (32, 28672, 4096),
+                                   (17, 5000, 896)])
 def test_linear_layouts_sampled(sv, T, N, K):
     """Activations kept in LDS across a workgroup's tiles, and reloaded with
     every tile when T x K does not fit (T = 16 at K = 14336 or 10240, and
@@ -228,6 +229,22 @@ def test_linear_layouts_sampled(sv, T, N, K):
     _, _, y = gpu_quant_linear(sv, wq, ws, x)
     rows = _sample_rows(N, 11, n=40)
     assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), f"T={T} N={N} K={K}")
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 48, 1 << 20), (8, 48, 1 << 20), (2, (1 << 24) - 16, 32)])
+def test_linear_maximum_sizes(sv, T, N, K):
+    """The ABI's limits: K = 2^20 (the reloading layout, 2048 iterations per
+    wave), every row against the oracle; N = 2^24 - 16 rows (a million
+    tiles over the grid), on sampled rows and the last tile's rows."""
+    case(f"linear maximum sizes T={T} N={N} K={K}")
+    wq, ws, x = sg.linear_case(13, T, N, K)
+    xq_o, xs_o = oracle.quantize_act(x)
+    _, _, y = gpu_quant_linear(sv, wq, ws, x)
+    if N <= 64:
+        assert_bits(y, oracle.w4a8_linear(wq, ws, xq_o, xs_o), f"T={T} N={N} K={K}")
+    else:
+        rows = np.concatenate([_sample_rows(N, 13, n=64), np.arange(N - 16, N, dtype=np.int32)])
+        assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), f"T={T} N={N} K={K}")
 
 
 @pytest.mark.parametrize("T,N,K", [(16, 4096, 14336), (16, 16400, 10240), (8, 128256, 896), (32, 8000, 4096)])
