@@ -317,15 +317,6 @@ constexpr int kAttnChunk = 256;   // logical positions per chunk
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;     // query heads per KV head
 
-// Padded fp16 row of the staged values (8 extra halves spread the rows of a
-// 16-lane group over the LDS banks).
-inline __host__ __device__ int attn_vstride(int hd) { return hd + 8; }
-
-inline size_t attn_lds_bytes(int hpg, int hd) {  // dynamic part: the staged value rows
-    (void)hpg;
-    return (size_t)2 * kAttnChunk * attn_vstride(hd);
-}
-
 inline size_t merge_lds_bytes(int nh, int nchunk_max) { return (size_t)4 * nh * (nchunk_max + 1); }
 
 // Rotate-half rotary position p of one head's pair (x_d, x_{d+h}), h = HD/2:
@@ -351,20 +342,22 @@ __device__ __forceinline__ void rope_pair(float a, float b, float c, float s, fl
 // One workgroup per (chunk, query head, node): the query heads that share a
 // KV head read the same rows, which the L2 serves after the first; one head
 // per workgroup keeps each workgroup's dependent chains short and gives the
-// chip more of them. Thread t owns position t of the chunk, its key row in
-// registers as fp32 and its value row staged in LDS. The query is loaded
-// first and committed rows right after it, so neither waits for the other;
-// only the tree positions wait for the ancestor list. For the value sums,
-// lane s of a 16-lane group takes R16 slot s (positions s, s+16, ... in
-// order) of HD/16 columns, and the group's butterfly adds the slots as the
-// index-order tree.
+// chip more of them. Thread t owns position t of the chunk and its key row.
+// For the value sums, lane s of 16-lane group q takes R16 slot s (positions
+// s, s+16, ... in order) of columns 4q .. 4q+3 (and 64 + 4q .. for head dims
+// above 64), and the group's butterfly adds the slots as the index-order
+// tree; each lane loads the value words of its slot straight into registers,
+// so the workgroup needs no LDS for value rows and more workgroups fit on a
+// CU. The query is loaded first and committed rows right after it, so
+// neither waits for the other; only the tree positions wait for the ancestor
+// list.
 template <int HD>
 __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
     int nh, int nkv, float scale, float* __restrict__ part, int nchunk_max, const specv_ctrl* ctrl) {
-    constexpr int VS = HD + 8;
     constexpr int HALF = HD / 2;
+    constexpr int NB = (HD + 63) / 64;  // column blocks of 64 (16 groups x 4 columns)
     const int c = blockIdx.x, hq = blockIdx.y, i = blockIdx.z, tid = threadIdx.x;
     const int depth_raw = tinfo[i];  // issued with the control loads (i < 16)
     if (ctrl->done || i >= ctrl->n_nodes) return;
@@ -382,9 +375,6 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t tv[kMaxNodes][HD];  // and value rows
     __shared__ float qs[HD];
     __shared__ float S[kAttnChunk];
-    __shared__ float s_m;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][VS]
 
     const size_t plane = (((size_t)layer * nkv + g) * cap) * HD;
     if (tid < HALF) {  // the node's rotated query
@@ -406,15 +396,25 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     }
     const bool live = tid < cnt;
     const int j = j0 + tid;
-    v4i kr[HD / 8], vr[HD / 8];
+    v4i kr[HD / 8];
     const bool early = live && j < L;
     if (early) {
         const v4i* ksrc = reinterpret_cast<const v4i*>(kc + plane + (size_t)j * HD);
-        const v4i* vsrc = reinterpret_cast<const v4i*>(vc + plane + (size_t)j * HD);
 #pragma unroll
-        for (int t = 0; t < HD / 8; t++) {
-            kr[t] = ksrc[t];
-            vr[t] = vsrc[t];
+        for (int t = 0; t < HD / 8; t++) kr[t] = ksrc[t];
+    }
+    // value words of this lane's slot: position s + 16k, columns d0 .. d0+3
+    const int s = tid & 15, q = tid >> 4;
+    uint2 vv[NB][16];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const int d0 = 64 * b + 4 * q;
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            const int jj = j0 + s + 16 * k;
+            vv[b][k] = make_uint2(0u, 0u);
+            if (d0 < HD && s + 16 * k < cnt && jj < L)
+                vv[b][k] = *reinterpret_cast<const uint2*>(vc + plane + (size_t)jj * HD + d0);
         }
     }
     if (tid <= depth) anc[tid] = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
@@ -438,11 +438,17 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
         __syncthreads();
         if (live && !early) {
             const v4i* ksrc = reinterpret_cast<const v4i*>(&tk[j - L][0]);
-            const v4i* vsrc = reinterpret_cast<const v4i*>(&tv[j - L][0]);
 #pragma unroll
-            for (int t = 0; t < HD / 8; t++) {
-                kr[t] = ksrc[t];
-                vr[t] = vsrc[t];
+            for (int t = 0; t < HD / 8; t++) kr[t] = ksrc[t];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const int d0 = 64 * b + 4 * q;
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                const int jj = j0 + s + 16 * k;
+                if (d0 < HD && s + 16 * k < cnt && jj >= L)
+                    vv[b][k] = *reinterpret_cast<const uint2*>(&tv[jj - L][d0]);
             }
         }
     }
@@ -451,10 +457,9 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     if (live) {
         float slot[16];
 #pragma unroll
-        for (int s = 0; s < 16; s++) slot[s] = 0.0f;
+        for (int r = 0; r < 16; r++) slot[r] = 0.0f;
 #pragma unroll
         for (int t = 0; t < HD / 8; t++) {
-            *reinterpret_cast<v4i*>(Vs + tid * VS + 8 * t) = vr[t];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const uint32_t wd = (uint32_t)kr[t][e];
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
 #pragma unroll
         for (int w = 1; w < 16; w <<= 1)
 #pragma unroll
-            for (int s = 0; s < 16; s += 2 * w) slot[s] = slot[s] + slot[s + w];
+            for (int r = 0; r < 16; r += 2 * w) slot[r] = slot[r] + slot[r + w];
         sc = slot[0] * scale;
     }
     S[tid] = sc;
@@ -474,7 +479,6 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     // max over the chunk, taken by every 16-lane group for itself (order-free;
     // only +0/-0 ties can differ, and a difference against either gives the
     // same exp input up to its sign)
-    const int s = tid & 15, q = tid >> 4;
     float m = -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < 16; k++)
@@ -502,7 +506,6 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
         o[0] = m;
         o[1] = l;
     }
-    constexpr int NB = (HD + 63) / 64;  // column blocks of 64 (16 groups x 4 columns)
 #pragma unroll
     for (int b = 0; b < NB; b++) {
         const int d0 = 64 * b + 4 * q;
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
         for (int k = 0; k < 16; k++) {
             const int p = s + 16 * k;
             if (p < cnt) {
-                const uint2 w = *reinterpret_cast<const uint2*>(Vs + p * VS + d0);
+                const uint2 w = vv[b][k];
                 acc[0] = acc[0] + e[k] * f16_to_f32((uint16_t)(w.x & 0xffff));
                 acc[1] = acc[1] + e[k] * f16_to_f32((uint16_t)(w.x >> 16));
                 acc[2] = acc[2] + e[k] * f16_to_f32((uint16_t)(w.y & 0xffff));
@@ -650,7 +653,6 @@ int validate_model(const specv_model* m) {
         m->head_dim % 16 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
         m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || m->max_pos < m->kv_capacity ||
         !(m->eps >= 0.0f) ||
-        attn_lds_bytes(m->n_heads / m->n_kv_heads, m->head_dim) > 150 * 1024 ||
         (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024 ||
         (size_t)m->n_heads * m->head_dim > (size_t)kMergeRegs * kRowThreads ||
         merge_lds_bytes(m->n_heads, (m->kv_capacity + kAttnChunk - 1) / kAttnChunk) > 64 * 1024)
@@ -671,26 +673,16 @@ int validate_model(const specv_model* m) {
         if (rc_ != SPECV_OK) return rc_; \
     } while (0)
 
-static int launch_attn_chunk(int hd, dim3 grid, size_t lds, hipStream_t s, const float* qkv, const float* cos_t,
+static int launch_attn_chunk(int hd, dim3 grid, hipStream_t s, const float* qkv, const float* cos_t,
                              const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
                              int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
                              const specv_ctrl* ctrl) {
     switch (hd) {
-#define SPECV_ATTN(HDV)                                                                                   \
-    case HDV: {                                                                                           \
-        static size_t enabled = 64 * 1024; /* dynamic LDS above 64 KB is enabled per kernel */          \
-        if (lds > enabled) {                                                                              \
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_chunk_kernel<HDV>),               \
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) { \
-                (void)hipGetLastError();                                                                  \
-                return SPECV_E_HIP;                                                                       \
-            }                                                                                             \
-            enabled = lds;                                                                                \
-        }                                                                                                 \
-        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), lds, s, qkv, cos_t, sin_t, kc, vc, \
-                           tinfo, layer, cap, nh, nkv, scale, part, nchunk_max, ctrl);                  \
-        return launch_status();                                                                           \
-    }
+#define SPECV_ATTN(HDV)                                                                                    \
+    case HDV:                                                                                              \
+        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), 0, s, qkv, cos_t, sin_t, kc, vc, \
+                           tinfo, layer, cap, nh, nkv, scale, part, nchunk_max, ctrl);                   \
+        return launch_status();
         SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
         SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
 #undef SPECV_ATTN
@@ -753,7 +745,7 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
 
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
                               true));
-        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nh, n), attn_lds_bytes(nh / nkv, hd), s, qkv,
+        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nh, n), s, qkv,
                                     m->rope_cos, m->rope_sin, m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale,
                                     attn, lay.nchunk_max, ctrl));
         hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kRowThreads),
