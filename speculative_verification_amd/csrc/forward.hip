@@ -316,6 +316,19 @@ __global__ __launch_bounds__(kRowThreads) void silu_mul_quant_kernel(const float
 constexpr int kAttnChunk = 256;   // logical positions per chunk
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;     // query heads per KV head
+// Trees of at most this many nodes take the value words of the attention
+// chunks straight into registers; larger ones stage the value rows in LDS
+// (measured on MI355X, 0.5B decoder: registers win at one node, 838 -> 826 us
+// per step, and lose from two, 927 -> 935 us, as the loads get narrower).
+constexpr int kAttnVregMaxNodes = 1;
+
+// Padded fp16 row of the staged values (8 extra halves spread the rows of a
+// 16-lane group over the LDS banks).
+inline __host__ __device__ int attn_vstride(int hd) { return hd + 8; }
+
+inline size_t attn_lds_bytes(int hd, bool vreg) {  // dynamic part: the staged value rows
+    return vreg ? 0 : (size_t)2 * kAttnChunk * attn_vstride(hd);
+}
 
 inline size_t merge_lds_bytes(int nh, int nchunk_max) { return (size_t)4 * nh * (nchunk_max + 1); }
 
@@ -346,12 +359,14 @@ __device__ __forceinline__ void rope_pair(float a, float b, float c, float s, fl
 // For the value sums, lane s of 16-lane group q takes R16 slot s (positions
 // s, s+16, ... in order) of columns 4q .. 4q+3 (and 64 + 4q .. for head dims
 // above 64), and the group's butterfly adds the slots as the index-order
-// tree; each lane loads the value words of its slot straight into registers,
-// so the workgroup needs no LDS for value rows and more workgroups fit on a
-// CU. The query is loaded first and committed rows right after it, so
-// neither waits for the other; only the tree positions wait for the ancestor
-// list.
-template <int HD>
+// tree. With VREG each lane loads the value words of its slot straight into
+// registers (no LDS for value rows, and no LDS round trip: faster for a
+// single node); otherwise thread t also loads the value row of position t
+// and stages it in LDS (16-byte row loads: faster for larger trees). Both
+// compute the same sums. The query is loaded first and committed rows right
+// after it, so neither waits for the other; only the tree positions wait for
+// the ancestor list.
+template <int HD, bool VREG>
 __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
@@ -375,6 +390,9 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t tv[kMaxNodes][HD];  // and value rows
     __shared__ float qs[HD];
     __shared__ float S[kAttnChunk];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][HD + 8] without VREG
+    constexpr int VS = HD + 8;
 
     const size_t plane = (((size_t)layer * nkv + g) * cap) * HD;
     if (tid < HALF) {  // the node's rotated query
@@ -396,25 +414,33 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     }
     const bool live = tid < cnt;
     const int j = j0 + tid;
-    v4i kr[HD / 8];
+    v4i kr[HD / 8], vr[VREG ? 1 : HD / 8];
     const bool early = live && j < L;
     if (early) {
         const v4i* ksrc = reinterpret_cast<const v4i*>(kc + plane + (size_t)j * HD);
 #pragma unroll
         for (int t = 0; t < HD / 8; t++) kr[t] = ksrc[t];
+        if constexpr (!VREG) {
+            const v4i* vsrc = reinterpret_cast<const v4i*>(vc + plane + (size_t)j * HD);
+#pragma unroll
+            for (int t = 0; t < HD / 8; t++) vr[t] = vsrc[t];
+        }
     }
-    // value words of this lane's slot: position s + 16k, columns d0 .. d0+3
+    // with VREG, the value words of this lane's slot: position s + 16k,
+    // columns d0 .. d0+3
     const int s = tid & 15, q = tid >> 4;
-    uint2 vv[NB][16];
+    uint2 vv[VREG ? NB : 1][16];
+    if constexpr (VREG) {
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-        const int d0 = 64 * b + 4 * q;
+        for (int b = 0; b < NB; b++) {
+            const int d0 = 64 * b + 4 * q;
 #pragma unroll
-        for (int k = 0; k < 16; k++) {
-            const int jj = j0 + s + 16 * k;
-            vv[b][k] = make_uint2(0u, 0u);
-            if (d0 < HD && s + 16 * k < cnt && jj < L)
-                vv[b][k] = *reinterpret_cast<const uint2*>(vc + plane + (size_t)jj * HD + d0);
+            for (int k = 0; k < 16; k++) {
+                const int jj = j0 + s + 16 * k;
+                vv[b][k] = make_uint2(0u, 0u);
+                if (d0 < HD && s + 16 * k < cnt && jj < L)
+                    vv[b][k] = *reinterpret_cast<const uint2*>(vc + plane + (size_t)jj * HD + d0);
+            }
         }
     }
     if (tid <= depth) anc[tid] = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
@@ -440,15 +466,22 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
             const v4i* ksrc = reinterpret_cast<const v4i*>(&tk[j - L][0]);
 #pragma unroll
             for (int t = 0; t < HD / 8; t++) kr[t] = ksrc[t];
+            if constexpr (!VREG) {
+                const v4i* vsrc = reinterpret_cast<const v4i*>(&tv[j - L][0]);
+#pragma unroll
+                for (int t = 0; t < HD / 8; t++) vr[t] = vsrc[t];
+            }
         }
+        if constexpr (VREG) {
 #pragma unroll
-        for (int b = 0; b < NB; b++) {
-            const int d0 = 64 * b + 4 * q;
+            for (int b = 0; b < NB; b++) {
+                const int d0 = 64 * b + 4 * q;
 #pragma unroll
-            for (int k = 0; k < 16; k++) {
-                const int jj = j0 + s + 16 * k;
-                if (d0 < HD && s + 16 * k < cnt && jj >= L)
-                    vv[b][k] = *reinterpret_cast<const uint2*>(&tv[jj - L][d0]);
+                for (int k = 0; k < 16; k++) {
+                    const int jj = j0 + s + 16 * k;
+                    if (d0 < HD && s + 16 * k < cnt && jj >= L)
+                        vv[b][k] = *reinterpret_cast<const uint2*>(&tv[jj - L][d0]);
+                }
             }
         }
     }
@@ -460,6 +493,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
         for (int r = 0; r < 16; r++) slot[r] = 0.0f;
 #pragma unroll
         for (int t = 0; t < HD / 8; t++) {
+            if constexpr (!VREG) *reinterpret_cast<v4i*>(Vs + tid * VS + 8 * t) = vr[t];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const uint32_t wd = (uint32_t)kr[t][e];
@@ -515,7 +549,11 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
         for (int k = 0; k < 16; k++) {
             const int p = s + 16 * k;
             if (p < cnt) {
-                const uint2 w = vv[b][k];
+                uint2 w;
+                if constexpr (VREG)
+                    w = vv[b][k];
+                else
+                    w = *reinterpret_cast<const uint2*>(Vs + p * VS + d0);
                 acc[0] = acc[0] + e[k] * f16_to_f32((uint16_t)(w.x & 0xffff));
                 acc[1] = acc[1] + e[k] * f16_to_f32((uint16_t)(w.x >> 16));
                 acc[2] = acc[2] + e[k] * f16_to_f32((uint16_t)(w.y & 0xffff));
@@ -652,7 +690,7 @@ int validate_model(const specv_model* m) {
         m->n_heads % m->n_kv_heads || m->n_heads / m->n_kv_heads > kMaxGroup || m->head_dim < 16 ||
         m->head_dim % 16 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
         m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || m->max_pos < m->kv_capacity ||
-        !(m->eps >= 0.0f) ||
+        !(m->eps >= 0.0f) || attn_lds_bytes(m->head_dim, false) > 150 * 1024 ||
         (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024 ||
         (size_t)m->n_heads * m->head_dim > (size_t)kMergeRegs * kRowThreads ||
         merge_lds_bytes(m->n_heads, (m->kv_capacity + kAttnChunk - 1) / kAttnChunk) > 64 * 1024)
@@ -677,12 +715,25 @@ static int launch_attn_chunk(int hd, dim3 grid, hipStream_t s, const float* qkv,
                              const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
                              int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
                              const specv_ctrl* ctrl) {
+    const bool vreg = (int)grid.z <= kAttnVregMaxNodes;
+    const size_t lds = attn_lds_bytes(hd, vreg);
     switch (hd) {
 #define SPECV_ATTN(HDV)                                                                                    \
-    case HDV:                                                                                              \
-        hipLaunchKernelGGL(attn_chunk_kernel<HDV>, grid, dim3(kFwdThreads), 0, s, qkv, cos_t, sin_t, kc, vc, \
-                           tinfo, layer, cap, nh, nkv, scale, part, nchunk_max, ctrl);                   \
-        return launch_status();
+    case HDV: {                                                                                            \
+        auto kernel = vreg ? &attn_chunk_kernel<HDV, true> : &attn_chunk_kernel<HDV, false>;               \
+        static size_t enabled = 64 * 1024; /* dynamic LDS above 64 KB is enabled per kernel */           \
+        if (lds > enabled) {                                                                               \
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_chunk_kernel<HDV, false>),         \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {  \
+                (void)hipGetLastError();                                                                   \
+                return SPECV_E_HIP;                                                                        \
+            }                                                                                              \
+            enabled = lds;                                                                                 \
+        }                                                                                                  \
+        hipLaunchKernelGGL(kernel, grid, dim3(kFwdThreads), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, \
+                           cap, nh, nkv, scale, part, nchunk_max, ctrl);                                   \
+        return launch_status();                                                                            \
+    }
         SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
         SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
 #undef SPECV_ATTN
