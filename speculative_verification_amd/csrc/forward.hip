@@ -316,18 +316,28 @@ __global__ __launch_bounds__(kRowThreads) void silu_mul_quant_kernel(const float
 constexpr int kAttnChunk = 256;   // logical positions per chunk
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;     // query heads per KV head
-// Trees of at most this many nodes take the value words of the attention
-// chunks straight into registers; larger ones stage the value rows in LDS
-// (measured on MI355X, 0.5B decoder: registers win at one node, 838 -> 826 us
-// per step, and lose from two, 927 -> 935 us, as the loads get narrower).
+// How the attention chunks hold the value rows, by the step's node count
+// (measured on MI355X, 0.5B decoder, per window step):
+// - at most kAttnVregMaxNodes nodes: each summing lane loads its value words
+//   straight into registers (width 1: 838 -> 826 us); from two nodes the
+//   narrower loads cost more (927 -> 935 us at width 2);
+// - otherwise the rows are staged in LDS, padded by 8 halves per row;
+// - from kAttnSwizzleMinNodes nodes, for head dims that are a multiple of 64,
+//   unpadded with the 16-byte chunks of row p XOR-swizzled (chunk t stored
+//   at t ^ ((p >> 1) & 7)). Rows are then 128 or 256 bytes, and the 16 rows
+//   a 16-lane group reads at one column land on 16 distinct 4-bank offsets
+//   of the 64 banks. The 32 KB of rows (against 36 KB) let 4 workgroups
+//   share a CU instead of 3: width 8 1233 -> 1213 us, width 16 1646 ->
+//   1582 us, but width 4 1026 -> 1043 us.
 constexpr int kAttnVregMaxNodes = 1;
+constexpr int kAttnSwizzleMinNodes = 8;
 
-// Padded fp16 row of the staged values (8 extra halves spread the rows of a
-// 16-lane group over the LDS banks).
-inline __host__ __device__ int attn_vstride(int hd) { return hd + 8; }
+inline __host__ __device__ constexpr bool attn_swizzle_ok(int hd) { return hd % 64 == 0; }
+// Row of the staged values, in fp16 elements.
+inline __host__ __device__ constexpr int attn_vstride(int hd, bool swz) { return swz ? hd : hd + 8; }
 
-inline size_t attn_lds_bytes(int hd, bool vreg) {  // dynamic part: the staged value rows
-    return vreg ? 0 : (size_t)2 * kAttnChunk * attn_vstride(hd);
+inline size_t attn_lds_bytes(int hd, bool vreg, bool swz) {  // dynamic part: the staged value rows
+    return vreg ? 0 : (size_t)2 * kAttnChunk * attn_vstride(hd, swz);
 }
 
 inline size_t merge_lds_bytes(int nh, int nchunk_max) { return (size_t)4 * nh * (nchunk_max + 1); }
@@ -360,13 +370,12 @@ __device__ __forceinline__ void rope_pair(float a, float b, float c, float s, fl
 // s, s+16, ... in order) of columns 4q .. 4q+3 (and 64 + 4q .. for head dims
 // above 64), and the group's butterfly adds the slots as the index-order
 // tree. With VREG each lane loads the value words of its slot straight into
-// registers (no LDS for value rows, and no LDS round trip: faster for a
-// single node); otherwise thread t also loads the value row of position t
-// and stages it in LDS (16-byte row loads: faster for larger trees). Both
-// compute the same sums. The query is loaded first and committed rows right
+// registers; otherwise thread t also loads the value row of position t
+// (16-byte loads) and stages it in LDS, padded or, with SWZ, swizzled. All
+// three compute the same sums. The query is loaded first and committed rows right
 // after it, so neither waits for the other; only the tree positions wait for
 // the ancestor list.
-template <int HD, bool VREG>
+template <int HD, bool VREG, bool SWZ>
 __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
@@ -391,8 +400,9 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     __shared__ float qs[HD];
     __shared__ float S[kAttnChunk];
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][HD + 8] without VREG
-    constexpr int VS = HD + 8;
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][VS] without VREG
+    constexpr int VS = attn_vstride(HD, SWZ);
+    static_assert(!SWZ || attn_swizzle_ok(HD), "the swizzle permutes 8 chunks of 16 bytes");
 
     const size_t plane = (((size_t)layer * nkv + g) * cap) * HD;
     if (tid < HALF) {  // the node's rotated query
@@ -493,7 +503,8 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
         for (int r = 0; r < 16; r++) slot[r] = 0.0f;
 #pragma unroll
         for (int t = 0; t < HD / 8; t++) {
-            if constexpr (!VREG) *reinterpret_cast<v4i*>(Vs + tid * VS + 8 * t) = vr[t];
+            if constexpr (!VREG)
+                *reinterpret_cast<v4i*>(Vs + tid * VS + 8 * (SWZ ? t ^ ((tid >> 1) & 7) : t)) = vr[t];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const uint32_t wd = (uint32_t)kr[t][e];
@@ -553,7 +564,8 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
                 if constexpr (VREG)
                     w = vv[b][k];
                 else
-                    w = *reinterpret_cast<const uint2*>(Vs + p * VS + d0);
+                    w = *reinterpret_cast<const uint2*>(
+                        Vs + p * VS + (SWZ ? 8 * ((d0 >> 3) ^ ((p >> 1) & 7)) + (d0 & 7) : d0));
                 acc[0] = acc[0] + e[k] * f16_to_f32((uint16_t)(w.x & 0xffff));
                 acc[1] = acc[1] + e[k] * f16_to_f32((uint16_t)(w.x >> 16));
                 acc[2] = acc[2] + e[k] * f16_to_f32((uint16_t)(w.y & 0xffff));
@@ -690,7 +702,7 @@ int validate_model(const specv_model* m) {
         m->n_heads % m->n_kv_heads || m->n_heads / m->n_kv_heads > kMaxGroup || m->head_dim < 16 ||
         m->head_dim % 16 || m->head_dim > kMaxHeadDim || (m->n_heads * m->head_dim) % 32 || m->inter < 32 ||
         m->inter % 32 || m->vocab < 1 || m->max_pos < 1 || m->kv_capacity < 1 || m->max_pos < m->kv_capacity ||
-        !(m->eps >= 0.0f) || attn_lds_bytes(m->head_dim, false) > 150 * 1024 ||
+        !(m->eps >= 0.0f) || attn_lds_bytes(m->head_dim, false, false) > 150 * 1024 ||
         (size_t)std::max(m->hidden, m->inter) * 4 > 64 * 1024 ||
         (size_t)m->n_heads * m->head_dim > (size_t)kMergeRegs * kRowThreads ||
         merge_lds_bytes(m->n_heads, (m->kv_capacity + kAttnChunk - 1) / kAttnChunk) > 64 * 1024)
@@ -711,29 +723,41 @@ int validate_model(const specv_model* m) {
         if (rc_ != SPECV_OK) return rc_; \
     } while (0)
 
+template <int HD>
+static int launch_attn_hd(bool vreg, bool swz, dim3 grid, size_t lds, hipStream_t s, const float* qkv,
+                          const float* cos_t, const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo,
+                          int layer, int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
+                          const specv_ctrl* ctrl) {
+    auto kernel = vreg  ? &attn_chunk_kernel<HD, true, false>
+                  : swz ? &attn_chunk_kernel<HD, false, attn_swizzle_ok(HD)>
+                        : &attn_chunk_kernel<HD, false, false>;
+    static size_t enabled[2] = {64 * 1024, 64 * 1024};  // dynamic LDS above 64 KB is enabled per kernel
+    size_t& en = enabled[swz ? 1 : 0];
+    if (lds > en) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess) {
+            (void)hipGetLastError();
+            return SPECV_E_HIP;
+        }
+        en = lds;
+    }
+    hipLaunchKernelGGL(kernel, grid, dim3(kFwdThreads), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh,
+                       nkv, scale, part, nchunk_max, ctrl);
+    return launch_status();
+}
+
 static int launch_attn_chunk(int hd, dim3 grid, hipStream_t s, const float* qkv, const float* cos_t,
                              const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
                              int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
                              const specv_ctrl* ctrl) {
     const bool vreg = (int)grid.z <= kAttnVregMaxNodes;
-    const size_t lds = attn_lds_bytes(hd, vreg);
+    const bool swz = !vreg && (int)grid.z >= kAttnSwizzleMinNodes && attn_swizzle_ok(hd);
+    const size_t lds = attn_lds_bytes(hd, vreg, swz);
     switch (hd) {
-#define SPECV_ATTN(HDV)                                                                                    \
-    case HDV: {                                                                                            \
-        auto kernel = vreg ? &attn_chunk_kernel<HDV, true> : &attn_chunk_kernel<HDV, false>;               \
-        static size_t enabled = 64 * 1024; /* dynamic LDS above 64 KB is enabled per kernel */           \
-        if (lds > enabled) {                                                                               \
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_chunk_kernel<HDV, false>),         \
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {  \
-                (void)hipGetLastError();                                                                   \
-                return SPECV_E_HIP;                                                                        \
-            }                                                                                              \
-            enabled = lds;                                                                                 \
-        }                                                                                                  \
-        hipLaunchKernelGGL(kernel, grid, dim3(kFwdThreads), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, \
-                           cap, nh, nkv, scale, part, nchunk_max, ctrl);                                   \
-        return launch_status();                                                                            \
-    }
+#define SPECV_ATTN(HDV) \
+    case HDV:           \
+        return launch_attn_hd<HDV>(vreg, swz, grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv, \
+                                   scale, part, nchunk_max, ctrl);
         SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
         SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
 #undef SPECV_ATTN
