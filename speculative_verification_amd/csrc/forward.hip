@@ -365,7 +365,10 @@ __device__ __forceinline__ void rope_pair(float a, float b, float c, float s, fl
 // One workgroup per (chunk, query head, node): the query heads that share a
 // KV head read the same rows, which the L2 serves after the first; one head
 // per workgroup keeps each workgroup's dependent chains short and gives the
-// chip more of them. Thread t owns position t of the chunk and its key row.
+// chip more of them. The grid is (query head, node, chunk), so workgroups
+// are dispatched chunk by chunk: those of the chunks past a node's sequence,
+// which only read the control block and exit, come last instead of taking
+// slots between the working ones. Thread t owns position t of the chunk and its key row.
 // For the value sums, lane s of 16-lane group q takes R16 slot s (positions
 // s, s+16, ... in order) of columns 4q .. 4q+3 (and 64 + 4q .. for head dims
 // above 64), and the group's butterfly adds the slots as the index-order
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     int nh, int nkv, float scale, float* __restrict__ part, int nchunk_max, const specv_ctrl* ctrl) {
     constexpr int HALF = HD / 2;
     constexpr int NB = (HD + 63) / 64;  // column blocks of 64 (16 groups x 4 columns)
-    const int c = blockIdx.x, hq = blockIdx.y, i = blockIdx.z, tid = threadIdx.x;
+    const int hq = blockIdx.x, i = blockIdx.y, c = blockIdx.z, tid = threadIdx.x;
     const int depth_raw = tinfo[i];  // issued with the control loads (i < 16)
     if (ctrl->done || i >= ctrl->n_nodes) return;
     const int L = ctrl->committed_len;
@@ -750,8 +753,8 @@ static int launch_attn_chunk(int hd, dim3 grid, hipStream_t s, const float* qkv,
                              const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
                              int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
                              const specv_ctrl* ctrl) {
-    const bool vreg = (int)grid.z <= kAttnVregMaxNodes;
-    const bool swz = !vreg && (int)grid.z >= kAttnSwizzleMinNodes && attn_swizzle_ok(hd);
+    const bool vreg = (int)grid.y <= kAttnVregMaxNodes;
+    const bool swz = !vreg && (int)grid.y >= kAttnSwizzleMinNodes && attn_swizzle_ok(hd);
     const size_t lds = attn_lds_bytes(hd, vreg, swz);
     switch (hd) {
 #define SPECV_ATTN(HDV) \
@@ -820,7 +823,7 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
 
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
                               true));
-        SPECV_TRY(launch_attn_chunk(hd, dim3(lay.nchunk_max, nh, n), s, qkv,
+        SPECV_TRY(launch_attn_chunk(hd, dim3(nh, n, lay.nchunk_max), s, qkv,
                                     m->rope_cos, m->rope_sin, m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale,
                                     attn, lay.nchunk_max, ctrl));
         hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kRowThreads),
