@@ -17,6 +17,11 @@ buffers plus one lm_head, 4.22 GB in total, so every step streams each byte
 from HBM once (far above the 256 MB last-level cache). The step is captured
 once as a HIP graph and replayed.
 
+The line also times the same step on the Qwen2.5-0.5B linear set
+(`small_set`: 24 layers of qkv 1152x896, o 896x896, gate_up 9728x896,
+down 896x4864, then lm_head 151936x896; four copies of its 278 MB of weights
+in rotation, so that each step reads its copy cold) at T = 1, 2, 4, 8.
+
 Prints one JSON line (rank 0). `value` is the algorithmic bytes of the step
 (weights, activation codes and scales, linear outputs, quantisation traffic,
 argmax pairs, compaction moves) divided by the step time, in
@@ -283,6 +288,8 @@ def run_T(model, T, steps, warmup, torch):
     model.reset_ctrl(T)
     for i in range(warmup):
         graphs[i % copies].replay()
+    # the eager outputs are those of copy 0 (copies differ in layer order)
+    graphs[0].replay()
     torch.cuda.synchronize()
     replay_ok = snapshot().view(torch.int32).equal(eager_out.view(torch.int32))
     model.reset_ctrl(T)
@@ -305,6 +312,8 @@ def run_T(model, T, steps, warmup, torch):
         e1.record()
         torch.cuda.synchronize()
         runs.append(e0.elapsed_time(e1) / steps)
+    graphs[0].replay()
+    torch.cuda.synchronize()
     replay_ok = replay_ok and snapshot().view(torch.int32).equal(eager_out.view(torch.int32))
     del graphs
     return ms, m_acc, replay_ok, float(np.median(runs))
@@ -560,6 +569,36 @@ def cm_window_bench(torch, sv, dm, ref, widths, L0, ctx, root, vocab, W, max_win
             "by_width": out, "controller": ctl_out}
 
 
+def linear_set(name, Ts, steps, warmup, reps, torch, sv, sg):
+    """The same verify step on another shape set (the 0.5B linear set): the
+    T sweep and the linear kernel's live per-launch roofline at the largest T,
+    in a compact form for the JSON line."""
+    model = Model(name, torch, sv, sg, max(Ts))
+    per_T = {}
+    for T in Ts:
+        ms, m_acc, ok, med5 = run_T(model, T, steps, warmup, torch)
+        nb = model.step_bytes(T, m_acc)
+        per_T[str(T)] = {"us": round(ms * 1e3, 2), "us_median5": round(med5 * 1e3, 2),
+                         "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                         "pct_hbm_peak": round(100 * nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                         "graph_replay_exact": ok}
+        print(f"[bench] {name} T={T}: {per_T[str(T)]}", file=sys.stderr, flush=True)
+    Tr = max(Ts)
+    ach, avg_s, _, nlaunch, by_shape = roofline_linear(model, Tr, reps, torch)
+    m = MODELS[name]
+    out = {"workload": (f"{name}-shaped verify step: {m['layers']} x (qkv, o, gate_up, down) + lm_head W4A8 g32 "
+                        f"with fused argmax, tree accept + KV compaction, HIP-graph replay; "
+                        f"{len(model.copies)} copies of the weights in rotation (cold)"),
+           "weight_bytes": model.weight_bytes_total(), "per_T": per_T,
+           "t8_over_t1": round(per_T["8"]["us"] / per_T["1"]["us"], 4) if "8" in per_T and "1" in per_T else None,
+           "linear_roofline": {"T": Tr, "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4),
+                               "avg_launch_us": round(avg_s * 1e6, 3), "launches_per_step": nlaunch,
+                               "by_shape": by_shape}}
+    del model
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -574,6 +613,8 @@ def main():
                     help="tree widths of the speculation-window measurement (empty: skip)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
                     help="skip the plain streaming-read ceilings")
+    ap.add_argument("--small-set", default="qwen2.5-0.5b",
+                    help="second shape set whose verify step is timed at T = 1, 2, 4, 8 (empty: skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -611,6 +652,10 @@ def main():
               f"replay exact={ok}", file=sys.stderr, flush=True)
 
     ach, avg_s, avg_b, nlaunch, by_shape = roofline_linear(model, args.T, args.roofline_reps, torch)
+    small = None
+    if args.small_set and args.small_set != args.workload:
+        small = linear_set(args.small_set, [1, 2, 4, 8], max(5, args.steps // 2), args.warmup,
+                           args.roofline_reps, torch, sv, sg)
     ceil = ceilings(model, args.T, torch, sv) if args.ceilings else None
     if ceil:
         ceil["step_pct_of_read_all"] = round(100 * per_T[args.T]["GB/s"] / ceil["read_all_weights_GBs"], 1)
@@ -657,6 +702,7 @@ def main():
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
                      "by_shape": by_shape},
         "ceilings": ceil,
+        "small_set": small,
         "window": window,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(model, args.T),
     }
