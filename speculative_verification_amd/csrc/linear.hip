@@ -769,24 +769,33 @@ static int launch_one(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, c
     return launch_status();
 }
 
-// Tiles of fewer iterations than the default stage count (K <= 1536) run
-// with one stage per iteration, so no tile is padded with empty iterations
-// (the 896-input matrices of the 0.5B shape have 2: measured on MI355X, qkv
-// 2.77 -> 2.36 us, gate_up 3.59 -> 3.22 us and the lm_head at T = 8 31.1 ->
-// 23.4 us per launch). Longer tiles keep the default: two stages for the
-// 10-iteration 4864-input matrix were slower (4.22 -> 5.00 us).
-inline int short_stages(int K) {
+// A stage count that divides a tile's J iterations where the default would
+// pad the tile with empty iterations (0: the default applies). Tiles shorter
+// than the default pipeline (K <= 1536) take one stage per iteration, and
+// those whose J is a multiple of 5 but not of 4 take 5. Measured on MI355X,
+// per launch: the 896-input matrices of the 0.5B shape (J = 2) qkv 2.77 ->
+// 2.36 us, gate_up 3.59 -> 3.22 us, lm_head at T = 8 31.1 -> 23.4 us; the
+// 4864-input down projection (J = 10) 4.25 -> 3.61 us at T = 1 and 4.58 ->
+// 4.40 us at T = 8 (two stages there: 5.00 us).
+inline int exact_stages(int T, int K) {
     const int J = (K / 32 + 15) / 16;
-    return J < SPECV_STREAM_STAGES ? J : 0;
+    int P = 0;
+    if (J < SPECV_STREAM_STAGES)
+        P = J;
+    else if (J % SPECV_STREAM_STAGES != 0 && J % 5 == 0)
+        P = 5;
+    if (P && stream_lds_bytes(T, K, false, false, P) + (size_t)T * 512 > kLdsBudget) P = 0;
+    return P;
 }
 
 template <int T, bool AMAX, int PROD = kProdNone>
-static int launch_short(int P, const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
+static int launch_exact(int P, const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
                         Best* amax, int Tr, int N, int K, hipStream_t s, const ProdArgs& pa = ProdArgs{}) {
     switch (P) {
         case 1: return launch_one<T, AMAX, false, false, PROD, 1>(wq, ws, xq, xs, y, amax, Tr, N, K, s, pa);
         case 2: return launch_one<T, AMAX, false, false, PROD, 2>(wq, ws, xq, xs, y, amax, Tr, N, K, s, pa);
         case 3: return launch_one<T, AMAX, false, false, PROD, 3>(wq, ws, xq, xs, y, amax, Tr, N, K, s, pa);
+        case 5: return launch_one<T, AMAX, false, false, PROD, 5>(wq, ws, xq, xs, y, amax, Tr, N, K, s, pa);
         default: return SPECV_E_SHAPE;
     }
 }
@@ -796,14 +805,14 @@ static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, con
                     int Tr, int N, int K, hipStream_t s) {
     const bool keep = stream_keeps(T, K, BS);
     if constexpr (T <= 16 && !BS) {
-        if (const int P = short_stages(K))
-            return amax ? launch_short<T, true>(P, wq, ws, xq, xs, y, amax, Tr, N, K, s)
-                        : launch_short<T, false>(P, wq, ws, xq, xs, y, nullptr, Tr, N, K, s);
         if (deep_stream(T, N, K))
             return amax ? launch_one<T, true, false, false, kProdNone, kDeepStages>(wq, ws, xq, xs, y, amax, Tr, N,
                                                                                     K, s)
                         : launch_one<T, false, false, false, kProdNone, kDeepStages>(wq, ws, xq, xs, y, nullptr, Tr,
                                                                                      N, K, s);
+        if (const int P = exact_stages(T, K))
+            return amax ? launch_exact<T, true>(P, wq, ws, xq, xs, y, amax, Tr, N, K, s)
+                        : launch_exact<T, false>(P, wq, ws, xq, xs, y, nullptr, Tr, N, K, s);
     }
     if constexpr (T <= 16 && !BS) {
         if (amax)
@@ -827,12 +836,13 @@ bool linear_fused_supported(int prod, int T, int K) {
 template <int T>
 static int launch_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const uint16_t* ws, float* y, Best* amax,
                         int N, int K, hipStream_t s) {
-    if (const int P = short_stages(K)) {
+    if (const int P = exact_stages(T, K); P && stream_lds_bytes(T, K, false, false, P) +
+                                                          prod_scratch_bytes(prod, K) + (size_t)T * 512 <= kLdsBudget) {
         if (prod == kProdNorm)
-            return amax ? launch_short<T, true, kProdNorm>(P, wq, ws, nullptr, nullptr, y, amax, T, N, K, s, pa)
-                        : launch_short<T, false, kProdNorm>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
+            return amax ? launch_exact<T, true, kProdNorm>(P, wq, ws, nullptr, nullptr, y, amax, T, N, K, s, pa)
+                        : launch_exact<T, false, kProdNorm>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
         if (amax) return SPECV_E_SHAPE;
-        return launch_short<T, false, kProdSilu>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
+        return launch_exact<T, false, kProdSilu>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
     }
     if (prod == kProdNorm)
         return amax ? launch_one<T, true, false, false, kProdNorm>(wq, ws, nullptr, nullptr, y, amax, T, N, K, s, pa)
