@@ -46,8 +46,8 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
 # WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
 # valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "36793d16117fe33614a633dd2c2e5101d889052b0108ab3341611cfb905b4ee9",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33629750}
+LINEAR_TRAFFIC = {"source_sha256": "7ab669ecf46638aaec8a4d6c51e80d972f4d2cd91c1e7208282eb20d67fca77a",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33624842}
 
 
 def linear_traffic(T, workload):
