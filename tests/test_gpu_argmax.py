@@ -51,7 +51,7 @@ def plant_ties(wq, ws, y):
 
 @pytest.mark.parametrize("T,N,K", [(1, 16, 32), (3, 17, 64), (8, 100, 896), (16, 300, 64), (5, 2048, 896),
                                    (8, 1000, 4096), (2, 16385, 128), (8, 151936, 896), (16, 151936, 896),
-                                   (1, 1, 32)])
+                                   (1, 1, 32), (4, 3000, 1280), (8, 2000, 2560), (3, 1500, 4864)])
 def test_linear_argmax_parity(sv, T, N, K):
     case(f"linear argmax T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(70 + T, T, N, K)

@@ -127,6 +127,9 @@ def test_quantize_misaligned_rows(sv):
 @pytest.mark.parametrize("T,N,K", [(1, 16, 32), (3, 17, 64), (5, 33, 96), (7, 40, 544), (8, 100, 896),
                                    (16, 50, 4864), (4, 1, 4096), (2, 15, 14336), (9, 31, 512),
                                    (12, 64, 1024), (6, 48, 160), (16, 130, 14336),
+                                   # 3 and 5 pipeline stages (3 and 5 iterations per tile), and 7
+                                   # iterations (padded to two blocks of 4)
+                                   (4, 70, 1280), (16, 33, 1536), (3, 40, 2560), (5, 45, 3200),
                                    # K split in 2 (>= 256 row groups) and unsplit (>= 1024)
                                    (3, 16400, 96), (8, 16385, 544), (5, 65601, 64), (16, 65600, 160),
                                    # several 16-row tiles per workgroup, ragged rows and groups
