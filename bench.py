@@ -352,7 +352,9 @@ def ceilings(model, T, torch, sv):
     the same device, as ceilings for the step: one read of all the step's
     weight bytes; an empty launch per graph node; and a dependent chain of
     129 reads, one per linear launch of the step, of the same byte counts
-    from distinct regions (cold), in graph replays."""
+    from distinct regions (cold), in graph replays; and per linear shape, a
+    chain of that shape's reads alone (its 32 layer regions, or the lm_head
+    region), in us per launch beside the shape's weight bytes."""
     m = model.m
     sizes = []
     for _ in range(m["layers"]):
@@ -394,12 +396,20 @@ def ceilings(model, T, torch, sv):
     empty = graph_us(lambda st: [read(base, 0, 512, st) for _ in range(200)], 200)
     whole = min(graph_us(lambda st: read(base, tot, g, st), 1) for g in (512, 1024, 2048))
     chain = graph_us(lambda st: [read(base + o, b, 512, st) for o, b in zip(offs, sizes)], 1)
+    names = [nm for nm, _, _ in layer_linears(m)]
+    per_shape = {}
+    for si, nm in enumerate(names + ["lm_head"]):
+        idx = list(range(si, len(sizes) - 1, len(names))) if nm != "lm_head" else [len(sizes) - 1]
+        us = graph_us(lambda st: [read(base + offs[i], sizes[i], 512, st) for i in idx], len(idx))
+        per_shape[nm] = {"us": round(us, 2), "weight_bytes": sizes[idx[0]],
+                         "GB/s": round(sizes[idx[0]] / us / 1e3, 1)}
     del buf
     return {"read_all_weights_GBs": round(tot / whole / 1e3, 1), "empty_launch_us": round(empty, 3),
             "read_chain_us": round(chain, 2), "read_chain_GBs": round(sum(sizes) / chain / 1e3, 1),
+            "read_per_shape": per_shape,
             "note": "plain streaming reads with no arithmetic (specv_stream_read), graph replays, cold: one read "
                     "of the step's weight bytes; an empty launch; a dependent chain of 129 reads with the byte "
-                    "counts of the step's linear launches"}
+                    "counts of the step's linear launches; per shape, a chain of that shape's reads (us per launch)"}
 
 
 def cpu_baseline(model, T, seconds=(6.0, 6.0)):
