@@ -629,7 +629,7 @@ def main():
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the verification step of one request runs on one device).", file=sys.stderr)
         sys.exit(2)
 
