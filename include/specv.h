@@ -403,7 +403,11 @@ size_t spec_window_workspace(const specv_model* m, int32_t width);
  * One step's launches are captured once into a HIP graph (on a stream the
  * library creates) and replayed W times on `stream`; the executable graph is
  * kept for the process, keyed by every argument except W and
- * host_readback (at most 32 kept; the oldest key is released first).
+ * host_readback. At most 32 are kept: the least recently used one is then
+ * retired, and destroyed only after its last enqueued window has finished
+ * (an event recorded after that window's replays), so windows still queued
+ * on any stream are never cut short. Calls from several threads are
+ * serialised from the graph lookup to the last replay's enqueue.
  * Windows that share a workspace, control block or cache must not overlap.
  */
 int spec_window_run(const specv_model* m, specv_ctrl* ctrl, specv_step_stats* stats,

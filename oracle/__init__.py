@@ -31,11 +31,14 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library: liboracle.so, or the build named by SPECV_ORACLE_SO
+    (e.g. one compiled with sanitizers)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(SO):
+        path = os.environ.get("SPECV_ORACLE_SO") or SO
+        if path == SO and not os.path.exists(SO):
             build()
-        _lib = ctypes.CDLL(SO)
+        _lib = ctypes.CDLL(path)
         _declare(_lib)
     return _lib
 

@@ -100,12 +100,16 @@ static void rope(float* x, int hd, const float* cos_t, const float* sin_t, int p
 
 /* ---------------------------------------------------------------- blocks */
 
-/* quantize rows then W4A8 linear: y [T][N] */
+/* quantize rows then W4A8 linear: y [T][N]. A non-finite activation is
+ * outside the quantiser's domain; the outputs are then NaN, so no comparison
+ * can pass on them. */
 static void qlinear(const float* x, int T, int K, const uint8_t* w, const uint16_t* s, int N, float* y) {
     int8_t* xq = (int8_t*)malloc((size_t)T * K);
     float* xs = (float*)malloc(sizeof(float) * (size_t)T);
-    orc_quantize_act(x, T, K, xq, xs);
-    orc_w4a8_linear(w, s, xq, xs, y, T, N, K);
+    if (orc_quantize_act(x, T, K, xq, xs) != 0)
+        for (int64_t i = 0; i < (int64_t)T * N; i++) y[i] = NAN;
+    else
+        orc_w4a8_linear(w, s, xq, xs, y, T, N, K);
     free(xq);
     free(xs);
 }

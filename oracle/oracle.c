@@ -98,9 +98,20 @@ float orc_r16(const float* v, int64_t n) {
  * (not per block of 32); symmetric codes in [-127, 127]; scale = absmax/127
  * and codes round(x * (127/absmax)) to nearest-even, both as single IEEE
  * divisions; an all-zero token has scale 0 and codes 0.
+ *
+ * Tiny rows. For absmax below about 3.7e-37 the reciprocal 127/absmax
+ * overflows to infinity, and every nonzero code would saturate. Reading:
+ * when absmax < 2^-64 the row and absmax are first multiplied by 2^64, which
+ * is exact, and the codes are round(fl(x * 2^64) * fl(127 / fl(absmax * 2^64))).
+ * Wherever 127/absmax is finite this gives exactly the bits of the plain
+ * formula: the factor 2^64 commutes with each correctly rounded operation,
+ * whose results all stay normal. The scale is absmax/127 either way.
+ * Input values must be finite; a NaN or infinity is rejected (-1).
  */
 int orc_quantize_act(const float* x, int T, int K, int8_t* xq, float* xs) {
     if (T < 0 || K < 0 || (T > 0 && K > 0 && (!x || !xq || !xs))) return -1;
+    for (int64_t i = 0; i < (int64_t)T * K; i++)
+        if (!isfinite(x[i])) return -1;
     for (int t = 0; t < T; t++) {
         const float* row = x + (int64_t)t * K;
         float a = 0.0f;
@@ -114,9 +125,10 @@ int orc_quantize_act(const float* x, int T, int K, int8_t* xq, float* xs) {
             continue;
         }
         xs[t] = a / 127.0f;
-        float inv = 127.0f / a;
+        const float pre = a < 0x1p-64f ? 0x1p64f : 1.0f;
+        float inv = 127.0f / (a * pre);
         for (int k = 0; k < K; k++) {
-            float r = nearbyintf(row[k] * inv); /* default mode: nearest-even */
+            float r = nearbyintf((row[k] * pre) * inv); /* default mode: nearest-even */
             if (r > 127.0f) r = 127.0f;
             if (r < -127.0f) r = -127.0f;
             xq[(int64_t)t * K + k] = (int8_t)r;

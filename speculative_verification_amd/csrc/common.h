@@ -113,6 +113,24 @@ __device__ __forceinline__ float det_exp(float x) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + det_exp(-g)); }
 
+// Per-token (or per-block) int8 quantisation with absmax a: scale a / 127,
+// codes rint(x * 127 / a) clamped to +-127, nearest-even. Below 2^-64, x and
+// a are first multiplied by 2^64 (exact), so 127 / a cannot overflow for a
+// tiny but nonzero absmax; wherever 127 / a is finite the scaled form gives
+// the bits of the plain one, since a power-of-two factor commutes with each
+// rounding while the results stay normal. a == 0 gives inv = 0 (codes 0).
+struct QuantScale {
+    float pre, inv;
+};
+__device__ __forceinline__ QuantScale quant_scale(float a) {
+    const float pre = a < 0x1p-64f ? 0x1p64f : 1.0f;
+    return QuantScale{pre, a == 0.0f ? 0.0f : 127.0f / (a * pre)};
+}
+__device__ __forceinline__ float quant_code(float x, QuantScale s) {
+    const float r = __builtin_rintf((x * s.pre) * s.inv);  // v_rndne_f32: nearest-even
+    return fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? SPECV_OK : SPECV_E_HIP;
 }

@@ -106,7 +106,7 @@ __device__ void quantize_regs(const float (&y)[R][V], int K, int8_t* __restrict_
 #pragma unroll
             for (int e = 0; e < V; e++) a = fmaxf(a, fabsf(y[r][e]));
     a = block_max(a, red);
-    const float inv = a == 0.0f ? 0.0f : 127.0f / a;
+    const QuantScale qs = quant_scale(a);
     if (tid == 0) *xs_i = a == 0.0f ? 0.0f : a / 127.0f;
 #pragma unroll
     for (int r = 0; r < R; r++) {
@@ -114,11 +114,7 @@ __device__ void quantize_regs(const float (&y)[R][V], int K, int8_t* __restrict_
         if (c0 >= K) continue;
         uint32_t packed = 0;
 #pragma unroll
-        for (int e = 0; e < V; e++) {
-            float q = __builtin_rintf(y[r][e] * inv);  // v_rndne_f32: nearest-even
-            q = fminf(fmaxf(q, -127.0f), 127.0f);
-            packed |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
-        }
+        for (int e = 0; e < V; e++) packed |= (uint32_t)(uint8_t)(int8_t)(int)quant_code(y[r][e], qs) << (8 * e);
         if (V == 4)
             *reinterpret_cast<uint32_t*>(xrow + c0) = packed;
         else

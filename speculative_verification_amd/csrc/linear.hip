@@ -202,16 +202,14 @@ __device__ __forceinline__ float max4(const float4 v) {
 // 8-byte slot and chunk 2m + 1 bytes 2, 6, 3, 7: the even lane of a pair
 // (c even, its neighbour lane holding c + 1) writes all 8 bytes. Both lanes
 // of a pair must call this together, with chunks in range or not together.
-__device__ __forceinline__ uint32_t code_of(float v, float inv) {
-    float q = __builtin_rintf(v * inv);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (uint32_t)(uint8_t)(int8_t)(int)q;
+__device__ __forceinline__ uint32_t code_of(float v, QuantScale qs) {
+    return (uint32_t)(uint8_t)(int8_t)(int)quant_code(v, qs);
 }
 
-__device__ __forceinline__ void put_codes(int8_t* rowb, int c, const float4 y, float inv) {
+__device__ __forceinline__ void put_codes(int8_t* rowb, int c, const float4 y, QuantScale qs) {
     // this lane's evens (inputs 0, 2 of the chunk) and odds (1, 3), as byte pairs
-    const uint32_t ev = code_of(y.x, inv) | code_of(y.z, inv) << 8;
-    const uint32_t od = code_of(y.y, inv) | code_of(y.w, inv) << 8;
+    const uint32_t ev = code_of(y.x, qs) | code_of(y.z, qs) << 8;
+    const uint32_t od = code_of(y.y, qs) | code_of(y.w, qs) << 8;
     const uint32_t ev2 = (uint32_t)swap_pair((int)ev);
     const uint32_t od2 = (uint32_t)swap_pair((int)od);
     if ((c & 1) == 0) {
@@ -324,11 +322,11 @@ __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP
                     amax = fmaxf(amax, max4(v));
                 }
             amax = wave_max(amax);
-            const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+            const QuantScale qs = quant_scale(amax);
             if (lane == 0) s_xs[t] = amax == 0.0f ? 0.0f : amax / 127.0f;
 #pragma unroll
             for (int i = 0; i < kProdRegs; i++)
-                if (lane + 64 * i < K4) put_codes(rowb, lane + 64 * i, x[u][i], inv);
+                if (lane + 64 * i < K4) put_codes(rowb, lane + 64 * i, x[u][i], qs);
         }
         return;
     }
@@ -363,9 +361,9 @@ __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP
         float amax = 0.0f;
         for (int c = lane; c < K4; c += 64) amax = fmaxf(amax, max4(value4(c)));
         amax = wave_max(amax);
-        const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+        const QuantScale qs = quant_scale(amax);
         if (lane == 0) s_xs[t] = amax == 0.0f ? 0.0f : amax / 127.0f;
-        for (int c = lane; c < K4; c += 64) put_codes(rowb, c, value4(c), inv);
+        for (int c = lane; c < K4; c += 64) put_codes(rowb, c, value4(c), qs);
     }
 }
 
@@ -412,12 +410,12 @@ __device__ void produce_silu(const ProdArgs& pa, int Tr, int live, int K, int JP
     for (int t = 0; t < TS; t++) {
         if (t >= Tr || t >= live) continue;
         const float m = fmaxf(fmaxf(part[4 * t], part[4 * t + 1]), fmaxf(part[4 * t + 2], part[4 * t + 3]));
-        const float inv = m == 0.0f ? 0.0f : 127.0f / m;
+        const QuantScale qs = quant_scale(m);
         if (tid == 0) s_xs[t] = m == 0.0f ? 0.0f : m / 127.0f;
         int8_t* rowb = act + (size_t)t * JP * 512;
 #pragma unroll
         for (int i = 0; i < kSiluRegs; i++)
-            if (tid + 256 * i < K4) put_codes(rowb, tid + 256 * i, gv[t][i], inv);
+            if (tid + 256 * i < K4) put_codes(rowb, tid + 256 * i, gv[t][i], qs);
     }
 }
 

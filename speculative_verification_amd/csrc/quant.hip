@@ -29,13 +29,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_kernel(
         for (int k = threadIdx.x; k < K; k += kQuantThreads) out[k] = 0;
         return;
     }
-    const float inv = 127.0f / a;
+    const QuantScale qs = quant_scale(a);
     if (threadIdx.x == 0) xs[t] = a / 127.0f;
-    for (int k = threadIdx.x; k < K; k += kQuantThreads) {
-        float r = __builtin_rintf(row[k] * inv);  // v_rndne_f32: nearest-even
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        out[k] = (int8_t)(int)r;
-    }
+    for (int k = threadIdx.x; k < K; k += kQuantThreads) out[k] = (int8_t)(int)quant_code(row[k], qs);
 }
 
 // Register-resident variant for rows of up to 4*CH*256 values with K % 4 == 0
@@ -68,7 +64,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_reg_kernel(
     for (int w = 1; w < kQuantThreads / 64; w++) a = fmaxf(a, wave_max[w]);
 
     const bool zero = (a == 0.0f);
-    const float inv = zero ? 0.0f : 127.0f / a;
+    const QuantScale qs = quant_scale(a);
     if (threadIdx.x == 0) xs[t] = zero ? 0.0f : a / 127.0f;
     uint32_t* out = reinterpret_cast<uint32_t*>(xq + (int64_t)t * K);
 #pragma unroll
@@ -77,11 +73,8 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_reg_kernel(
         if (i < K4) {
             uint32_t packed = 0;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float r = __builtin_rintf(lane_f32(raw[c][e]) * inv);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                packed |= ((uint32_t)(int)r & 0xffu) << (8 * e);
-            }
+            for (int e = 0; e < 4; e++)
+                packed |= ((uint32_t)(int)quant_code(lane_f32(raw[c][e]), qs) & 0xffu) << (8 * e);
             out[i] = packed;
         }
     }
@@ -105,17 +98,13 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_blocks_kernel(
     a = fmaxf(a, __shfl_xor(a, 2, 64));
     a = fmaxf(a, __shfl_xor(a, 4, 64));
     const bool zero = (a == 0.0f);
-    const float inv = zero ? 0.0f : 127.0f / a;
+    const QuantScale qs = quant_scale(a);
     if (!ok) return;
     if (part == 0) xs[blk] = zero ? 0.0f : a / 127.0f;
     const float e[4] = {v.x, v.y, v.z, v.w};
     uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        float r = __builtin_rintf(e[i] * inv);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        packed |= ((uint32_t)(int)r & 0xffu) << (8 * i);
-    }
+    for (int i = 0; i < 4; i++) packed |= ((uint32_t)(int)quant_code(e[i], qs) & 0xffu) << (8 * i);
     *reinterpret_cast<uint32_t*>(xq + 32 * blk + 4 * part) = packed;
 }
 

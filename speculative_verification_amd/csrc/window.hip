@@ -11,6 +11,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <vector>
 
 #include "common.h"
 #include "internal.h"
@@ -90,15 +91,55 @@ struct WindowKey {
     bool operator<(const WindowKey& o) const { return std::memcmp(this, &o, sizeof(WindowKey)) < 0; }
 };
 
+// Cached step graphs. An entry keeps its last use (a counter) and an event
+// recorded on the caller's stream after the window's last replay. The cache
+// holds at most kGraphCacheMax entries; when full, the least recently used
+// one is retired: it leaves the map, and its graph is destroyed only once
+// its event reports that every replay enqueued so far has finished (checked
+// on every later call, without blocking). The lock is held from the lookup
+// to the event record, so no thread can retire a graph between another
+// thread's lookup and its launches.
+constexpr size_t kGraphCacheMax = 32;
+
+struct GraphEntry {
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;  // recorded after the entry's latest window
+    uint64_t last_use = 0;
+};
+
 struct GraphCache {
     std::mutex mu;
-    std::map<WindowKey, hipGraphExec_t> execs;
+    std::map<WindowKey, GraphEntry> entries;
+    std::vector<GraphEntry> retired;  // evicted, waiting for their last window
+    uint64_t clock = 0;
     hipStream_t capture_stream = nullptr;
 };
 
 static GraphCache& graph_cache() {
     static GraphCache* c = new GraphCache();  // lives for the process
     return *c;
+}
+
+static void destroy_entry(GraphEntry& e) {
+    if (e.exec) (void)hipGraphExecDestroy(e.exec);
+    if (e.done) (void)hipEventDestroy(e.done);
+    e.exec = nullptr;
+    e.done = nullptr;
+}
+
+// Destroys the retired graphs whose windows have all finished. Called with
+// the cache lock held.
+static void reap_retired(GraphCache& gc) {
+    for (size_t i = 0; i < gc.retired.size();) {
+        if (hipEventQuery(gc.retired[i].done) == hipSuccess) {
+            destroy_entry(gc.retired[i]);
+            gc.retired[i] = gc.retired.back();
+            gc.retired.pop_back();
+        } else {
+            (void)hipGetLastError();  // hipErrorNotReady is not an error here
+            i++;
+        }
+    }
 }
 
 static int enqueue_window_step(const WindowKey& k, const StepLayout& lay, hipStream_t s) {
@@ -125,13 +166,12 @@ static int enqueue_window_step(const WindowKey& k, const StepLayout& lay, hipStr
                         k.ring_cap, ws, lay, s);
 }
 
-// Capture one window step into an executable graph (cached by arguments).
-static int window_graph(const WindowKey& k, const StepLayout& lay, hipGraphExec_t* out) {
-    GraphCache& gc = graph_cache();
-    std::lock_guard<std::mutex> lock(gc.mu);
-    auto it = gc.execs.find(k);
-    if (it != gc.execs.end()) {
-        *out = it->second;
+// The cache entry of a window step, captured into an executable graph on
+// first use. Called with the cache lock held.
+static int window_graph(GraphCache& gc, const WindowKey& k, const StepLayout& lay, GraphEntry** out) {
+    auto it = gc.entries.find(k);
+    if (it != gc.entries.end()) {
+        *out = &it->second;
         return SPECV_OK;
     }
     if (!gc.capture_stream && hipStreamCreateWithFlags(&gc.capture_stream, hipStreamNonBlocking) != hipSuccess)
@@ -147,16 +187,22 @@ static int window_graph(const WindowKey& k, const StepLayout& lay, hipGraphExec_
         (void)hipGetLastError();
         return rc != SPECV_OK ? rc : SPECV_E_HIP;
     }
-    hipGraphExec_t exec = nullptr;
-    const bool inst = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) == hipSuccess;
+    GraphEntry e;
+    const bool inst = hipGraphInstantiate(&e.exec, g, nullptr, nullptr, 0) == hipSuccess;
     (void)hipGraphDestroy(g);
     if (!inst) return SPECV_E_HIP;
-    if (gc.execs.size() >= 32) {  // bounded cache
-        (void)hipGraphExecDestroy(gc.execs.begin()->second);
-        gc.execs.erase(gc.execs.begin());
+    if (hipEventCreateWithFlags(&e.done, hipEventDisableTiming) != hipSuccess) {
+        destroy_entry(e);
+        return SPECV_E_HIP;
     }
-    gc.execs.emplace(k, exec);
-    *out = exec;
+    if (gc.entries.size() >= kGraphCacheMax) {  // retire the least recently used entry
+        auto lru = gc.entries.begin();
+        for (auto i = gc.entries.begin(); i != gc.entries.end(); ++i)
+            if (i->second.last_use < lru->second.last_use) lru = i;
+        gc.retired.push_back(lru->second);
+        gc.entries.erase(lru);
+    }
+    *out = &gc.entries.emplace(k, e).first->second;
     return SPECV_OK;
 }
 
@@ -166,15 +212,20 @@ static int run_window(const WindowKey& k, const StepLayout& lay, int W, void* ho
     specv_ctrl* ctrl = k.ctrl;
     specv_step_stats* stats = k.stats;
     void* workspace = k.workspace;
-    hipGraphExec_t exec = nullptr;
-    int rc = window_graph(k, lay, &exec);
+    GraphCache& gc = graph_cache();
+    std::lock_guard<std::mutex> lock(gc.mu);
+    reap_retired(gc);
+    GraphEntry* entry = nullptr;
+    int rc = window_graph(gc, k, lay, &entry);
     if (rc != SPECV_OK) return rc;
+    entry->last_use = ++gc.clock;
     int32_t* wcounter = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.wcounter);
     hipLaunchKernelGGL(window_begin_kernel, dim3(1), dim3(64), 0, s, wcounter);
     rc = launch_status();
     if (rc != SPECV_OK) return rc;
     for (int i = 0; i < W; i++)
-        if (hipGraphLaunch(exec, s) != hipSuccess) return SPECV_E_HIP;
+        if (hipGraphLaunch(entry->exec, s) != hipSuccess) return SPECV_E_HIP;
+    if (hipEventRecord(entry->done, s) != hipSuccess) return SPECV_E_HIP;
     if (host_readback) {
         char* hb = static_cast<char*>(host_readback);
         if (hipMemcpyAsync(hb, ctrl, sizeof(specv_ctrl), hipMemcpyDeviceToHost, s) != hipSuccess ||

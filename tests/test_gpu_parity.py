@@ -100,7 +100,11 @@ def test_quantize_parity(sv, T, K):
         x[1] = 0.0
         x[1, ::3] = -0.0
     if T >= 3:
-        x[2] *= np.float32(1e-39)     # subnormal inputs
+        x[2] *= np.float32(1e-39)     # subnormal inputs: 127/absmax overflows binary32
+    if T >= 4:
+        # absmax 2^-130 with zeros, +-absmax/2 (ties), 3/4 and -1/4 of it
+        tiny = np.array([2.0 ** -130, 0.0, -2.0 ** -131, 2.0 ** -131, 1.5 * 2.0 ** -131, -2.0 ** -132], np.float32)
+        x[3] = np.resize(tiny, K)
     xq_o, xs_o = oracle.quantize_act(x)
     xq, xs = sv.quantize_act(to_dev(x))
     torch.cuda.synchronize()
@@ -293,6 +297,7 @@ def test_quantize_blocks_parity(sv, T, K):
     x[0, :32] = 0.0                                  # an all-zero block
     if K >= 96:
         x[-1, 64:96] *= np.float32(1e-30)            # a block of tiny values
+        x[0, 32:64] *= np.float32(1e-39)             # subnormals: 127/absmax overflows binary32
     xq, xs = sv.quantize_act_blocks(to_dev(x))
     torch.cuda.synchronize()
     xq_o, xs_o = oracle.quantize_act_blocks(x)

@@ -184,6 +184,38 @@ def test_tiny_device_reaches_context_limit(sv, width):
     assert any(m >= 0 for m, _, _ in stats)
 
 
+def test_tiny_graph_cache_cycles_past_its_bound(sv):
+    """Forty windows with forty control blocks (forty cached graphs, more
+    than the 32 the cache keeps), enqueued back to back with no host
+    synchronisation: graphs are retired while earlier windows are still
+    queued. Every window starts from the same committed prefix, so each must
+    equal the oracle's window; then the first eight keys, long evicted, run
+    again the same way."""
+    case("tiny window graph cache: 40 keys back to back, width 4")
+    cfg, _, om = model_pair("tiny")
+    width, W, n_keys = 4, 4, 40
+    kc0, vc0 = sg.kv_prefix(13, cfg, TINY_L0, TINY_CAP)
+    oc = ctrl_dict(TINY_L0, width, TINY_CAP - 16, TINY_ROOT)
+    kc, vc = kc0.copy(), vc0.copy()
+    want_ctrl = dict(oc)
+    o_stats, _ = oracle.window(om, kc, vc, want_ctrl, width, W, tiny_ref(), sg.draft_draws(3, 64), THR06)
+    g = GpuRun(sv, "tiny", kc0, vc0, TINY_CAP, oc, ring_cap=64)
+    ref_t = torch.from_numpy(np.ascontiguousarray(tiny_ref(), np.int32)).cuda()
+    dr_t = torch.from_numpy(sg.draft_draws(3, 64).view(np.int32)).cuda()
+    for keys in (range(n_keys), range(8)):
+        ctrls = [ctrl_tensor(oc) for _ in keys]
+        stats = [torch.full((W, 3), 7777, dtype=torch.int32, device="cuda") for _ in keys]
+        for c, st in zip(ctrls, stats):
+            g.dm.window(c, st, width, W, ref_t, dr_t, THR06)
+        torch.cuda.synchronize()
+        for i, (c, st) in enumerate(zip(ctrls, stats)):
+            assert [int(x) for x in c.cpu().numpy()] == [want_ctrl[f] for f in FIELDS], f"window {i}"
+            assert [tuple(int(v) for v in r) for r in st.cpu().numpy()] == [tuple(x) for x in o_stats], f"window {i}"
+    gk, gv = g.caches()
+    assert np.array_equal(gk[:, :, : want_ctrl["committed_len"]], kc[:, :, : want_ctrl["committed_len"]])
+    assert np.array_equal(gv[:, :, : want_ctrl["committed_len"]], vc[:, :, : want_ctrl["committed_len"]])
+
+
 def test_tiny_done_before_window_changes_nothing(sv):
     case("tiny window with done preset")
     cfg, _, _ = model_pair("tiny")

@@ -5,11 +5,26 @@ central invariant that a tree step reproduces sequential single-token steps
 (GPU-Resident Speculative Decoding for In-Browser LLM Inference with WebGPU,
 Implementation and GPU-Resident Speculation Loop)."""
 import math
+import os
 
 import numpy as np
 import pytest
 
 import synthgen as sg
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _num(text: str) -> float:
+    text = text.strip()
+    return float.fromhex(text) if "0x" in text else float(text)
+
+
+def _golden_lines(name: str):
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            yield [part.strip() for part in line.split("|")]
 
 
 # ------------------------------------------------------------------ exp, silu, norm, rope
@@ -60,6 +75,20 @@ def test_rmsnorm_bound_and_closed_form(orc):
     assert np.all(yo == rs)
 
 
+def _rmsnorm_cases():
+    return [tuple(np.array([_num(a) for a in part.split(",")], np.float32) for part in parts)
+            for parts in _golden_lines("rmsnorm_worked.txt")]
+
+
+@pytest.mark.parametrize("x,w,want", _rmsnorm_cases())
+def test_rmsnorm_worked_example(orc, x, w, want):
+    """Hand-worked bits (tests/golden/rmsnorm_worked.txt): with |x| = 3072,
+    (x * rs) rounds to +-1, so the stated order (x * rs) * w returns +-w
+    exactly, where x * (rs * w) would not."""
+    y = orc.rmsnorm(x, w)
+    assert y.tobytes() == want.tobytes(), [float(v).hex() for v in y]
+
+
 def test_rope_table_matches_library(orc):
     c, s = orc.rope_table(300, 64, 1e6)
     p = np.arange(300, dtype=np.float64)[:, None]
@@ -98,6 +127,44 @@ def test_attention_uniform_scores_is_exact_mean(orc, length):
     out = orc.attention(np.zeros(hd, np.float32), k, v, rows)
     want = np.array([np.float32(np.float32(vals[rows, d].sum()) / np.float32(length)) for d in range(hd)])
     assert np.array_equal(out, want)
+
+
+def _attention_cases():
+    def plane(n, items):
+        a = np.zeros((n, 64), np.float16)
+        for item in items.split():
+            rows, dim, val = item.split(":")
+            lo, _, hi = rows.partition("..")
+            a[int(lo): int(hi or lo) + 1, int(dim)] = np.float16(_num(val))
+        return a
+
+    out = []
+    for name, n, vnz, knz, qtext, want in _golden_lines("attention_chunks_worked.txt"):
+        n = int(n)
+        v = plane(n, vnz)
+        k = plane(n, "" if knz == "-" else knz)
+        q = np.ones(64, np.float32)
+        if qtext != "ones":
+            q[:] = 0
+            for item in qtext.split():
+                d, val = item.split(":")
+                q[int(d)] = np.float32(_num(val))
+        d, val = want.split(":")
+        out.append(pytest.param(q, k, v, int(d), np.float32(_num(val)), id=name))
+    return out
+
+
+@pytest.mark.parametrize("q,k,v,dim,want", _attention_cases())
+def test_attention_chunking_worked_example(orc, q, k, v, dim, want):
+    """Hand-worked bits (tests/golden/attention_chunks_worked.txt) whose value
+    depends on the chunk size (256 logical positions), on R16 inside a chunk,
+    on R16 across chunks and on R16 in the score: 128- or 512-position
+    chunks, or a sequential sum at any of these places, give other bits."""
+    n = v.shape[0]
+    out = orc.attention(q, k.view(np.uint16), v.view(np.uint16), np.arange(n, dtype=np.int32))
+    assert out[dim].tobytes() == want.tobytes(), float(out[dim]).hex()
+    others = np.delete(out, dim)
+    assert np.all(others == 0)
 
 
 def test_attention_close_to_softmax(orc):

@@ -115,9 +115,15 @@ def _golden_quant():
         if not line or line.startswith("#"):
             continue
         xs, codes, scale = [s.strip() for s in line.split("|")]
-        out.append((np.array([float(a) for a in xs.split(",")], np.float32),
-                    np.array([int(c) for c in codes.split(",")], np.int8), np.float32(float(scale))))
+        out.append((np.array([_num(a) for a in xs.split(",")], np.float32),
+                    np.array([int(c) for c in codes.split(",")], np.int8), np.float32(_num(scale))))
     return out
+
+
+def _num(text: str) -> float:
+    """A decimal or hex float ("0x1p-130"), as written in the golden files."""
+    text = text.strip()
+    return float.fromhex(text) if "0x" in text else float(text)
 
 
 @pytest.mark.parametrize("x,codes,scale", _golden_quant())
@@ -152,6 +158,47 @@ def test_quant_invariants(orc):
         bound = s * (Fraction(1, 2) + Fraction(1, 2 ** 14)) + a * Fraction(1, 2 ** 23)
         for k in range(0, 896, 7):
             assert abs(Fraction(float(x[t, k])) - s * int(xq[t, k])) <= bound
+
+
+def test_quant_codes_invariant_under_power_of_two_scaling(orc):
+    """Multiplying a row by 2^e (exactly) leaves its codes unchanged, also
+    when 2^e makes 127/absmax overflow: the codes are round(x * 127/absmax),
+    a function of the ratios only. The scales scale by 2^e where they stay
+    normal."""
+    x = sg.normal_f32(sg.stream_key(6, 4), 4 * 896).reshape(4, 896)
+    # magnitudes in [1/4, 3.9]: at 2^-124 every value stays normal (exact),
+    # and absmax * 2^-124 < 2^-122 makes 127/absmax overflow binary32
+    x[np.abs(x) < 0.25] = np.float32(0.5)
+    x = np.clip(x, -3.9, 3.9).astype(np.float32)
+    xq, xs = orc.quantize_act(x)
+    for e in (-124, -110, -100, -60, 40, 100):
+        xe = (x * np.float32(2.0 ** e)).astype(np.float32)
+        assert np.array_equal((xe * np.float32(2.0 ** -e)).astype(np.float32), x)
+        if e == -124:
+            assert float(np.abs(xe).max()) < 127.0 / float(np.finfo(np.float32).max)
+        xqe, xse = orc.quantize_act(xe)
+        assert np.array_equal(xqe, xq), f"codes changed at 2^{e}"
+        if float(xs.min()) * 2.0 ** e >= 2.0 ** -126:
+            assert np.array_equal(xse, (xs * np.float32(2.0 ** e)).astype(np.float32))
+
+
+def test_quant_tiny_subnormal_rows_near_exact(orc):
+    """Rows of subnormals (bits lost against N(0,1), absmax around 1e-40):
+    every code is within one of the exact rational round(x * 127/absmax),
+    and equal to it where the exact value is not within 2^-10 of a tie."""
+    x = (sg.normal_f32(sg.stream_key(6, 5), 2 * 300).reshape(2, 300) * np.float32(1e-40)).astype(np.float32)
+    xq, xs = orc.quantize_act(x)
+    for t in range(2):
+        a = Fraction(float(np.abs(x[t]).max()))
+        assert xs[t] == np.float32(float(a) / 127.0) or abs(Fraction(float(xs[t])) - a / 127) <= Fraction(1, 2 ** 150)
+        for k in range(300):
+            r = Fraction(float(x[t, k])) * 127 / a
+            fl = math.floor(r)
+            frac = r - fl
+            want = fl + (1 if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2) else 0)
+            assert abs(int(xq[t, k]) - want) <= 1
+            if abs(frac - Fraction(1, 2)) > Fraction(1, 2 ** 10):
+                assert int(xq[t, k]) == want
 
 
 # ------------------------------------------------------------------ W4A8 linear
