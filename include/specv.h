@@ -199,6 +199,22 @@ int w4a8_linear_argmax_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq
                          size_t workspace_bytes, void* stream);
 
 /*
+ * w4a8_linear_argmax_T without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workgroups' (value, row) pairs go to
+ * a static device array of the library (128 KiB per device, held until the
+ * process ends), so the call allocates nothing. Same arguments, results and
+ * errors as w4a8_linear_argmax_T; shapes whose pairs need more than 128 KiB
+ * (T * chunks * 8 bytes; chunks is at most two per compute unit) return
+ * SPECV_E_WORKSPACE and enqueue nothing. Every call on one device shares that
+ * array: calls that overlap on one device (two streams, or two threads)
+ * race and give undefined predictions; calls on one stream are ordered.
+ */
+int w4a8_linear_argmax_T_noalloc(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
+                                 const float* xs, float* y, int32_t* argmax, int32_t T, int32_t N,
+                                 int32_t K, void* stream);
+
+/*
  * Timing diagnostic (not part of the computation): the next w4a8_linear_T
  * launch made by the calling host thread records `start_event` and
  * `stop_event` (hipEvent_t created with timing) at the beginning and end of

@@ -14,7 +14,7 @@ import torch
 from ._lib import CM_WEIGHT, LIB, SpecvError, check, cm_params
 from .model import DeviceModel
 
-__all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "tree_argmax_accept",
+__all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "linear_argmax_noalloc", "tree_argmax_accept",
            "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace", "cm_params", "cm_draft", "CM_WEIGHT",
            "quantize_act_blocks", "linear_blocks", "Packed", "pack_weights"]
 
@@ -187,6 +187,21 @@ def linear_argmax(w: Packed, xq: torch.Tensor, xs: torch.Tensor, y: torch.Tensor
         _dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype), _dev(xq, "xq", torch.int8),
         _dev(xs, "xs", torch.float32), yp, _dev(argmax, "argmax", torch.int32), T, N, K,
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream()))
+    return argmax
+
+
+def linear_argmax_noalloc(w: Packed, xq: torch.Tensor, xs: torch.Tensor, argmax: torch.Tensor,
+                          y: torch.Tensor | None = None) -> torch.Tensor:
+    """linear_argmax through w4a8_linear_argmax_T_noalloc: the caller passes
+    the output buffer and the library uses its static device scratch, so
+    nothing is allocated (calls that overlap on one device race)."""
+    T, N, K = _check_packed(w, xq, tuple(xs.shape))
+    if xs.shape != (T,):
+        raise ValueError("xs must be [T]")
+    yp = _dev(y, "y", torch.float32) if y is not None else None
+    check("w4a8_linear_argmax_T_noalloc", LIB.w4a8_linear_argmax_T_noalloc(
+        _dev(w.wp, "wq", torch.uint8), _dev(w.sp, "ws", w.sp.dtype), _dev(xq, "xq", torch.int8),
+        _dev(xs, "xs", torch.float32), yp, _dev(argmax, "argmax", torch.int32), T, N, K, _stream()))
     return argmax
 
 

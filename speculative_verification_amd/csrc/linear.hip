@@ -58,6 +58,7 @@
 // -0).
 #include <hip/hip_ext.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -933,6 +934,39 @@ static bool empty_call(int32_t T, int32_t N, int32_t K) {
     return T >= 1 && T <= 32 && N == 0 && K >= 32 && K <= (1 << 20) && K % 32 == 0;
 }
 
+// Scratch of w4a8_linear_argmax_T_noalloc: the (value, lowest row) pair of
+// every token and workgroup, T * chunks * 8 bytes (16 tokens x 1024
+// workgroups at most). Each device holds its own copy until the process
+// ends. Host code takes its device address from hipGetSymbolAddress, once per
+// device, and passes that address to the kernels: the array's name itself is
+// not a device address in host code.
+constexpr size_t kNoAllocScratchBytes = 128 * 1024;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`.
+static int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return SPECV_E_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return SPECV_E_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPECV_OK;
+}
+
 }  // namespace specv
 
 extern "C" int specv_time_next_linear(void* start_event, void* stop_event) {
@@ -992,5 +1026,26 @@ extern "C" int w4a8_linear_argmax_T(const uint8_t* wq, const uint16_t* ws, const
     const int lrc = linear_dispatch(wq, ws, xq, xs, y, part, T, N, K, false, s);
     if (lrc != SPECV_OK) return lrc;
     hipLaunchKernelGGL(argmax_finish_kernel, dim3(T), dim3(256), 0, s, part, linear_argmax_chunks(T, N, K), argmax);
+    return launch_status();
+}
+
+extern "C" int w4a8_linear_argmax_T_noalloc(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
+                                            const float* xs, float* y, int32_t* argmax, int32_t T, int32_t N,
+                                            int32_t K, void* stream) {
+    using namespace specv;
+    if (T < 1 || T > 16) return SPECV_E_SHAPE;
+    const int rc = linear_args(wq, ws, xq, xs, T, N, K);
+    if (rc != SPECV_OK) return rc;
+    if (!argmax) return SPECV_E_INVAL;
+    if (!aligned(y, 4) || !aligned(argmax, 4)) return SPECV_E_ALIGN;
+    if (w4a8_linear_argmax_workspace(T, N, K) > kNoAllocScratchBytes) return SPECV_E_WORKSPACE;
+    void* part = nullptr;
+    const int src = scratch_address(&part);
+    if (src != SPECV_OK) return src;
+    hipStream_t s = (hipStream_t)stream;
+    const int lrc = linear_dispatch(wq, ws, xq, xs, y, static_cast<Best*>(part), T, N, K, false, s);
+    if (lrc != SPECV_OK) return lrc;
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(T), dim3(256), 0, s, static_cast<const Best*>(part),
+                       linear_argmax_chunks(T, N, K), argmax);
     return launch_status();
 }

@@ -260,6 +260,21 @@ def test_linear_argmax_rejects_bad_arguments(lib):
     assert f(A + 8, A, A, A, None, A, 8, 151936, 896, A, need, None) == E_ALIGN
 
 
+def test_linear_argmax_noalloc_rejects_bad_arguments(lib):
+    """The no-allocation variant validates like w4a8_linear_argmax_T, with no
+    workspace arguments (no GPU is touched on these paths)."""
+    f = lib.w4a8_linear_argmax_T_noalloc
+    assert f(A, A, A, A, None, A, 17, 4096, 4096, None) == E_SHAPE      # argmax only up to 16 tokens
+    assert f(A, A, A, A, None, A, 0, 896, 896, None) == E_SHAPE
+    assert f(A, A, A, A, None, A, 8, 0, 896, None) == E_SHAPE
+    assert f(A, A, A, A, None, A, 8, 896, 100, None) == E_SHAPE        # K not a multiple of 32
+    assert f(A, A, A, A, None, None, 8, 151936, 896, None) == E_INVAL  # no argmax output
+    assert f(None, A, A, A, None, A, 8, 151936, 896, None) == E_INVAL
+    assert f(A, A, A, A, A + 2, A, 8, 151936, 896, None) == E_ALIGN
+    assert f(A, A, A, A, None, A + 2, 8, 151936, 896, None) == E_ALIGN
+    assert f(A + 8, A, A, A, None, A, 8, 151936, 896, None) == E_ALIGN
+
+
 def test_tree_accept_rejects_bad_arguments(lib):
     f = lib.tree_accept
     assert f(A, 0, A, A, A, A, None, None, 0, None) == E_SHAPE
