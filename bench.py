@@ -22,6 +22,12 @@ The line also times the same step on the Qwen2.5-0.5B linear set
 down 896x4864, then lm_head 151936x896; four copies of its 278 MB of weights
 in rotation, so that each step reads its copy cold) at T = 1, 2, 4, 8.
 
+The line also carries the single 896x896 linear at T = 1 (`config1`, a
+latency: its weights stay in the L2 cache), the full 8-node tree
+verification step on the 24-layer Qwen2.5-0.5B shape at a 1024-row cache
+(`decoder`), the device-resident windows on that decoder (`window`), and the
+CPU oracle on bounded samples of these workloads (`cpu_baseline`).
+
 Prints one JSON line (rank 0). `value` is the algorithmic bytes of the step
 (weights, activation codes and scales, linear outputs, quantisation traffic,
 argmax pairs, compaction moves) divided by the step time, in
@@ -43,21 +49,67 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per linear launch of the T = 8 step from the FETCH_SIZE and
-# WRITE_SIZE counter passes (each scaled by a plain 256 MiB device copy),
-# valid for the kernel source they were taken on.
-LINEAR_TRAFFIC = {"source_sha256": "7ab669ecf46638aaec8a4d6c51e80d972f4d2cd91c1e7208282eb20d67fca77a",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33624842}
+# Figures of the linear kernel taken by rocprofv3 on this bench's own command
+# (profiles/w4a8_linear_llama8b_T8*.md), stored with the hash of the kernel
+# source they were taken on: HBM bytes per linear launch of the T = 8 step
+# from the FETCH_SIZE and WRITE_SIZE counter passes (each scaled by a plain
+# 256 MiB device copy), and the kernel trace's mean duration per launch.
+LINEAR_PROFILE = {"source_sha256": "7ab669ecf46638aaec8a4d6c51e80d972f4d2cd91c1e7208282eb20d67fca77a",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33624842,
+                  "rocprof_mean_us": 8.098, "summary": "profiles/w4a8_linear_llama8b_T8.md"}
 
 
-def linear_traffic(T, workload):
-    """Counter-measured bytes per launch, or None when the kernel source has
-    changed since the counters were taken (or the workload differs)."""
+def linear_profile(T, workload):
+    """The stored rocprofv3 figures, or None when the kernel source has
+    changed since they were taken (or the workload differs)."""
     import hashlib
     src = os.path.join(ROOT, "speculative_verification_amd", "csrc", "linear.hip")
     h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    ok = h == LINEAR_TRAFFIC["source_sha256"] and T == LINEAR_TRAFFIC["T"] and workload == LINEAR_TRAFFIC["workload"]
-    return LINEAR_TRAFFIC["bytes_per_launch"] if ok else None
+    ok = h == LINEAR_PROFILE["source_sha256"] and T == LINEAR_PROFILE["T"] and workload == LINEAR_PROFILE["workload"]
+    return LINEAR_PROFILE if ok else None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def host_threads():
+    """Host CPUs this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def graph_us(torch, fn, n, reps=5):
+    """Median time of a graph of fn's launches divided by n (fn enqueues on
+    the current stream); fn runs once eagerly first."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    del g
+    return float(np.median(ts)) / n
 METRIC = "W4A8 verify GB/s & % HBM peak at T=1..8; T=8/T=1 cost ratio; µs/verify"
 
 MODELS = {
@@ -150,10 +202,6 @@ class Model:
         self.act_T = None
         self.y = {nm: torch.empty((Tmax * N,), dtype=torch.float32, device=dev)
                   for nm, N, _ in layer_linears(m)}
-        # size the shared split-K workspace once, before any graph capture
-        for T in range(1, Tmax + 1):
-            for _, N, K in layer_linears(m) + [("lm_head", m["vocab"], m["hidden"])]:
-                sv.linear_workspace(T, N, K, dev)
         # tree, control block and KV cache
         self.L0 = 1024
         self.cap = self.L0 + 4096
@@ -368,39 +416,20 @@ def ceilings(model, T, torch, sv):
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     base, sp = buf.data_ptr(), sink.data_ptr()
 
-    def graph_us(fn, n, reps=5):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            fn(s.cuda_stream)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            fn(s.cuda_stream)
-        g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        del g
-        return float(np.median(ts)) / n
+    def graph_chain(fn, n):   # fn takes the capture stream's handle
+        return graph_us(torch, lambda: fn(torch.cuda.current_stream().cuda_stream), n)
 
     def read(ptr, nb, grid, st):
         sv.check("specv_stream_read", sv.LIB.specv_stream_read(ptr, nb, sp, grid, st))
 
-    empty = graph_us(lambda st: [read(base, 0, 512, st) for _ in range(200)], 200)
-    whole = min(graph_us(lambda st: read(base, tot, g, st), 1) for g in (512, 1024, 2048))
-    chain = graph_us(lambda st: [read(base + o, b, 512, st) for o, b in zip(offs, sizes)], 1)
+    empty = graph_chain(lambda st: [read(base, 0, 512, st) for _ in range(200)], 200)
+    whole = min(graph_chain(lambda st: read(base, tot, g, st), 1) for g in (512, 1024, 2048))
+    chain = graph_chain(lambda st: [read(base + o, b, 512, st) for o, b in zip(offs, sizes)], 1)
     names = [nm for nm, _, _ in layer_linears(m)]
     per_shape = {}
     for si, nm in enumerate(names + ["lm_head"]):
         idx = list(range(si, len(sizes) - 1, len(names))) if nm != "lm_head" else [len(sizes) - 1]
-        us = graph_us(lambda st: [read(base + offs[i], sizes[i], 512, st) for i in idx], len(idx))
+        us = graph_chain(lambda st: [read(base + offs[i], sizes[i], 512, st) for i in idx], len(idx))
         per_shape[nm] = {"us": round(us, 2), "weight_bytes": sizes[idx[0]],
                          "GB/s": round(sizes[idx[0]] / us / 1e3, 1)}
     del buf
@@ -412,17 +441,25 @@ def ceilings(model, T, torch, sv):
                     "counts of the step's linear launches; per shape, a chain of that shape's reads (us per launch)"}
 
 
-def cpu_baseline(model, T, seconds=(6.0, 6.0)):
-    """The oracle, as it stands, on a bounded sample: quantize + W4A8 linear
-    over the generated layer sets (qkv, o, gate_up, down) at T tokens, one
-    linear after another, first on one host thread for at least seconds[0],
-    then with the linear's output rows split over every host thread (the C
-    oracle releases the interpreter lock; rows are independent, so results
-    are identical) for at least seconds[1]. `value` is the all-threads rate."""
+def cpu_baseline(model, T, dec=None, seconds=(6.0, 6.0)):
+    """The oracle, as it stands, on bounded samples of the same workloads, on
+    this host:
+    - the 8B linear set (`value`): quantize + W4A8 linear over the generated
+      layer sets (qkv, o, gate_up, down) at T tokens, one linear after
+      another, first on one host thread for at least seconds[0], then with
+      each linear's output rows split over every host thread this process
+      may use (the C oracle releases the interpreter lock; rows are
+      independent, so results are identical) for at least seconds[1];
+    - the single 896x896 linear at T = 1 (quantize + linear, one thread);
+    - the 0.5B linear set at T: its seven matrices and the lm_head, once, on
+      every thread;
+    - the 0.5B decoder (`dec`: model arrays, configuration, cache, L0): one
+      8-node tree step and the 8 sequential single-token steps of a chain,
+      each on one thread (the oracle's forward is not threaded)."""
     import oracle
     sg = model.sg
     lins = [(s, nm, N, K) for s in model.host_sets for nm, N, K in layer_linears(model.m)]
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
 
     def run(nthreads, min_s):
         t0 = time.perf_counter()
@@ -441,16 +478,134 @@ def cpu_baseline(model, T, seconds=(6.0, 6.0)):
 
     b1, n1, t1 = run(1, seconds[0])
     bt, nt, tt = run(threads, seconds[1])
-    return {"value": round(bt / tt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "single_thread_value": round(b1 / t1 / 1e9, 4),
-            "sample": f"quantize + W4A8 linear over the {model.m['hidden']}-hidden layer sets (qkv, o, gate_up, "
-                      f"down) at T={T}, one linear after another: {n1} linears ({b1/1e6:.1f} MB algorithmic) in "
-                      f"{t1:.2f} s on one thread, then {nt} linears ({bt/1e6:.1f} MB) in {tt:.2f} s with output "
-                      f"rows split over {threads} threads, on {platform.machine()} ({os.cpu_count()} host cpus "
-                      f"visible)"}
+    out = {"value": round(bt / tt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "single_thread_value": round(b1 / t1 / 1e9, 4), "cpu_model": cpu_model(),
+           "sample": f"quantize + W4A8 linear over the {model.m['hidden']}-hidden layer sets (qkv, o, gate_up, "
+                     f"down) at T={T}, one linear after another: {n1} linears ({b1/1e6:.1f} MB algorithmic) in "
+                     f"{t1:.2f} s on one thread, then {nt} linears ({bt/1e6:.1f} MB) in {tt:.2f} s with output "
+                     f"rows split over {threads} threads, on {platform.machine()} ({os.cpu_count()} host cpus "
+                     f"visible, {threads} usable)"}
+
+    # the single-linear configuration: 896 x 896 at T = 1
+    wq, ws, x = sg.linear_case(0, 1, 896, 896)
+    ts = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        xq, xs = oracle.quantize_act(x)
+        oracle.w4a8_linear(wq, ws, xq, xs)
+        ts.append(time.perf_counter() - t0)
+    out["config1_us"] = round(float(np.median(ts)) * 1e6, 1)
+
+    # the 0.5B linear set at T, every matrix once, on every thread
+    m5 = MODELS["qwen2.5-0.5b"]
+    shapes = layer_linears(m5) + [("lm_head", m5["vocab"], m5["hidden"])]
+    gen = [(sg.linear_case(0, T, N, K, layer=i), N, K) for i, (nm, N, K) in enumerate(shapes)]
+    nb = sum(linear_bytes(T, N, K) + quant_bytes(T, K) for _, N, K in gen)
+    t0 = time.perf_counter()
+    for (wq, ws, x), N, K in gen:
+        xq, xs = oracle.quantize_act(x)
+        oracle.w4a8_linear_threads(wq, ws, xq, xs, threads)
+    dt = time.perf_counter() - t0
+    out["small_set"] = {"us": round(dt * 1e6, 1), "GB/s": round(nb / dt / 1e9, 4), "threads": threads,
+                        "sample": f"quantize + W4A8 linear of the 0.5B set (qkv, o, gate_up, down, lm_head) at "
+                                  f"T={T}, each matrix once"}
+    del gen
+
+    if dec is not None:
+        arrays, cfg, kc, vc, L0 = dec
+        c, sn = oracle.rope_table(cfg["max_pos"], cfg["head_dim"], 1e6)
+        om = oracle.Model(dict(arrays, rope_cos=c, rope_sin=sn), cfg)
+        parent, token = decoder_tree(sg, cfg, 8)
+        t0 = time.perf_counter()
+        r = oracle.tree_step(om, kc.copy(), vc.copy(), L0, parent, token)
+        t_tree = time.perf_counter() - t0
+        ks, vs = kc.copy(), vc.copy()
+        t0 = time.perf_counter()
+        for d in range(8):
+            oracle.forward(om, ks, vs, L0 + d, np.array([-1], np.int32), np.array([token[min(d, 7)]], np.int32))
+        t_seq = time.perf_counter() - t0
+        out["config3"] = {"tree8_s": round(t_tree, 3), "sequential8_s": round(t_seq, 3), "threads": 1,
+                          "accepted": int(r["m"]),
+                          "sample": f"24-layer qwen2.5-0.5b-shaped decoder at L={L0}: one 8-node tree step "
+                                    "(forward, argmax, acceptance, compaction), then 8 single-token forwards of "
+                                    "a chain"}
+    return out
 
 
-def window_bench(torch, sv, sg, widths, W=16, max_windows=400):
+def config1_bench(torch, sv, sg, reps=200):
+    """One W4A8 linear, K = N = 896, T = 1, seed 0 (the single-linear
+    configuration). Its 451,584 weight bytes stay in the L2 cache, so this is
+    a latency: us per launch in a graph of `reps` launches, the kernel's own
+    duration from kernel-attached events (median of 20 back-to-back
+    launches), and quantisation + linear as a pair per graph node pair."""
+    T, N, K = 1, 896, 896
+    wq, ws, x = sg.linear_case(0, T, N, K)
+    dev = torch.device("cuda")
+    w = sv.pack_weights(torch.from_numpy(wq).to(dev), torch.from_numpy(ws.view(np.int16)).to(dev))
+    xd = torch.from_numpy(x).to(dev)
+    xq, xs = sv.quantize_act(xd)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    lin_us = graph_us(torch, lambda: [sv.linear(w, xq, xs, y) for _ in range(reps)], reps)
+    pair_us = graph_us(torch, lambda: [(sv.quantize_act(xd, xq, xs), sv.linear(w, xq, xs, y))
+                                       for _ in range(reps)], reps)
+    # kernel-attached events on 21 launches enqueued behind a spin kernel, so
+    # they run back to back (as in a step), not each after an idle gap
+    evs = []
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(50_000_000)
+    for _ in range(21):
+        e0, e1 = timing_events(torch)
+        sv.check("specv_time_next_linear", sv.LIB.specv_time_next_linear(e0.cuda_event, e1.cuda_event))
+        sv.linear(w, xq, xs, y)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    kern = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs[1:]]))
+    wb = weight_bytes(N, K)
+    return {"workload": "W4A8 linear 896x896, T=1, int4 g32 fp16 scales U(0.005,0.02), N(0,1) activations, "
+                        "seed 0 (L2-resident: a latency)",
+            "us_per_launch": round(lin_us, 3), "kernel_us": round(kern, 3),
+            "quant_plus_linear_us": round(pair_us, 3), "weight_bytes": wb,
+            "kernel_GBs": round(wb / kern / 1e3, 1)}
+
+
+def decoder_tree(sg, cfg, N):
+    """The configuration's tree: random topological parents and random draft
+    tokens in [0, V), seed 0."""
+    parent = sg.random_tree_parents(sg.stream_key(0, sg.TID_PARENT), N)
+    token = sg.tokens(sg.stream_key(0, sg.TID_TOKEN), N, cfg["vocab"])
+    return parent, token
+
+
+def decoder_bench(torch, sv, sg, dm, cfg, L0, reps=20):
+    """Full tree verification on the 24-layer Qwen2.5-0.5B shape over a
+    1024-row fp16 KV cache: one 8-node step (tree-masked forward, the
+    lm_head reduced to each node's argmax in its epilogue, acceptance,
+    compaction), and a single-token step (a root-only tree) for comparison.
+    Graph replays of (control-block reset + step): every replay verifies the
+    same tree from the same committed state."""
+    out = {}
+    for N in (8, 1):
+        parent, token = decoder_tree(sg, cfg, N)
+        p = torch.from_numpy(parent).cuda()
+        t = torch.from_numpy(token).cuda()
+        c0 = sv.new_ctrl(L0, N, dm.c.kv_capacity - 16, root_token=int(token[0]))
+        ctrl = c0.clone()
+        stats = torch.zeros(3, dtype=torch.int32, device="cuda")
+
+        def step():
+            torch.mul(c0, 1, out=ctrl)      # reset by a kernel, not a memset or copy node
+            dm.tree_step(ctrl, p, t, N, stats=stats, want_logits=False)
+        us = graph_us(torch, lambda: [step() for _ in range(reps)], reps)
+        out[str(N)] = {"us": round(us, 2), "accepted": int(ctrl[4].item())}
+        print(f"[bench] decoder step N={N}: {out[str(N)]}", file=sys.stderr, flush=True)
+    return {"workload": f"qwen2.5-0.5b-shaped 24-layer decoder, tree verification at L={L0} (fp16 KV), random "
+                        "topological tree with random drafts, seed 0: forward + fused argmax + acceptance + "
+                        "KV compaction, HIP-graph replay",
+            "tree8_us": out["8"]["us"], "single_token_us": out["1"]["us"],
+            "tree8_over_single": round(out["8"]["us"] / out["1"]["us"], 4), "by_N": out}
+
+
+def window_bench(torch, sv, sg, dm, widths, L0, W=16, max_windows=400):
     """Device-resident windows on the Qwen2.5-0.5B shape: W-step windows of
     draft -> tree verify -> accept -> compact, each ending in a pinned
     readback of the control block and W statistics records. The context
@@ -459,11 +614,7 @@ def window_bench(torch, sv, sg, widths, W=16, max_windows=400):
     acceptance 0.6. Each window is timed with events on the stream; only
     windows whose W steps all ran (none after done) are counted."""
     cfg = sg.QWEN05
-    arrays = sg.model_case(3, cfg)
-    L0, ctx, cap, root = 1024, 4096, 4096 + 32, 9
-    kc, vc = sg.kv_prefix(41, cfg, L0, cap)
-    dm = sv.DeviceModel(arrays, cfg, cap, kc, vc)
-    del arrays, kc, vc
+    ctx, root = 4096, 9
     stats = torch.zeros((W, 3), dtype=torch.int32, device="cuda")
     ring = torch.zeros(8192, dtype=torch.int32, device="cuda")
     rb = torch.zeros(32 + 12 * W, dtype=torch.uint8, pin_memory=True)
@@ -514,9 +665,11 @@ def cm_window_bench(torch, sv, dm, ref, widths, L0, ctx, root, vocab, W, max_win
     random page in which the root and the next `echo` tokens of the greedy
     reply appear once, as a passage the reply repeats; after the passage the
     history no longer predicts the reply. Fixed widths first, then the width
-    controller (its load-time costs are the fixed-width step costs), two
-    windows in flight."""
-    from speculative_verification_amd.controller import WidthController, run_controlled
+    controller (its load-time costs are the fixed-width step costs, its window
+    size calibrated at load from windows of 1, 2 and 4 steps), two windows in
+    flight."""
+    from speculative_verification_amd.controller import (WidthController, WindowBuffers, calibrate_window,
+                                                         run_controlled)
     page = np.random.default_rng(5).integers(0, vocab, size=L0).astype(np.int32)
     page[199] = root
     page[200:200 + echo] = ref[L0 + 1:L0 + 1 + echo].cpu().numpy()
@@ -525,11 +678,14 @@ def cm_window_bench(torch, sv, dm, ref, widths, L0, ctx, root, vocab, W, max_win
     stats = torch.zeros((W, 3), dtype=torch.int32, device="cuda")
     rb = torch.zeros(32 + 12 * W, dtype=torch.uint8, pin_memory=True)
 
-    def reset():
+    def reset(c=None):
         ring.zero_()
         ring[:L0 + 1] = hist
-        c = sv.new_ctrl(L0, 1, ctx, root_token=root)
-        c[7] = L0 + 1   # ring_head: the ring holds the whole stream
+        v = sv.new_ctrl(L0, 1, ctx, root_token=root)
+        v[7] = L0 + 1   # ring_head: the ring holds the whole stream
+        if c is None:
+            return v
+        c.copy_(v)
         return c
 
     out = {}
@@ -556,13 +712,19 @@ def cm_window_bench(torch, sv, dm, ref, widths, L0, ctx, root, vocab, W, max_win
                            "tokens_per_s": round(tokens / (t_us * 1e-6), 1) if t_us else None,
                            "windows": steps // W}
         print(f"[bench] cm window width={width}: {out[str(width)]}", file=sys.stderr, flush=True)
-    ctl = WidthController({int(w): v["us_per_step"] for w, v in out.items()})
+    costs = {int(w): v["us_per_step"] for w, v in out.items()}
+    # window size at load: short decodes with windows of 1, 2 and 4 steps
+    bufs = WindowBuffers(4, ring.device)
+    W_cal, us_by_W = calibrate_window(dm, reset, lambda: WidthController(costs), ring, sizes=(1, 2, 4),
+                                      steps=16, bufs=bufs)
+    print(f"[bench] cm window size {W_cal}: us per token {us_by_W}", file=sys.stderr, flush=True)
+    ctl = WidthController(costs)
     first = ctl.width
     ctrl = reset()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    log = run_controlled(dm, ctrl, ring, ctl, W, max_windows)
+    log = run_controlled(dm, ctrl, ring, ctl, W_cal, 10 ** 6, bufs=bufs)
     e1.record()
     torch.cuda.synchronize()
     tokens = int(ctrl[0].item()) - L0
@@ -570,9 +732,13 @@ def cm_window_bench(torch, sv, dm, ref, widths, L0, ctx, root, vocab, W, max_win
     hist_w = {}
     for w, _, _ in log:
         hist_w[str(w)] = hist_w.get(str(w), 0) + 1
-    ctl_out = {"first_width": first, "windows_by_width": hist_w, "tokens": tokens,
+    ctl_out = {"first_width": first, "window_size": W_cal,
+               "window_size_us_per_token": {str(k): round(v, 2) for k, v in us_by_W.items()},
+               "windows_by_width": hist_w, "tokens": tokens,
                "tokens_per_s": round(tokens / (us * 1e-6), 1),
-               "note": "wall time from the first enqueue to the last completion, host decisions included"}
+               "note": "window size chosen at load (smallest of 1, 2, 4 steps within 10 % of the fastest time "
+                       "per token on a 16-step decode); wall time from the first enqueue to the last "
+                       "completion, host decisions included"}
     print(f"[bench] cm controller: {ctl_out}", file=sys.stderr, flush=True)
     return {"workload": f"context-mixing drafter on a 1024-token synthetic page echoing {echo} tokens of the "
                         f"reply; {W}-step windows to the 4096 context",
@@ -671,8 +837,20 @@ def main():
         ceil["step_pct_of_read_all"] = round(100 * per_T[args.T]["GB/s"] / ceil["read_all_weights_GBs"], 1)
         ceil["step_over_read_chain"] = round(per_T[args.T]["ms"] * 1e3 / ceil["read_chain_us"], 3)
         print(f"[bench] ceilings: {ceil}", file=sys.stderr, flush=True)
+    config1 = config1_bench(torch, sv, sg)
+    print(f"[bench] config1: {config1}", file=sys.stderr, flush=True)
+    # the 24-layer 0.5B decoder: the tree verification step, then the windows
+    cfg5 = sg.QWEN05
+    L0, cap5 = 1024, 4096 + 32
+    arrays5 = sg.model_case(3, cfg5)
+    kc5, vc5 = sg.kv_prefix(41, cfg5, L0, cap5)
+    dm5 = sv.DeviceModel(arrays5, cfg5, cap5, kc5, vc5)
+    decoder = decoder_bench(torch, sv, sg, dm5, cfg5, L0)
     widths = [int(w) for w in args.window_widths.split(",") if w]
-    window = window_bench(torch, sv, sg, widths) if widths else None
+    window = window_bench(torch, sv, sg, dm5, widths, L0) if widths else None
+    del dm5
+    torch.cuda.empty_cache()
+    prof = linear_profile(args.T, args.workload)
     main_T = per_T[args.T]
     out = {
         "metric": METRIC,
@@ -704,7 +882,17 @@ def main():
                            "accepted": v["accepted"], "graph_replay_exact": v["graph_replay_exact"]}
                   for T, v in per_T.items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": linear_traffic(args.T, args.workload),
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "frac_basis": "live: kernel-attached HIP events (hipExtLaunchKernel begin/end on the launch's "
+                                   "stream) around every linear launch of one eager step, mean over the launches",
+                     "traffic": prof["bytes_per_launch"] if prof else None,
+                     "frac_rocprof": (round(avg_b / (prof["rocprof_mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                      if prof else None),
+                     "profile_source": (f"stored, not of this run: rocprofv3 kernel trace (mean "
+                                        f"{prof['rocprof_mean_us']} us per launch) and FETCH_SIZE + WRITE_SIZE "
+                                        f"counter passes of this command on linear.hip sha256 "
+                                        f"{prof['source_sha256'][:16]}, {prof['summary']}") if prof else
+                                       "none: linear.hip changed since the stored rocprofv3 figures were taken",
                      "kernel": f"w4a8_linear_stream_kernel<{args.T},P,*,false,false> (P = 7 for down, 4 otherwise; "
                                f"the lm_head runs the argmax specialisation)",
                      "lm_head_chunks": model.lm_chunks(args.T),
@@ -713,8 +901,11 @@ def main():
                      "by_shape": by_shape},
         "ceilings": ceil,
         "small_set": small,
+        "config1": config1,
+        "decoder": decoder,
         "window": window,
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(model, args.T),
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(model, args.T,
+                                                                        dec=(arrays5, cfg5, kc5, vc5, L0)),
     }
     print(json.dumps(out), flush=True)
 

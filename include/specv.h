@@ -360,7 +360,11 @@ size_t spec_step_workspace(const specv_model* m, int32_t n_max);
  * One verification step: the tree-masked forward over ctrl->n_nodes nodes
  * (parent/token as in tree_argmax_accept), then tree_argmax_accept and
  * kv_compact, with the same control-state semantics.
- *   logits  fp32 [n_max][V] out (16-byte aligned); argmax, path int32 [n_max].
+ *   logits  nullable fp32 [n_max][V] out (16-byte aligned): every node's
+ *           logits. When NULL they are not written: the lm_head reduces its
+ *           rows to each node's (maximum, lowest index) in its epilogue, and
+ *           acceptance reads those ([P3]'s greedy rule needs no more).
+ *   argmax, path int32 [n_max].
  *   workspace  spec_step_workspace(m, n_max) bytes, 256-byte aligned,
  *              zero-filled before its first use (as for w4a8_linear_T).
  * n_max in [1, 16].

@@ -148,7 +148,20 @@ def measure_costs(run_window, widths, W: int = 8, reps: int = 2) -> dict:
     return {w: min(run_window(w, W) for _ in range(reps)) / W for w in widths}
 
 
-def run_controlled(dm, ctrl, ring, ctl: WidthController, W: int, max_windows: int, params=None):
+class WindowBuffers:
+    """The readback and statistics buffers of two windows in flight, for
+    windows of up to W_max steps. Reusing one set keeps the buffers, and so
+    the cached window graphs, the same from one run to the next."""
+
+    def __init__(self, W_max: int, device):
+        import torch
+        self.W_max = W_max
+        self.rbs = [torch.zeros(32 + 12 * W_max, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self.stats = [torch.zeros((W_max, 3), dtype=torch.int32, device=device) for _ in range(2)]
+
+
+def run_controlled(dm, ctrl, ring, ctl: WidthController, W: int, max_windows: int, params=None,
+                   bufs: WindowBuffers | None = None):
     """Context-mixing windows of W steps with the width chosen by `ctl`, two
     windows in flight: while window k+1 runs, the host reads window k's
     readback, folds its statistics and the interval between the two
@@ -158,8 +171,10 @@ def run_controlled(dm, ctrl, ring, ctl: WidthController, W: int, max_windows: in
     import numpy as np
     import torch
 
-    rbs = [torch.zeros(32 + 12 * W, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
-    stats = [torch.zeros((W, 3), dtype=torch.int32, device=ring.device) for _ in range(2)]
+    bufs = bufs if bufs is not None else WindowBuffers(W, ring.device)
+    if W > bufs.W_max:
+        raise ValueError("window longer than its buffers")
+    rbs, stats = bufs.rbs, bufs.stats
     events, widths, log = [], [], []
 
     def enqueue(k, width):
@@ -174,7 +189,7 @@ def run_controlled(dm, ctrl, ring, ctl: WidthController, W: int, max_windows: in
         enqueue(1, ctl.width)
     for k in range(max_windows):
         events[k].synchronize()
-        rb = rbs[k % 2].numpy().copy()
+        rb = rbs[k % 2].numpy()[: 32 + 12 * W].copy()
         c = rb[:32].view(np.int32)
         st = rb[32:].view(np.int32).reshape(W, 3)
         us = events[k - 1].elapsed_time(events[k]) * 1e3 if k > 0 else None
@@ -187,3 +202,34 @@ def run_controlled(dm, ctrl, ring, ctl: WidthController, W: int, max_windows: in
         if k + 2 < max_windows:
             enqueue(k + 2, ctl.next())
     return log
+
+
+def calibrate_window(dm, reset, make_controller, ring, sizes=(1, 2, 4), steps: int = 16, params=None,
+                     bufs: WindowBuffers | None = None):
+    """The window size, chosen at load time: a short decode of `steps` steps
+    from the same state is timed with windows of each size (two windows in
+    flight, widths chosen by a fresh controller from make_controller()), and
+    the smallest size whose time per emitted token is within 10 % of the
+    fastest is kept (window_size). reset(ctrl=None) restores the decode
+    state, ring included, into ctrl (a fresh control block when None) and
+    returns it. Each size runs once untimed first, so graph captures stay
+    out of the timing. Returns (size, {size: us per token})."""
+    import torch
+
+    bufs = bufs if bufs is not None else WindowBuffers(max(sizes), ring.device)
+    ctrl = reset()
+    us = {}
+    for timed in (False, True):
+        for W in sizes:
+            reset(ctrl)
+            L0 = int(ctrl[0].item())
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run_controlled(dm, ctrl, ring, make_controller(), W, max(1, steps // W), params, bufs)
+            e1.record()
+            torch.cuda.synchronize()
+            if timed:
+                tokens = int(ctrl[0].item()) - L0
+                us[W] = e0.elapsed_time(e1) * 1e3 / max(tokens, 1)
+    return window_size(us), us

@@ -891,7 +891,7 @@ extern "C" int spec_tree_step(const specv_model* m, specv_ctrl* ctrl, const int3
     using namespace specv;
     SPECV_TRY(validate_model(m));
     if (n_max < 1 || n_max > 16) return SPECV_E_SHAPE;
-    if (!ctrl || !parent || !token || !logits || !argmax || !path) return SPECV_E_INVAL;
+    if (!ctrl || !parent || !token || !argmax || !path) return SPECV_E_INVAL;
     if (ring && ring_cap < 1) return SPECV_E_INVAL;
     if (!aligned(ctrl, 4) || !aligned(parent, 4) || !aligned(token, 4) || !aligned(logits, 16) ||
         !aligned(argmax, 4) || !aligned(path, 4))

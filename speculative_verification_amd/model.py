@@ -96,15 +96,19 @@ class DeviceModel:
 
     def tree_step(self, ctrl: torch.Tensor, parent: torch.Tensor, token: torch.Tensor, n_max: int,
                   logits: torch.Tensor | None = None, stats: torch.Tensor | None = None,
-                  ring: torch.Tensor | None = None):
+                  ring: torch.Tensor | None = None, want_logits: bool = True):
+        """One verification step (spec_tree_step). Returns (logits, argmax,
+        path); logits is None when want_logits is false (not written)."""
         dev = self.k_cache.device
         V = self.cfg["vocab"]
-        logits = torch.empty((n_max, V), dtype=torch.float32, device=dev) if logits is None else logits
+        if want_logits and logits is None:
+            logits = torch.empty((n_max, V), dtype=torch.float32, device=dev)
         argmax = torch.empty(n_max, dtype=torch.int32, device=dev)
         path = torch.zeros(n_max, dtype=torch.int32, device=dev)
         ws = self.workspace(n_max)
         check("spec_tree_step", LIB.spec_tree_step(
-            self.ptr(), ctrl.data_ptr(), parent.data_ptr(), token.data_ptr(), n_max, logits.data_ptr(),
+            self.ptr(), ctrl.data_ptr(), parent.data_ptr(), token.data_ptr(), n_max,
+            logits.data_ptr() if want_logits else None,
             argmax.data_ptr(), path.data_ptr(), stats.data_ptr() if stats is not None else None,
             ring.data_ptr() if ring is not None else None, ring.numel() if ring is not None else 0,
             ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))

@@ -3,7 +3,8 @@ windows in flight (GPU-Resident Speculative Decoding for In-Browser LLM
 Inference with WebGPU, Feedback Control of Speculation Width). Whatever
 widths it picks, tree verification is exact, so the emitted stream must equal
 the oracle's greedy stream; the load-time cost measurement must give a
-positive cost per width."""
+positive cost per width, and windows of the size calibrated at load time
+must emit the same greedy stream."""
 import numpy as np
 import pytest
 import torch
@@ -90,3 +91,40 @@ def test_measure_costs(sv):
 
     costs = measure_costs(run_window, (1, 2, 4, 8, 16), W=4, reps=1)
     assert set(costs) == {1, 2, 4, 8, 16} and all(v > 0 for v in costs.values())
+
+
+def test_calibrated_window_emits_the_greedy_stream(sv):
+    """Load-time window size: short decodes from the same state with windows
+    of 1, 2 and 4 steps; the chosen size is within 10 % of the fastest time
+    per token, and a controlled decode at that size emits the oracle's
+    greedy stream."""
+    from speculative_verification_amd.controller import (WidthController, WindowBuffers, calibrate_window,
+                                                         run_controlled)
+    cfg, arrays, kc, vc, hist, greedy = setup(sv)
+    dm, ctrl0, ring = fresh(sv, cfg, arrays, kc, vc, hist, L0 + 150)
+    init = ctrl0.clone()
+    hist_t = torch.tensor(hist, dtype=torch.int32, device="cuda")
+
+    def reset(c=None):
+        ring.zero_()
+        ring[:L0 + 1] = hist_t
+        if c is None:
+            return init.clone()
+        c.copy_(init)
+        return c
+
+    costs = {1: 1000.0, 2: 1020.0, 4: 1080.0, 8: 1150.0, 16: 1700.0}
+    bufs = WindowBuffers(4, "cuda")
+    W, us = calibrate_window(dm, reset, lambda: WidthController(costs), ring, steps=16, bufs=bufs)
+    case(f"calibrated window size {W}: {us}")
+    assert set(us) == {1, 2, 4} and all(v > 0 for v in us.values())
+    assert W in us and us[W] <= 1.1 * min(us.values())
+    assert all(us[w] > 1.1 * min(us.values()) for w in us if w < W)
+    ctrl = reset()
+    log = run_controlled(dm, ctrl, ring, WidthController(costs), W, 400, bufs=bufs)
+    torch.cuda.synchronize()
+    c = ctrl.cpu().tolist()
+    n_emit = c[0] - L0
+    assert n_emit > 0 and c[3] == 1         # ran to the context limit
+    assert ring.cpu().numpy()[L0 + 1:L0 + 1 + n_emit].tolist() == greedy[:n_emit]
+    assert all(len(st) == W for _, st, _ in log)

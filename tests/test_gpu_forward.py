@@ -125,6 +125,32 @@ def test_qwen05_tree_step_parity(sv):
     assert m >= 1
 
 
+@pytest.mark.parametrize("name,seed,N,L", [("tiny", 31, 8, 200), ("tiny", 32, 1, 50), ("qwen", 23, 8, 1024)])
+def test_tree_step_without_logits(sv, name, seed, N, L):
+    """With no logits buffer the step writes no logits (the lm_head reduces
+    to each node's argmax in its epilogue) and gives the oracle's
+    predictions, path, control block and caches."""
+    case(f"{name} tree step without logits N={N} L={L}")
+    cfg, arrays, om = model_pair(name)
+    cap = L + N + 8
+    kc0, vc0 = sg.kv_prefix(seed, cfg, L, cap)
+    parent, token = planted_tree(seed, N, L, cfg, om, kc0, vc0)
+    kc, vc = kc0.copy(), vc0.copy()
+    ro = oracle.tree_step(om, kc, vc, L, parent, token)
+    dm = sv.DeviceModel(arrays, cfg, cap, kc0, vc0)
+    ctrl = sv.new_ctrl(L, N, cap - N, root_token=int(token[0]))
+    logits, amax, path = dm.tree_step(ctrl, dev_i32(parent), dev_i32(token), N, want_logits=False)
+    torch.cuda.synchronize()
+    assert logits is None
+    assert np.array_equal(amax.cpu().numpy(), ro["amax"])
+    m = ro["m"]
+    assert np.array_equal(path.cpu().numpy()[: m + 1], ro["path"])
+    c = ctrl.cpu().numpy()
+    assert (c[0], c[4], c[5], c[6]) == (ro["L"], m, ro["bonus"], 1)
+    assert np.array_equal(dm.k_cache.cpu().numpy().view(np.uint16), kc)
+    assert np.array_equal(dm.v_cache.cpu().numpy().view(np.uint16), vc)
+
+
 def test_qwen05_tree_equals_sequential_on_gpu(sv):
     """On the GPU alone: each node's logits and K/V equal those of the
     single-token steps along its root path."""
