@@ -137,6 +137,10 @@ int w4a8_pack_weights(const uint8_t* wq, const uint16_t* ws, int32_t N, int32_t 
                       void* stream);
 
 /*
+ * The weights must be in the packed tile layout of w4a8_pack_weights: the
+ * interchange layout ([N][K/2] nibbles, [N][K/32] scales) passed here gives
+ * wrong outputs with status SPECV_OK, since a layout cannot be checked.
+ *
  * W4A8 linear for T = 1..32 tokens ([P1], Small-Batch Verification Kernels
  * and Implementation; packing of [P2]):
  *   y[t][n] = xs[t] * R16_g( f32(ws[g][n]) * f32(d[t][n][g]) ),
