@@ -48,6 +48,11 @@ __device__ __forceinline__ uint16_t load2_stream(__amdgpu_buffer_rsrc_t r, uint3
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kCachePolicyNT);
 }
 
+// Agent-coherent cache policy (sc1) for data one workgroup publishes to
+// another of the same launch: such stores and loads are coherent across the
+// chip's separate L2 caches without whole-cache write-backs.
+constexpr int kCachePolicySC1 = 16;
+
 // (value, index) pair of an argmax reduction. "Better" is the larger value,
 // or an equal value at a lower index: a total order on (value, -index) with
 // -0 == +0, so every reduction shape yields the lowest index of the maximum.

@@ -579,6 +579,393 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
     }
 }
 
+// Attention of one node for all the query heads that share one KV head,
+// over one chunk of its visible sequence, with the merge fused: one
+// workgroup per (KV head g, node i, chunk c), so each value row is read and
+// widened once for the group's heads ([P1] Small-Batch Verification
+// Kernels). The workgroup's 1024 threads form four sets of 256; set k takes
+// the group's heads k, k + 4 (at most two), so the four SIMDs of a CU share
+// the heads' arithmetic. In a set, thread t owns position t of the chunk: its
+// key row meets each of its heads' queries, s_{h,t} = R16_d(q_d * K_td) *
+// scale; each head's chunk maximum is taken over the set's waves (order-free);
+// e_{h,t} = E(s_{h,t} - m_h). For the value sums, lane s of the set's 16-lane
+// group q owns R16 slot s (positions s, s+16, ... in order) of columns
+// 4q .. 4q+3 (and 64 + 4q .. for head dims above 64) and of l, then the
+// group's butterfly adds the slots as the index-order tree: exactly the sums
+// of the per-head kernel. The partials (m, l, o) are stored agent-coherently;
+// the workgroup that arrives last for node i (one counter per node, reset by
+// that workgroup) merges every head's chunks, m = max_c m_c, w_c = E(m_c -
+// m), l = R16_c(w_c * l_c), o_d = R16_c(w_c * o_cd), out_d = o_d / l, and
+// quantises the node's attention row for the output projection. No
+// workgroup waits for another. Nodes past the live count quantise to zero.
+constexpr int kGrpThreads = 1024;
+constexpr int kGrpSets = kGrpThreads / kFwdThreads;  // sets of 256 threads
+constexpr int kGrpMaxHeads = 8;                        // query heads per KV head the grouped kernel takes
+constexpr int kGrpSetHeads = kGrpMaxHeads / kGrpSets;  // heads per set
+constexpr int kGrpMaxRow = kGrpThreads;                // attention row (heads x head dim) its merge takes
+constexpr int kGrpMaxChunks = 32;                      // chunks per node its merge takes
+
+template <int HD>
+__global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
+    const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
+    int nh, int nkv, float scale, float* __restrict__ part, int nchunk_max, uint32_t* __restrict__ arrivals,
+    int8_t* __restrict__ xq, float* __restrict__ xs, const specv_ctrl* ctrl) {
+    constexpr int HALF = HD / 2;
+    constexpr int NB = (HD + 63) / 64;
+    constexpr bool SWZ = attn_swizzle_ok(HD);
+    constexpr int VS = attn_vstride(HD, SWZ);
+    constexpr bool KF = HD <= 64;  // key row widened to fp32 registers once
+    constexpr int SH = kGrpSetHeads;
+    const int g = blockIdx.x, i = blockIdx.y, c = blockIdx.z, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int set = __builtin_amdgcn_readfirstlane(tid >> 8);  // uniform in a wave
+    const int t8 = tid & 255;                                  // position / lane of the set
+    const int wset = wave & 3;                                 // wave within the set
+    const int depth_raw = tinfo[i];  // issued with the control loads (i < 16)
+    if (ctrl->done) return;
+    const int K = nh * HD;
+    if (i >= ctrl->n_nodes) {
+        if (g == 0 && c == 0) zero_row(xq + (size_t)i * K, xs + i, K);
+        return;
+    }
+    const int L = ctrl->committed_len;
+    if (L + i >= cap) return;  // its rows were not written (no room left)
+    const int depth = min(max(depth_raw, 0), i);
+    const int len = L + depth + 1;
+    const int j0 = c * kAttnChunk;
+    if (j0 >= len) return;
+    const int cnt = len - j0 < kAttnChunk ? len - j0 : kAttnChunk;
+    const int G = nh / nkv;
+    const int QKV = (nh + 2 * nkv) * HD;
+    __shared__ int anc[kMaxNodes];
+    __shared__ __attribute__((aligned(16))) uint16_t tk[kMaxNodes][HD];
+    __shared__ __attribute__((aligned(16))) uint16_t tv[kMaxNodes][HD];
+    __shared__ __attribute__((aligned(16))) float qs[kGrpMaxHeads][HD];
+    // e of position s + 16k at Et[h][s][4 * ((k >> 2) ^ ((s >> 2) & 3)) + (k & 3)]: each lane s reads its
+    // 16 values as four 16-byte words, and the 16 lanes of a group hit distinct banks
+    __shared__ __attribute__((aligned(16))) float Et[kGrpMaxHeads][16][16];
+    __shared__ float wmax[kGrpThreads / 64][SH];
+    __shared__ int s_last;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][VS] value rows, then the key rows; later the
+                                                       // merge's weights
+
+    const size_t plane = (((size_t)layer * nkv + g) * cap) * HD;
+    // Committed rows first, coalesced: set 0 loads the chunk's key rows and
+    // set 1 its value rows, consecutive lanes reading consecutive 16-byte
+    // pieces of a row, every load issued (rows past the committed ones read
+    // zeros); both are staged in LDS, swizzled or padded as the value rows.
+    constexpr int CH = HD / 8;          // 16-byte pieces per row
+    constexpr int RPP = kFwdThreads / CH;  // rows per pass of a set
+    uint16_t* Ks = Vs + kAttnChunk * VS;
+    const int ncommit = L > j0 ? (L - j0 < cnt ? L - j0 : cnt) : 0;  // committed rows of the chunk
+    v4i stage[CH];
+    if (set < 2) {
+        const auto rkv = make_rsrc((set == 0 ? kc : vc) + plane, (uint32_t)((size_t)cap * HD * 2));
+        const int piece = t8 % CH;
+#pragma unroll
+        for (int pass = 0; pass < CH; pass++) {
+            const int row = pass * RPP + t8 / CH;
+            const bool ok = row < ncommit;
+            stage[pass] = load16(rkv, ((uint32_t)(j0 + row) * (uint32_t)(HD * 2) + 16u * (uint32_t)piece) |
+                                          (ok ? 0u : kOOB));
+        }
+    }
+    for (int w = tid; w < G * HALF; w += kGrpThreads) {  // the group's rotated queries of node i
+        const int h = w / HALF, d = w - h * HALF;
+        const size_t tp = (size_t)(L + depth) * HALF + d;
+        const float* src = qkv + (size_t)i * QKV + (g * G + h) * HD;
+        rope_pair(src[d], src[d + HALF], cos_t[tp], sin_t[tp], qs[h][d], qs[h][d + HALF]);
+    }
+    if (c == 0 && tid >= kGrpThreads - HALF) {  // node i's key and value rows to the caches
+        const int d = tid - (kGrpThreads - HALF);
+        const size_t tp = (size_t)(L + depth) * HALF + d;
+        const float* ks = qkv + (size_t)i * QKV + (nh + g) * HD;
+        const float* vsrc = qkv + (size_t)i * QKV + (nh + nkv + g) * HD;
+        float ra, rb;
+        rope_pair(ks[d], ks[d + HALF], cos_t[tp], sin_t[tp], ra, rb);
+        const size_t row = plane + (size_t)(L + i) * HD;
+        kc[row + d] = f32_to_f16(ra);
+        kc[row + d + HALF] = f32_to_f16(rb);
+        vc[row + d] = f32_to_f16(vsrc[d]);
+        vc[row + d + HALF] = f32_to_f16(vsrc[d + HALF]);
+    }
+    if (tid <= depth) anc[tid] = min(max(tinfo_anc(tinfo, i)[tid], 0), i);
+    if (set < 2) {
+        uint16_t* dst = set == 0 ? Ks : Vs;
+        const int piece = t8 % CH;
+#pragma unroll
+        for (int pass = 0; pass < CH; pass++) {
+            const int row = pass * RPP + t8 / CH;
+            if (row < ncommit)
+                *reinterpret_cast<v4i*>(dst + row * VS + 8 * (SWZ ? piece ^ ((row >> 1) & 7) : piece)) = stage[pass];
+        }
+    }
+    __syncthreads();
+    if (j0 + cnt > L) {  // the chunk holds tree positions: their rows, made once into LDS
+        // the ancestor at depth t has depth t itself, so its rotary position is L + t
+        for (int w = tid; w < (depth + 1) * HALF; w += kGrpThreads) {
+            const int t = w / HALF, d = w - t * HALF;
+            const int a = anc[t];
+            const float* ks = qkv + (size_t)a * QKV + (nh + g) * HD;
+            const float* vsrc = qkv + (size_t)a * QKV + (nh + nkv + g) * HD;
+            const size_t tp = (size_t)(L + t) * HALF + d;
+            float ra, rb;
+            rope_pair(ks[d], ks[d + HALF], cos_t[tp], sin_t[tp], ra, rb);
+            tk[t][d] = f32_to_f16(ra);
+            tk[t][d + HALF] = f32_to_f16(rb);
+            tv[t][d] = f32_to_f16(vsrc[d]);
+            tv[t][d + HALF] = f32_to_f16(vsrc[d + HALF]);
+        }
+        __syncthreads();
+        // positions L .. len-1 of the chunk take the ancestors' rows
+        if (set < 2 && t8 >= ncommit && t8 < cnt) {
+            const uint16_t* src = set == 0 ? &tk[j0 + t8 - L][0] : &tv[j0 + t8 - L][0];
+            uint16_t* dst = set == 0 ? Ks : Vs;
+#pragma unroll
+            for (int t = 0; t < CH; t++)
+                *reinterpret_cast<v4i*>(dst + t8 * VS + 8 * (SWZ ? t ^ ((t8 >> 1) & 7) : t)) =
+                    *reinterpret_cast<const v4i*>(src + 8 * t);
+        }
+        __syncthreads();
+    }
+    const bool live = t8 < cnt;
+    v4i kr[HD / 8];
+    if (live) {
+#pragma unroll
+        for (int t = 0; t < CH; t++)
+            kr[t] = *reinterpret_cast<const v4i*>(Ks + t8 * VS + 8 * (SWZ ? t ^ ((t8 >> 1) & 7) : t));
+    }
+    // scores of this thread's position for the set's heads h = set + 4u
+    float sc[SH];
+    {
+        float kf[KF ? HD : 1];
+        if constexpr (KF) {
+#pragma unroll
+            for (int t = 0; t < HD / 8; t++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t wd = (uint32_t)kr[t][e];
+                    kf[8 * t + 2 * e] = f16_to_f32((uint16_t)(wd & 0xffff));
+                    kf[8 * t + 2 * e + 1] = f16_to_f32((uint16_t)(wd >> 16));
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < SH; u++) {
+            const int h = set + kGrpSets * u;
+            sc[u] = -__builtin_inff();
+            if (h >= G || !live) continue;
+            float slot[16];
+#pragma unroll
+            for (int r = 0; r < 16; r++) slot[r] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < HD / 8; t++) {
+                const float4 qa = *reinterpret_cast<const float4*>(&qs[h][8 * t]);
+                const float4 qb = *reinterpret_cast<const float4*>(&qs[h][8 * t + 4]);
+                const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int d = 8 * t + e;
+                    float kd;
+                    if constexpr (KF)
+                        kd = kf[d];
+                    else
+                        kd = f16_to_f32((uint16_t)(((uint32_t)kr[t][e >> 1]) >> (16 * (e & 1))));
+                    slot[d & 15] = slot[d & 15] + qv[e] * kd;
+                }
+            }
+#pragma unroll
+            for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2 * w) slot[r] = slot[r] + slot[r + w];
+            sc[u] = slot[0] * scale;
+        }
+    }
+    // each head's maximum over the chunk (order-free): rows by DPP, the four
+    // rows of a wave by lane reads, the set's four waves through LDS
+#pragma unroll
+    for (int u = 0; u < SH; u++) {
+        const float m16 = max16(sc[u]);
+        const int b = __builtin_bit_cast(int, m16);
+        const float mw = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+                               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+        if (lane == 0) wmax[wave][u] = mw;
+    }
+    __syncthreads();
+    float mh[SH];
+#pragma unroll
+    for (int u = 0; u < SH; u++) {
+        const int h = set + kGrpSets * u;
+        const int w0 = 4 * set;
+        mh[u] = fmaxf(fmaxf(wmax[w0][u], wmax[w0 + 1][u]), fmaxf(wmax[w0 + 2][u], wmax[w0 + 3][u]));
+        const int es = t8 & 15, ek = t8 >> 4;
+        if (h < G) Et[h][es][4 * ((ek >> 2) ^ ((es >> 2) & 3)) + (ek & 3)] = live ? det_exp(sc[u] - mh[u]) : 0.0f;
+    }
+    __syncthreads();
+
+    const int s = t8 & 15, q = t8 >> 4;
+    const auto rp = make_rsrc(part, 0x7fffffffu);
+    auto put = [&](float* at, float v) {  // agent-coherent store of a partial
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), rp, (uint32_t)((at - part) * 4), 0,
+                                              kCachePolicySC1);
+    };
+    float* pnode = part + ((size_t)i * nh + (size_t)g * G) * nchunk_max * (HD + 2) + (size_t)c * (HD + 2);
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const int d0 = 64 * b + 4 * q;
+        if (d0 >= HD) break;
+        float v[16][4];
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            const int p = s + 16 * k;
+            uint2 w = make_uint2(0u, 0u);
+            if (p < cnt)
+                w = *reinterpret_cast<const uint2*>(Vs + p * VS + (SWZ ? 8 * ((d0 >> 3) ^ ((p >> 1) & 7)) + (d0 & 7)
+                                                                        : d0));
+            v[k][0] = f16_to_f32((uint16_t)(w.x & 0xffff));
+            v[k][1] = f16_to_f32((uint16_t)(w.x >> 16));
+            v[k][2] = f16_to_f32((uint16_t)(w.y & 0xffff));
+            v[k][3] = f16_to_f32((uint16_t)(w.y >> 16));
+        }
+#pragma unroll
+        for (int u = 0; u < SH; u++) {
+            const int h = set + kGrpSets * u;
+            if (h >= G) continue;
+            float e[16];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; k4++) {
+                const float4 ev = *reinterpret_cast<const float4*>(&Et[h][s][4 * (k4 ^ ((s >> 2) & 3))]);
+                e[4 * k4] = ev.x;
+                e[4 * k4 + 1] = ev.y;
+                e[4 * k4 + 2] = ev.z;
+                e[4 * k4 + 3] = ev.w;
+            }
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float l = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                acc[0] = acc[0] + e[k] * v[k][0];
+                acc[1] = acc[1] + e[k] * v[k][1];
+                acc[2] = acc[2] + e[k] * v[k][2];
+                acc[3] = acc[3] + e[k] * v[k][3];
+                if (b == 0) l = l + e[k];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] = tree16(acc[r]);
+            float* o = pnode + (size_t)h * nchunk_max * (HD + 2);
+            if (s == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) put(o + 2 + d0 + r, acc[r]);
+            }
+            if (b == 0 && q == 0) {
+                l = tree16(l);
+                if (s == 0) {
+                    put(o, mh[u]);
+                    put(o + 1, l);
+                }
+            }
+        }
+    }
+    // arrival: this workgroup's partials are complete before its count (the
+    // memory clobber keeps the compiler from moving the stores past the wait)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int nch = (len + kAttnChunk - 1) / kAttnChunk;
+    if (tid == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(&arrivals[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = before + 1 == (uint32_t)(nkv * nch);
+        if (last) __hip_atomic_store(&arrivals[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    // The merge of node i, by the last workgroup. Every load is issued
+    // unconditionally, 16 chunks at a time, in one batch per thread: chunks
+    // past nch read as zeros (out-of-range offsets) and are masked by
+    // selects, so they add +0, which leaves a slot (never -0) unchanged.
+    // First the chunk weights of each head (16 lanes per head, chunks s and
+    // s + 16), with the thread's own partial outputs already in flight; then
+    // the element of the attention row this thread owns.
+    const int stride = HD + 2;
+    const uint32_t rec = (uint32_t)stride * 4u;  // one chunk's record, bytes
+    const uint32_t node_off = (uint32_t)((size_t)i * nh * nchunk_max * stride) * 4u;
+    auto get = [&](uint32_t byte_off, bool ok) {  // agent-coherent load of node i's partials
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rp, (node_off + byte_off) | (ok ? 0u : kOOB), 0, kCachePolicySC1));
+    };
+    float* wts = reinterpret_cast<float*>(smem);  // [nh][nchunk_max], then l[nh]
+    float* lsum = wts + (size_t)nh * nchunk_max;
+    const int hh0 = tid / HD, d0e = tid - hh0 * HD;
+    const bool own = tid < K;
+    const uint32_t ebase = (uint32_t)((size_t)hh0 * nchunk_max * stride + 2 + d0e) * 4u;
+    float slot[16];
+#pragma unroll
+    for (int sl = 0; sl < 16; sl++) slot[sl] = 0.0f;
+    for (int c0 = 0; c0 < nch; c0 += 16) {
+        float ov[16];
+#pragma unroll
+        for (int sl = 0; sl < 16; sl++) ov[sl] = get(ebase + (uint32_t)(c0 + sl) * rec, own && c0 + sl < nch);
+        if (c0 == 0) {
+            const int hw = tid >> 4, sw = tid & 15;  // 16 lanes per head
+            if (hw < nh) {
+                const uint32_t hbase = (uint32_t)((size_t)hw * nchunk_max * stride) * 4u;
+                const float mr0 = get(hbase + (uint32_t)sw * rec, sw < nch);
+                const float mr1 = get(hbase + (uint32_t)(sw + 16) * rec, sw + 16 < nch);
+                const float l0 = get(hbase + (uint32_t)sw * rec + 4u, sw < nch);
+                const float l1 = get(hbase + (uint32_t)(sw + 16) * rec + 4u, sw + 16 < nch);
+                const float m0 = sw < nch ? mr0 : -__builtin_inff();
+                const float m1 = sw + 16 < nch ? mr1 : -__builtin_inff();
+                const float m = max16(fmaxf(m0, m1));
+                const float w0 = det_exp(m0 - m), w1 = det_exp(m1 - m);
+                if (sw < nch) wts[hw * nchunk_max + sw] = w0;
+                if (sw + 16 < nch) wts[hw * nchunk_max + sw + 16] = w1;
+                float acc = 0.0f;
+                acc = acc + (sw < nch ? w0 * l0 : 0.0f);
+                acc = acc + (sw + 16 < nch ? w1 * l1 : 0.0f);
+                acc = tree16(acc);
+                if (sw == 0) lsum[hw] = acc;
+            }
+            __syncthreads();
+        }
+        if (own) {
+            const float* wh = wts + hh0 * nchunk_max;
+#pragma unroll
+            for (int sl = 0; sl < 16; sl++) {
+                const float wc = c0 + sl < nch ? wh[c0 + sl] : 0.0f;
+                slot[sl] = slot[sl] + wc * ov[sl];
+            }
+        }
+    }
+    float y = 0.0f;
+    if (own) {
+#pragma unroll
+        for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+            for (int sl = 0; sl < 16; sl += 2 * w) slot[sl] = slot[sl] + slot[sl + w];
+        y = slot[0] / lsum[hh0];
+    }
+    {
+        const float m16 = max16(fabsf(y));
+        const int b = __builtin_bit_cast(int, m16);
+        const float mw = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+                               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+        if (lane == 0) wmax[wave][0] = mw;
+    }
+    __syncthreads();
+    float a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGrpThreads / 64; w++) a = fmaxf(a, wmax[w][0]);
+    const QuantScale qsc = quant_scale(a);
+    if (tid == 0) xs[i] = a == 0.0f ? 0.0f : a / 127.0f;
+    if (own) xq[(size_t)i * K + tid] = (int8_t)(int)quant_code(y, qsc);
+}
+
 // Merge of the chunks of each head of node i: m = max_c m_c,
 // w_c = E(m_c - m), l = R16_c(w_c * l_c), o_d = R16_c(w_c * o_cd),
 // out_d = o_d / l; then the attention output row [nh*hd] is quantised for
@@ -684,6 +1071,7 @@ StepLayout step_layout(const specv_model* m, int n) {
     s.tree = take(4 * 16 * 4);  // parent, token, argmax, path for up to 16 nodes
     s.tinfo = take(4 * kTreeInfoInts);  // depths and ancestor lists of the step's tree
     s.wcounter = take(4);
+    s.arrivals = take(4 * kMaxNodes);  // per node: chunk workgroups of the attention that have finished
     size_t lin = 0;
     for (size_t Nk : {QKV, H, 2 * I}) lin = std::max(lin, w4a8_linear_workspace(n, (int)Nk, (int)H));
     lin = std::max(lin, w4a8_linear_workspace(n, (int)H, (int)A));
@@ -743,6 +1131,54 @@ static int launch_attn_hd(bool vreg, bool swz, dim3 grid, size_t lds, hipStream_
     hipLaunchKernelGGL(kernel, grid, dim3(kFwdThreads), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh,
                        nkv, scale, part, nchunk_max, ctrl);
     return launch_status();
+}
+
+// The grouped attention with the fused merge takes at most kGrpMaxHeads query
+// heads per KV head and an attention row of at most kGrpMaxRow values.
+static bool attn_grouped_ok(const specv_model* m) {
+    return m->n_heads / m->n_kv_heads <= kGrpMaxHeads && m->n_heads * m->head_dim <= kGrpMaxRow &&
+           (m->kv_capacity + kAttnChunk - 1) / kAttnChunk <= kGrpMaxChunks;
+}
+
+inline size_t attn_group_lds_bytes(int hd, int nh, int nchunk_max) {  // key and value rows, or the merge
+    return std::max(2 * attn_lds_bytes(hd, false, attn_swizzle_ok(hd)), merge_lds_bytes(nh, nchunk_max));
+}
+
+template <int HD>
+static int launch_attn_group_hd(dim3 grid, size_t lds, hipStream_t s, const float* qkv, const float* cos_t,
+                                const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
+                                int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
+                                uint32_t* arrivals, int8_t* xq, float* xs, const specv_ctrl* ctrl) {
+    auto kernel = &attn_group_kernel<HD>;
+    static size_t enabled = 64 * 1024;  // dynamic LDS above 64 KB is enabled per kernel
+    if (lds > enabled) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess) {
+            (void)hipGetLastError();
+            return SPECV_E_HIP;
+        }
+        enabled = lds;
+    }
+    hipLaunchKernelGGL(kernel, grid, dim3(kGrpThreads), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh,
+                       nkv, scale, part, nchunk_max, arrivals, xq, xs, ctrl);
+    return launch_status();
+}
+
+static int launch_attn_group(int hd, dim3 grid, hipStream_t s, const float* qkv, const float* cos_t,
+                             const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
+                             int cap, int nh, int nkv, float scale, float* part, int nchunk_max, uint32_t* arrivals,
+                             int8_t* xq, float* xs, const specv_ctrl* ctrl) {
+    const size_t lds = attn_group_lds_bytes(hd, nh, nchunk_max);
+    switch (hd) {
+#define SPECV_ATTN(HDV)                                                                                             \
+    case HDV:                                                                                                       \
+        return launch_attn_group_hd<HDV>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv, scale, \
+                                         part, nchunk_max, arrivals, xq, xs, ctrl);
+        SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
+        SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
+#undef SPECV_ATTN
+        default: return SPECV_E_SHAPE;
+    }
 }
 
 static int launch_attn_chunk(int hd, dim3 grid, hipStream_t s, const float* qkv, const float* cos_t,
@@ -806,6 +1242,8 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
         return w4a8_linear_T(wq, ws_, xq, xs, y, n, N, H, lin, linb, s);
     };
     const bool fuse_silu = (int64_t)n * I <= kSiluFuseMax && linear_fused_supported(kProdSilu, n, I);
+    const bool grouped = attn_grouped_ok(m);
+    uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + lay.arrivals);
     for (int l = 0; l < m->n_layers; l++) {
         // each layer's matrices in the packed tile layout, one after another
         const uint8_t* wqkv = m->w_qkv + (size_t)l * packed_weight_bytes(QKV, H);
@@ -819,13 +1257,19 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
 
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
                               true));
-        SPECV_TRY(launch_attn_chunk(hd, dim3(nh, n, lay.nchunk_max), s, qkv,
-                                    m->rope_cos, m->rope_sin, m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale,
-                                    attn, lay.nchunk_max, ctrl));
-        hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kRowThreads),
-                           merge_lds_bytes(nh, lay.nchunk_max), s, attn, tinfo, nh, hd, lay.nchunk_max, xq, xs,
-                           ctrl);
-        SPECV_TRY(launch_status());
+        if (grouped) {  // chunks of every head of a KV group, the merge by the last workgroup of each node
+            SPECV_TRY(launch_attn_group(hd, dim3(nkv, n, lay.nchunk_max), s, qkv, m->rope_cos, m->rope_sin,
+                                        m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
+                                        arrivals, xq, xs, ctrl));
+        } else {
+            SPECV_TRY(launch_attn_chunk(hd, dim3(nh, n, lay.nchunk_max), s, qkv, m->rope_cos, m->rope_sin,
+                                        m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
+                                        ctrl));
+            hipLaunchKernelGGL(attn_merge_quant_kernel, dim3(n), dim3(kRowThreads),
+                               merge_lds_bytes(nh, lay.nchunk_max), s, attn, tinfo, nh, hd, lay.nchunk_max, xq, xs,
+                               ctrl);
+            SPECV_TRY(launch_status());
+        }
         SPECV_TRY(w4a8_linear_T(wo, so, xq, xs, delta, n, H, A, lin, linb, s));
         SPECV_TRY(norm_linear(delta, m->norm_mlp + (size_t)l * H, wgu, sgu, gu, nullptr, 2 * I, true));
         if (fuse_silu) {

@@ -9,7 +9,7 @@ namespace specv {
 
 // Byte offsets of one step's buffers inside the caller's workspace.
 struct StepLayout {
-    size_t h, h2, delta, xq, xs, qkv, attn, gu, logits, argmax_part, tree, tinfo, wcounter, linear;
+    size_t h, h2, delta, xq, xs, qkv, attn, gu, logits, argmax_part, tree, tinfo, wcounter, arrivals, linear;
     size_t linear_bytes, total;
     int nchunk_max;
 };

@@ -31,12 +31,18 @@ def sv():
 # intermediate of 2176 the fused SiLU up to 4 tokens.
 WIDE = dict(n_layers=2, hidden=1280, n_heads=10, n_kv_heads=2, head_dim=128, inter=2176, vocab=1000,
             eps=1e-6, max_pos=640)
+# Head dim 128 with an attention row of 1024 values: the grouped attention
+# (every head of a KV group in one workgroup, merge fused) over two column
+# blocks; the wide configuration's 1280-value row takes the per-head kernel
+# and the separate merge.
+HD128 = dict(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128, inter=1024, vocab=700,
+             eps=1e-6, max_pos=640)
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=3)
 def model_pair(name):
-    cfg = {"tiny": sg.TINY, "wide": WIDE}.get(name, sg.QWEN05)
-    arrays = sg.model_case({"tiny": 7, "wide": 11}.get(name, 3), cfg)
+    cfg = {"tiny": sg.TINY, "wide": WIDE, "hd128": HD128}.get(name, sg.QWEN05)
+    arrays = sg.model_case({"tiny": 7, "wide": 11, "hd128": 13}.get(name, 3), cfg)
     c, s = oracle.rope_table(cfg["max_pos"], cfg["head_dim"], 1e6)
     arrays = dict(arrays, rope_cos=c, rope_sin=s)
     return cfg, arrays, oracle.Model(arrays, cfg)
@@ -110,6 +116,12 @@ def test_tiny_tree_step_parity(sv, seed, N, L):
 def test_wide_tree_step_parity(sv, seed, N, L):
     case(f"wide (hidden 1280) tree step seed={seed} N={N} L={L}")
     compare_step(sv, "wide", seed, N, L)
+
+
+@pytest.mark.parametrize("seed,N,L", [(51, 1, 300), (52, 5, 256), (53, 16, 520), (54, 8, 0)])
+def test_hd128_tree_step_parity(sv, seed, N, L):
+    case(f"head dim 128 tree step seed={seed} N={N} L={L}")
+    compare_step(sv, "hd128", seed, N, L)
 
 
 def test_tiny_unplanted_tree(sv):
