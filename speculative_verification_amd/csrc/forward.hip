@@ -585,7 +585,11 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
 // widened once for the group's heads ([P1] Small-Batch Verification
 // Kernels). The workgroup's 1024 threads form four sets of 256; set k takes
 // the group's heads k, k + 4 (at most two), so the four SIMDs of a CU share
-// the heads' arithmetic. In a set, thread t owns position t of the chunk: its
+// the heads' arithmetic. With nsplit = 2 (small trees, where the grid is
+// short of workgroups) two workgroups share a (KV head, node, chunk), the
+// first taking heads 0..3 and the second the rest, one head per set: the
+// rows are read twice (the second time mostly from L2) and each set's chain
+// of dependent arithmetic is halved. In a set, thread t owns position t of the chunk: its
 // key row meets each of its heads' queries, s_{h,t} = R16_d(q_d * K_td) *
 // scale; each head's chunk maximum is taken over the set's waves (order-free);
 // e_{h,t} = E(s_{h,t} - m_h). For the value sums, lane s of the set's 16-lane
@@ -604,20 +608,22 @@ constexpr int kGrpMaxHeads = 8;                        // query heads per KV hea
 constexpr int kGrpSetHeads = kGrpMaxHeads / kGrpSets;  // heads per set
 constexpr int kGrpMaxRow = kGrpThreads;                // attention row (heads x head dim) its merge takes
 constexpr int kGrpMaxChunks = 32;                      // chunks per node its merge takes
+constexpr int kGrpSplitMaxNodes = 4;                   // trees up to this size split a group's heads
 
 template <int HD>
 __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
-    int nh, int nkv, float scale, float* __restrict__ part, int nchunk_max, uint32_t* __restrict__ arrivals,
-    int8_t* __restrict__ xq, float* __restrict__ xs, const specv_ctrl* ctrl) {
+    int nh, int nkv, int nsplit, float scale, float* __restrict__ part, int nchunk_max,
+    uint32_t* __restrict__ arrivals, int8_t* __restrict__ xq, float* __restrict__ xs, const specv_ctrl* ctrl) {
     constexpr int HALF = HD / 2;
     constexpr int NB = (HD + 63) / 64;
     constexpr bool SWZ = attn_swizzle_ok(HD);
     constexpr int VS = attn_vstride(HD, SWZ);
     constexpr bool KF = HD <= 64;  // key row widened to fp32 registers once
     constexpr int SH = kGrpSetHeads;
-    const int g = blockIdx.x, i = blockIdx.y, c = blockIdx.z, tid = threadIdx.x;
+    const int g = blockIdx.x / nsplit, sp = blockIdx.x - g * nsplit;
+    const int i = blockIdx.y, c = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int set = __builtin_amdgcn_readfirstlane(tid >> 8);  // uniform in a wave
     const int t8 = tid & 255;                                  // position / lane of the set
@@ -637,6 +643,8 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     if (j0 >= len) return;
     const int cnt = len - j0 < kAttnChunk ? len - j0 : kAttnChunk;
     const int G = nh / nkv;
+    const int hps = (G + nsplit * kGrpSets - 1) / (nsplit * kGrpSets);  // heads per set (1 or 2)
+    const int hbase = sp * kGrpSets * hps;                             // this workgroup's first head
     const int QKV = (nh + 2 * nkv) * HD;
     __shared__ int anc[kMaxNodes];
     __shared__ __attribute__((aligned(16))) uint16_t tk[kMaxNodes][HD];
@@ -678,7 +686,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
         const float* src = qkv + (size_t)i * QKV + (g * G + h) * HD;
         rope_pair(src[d], src[d + HALF], cos_t[tp], sin_t[tp], qs[h][d], qs[h][d + HALF]);
     }
-    if (c == 0 && tid >= kGrpThreads - HALF) {  // node i's key and value rows to the caches
+    if (c == 0 && sp == 0 && tid >= kGrpThreads - HALF) {  // node i's key and value rows to the caches
         const int d = tid - (kGrpThreads - HALF);
         const size_t tp = (size_t)(L + depth) * HALF + d;
         const float* ks = qkv + (size_t)i * QKV + (nh + g) * HD;
@@ -737,7 +745,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
         for (int t = 0; t < CH; t++)
             kr[t] = *reinterpret_cast<const v4i*>(Ks + t8 * VS + 8 * (SWZ ? t ^ ((t8 >> 1) & 7) : t));
     }
-    // scores of this thread's position for the set's heads h = set + 4u
+    // scores of this thread's position for the set's heads h = hbase + set + 4u
     float sc[SH];
     {
         float kf[KF ? HD : 1];
@@ -753,9 +761,9 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
         }
 #pragma unroll
         for (int u = 0; u < SH; u++) {
-            const int h = set + kGrpSets * u;
+            const int h = hbase + set + kGrpSets * u;
             sc[u] = -__builtin_inff();
-            if (h >= G || !live) continue;
+            if (u >= hps || h >= G || !live) continue;
             float slot[16];
 #pragma unroll
             for (int r = 0; r < 16; r++) slot[r] = 0.0f;
@@ -798,11 +806,11 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     float mh[SH];
 #pragma unroll
     for (int u = 0; u < SH; u++) {
-        const int h = set + kGrpSets * u;
+        const int h = hbase + set + kGrpSets * u;
         const int w0 = 4 * set;
         mh[u] = fmaxf(fmaxf(wmax[w0][u], wmax[w0 + 1][u]), fmaxf(wmax[w0 + 2][u], wmax[w0 + 3][u]));
         const int es = t8 & 15, ek = t8 >> 4;
-        if (h < G) Et[h][es][4 * ((ek >> 2) ^ ((es >> 2) & 3)) + (ek & 3)] = live ? det_exp(sc[u] - mh[u]) : 0.0f;
+        if (u < hps && h < G) Et[h][es][4 * ((ek >> 2) ^ ((es >> 2) & 3)) + (ek & 3)] = live ? det_exp(sc[u] - mh[u]) : 0.0f;
     }
     __syncthreads();
 
@@ -832,8 +840,8 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
         }
 #pragma unroll
         for (int u = 0; u < SH; u++) {
-            const int h = set + kGrpSets * u;
-            if (h >= G) continue;
+            const int h = hbase + set + kGrpSets * u;
+            if (u >= hps || h >= G) continue;
             float e[16];
 #pragma unroll
             for (int k4 = 0; k4 < 4; k4++) {
@@ -876,7 +884,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     const int nch = (len + kAttnChunk - 1) / kAttnChunk;
     if (tid == 0) {
         const uint32_t before = __hip_atomic_fetch_add(&arrivals[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = before + 1 == (uint32_t)(nkv * nch);
+        const bool last = before + 1 == (uint32_t)(nkv * nsplit * nch);
         if (last) __hip_atomic_store(&arrivals[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last;
     }
@@ -1147,7 +1155,7 @@ inline size_t attn_group_lds_bytes(int hd, int nh, int nchunk_max) {  // key and
 template <int HD>
 static int launch_attn_group_hd(dim3 grid, size_t lds, hipStream_t s, const float* qkv, const float* cos_t,
                                 const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
-                                int cap, int nh, int nkv, float scale, float* part, int nchunk_max,
+                                int cap, int nh, int nkv, int nsplit, float scale, float* part, int nchunk_max,
                                 uint32_t* arrivals, int8_t* xq, float* xs, const specv_ctrl* ctrl) {
     auto kernel = &attn_group_kernel<HD>;
     static size_t enabled = 64 * 1024;  // dynamic LDS above 64 KB is enabled per kernel
@@ -1160,11 +1168,11 @@ static int launch_attn_group_hd(dim3 grid, size_t lds, hipStream_t s, const floa
         enabled = lds;
     }
     hipLaunchKernelGGL(kernel, grid, dim3(kGrpThreads), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh,
-                       nkv, scale, part, nchunk_max, arrivals, xq, xs, ctrl);
+                       nkv, nsplit, scale, part, nchunk_max, arrivals, xq, xs, ctrl);
     return launch_status();
 }
 
-static int launch_attn_group(int hd, dim3 grid, hipStream_t s, const float* qkv, const float* cos_t,
+static int launch_attn_group(int hd, int nsplit, dim3 grid, hipStream_t s, const float* qkv, const float* cos_t,
                              const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
                              int cap, int nh, int nkv, float scale, float* part, int nchunk_max, uint32_t* arrivals,
                              int8_t* xq, float* xs, const specv_ctrl* ctrl) {
@@ -1172,8 +1180,8 @@ static int launch_attn_group(int hd, dim3 grid, hipStream_t s, const float* qkv,
     switch (hd) {
 #define SPECV_ATTN(HDV)                                                                                             \
     case HDV:                                                                                                       \
-        return launch_attn_group_hd<HDV>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv, scale, \
-                                         part, nchunk_max, arrivals, xq, xs, ctrl);
+        return launch_attn_group_hd<HDV>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv, nsplit, \
+                                         scale, part, nchunk_max, arrivals, xq, xs, ctrl);
         SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
         SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
 #undef SPECV_ATTN
@@ -1243,6 +1251,8 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     };
     const bool fuse_silu = (int64_t)n * I <= kSiluFuseMax && linear_fused_supported(kProdSilu, n, I);
     const bool grouped = attn_grouped_ok(m);
+    // small trees leave the grid short of workgroups: split each group's heads over two
+    const int nsplit = nh / nkv > kGrpSets && n <= kGrpSplitMaxNodes ? 2 : 1;
     uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + lay.arrivals);
     for (int l = 0; l < m->n_layers; l++) {
         // each layer's matrices in the packed tile layout, one after another
@@ -1258,7 +1268,7 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
                               true));
         if (grouped) {  // chunks of every head of a KV group, the merge by the last workgroup of each node
-            SPECV_TRY(launch_attn_group(hd, dim3(nkv, n, lay.nchunk_max), s, qkv, m->rope_cos, m->rope_sin,
+            SPECV_TRY(launch_attn_group(hd, nsplit, dim3(nkv * nsplit, n, lay.nchunk_max), s, qkv, m->rope_cos, m->rope_sin,
                                         m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
                                         arrivals, xq, xs, ctrl));
         } else {

@@ -37,12 +37,20 @@ WIDE = dict(n_layers=2, hidden=1280, n_heads=10, n_kv_heads=2, head_dim=128, int
 # and the separate merge.
 HD128 = dict(n_layers=2, hidden=512, n_heads=8, n_kv_heads=2, head_dim=128, inter=1024, vocab=700,
              eps=1e-6, max_pos=640)
+# Groups of 7 and 8 query heads per KV head: trees of up to four nodes split
+# a group's heads over two workgroups (heads 0..3 and the rest), larger
+# trees keep them in one.
+G7 = dict(n_layers=2, hidden=896, n_heads=14, n_kv_heads=2, head_dim=64, inter=1024, vocab=1000,
+          eps=1e-6, max_pos=640)
+G8 = dict(n_layers=2, hidden=512, n_heads=8, n_kv_heads=1, head_dim=128, inter=768, vocab=900,
+          eps=1e-6, max_pos=640)
+CFGS = {"tiny": (sg.TINY, 7), "wide": (WIDE, 11), "hd128": (HD128, 13), "g7": (G7, 17), "g8": (G8, 19)}
 
 
-@functools.lru_cache(maxsize=3)
+@functools.lru_cache(maxsize=4)
 def model_pair(name):
-    cfg = {"tiny": sg.TINY, "wide": WIDE, "hd128": HD128}.get(name, sg.QWEN05)
-    arrays = sg.model_case({"tiny": 7, "wide": 11, "hd128": 13}.get(name, 3), cfg)
+    cfg, seed = CFGS.get(name, (sg.QWEN05, 3))
+    arrays = sg.model_case(seed, cfg)
     c, s = oracle.rope_table(cfg["max_pos"], cfg["head_dim"], 1e6)
     arrays = dict(arrays, rope_cos=c, rope_sin=s)
     return cfg, arrays, oracle.Model(arrays, cfg)
@@ -124,6 +132,14 @@ def test_hd128_tree_step_parity(sv, seed, N, L):
     compare_step(sv, "hd128", seed, N, L)
 
 
+@pytest.mark.parametrize("name,seed,N,L", [("g7", 61, 1, 300), ("g7", 62, 2, 520), ("g7", 63, 3, 255),
+                                            ("g7", 64, 8, 0), ("g8", 65, 1, 256), ("g8", 66, 2, 511),
+                                            ("g8", 67, 5, 40)])
+def test_grouped_head_split_parity(sv, name, seed, N, L):
+    case(f"{name} tree step seed={seed} N={N} L={L}")
+    compare_step(sv, name, seed, N, L)
+
+
 def test_tiny_unplanted_tree(sv):
     case("tiny tree step, random drafts")
     compare_step(sv, "tiny", 12, 8, 130, plant=False)
@@ -137,7 +153,8 @@ def test_qwen05_tree_step_parity(sv):
     assert m >= 1
 
 
-@pytest.mark.parametrize("name,seed,N,L", [("tiny", 31, 8, 200), ("tiny", 32, 1, 50), ("qwen", 23, 8, 1024)])
+@pytest.mark.parametrize("name,seed,N,L", [("tiny", 31, 8, 200), ("tiny", 32, 1, 50), ("qwen", 23, 8, 1024),
+                                            ("qwen", 24, 1, 1024), ("qwen", 25, 2, 1100)])
 def test_tree_step_without_logits(sv, name, seed, N, L):
     """With no logits buffer the step writes no logits (the lm_head reduces
     to each node's argmax in its epilogue) and gives the oracle's
