@@ -309,7 +309,11 @@ int kv_compact(uint16_t* k_cache, uint16_t* v_cache, int32_t n_layers, int32_t n
  * the forward pass over the tree, in which each node attends to the
  * committed cache and to its ancestors; Small-Batch Verification Kernels:
  * chunked attention with a merge pass, query heads sharing a KV head read
- * each key and value once). Host struct of device pointers; per-layer
+ * each key and value once). The last holds for groups of at most 8 query
+ * heads with n_heads*head_dim <= 1024 and at most 32 chunks of 256 cache
+ * rows; other shapes run one attention workgroup per query head, whose
+ * repeated reads of a group's rows are served by the L2 cache. Results are
+ * the same bits either way. Host struct of device pointers; per-layer
  * tensors are stacked along a leading layer axis. With
  * QKV = (n_heads + 2*n_kv_heads)*head_dim, A = n_heads*head_dim,
  * H = hidden, I = inter, V = vocab. Every matrix is in the packed tile
