@@ -30,6 +30,10 @@ FLAGS = [
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
+# extra compile options, e.g. SPECV_HIPCC_FLAGS=-DSPECV_DOT4_MAX_T=8 (the
+# v_dot4 integer dots for token buckets up to 8, for an A/B against the
+# matrix core)
+FLAGS += os.environ.get("SPECV_HIPCC_FLAGS", "").split()
 
 
 def sources() -> list[str]:

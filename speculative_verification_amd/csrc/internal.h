@@ -47,6 +47,11 @@ int validate_model(const specv_model* m);
 // argmax epilogue (amax: [T][chunks] partials) needs linear_argmax_supported.
 int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
                    int T, int N, int K, void* workspace, hipStream_t s);
+// The 32-token bucket with dense matrix products (17..32 tokens, per-token
+// scales, at most 10 x 16 groups per row), in csrc/linear_dense.hip.
+bool linear_dense_supported(int T, int K);
+int linear_dense_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, int T,
+                         int N, int K, hipStream_t s);
 bool linear_argmax_supported(int T, int N, int K);
 int linear_argmax_chunks(int T, int N, int K);
 

@@ -74,6 +74,27 @@ namespace specv {
 #define SPECV_STREAM_WGS_PER_CU 2
 #endif
 
+// Token buckets up to this size take their integer dots from v_dot4_i32_i8
+// instead of the matrix core (0: none). Measured on MI355X with rocprofv3
+// on the 8B step's shapes: at T = 1 the two are within noise (965.5 against
+// 981.1 us over a step's 129 launches), at T = 8 v_dot4 costs 1.26-1.80x
+// per launch, so every bucket uses the matrix core.
+#ifndef SPECV_DOT4_MAX_T
+#define SPECV_DOT4_MAX_T 0
+#endif
+
+// The lane's 16 bytes of nibbles (32 inputs of one group) as int8 values
+// 16q: b[0] holds inputs 0..15, b[1] inputs 16..31, each 8-input chunk in
+// even-then-odd order (bytes 0, 2, 4, 6, then 1, 3, 5, 7).
+__device__ __forceinline__ void decode_nibbles(const v4i w, v4i (&b)[2]) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const unsigned W = (unsigned)w[c];
+        b[c >> 1][2 * (c & 1)] = (int)(((W << 4) ^ 0x80808080u) & 0xF0F0F0F0u);  // inputs 0, 2, 4, 6
+        b[c >> 1][2 * (c & 1) + 1] = (int)((W ^ 0x80808080u) & 0xF0F0F0F0u);     // inputs 1, 3, 5, 7
+    }
+}
+
 // Integer dots of one group per slot of a quad (see the header): w is the
 // lane's 16 bytes of nibbles (32 inputs of its slot's group, row l%16); a0
 // and a1 are the lane's A operands for inputs 0..15 and 16..31 of each token
@@ -81,12 +102,7 @@ namespace specv {
 template <int TT>
 __device__ __forceinline__ void quad_dots(const v4i w, const v4i (&a0)[TT], const v4i (&a1)[TT], v4i (&d)[TT]) {
     v4i b[2];
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-        const unsigned W = (unsigned)w[c];
-        b[c >> 1][2 * (c & 1)] = (int)(((W << 4) ^ 0x80808080u) & 0xF0F0F0F0u);  // inputs 0, 2, 4, 6
-        b[c >> 1][2 * (c & 1) + 1] = (int)((W ^ 0x80808080u) & 0xF0F0F0F0u);     // inputs 1, 3, 5, 7
-    }
+    decode_nibbles(w, b);
 #pragma unroll
     for (int tt = 0; tt < TT; tt++) d[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[tt], b[0], v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
@@ -557,33 +573,51 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
         abase[tt] = ok ? (t * JA * 4 + wave) * 128 + h * 32 : zero_off;
         astep[tt] = ok && !RELOAD ? 512 : 0;
     }
+    // dv[t]: 16 x the exact dot of row r, group 16j + 4 wave + q, token t
     auto compute = [&](const SStage<T, BS>& st, int j, float (&acc)[T]) {
-        v4i a0[TT], a1[TT], d[TT];
+        int dv[T];
+        if constexpr (T <= SPECV_DOT4_MAX_T) {
+            // each lane dots its own row's group with every token's 32 codes
+            // (the lanes of a slot read the same LDS words)
+            v4i b[2];
+            decode_nibbles(st.w, b);
 #pragma unroll
-        for (int tt = 0; tt < TT; tt++) {
-            const int off = abase[tt] + j * astep[tt];
-            a0[tt] = *reinterpret_cast<const v4i*>(act + off);
-            a1[tt] = *reinterpret_cast<const v4i*>(act + off + 16);
+            for (int t = 0; t < T; t++) {
+                const int off = ((t * JA + (RELOAD ? 0 : j)) * 4 + wave) * 128 + 32 * q;
+                const v4i x0 = *reinterpret_cast<const v4i*>(act + off);
+                const v4i x1 = *reinterpret_cast<const v4i*>(act + off + 16);
+                int a = 0;
+#pragma unroll
+                for (int e = 0; e < 4; e++) a = __builtin_amdgcn_sdot4(b[0][e], x0[e], a, false);
+#pragma unroll
+                for (int e = 0; e < 4; e++) a = __builtin_amdgcn_sdot4(b[1][e], x1[e], a, false);
+                dv[t] = a;
+            }
+        } else {
+            v4i a0[TT], a1[TT], d[TT];
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++) {
+                const int off = abase[tt] + j * astep[tt];
+                a0[tt] = *reinterpret_cast<const v4i*>(act + off);
+                a1[tt] = *reinterpret_cast<const v4i*>(act + off + 16);
+            }
+            quad_dots<TT>(st.w, a0, a1, d);
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++)
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    if (4 * tt + u < T) dv[4 * tt + u] = d[tt][u];
         }
-        quad_dots<TT>(st.w, a0, a1, d);
         if constexpr (BS) {
             // s = f32(scale) * xs[t][g], then s * f32(d), with d = 16d >> 4 exactly
             const float ws32 = (float)__builtin_bit_cast(_Float16, st.s);
             const float* xb = xbl + (((RELOAD ? 0 : j) * 4 + wave) * 4 + q) * T;
 #pragma unroll
-            for (int tt = 0; tt < TT; tt++)
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const int t = 4 * tt + u;
-                    if (t < T) acc[t] = acc[t] + (ws32 * xb[t]) * (float)(d[tt][u] >> 4);
-                }
+            for (int t = 0; t < T; t++) acc[t] = acc[t] + (ws32 * xb[t]) * (float)(dv[t] >> 4);
         } else {
             const float s16 = (float)__builtin_bit_cast(_Float16, st.s) * 0.0625f;
 #pragma unroll
-            for (int tt = 0; tt < TT; tt++)
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    if (4 * tt + u < T) acc[4 * tt + u] = acc[4 * tt + u] + s16 * (float)d[tt][u];
+            for (int t = 0; t < T; t++) acc[t] = acc[t] + s16 * (float)dv[t];
         }
     };
 
@@ -908,9 +942,12 @@ static int linear_dispatch(const uint8_t* wq, const uint16_t* ws, const int8_t* 
         SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
 #undef SPECV_CASE
         default:
-            if (T > 16 && T <= 32)  // the 32-token bucket
+            if (T > 16 && T <= 32) {  // the 32-token bucket: dense products where they apply
+                if (!bs && !amax && linear_dense_supported(T, K))
+                    return linear_dense_enqueue(wq, ws, xq, xs, y, T, N, K, s);
                 return bs ? launch_T<32, true>(wq, ws, xq, xs, y, amax, T, N, K, s)
                           : launch_T<32, false>(wq, ws, xq, xs, y, amax, T, N, K, s);
+            }
             return SPECV_E_SHAPE;
     }
 }

@@ -138,8 +138,13 @@ def test_quantize_misaligned_rows(sv):
                                    (3, 16400, 96), (8, 16385, 544), (5, 65601, 64), (16, 65600, 160),
                                    # several 16-row tiles per workgroup, ragged rows and groups
                                    (8, 4100, 4864), (16, 4097, 8192), (1, 4111, 96), (2, 8211, 1056),
-                                   # the 32-token bucket (17..32 tokens)
-                                   (20, 33, 896), (32, 100, 544), (25, 4100, 96), (17, 16, 32)])
+                                   # the 32-token bucket (17..32 tokens): dense products with 1, 2, 3
+                                   # (padded to 4), 8 (ragged groups), 9 (padded to 10) and 10
+                                   # iterations per tile, more tiles than workgroups, and past 10
+                                   # iterations the block-diagonal form
+                                   (20, 33, 896), (32, 100, 544), (25, 4100, 96), (17, 16, 32),
+                                   (18, 50, 1536), (31, 300, 4352), (30, 77, 5120), (32, 4117, 4064),
+                                   (24, 70, 5152), (29, 8211, 2048), (32, 17, 4096)])
 def test_linear_parity_ragged(sv, T, N, K):
     case(f"linear ragged T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(50 + T, T, N, K)
@@ -183,7 +188,7 @@ def test_linear_qwen_shapes(sv, name, T):
                         f"{name} T={T} seed={seed} sampled")
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 8])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 17, 32])
 @pytest.mark.parametrize("name", list(LLAMA))
 def test_linear_llama_shapes_sampled(sv, name, T):
     N, K = LLAMA[name]
