@@ -207,8 +207,10 @@ class Model:
         self.cap = self.L0 + 4096
         self.kc = torch.zeros((m["layers"], m["kv_heads"], self.cap, m["head_dim"]), dtype=torch.int16, device=dev)
         self.vc = torch.zeros_like(self.kc)
-        self.ws_lmarg = torch.empty(int(sv.LIB.w4a8_linear_argmax_workspace(Tmax, m["vocab"], m["hidden"])),
+        self.ws_lmarg = torch.empty(int(sv.LIB.w4a8_linear_argmax_workspace(min(Tmax, 16), m["vocab"],
+                                                                            m["hidden"])),
                                     dtype=torch.uint8, device=dev)
+        self.logits = None  # [T][vocab] of the prefill bucket, allocated on first use
         self.argmax = torch.empty(16, dtype=torch.int32, device=dev)
         self.path = torch.zeros(16, dtype=torch.int32, device=dev)
         self.stats = torch.zeros(3, dtype=torch.int32, device=dev)
@@ -279,6 +281,39 @@ class Model:
         sv.tree_accept(self.argmax[:T], self.parent, self.token, self.ctrl, path=self.path, stats=self.stats,
                        ring=self.ring)
         sv.kv_compact(self.kc, self.vc, self.path, self.ctrl)
+
+    def prefill_step(self, T, copy=0, events=None):
+        """The step's linears at T tokens (the prefill bucket, T up to 32):
+        the quantisation of every input row, the 128 layer linears and the
+        lm_head writing its logits (no tree: acceptance and the argmax
+        epilogue take at most 16 nodes)."""
+        sv, torch, m = self.sv, self.torch, self.m
+        layers, lm = self.copies[copy]
+        self.prepare_acts(T)
+        if self.logits is None or self.logits.shape[0] < T:
+            self.logits = torch.empty((T, m["vocab"]), dtype=torch.float32, device="cuda")
+        for K, x in self.xa.items():
+            n = x.shape[0]
+            sv.quantize_act(x.view(n * T, K), self.xqa[K].view(n * T, K), self.xsa[K].view(n * T))
+
+        def lin(name, w, K, N, y, i):
+            xq, xs = self.xqa[K][i], self.xsa[K][i]
+            if events is not None:
+                e0, e1 = timing_events(torch)
+                sv.check("specv_time_next_linear", sv.LIB.specv_time_next_linear(e0.cuda_event, e1.cuda_event))
+            sv.linear(w, xq, xs, y)
+            if events is not None:
+                events.append((e0, e1, linear_bytes(T, N, K), name))
+
+        for l, lay in enumerate(layers):
+            for nm, N, K in layer_linears(m):
+                lin(nm, lay[nm], K, N, self.y[nm][: T * N].view(T, N), self.in_index[l][nm])
+        lin("lm_head", lm, m["hidden"], m["vocab"], self.logits[:T], self.lm_index)
+
+    def prefill_bytes(self, T):
+        m = self.m
+        b = sum(m["layers"] * (linear_bytes(T, N, K) + quant_bytes(T, K)) for _, N, K in layer_linears(m))
+        return b + linear_bytes(T, m["vocab"], m["hidden"]) + quant_bytes(T, m["hidden"])
 
     def lm_chunks(self, T):
         """(value, index) pairs per token of the fused lm_head: one per workgroup."""
@@ -365,6 +400,51 @@ def run_T(model, T, steps, warmup, torch):
     replay_ok = replay_ok and snapshot().view(torch.int32).equal(eager_out.view(torch.int32))
     del graphs
     return ms, m_acc, replay_ok, float(np.median(runs))
+
+
+def prefill_bench(model, T, steps, torch, reps=3):
+    """The prefill bucket on the same weights: graph replays of
+    prefill_step at T tokens (µs, GB/s of its algorithmic bytes), and the
+    mean per-launch time of each shape from kernel-attached events in eager
+    steps."""
+    model.prefill_step(T)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        model.prefill_step(T)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del g
+    durs, names = [], []
+    for r in range(reps):
+        ev = []
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(200_000_000)
+        model.prefill_step(T, events=ev)
+        torch.cuda.synchronize()
+        for a, b, nb, nm in ev:
+            durs.append(a.elapsed_time(b) * 1e3)
+            names.append(nm)
+    by_shape = {}
+    for nm in dict.fromkeys(names):
+        v = [d for d, n in zip(durs, names) if n == nm]
+        by_shape[nm] = round(float(np.mean(v)), 2)
+    nb = model.prefill_bytes(T)
+    out = {"workload": f"the same {model.m['layers']}-layer set at T={T} tokens (the dense 32-token bucket; down, "
+                       f"K = 14336, runs the block-diagonal form): quantisation + 128 layer linears + lm_head "
+                       f"writing logits, HIP-graph replay",
+           "T": T, "us": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
+           "pct_hbm_peak": round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": nb, "by_shape_us": by_shape}
+    print(f"[bench] prefill: {out}", file=sys.stderr, flush=True)
+    return out
 
 
 def roofline_linear(model, T, reps, torch):
@@ -791,9 +871,13 @@ def main():
                     help="skip the plain streaming-read ceilings")
     ap.add_argument("--small-set", default="qwen2.5-0.5b",
                     help="second shape set whose verify step is timed at T = 1, 2, 4, 8 (empty: skip)")
+    ap.add_argument("--prefill-T", type=int, default=32,
+                    help="token count of the prefill-bucket measurement on the same weights (0: skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
+    if args.prefill_T > 32:
+        ap.error("--prefill-T takes at most 32 tokens (the largest bucket)")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the verification step of one request runs on one device).", file=sys.stderr)
@@ -813,7 +897,7 @@ def main():
         del a, b
 
     Ts = sorted({args.T, *[int(t) for t in args.sweep.split(",") if t]})
-    model = Model(args.workload, torch, sv, sg, max(Ts))
+    model = Model(args.workload, torch, sv, sg, max(Ts + [args.prefill_T]))
     print(f"[bench] {args.workload}: weights {model.weight_bytes_total()/1e9:.3f} GB x {len(model.copies)} "
           f"copies, generated in {model.gen_s:.1f} s", file=sys.stderr, flush=True)
 
@@ -828,6 +912,7 @@ def main():
               f"replay exact={ok}", file=sys.stderr, flush=True)
 
     ach, avg_s, avg_b, nlaunch, by_shape = roofline_linear(model, args.T, args.roofline_reps, torch)
+    prefill = prefill_bench(model, args.prefill_T, max(5, args.steps // 2), torch) if args.prefill_T > 16 else None
     small = None
     if args.small_set and args.small_set != args.workload:
         small = linear_set(args.small_set, [1, 2, 4, 8], max(5, args.steps // 2), args.warmup,
@@ -900,6 +985,7 @@ def main():
                      "avg_launch_bytes": round(avg_b), "launches_per_step": nlaunch,
                      "by_shape": by_shape},
         "ceilings": ceil,
+        "prefill": prefill,
         "small_set": small,
         "config1": config1,
         "decoder": decoder,

@@ -50,6 +50,9 @@ int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, cons
 // The 32-token bucket with dense matrix products (17..32 tokens, per-token
 // scales, at most 10 x 16 groups per row), in csrc/linear_dense.hip.
 bool linear_dense_supported(int T, int K);
+// The events set by specv_time_next_linear for the next linear launch, if
+// any (cleared by this call).
+bool take_linear_timing(hipEvent_t* start, hipEvent_t* stop);
 int linear_dense_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, int T,
                          int N, int K, hipStream_t s);
 bool linear_argmax_supported(int T, int N, int K);

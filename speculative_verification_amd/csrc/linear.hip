@@ -753,6 +753,14 @@ inline int stream_grid(int N) {
 // Events for the next linear launch of this host thread (timing diagnostics).
 static thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
 
+bool take_linear_timing(hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_time_start) return false;
+    *start = g_time_start;
+    *stop = g_time_stop;
+    g_time_start = g_time_stop = nullptr;
+    return true;
+}
+
 // Dynamic LDS above 64 KB must be enabled per kernel, up to what the launch
 // needs (the static LDS of the kernel counts towards the limit).
 static int enable_lds(const void* kernel, size_t lds, size_t& enabled) {

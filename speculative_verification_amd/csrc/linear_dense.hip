@@ -36,6 +36,8 @@
 // activation bytes of each 8-input chunk are put in the same order, so the
 // products come out as 16d (exact) and the scale is pre-divided by 16
 // (exact).
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -293,7 +295,12 @@ static int launch_dense(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
     const int NT = (N + 15) / 16;
     const int cus = dense_cus();
     const int grid = NT < cus ? NT : cus;  // one workgroup of 16 waves per CU
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kDenseThreads), kDenseLds, s, wq, ws, xq, N, K, grid, Tr, xs, y);
+    hipEvent_t e0, e1;
+    if (take_linear_timing(&e0, &e1))
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kDenseThreads), kDenseLds, s, e0, e1, 0, wq, ws, xq, N, K,
+                              grid, Tr, xs, y);
+    else
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kDenseThreads), kDenseLds, s, wq, ws, xq, N, K, grid, Tr, xs, y);
     return launch_status();
 }
 
