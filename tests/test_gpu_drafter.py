@@ -2,9 +2,10 @@
 LLM Inference with WebGPU, Draft-Free Drafting From Web Context) against the
 oracle: the tree of cm_draft on random and repetitive streams (one to several
 thousand tokens, so the scan spans many workgroups and a ragged last one), and
-the speculation window drafted by it (spec_window_run_cm) on the tiny decoder,
-compared bit for bit with the oracle's window: control block, statistics,
-ring, and both KV caches. All values are integers, so equality is exact."""
+the speculation window drafted by it (spec_window_run_cm) on the tiny decoder
+and on a two-layer decoder with Qwen2.5-0.5B's attention geometry, compared
+bit for bit with the oracle's window: control block, statistics, ring, and
+both KV caches. All values are integers, so equality is exact."""
 import numpy as np
 import pytest
 import torch
@@ -66,22 +67,26 @@ def test_cm_draft_parity(sv, n, vocab, periodic):
 L0, CAP, ROOT = 30, 400, 5
 
 
-def tiny():
-    cfg = sg.TINY
-    arrays = sg.model_case(7, cfg)
-    c, s = oracle.rope_table(cfg["max_pos"], cfg["head_dim"], 1e6)
-    arrays = dict(arrays, rope_cos=c, rope_sin=s)
-    return cfg, arrays, oracle.Model(arrays, cfg)
+# Qwen2.5-0.5B's attention geometry (14 query heads over 2 KV heads, head
+# dim 64, hidden 896) in two layers: the grouped attention with and without
+# the head split, under the drafter's trees.
+G7 = dict(n_layers=2, hidden=896, n_heads=14, n_kv_heads=2, head_dim=64, inter=1024, vocab=1000,
+          eps=1e-6, max_pos=640)
+_MODELS = {}
 
 
-_TINY = None
+def model_cached(name="tiny"):
+    if name not in _MODELS:
+        cfg, seed = {"tiny": (sg.TINY, 7), "g7": (G7, 17)}[name]
+        arrays = sg.model_case(seed, cfg)
+        c, s = oracle.rope_table(cfg["max_pos"], cfg["head_dim"], 1e6)
+        arrays = dict(arrays, rope_cos=c, rope_sin=s)
+        _MODELS[name] = (cfg, arrays, oracle.Model(arrays, cfg))
+    return _MODELS[name]
 
 
 def tiny_cached():
-    global _TINY
-    if _TINY is None:
-        _TINY = tiny()
-    return _TINY
+    return model_cached("tiny")
 
 
 def greedy_future(om, cfg, seed, n):
@@ -105,8 +110,8 @@ def history(kind, future):
     return h + [ROOT]
 
 
-def run_cm_pair(sv, width, windows, kind, ctx_len=CAP - 16, params=None, ring_cap=1024):
-    cfg, arrays, om = tiny_cached()
+def run_cm_pair(sv, width, windows, kind, ctx_len=CAP - 16, params=None, ring_cap=1024, model="tiny"):
+    cfg, arrays, om = model_cached(model)
     seed = 11
     hist = history(kind, greedy_future(om, cfg, seed, 40))
     kc0, vc0 = sg.kv_prefix(seed, cfg, L0, CAP)
@@ -152,6 +157,16 @@ def test_cm_window_echo(sv, width):
 def test_cm_window_random_history(sv, width):
     case(f"cm window width={width}, random history")
     run_cm_pair(sv, width, (16,), "random", params=(3, 32, 5, [0, 5, 9, 2, 7, 1, 1, 1, 1]))
+
+
+@pytest.mark.parametrize("width", [2, 4, 8])
+def test_cm_window_qwen_attention_geometry(sv, width):
+    """The same windows on a decoder with Qwen2.5-0.5B's attention geometry:
+    trees of 2 and 4 nodes split each KV group's heads over two workgroups,
+    8-node trees do not."""
+    case(f"cm window width={width}, 14 heads over 2 KV heads, hidden 896")
+    stats, _ = run_cm_pair(sv, width, (16, 8), "echo", model="g7")
+    assert sum(m for m, _, _ in stats) > 0
 
 
 def test_cm_window_reaches_context_limit(sv):
