@@ -9,8 +9,8 @@ a Llama-3-8B-shaped model and then accepts on the GPU:
   per layer (32): qkv (6144x4096, q/k/v rows concatenated), o (4096x4096),
   gate_up (28672x4096, gate/up rows concatenated), down (4096x14336);
   then lm_head (128256x4096) with the fused argmax epilogue (the logits are
-  not written), tree acceptance, and KV compaction of
-  the accepted rows (32 layers x 8 KV heads x head_dim 128).
+  not written) and tree acceptance from its (value, row) pairs, then KV
+  compaction of the accepted rows (32 layers x 8 KV heads x head_dim 128).
 Weights are int4 in groups of 32 with fp16 scales U(0.005, 0.02). The
 weights of 4 distinct generated layer sets are copied into 32 separate layer
 buffers plus one lm_head, 4.22 GB in total, so every step streams each byte
@@ -21,6 +21,10 @@ The line also times the same step on the Qwen2.5-0.5B linear set
 (`small_set`: 24 layers of qkv 1152x896, o 896x896, gate_up 9728x896,
 down 896x4864, then lm_head 151936x896; four copies of its 278 MB of weights
 in rotation, so that each step reads its copy cold) at T = 1, 2, 4, 8.
+
+The line also times the 32-token prefill bucket on the same 8B weights
+(`prefill`: the quantisation and the 129 linears at T = 32, the lm_head
+writing logits).
 
 The line also carries the single 896x896 linear at T = 1 (`config1`, a
 latency: its weights stay in the L2 cache), the full 8-node tree
@@ -250,7 +254,8 @@ class Model:
 
     def step(self, T, copy=0, events=None):
         """Enqueue one verify step: the quantisation of every input row of the
-        step (one launch per K), the linears, argmax + acceptance, compaction.
+        step (one launch per K), the linears, the lm_head with acceptance from
+        its argmax pairs, compaction.
         events: list to which (start, end, bytes, name) of each linear launch
         are appended (eager roofline timing only)."""
         sv, torch, m = self.sv, self.torch, self.m
@@ -265,8 +270,9 @@ class Model:
             if events is not None:   # kernel begin/end timestamps of this launch
                 e0, e1 = timing_events(torch)
                 sv.check("specv_time_next_linear", sv.LIB.specv_time_next_linear(e0.cuda_event, e1.cuda_event))
-            if y is None:            # lm_head: fused argmax epilogue, logits not written
-                sv.linear_argmax(w, xq, xs, argmax=self.argmax[:T], workspace=self.ws_lmarg)
+            if y is None:            # lm_head: argmax epilogue, then acceptance from its pairs
+                sv.linear_argmax_accept(w, xq, xs, self.parent, self.token, self.ctrl, argmax=self.argmax[:T],
+                                        path=self.path, stats=self.stats, ring=self.ring, workspace=self.ws_lmarg)
                 nb = argmax_linear_bytes(T, N, K, self.lm_chunks(T))
             else:
                 sv.linear(w, xq, xs, y[: T * N].view(T, N))
@@ -278,8 +284,6 @@ class Model:
             for nm, N, K in layer_linears(m):
                 lin(nm, lay[nm], K, N, self.y[nm], self.in_index[l][nm])
         lin("lm_head", lm, m["hidden"], m["vocab"], None, self.lm_index)
-        sv.tree_accept(self.argmax[:T], self.parent, self.token, self.ctrl, path=self.path, stats=self.stats,
-                       ring=self.ring)
         sv.kv_compact(self.kc, self.vc, self.path, self.ctrl)
 
     def prefill_step(self, T, copy=0, events=None):
@@ -326,7 +330,7 @@ class Model:
         for _, N, K in layer_linears(m):
             b += m["layers"] * (linear_bytes(T, N, K) + quant_bytes(T, K))
         b += argmax_linear_bytes(T, m["vocab"], m["hidden"], self.lm_chunks(T)) + quant_bytes(T, m["hidden"])
-        b += 8 * T * self.lm_chunks(T)                                  # the argmax finishing pass reads the pairs
+        b += 8 * T * self.lm_chunks(T)                                  # acceptance reads the argmax pairs
         b += 2 * 2 * m_acc * m["layers"] * m["kv_heads"] * m["head_dim"] * 2  # K and V rows read + written
         return b
 

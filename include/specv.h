@@ -287,6 +287,28 @@ int tree_accept(const int32_t* argmax, int32_t n_max, const int32_t* parent, con
                 int32_t ring_cap, void* stream);
 
 /*
+ * The lm_head of a verification step with its argmax epilogue, then tree
+ * acceptance from the workgroups' (value, row) pairs ([P1], GPU-Resident
+ * Speculation Loop: the greedy prediction of each node and the acceptance
+ * run on the device after the forward pass). The same results as
+ * w4a8_linear_argmax_T (y not written) followed by tree_accept, in two
+ * launches instead of three: the acceptance kernel finishes each node's
+ * argmax itself.
+ *   wq, ws, xq, xs  the lm_head and the final rows of the T = n_max nodes,
+ *                   as w4a8_linear_argmax_T.
+ *   argmax   nullable int32 [T] out: each node's greedy prediction.
+ *   parent, token, path, ctrl, stats, ring, ring_cap  as tree_argmax_accept.
+ *   workspace  w4a8_linear_argmax_workspace(T, N, K) bytes, 8-byte aligned,
+ *              no initialisation needed.
+ * T in [1, 16]; other shapes, ranges and alignments as w4a8_linear_argmax_T.
+ */
+int w4a8_linear_argmax_accept_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs,
+                                int32_t T, int32_t N, int32_t K, const int32_t* parent,
+                                const int32_t* token, int32_t* argmax, int32_t* path, specv_ctrl* ctrl,
+                                specv_step_stats* stats, int32_t* ring, int32_t ring_cap, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * KV-cache compaction of the accepted path ([P1], GPU-Resident Speculation
  * Loop: a compaction kernel moves the keys and values of the accepted path
  * into place; [P3], KV transaction model: rows past the committed pointer

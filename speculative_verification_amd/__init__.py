@@ -14,7 +14,8 @@ import torch
 from ._lib import CM_WEIGHT, LIB, SpecvError, check, cm_params
 from .model import DeviceModel
 
-__all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "linear_argmax_noalloc", "tree_argmax_accept",
+__all__ = ["SpecvError", "DeviceModel", "CTRL_FIELDS", "new_ctrl", "quantize_act", "linear", "linear_argmax",
+           "linear_argmax_noalloc", "linear_argmax_accept", "tree_accept", "tree_argmax_accept",
            "argmax_accept_workspace_bytes", "kv_compact", "linear_workspace", "cm_params", "cm_draft", "CM_WEIGHT",
            "quantize_act_blocks", "linear_blocks", "Packed", "pack_weights"]
 
@@ -218,6 +219,36 @@ def tree_accept(argmax: torch.Tensor, parent: torch.Tensor, token: torch.Tensor,
         _dev(token, "token", torch.int32), _dev(path, "path", torch.int32), _dev(ctrl, "ctrl", torch.int32),
         st, rp, ring.numel() if ring is not None else 0, _stream()))
     return path
+
+
+def linear_argmax_accept(w: Packed, xq: torch.Tensor, xs: torch.Tensor, parent: torch.Tensor, token: torch.Tensor,
+                         ctrl: torch.Tensor, argmax: torch.Tensor | None = None, path: torch.Tensor | None = None,
+                         stats: torch.Tensor | None = None, ring: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None):
+    """The lm_head's argmax epilogue, then acceptance from its pairs
+    (w4a8_linear_argmax_accept_T); returns (argmax, path), allocated when not
+    given."""
+    T, N, K = _check_packed(w, xq, tuple(xs.shape))
+    if xs.shape != (T,):
+        raise ValueError("xs must be [T]")
+    need = int(LIB.w4a8_linear_argmax_workspace(T, N, K))
+    if need == 0:
+        raise ValueError("shape not supported by the fused argmax linear")
+    dev = xq.device
+    argmax = torch.empty(T, dtype=torch.int32, device=dev) if argmax is None else argmax
+    path = torch.zeros(T, dtype=torch.int32, device=dev) if path is None else path
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _dev(stats, "stats", torch.int32) if stats is not None else None
+    rp = _dev(ring, "ring", torch.int32) if ring is not None else None
+    wq, ws = w.wp, w.sp
+    check("w4a8_linear_argmax_accept_T", LIB.w4a8_linear_argmax_accept_T(
+        _dev(wq, "wq", torch.uint8), _dev(ws, "ws", ws.dtype), _dev(xq, "xq", torch.int8),
+        _dev(xs, "xs", torch.float32), T, N, K, _dev(parent, "parent", torch.int32),
+        _dev(token, "token", torch.int32), _dev(argmax, "argmax", torch.int32), _dev(path, "path", torch.int32),
+        _dev(ctrl, "ctrl", torch.int32), st, rp, ring.numel() if ring is not None else 0,
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream()))
+    return argmax, path
 
 
 def argmax_accept_workspace_bytes(V: int, n_max: int) -> int:

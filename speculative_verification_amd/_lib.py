@@ -32,6 +32,7 @@ SIGNATURES = {
     "w4a8_linear_argmax_T": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, P, SZ, P]),
     "w4a8_linear_argmax_T_noalloc": (ctypes.c_int, [P, P, P, P, P, P, I32, I32, I32, P]),
     "tree_accept": (ctypes.c_int, [P, I32, P, P, P, P, P, P, I32, P]),
+    "w4a8_linear_argmax_accept_T": (ctypes.c_int, [P, P, P, P, I32, I32, I32, P, P, P, P, P, P, P, I32, P, SZ, P]),
     "tree_argmax_accept_workspace": (SZ, [I64, I32]),
     "tree_argmax_accept": (ctypes.c_int, [P, I64, I32, P, P, P, P, P, P, P, I32, P, SZ, P]),
     "kv_compact": (ctypes.c_int, [P, P, I32, I32, I32, I32, P, P, P]),

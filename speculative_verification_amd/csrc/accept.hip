@@ -250,3 +250,34 @@ extern "C" int tree_accept(const int32_t* argmax, int32_t n_max, const int32_t* 
     return enqueue_accept(nullptr, 0, argmax, n_max, parent, token, nullptr, path, ctrl, stats, nullptr, ring,
                           ring_cap, (hipStream_t)stream);
 }
+
+// The lm_head with its argmax epilogue, then acceptance straight from the
+// workgroups' (value, row) pairs: two launches, where w4a8_linear_argmax_T
+// followed by tree_accept takes three (the finishing pass of the argmax is
+// the acceptance kernel's first phase).
+extern "C" int w4a8_linear_argmax_accept_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
+                                           const float* xs, int32_t T, int32_t N, int32_t K,
+                                           const int32_t* parent, const int32_t* token, int32_t* argmax,
+                                           int32_t* path, specv_ctrl* ctrl, specv_step_stats* stats,
+                                           int32_t* ring, int32_t ring_cap, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+    using namespace specv;
+    if (T < 1 || T > kMaxNodes || N < 1 || N > (1 << 24) || K < 32 || K > (1 << 20) || K % 32)
+        return SPECV_E_SHAPE;
+    if (packed_weight_bytes(N, K) >= (int64_t)1 << 31 || !linear_argmax_supported(T, N, K)) return SPECV_E_SHAPE;
+    if (!wq || !ws || !xq || !xs || !parent || !token || !path || !ctrl) return SPECV_E_INVAL;
+    if (ring && ring_cap < 1) return SPECV_E_INVAL;
+    if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(ws, 2) || !aligned(xs, 4) || !aligned(parent, 4) ||
+        !aligned(token, 4) || !aligned(argmax, 4) || !aligned(path, 4) || !aligned(ctrl, 4) ||
+        !aligned(stats, 4) || !aligned(ring, 4))
+        return SPECV_E_ALIGN;
+    const size_t need = w4a8_linear_argmax_workspace(T, N, K);
+    if (!workspace || workspace_bytes < need) return SPECV_E_WORKSPACE;
+    if (!aligned(workspace, 8)) return SPECV_E_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    Best* part = static_cast<Best*>(workspace);
+    const int rc = linear_enqueue(wq, ws, xq, xs, nullptr, part, T, N, K, nullptr, s);
+    if (rc != SPECV_OK) return rc;
+    return enqueue_accept(part, linear_argmax_chunks(T, N, K), nullptr, T, parent, token, argmax, path, ctrl, stats,
+                          nullptr, ring, ring_cap, s);
+}

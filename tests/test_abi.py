@@ -275,6 +275,36 @@ def test_linear_argmax_noalloc_rejects_bad_arguments(lib):
     assert f(A + 8, A, A, A, None, A, 8, 151936, 896, None) == E_ALIGN
 
 
+def test_linear_argmax_accept_rejects_bad_arguments(lib):
+    """The lm_head + acceptance entry validates like w4a8_linear_argmax_T and
+    tree_accept together (no GPU is touched on these paths)."""
+    f = lib.w4a8_linear_argmax_accept_T
+    need = lib.w4a8_linear_argmax_workspace(8, 151936, 896)
+    ok = (A, A, A, A, 8, 151936, 896, A, A, A, A, A, None, None, 0, A, need, None)
+
+    def call(**kw):
+        names = ("wq", "ws", "xq", "xs", "T", "N", "K", "parent", "token", "argmax", "path", "ctrl", "stats",
+                 "ring", "ring_cap", "ws_ptr", "ws_bytes", "stream")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+
+    assert call(T=17, N=4096, K=4096) == E_SHAPE      # acceptance takes at most 16 nodes
+    assert call(T=0) == E_SHAPE
+    assert call(N=0) == E_SHAPE
+    assert call(K=100) == E_SHAPE
+    assert call(wq=None) == E_INVAL
+    assert call(parent=None) == E_INVAL
+    assert call(path=None) == E_INVAL
+    assert call(ctrl=None) == E_INVAL
+    assert call(ring=A, ring_cap=0) == E_INVAL       # ring without capacity
+    assert call(ws_bytes=need - 1) == E_WORKSPACE
+    assert call(ws_ptr=None) == E_WORKSPACE
+    assert call(wq=A + 8) == E_ALIGN
+    assert call(argmax=A + 2) == E_ALIGN
+    assert call(ws_ptr=A + 4) == E_ALIGN
+
+
 def test_tree_accept_rejects_bad_arguments(lib):
     f = lib.tree_accept
     assert f(A, 0, A, A, A, A, None, None, 0, None) == E_SHAPE

@@ -127,3 +127,48 @@ def test_tree_accept_parity(sv):
         assert stats.cpu().numpy().tolist() == [m_o, 0, n]
         emitted = [int(token[p]) for p in path_o[1:]] + [bonus_o]
         assert ring.cpu().numpy()[: m_o + 1].tolist() == emitted
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 300, 896), (8, 151936, 896), (16, 5000, 4096), (5, 128256, 4096)])
+def test_linear_argmax_accept_parity(sv, T, N, K):
+    """The lm_head with acceptance from its pairs (w4a8_linear_argmax_accept_T)
+    against the oracle: the oracle's predictions of the oracle's linear,
+    drafts planted along a random tree so that some nodes are accepted, and
+    the oracle's acceptance; the same as linear_argmax then tree_accept."""
+    case(f"linear argmax + accept T={T} N={N} K={K}")
+    wq, ws, x = sg.linear_case(110 + T, T, N, K)
+    xq, xs = oracle.quantize_act(x)
+    y_o = (oracle.w4a8_linear_threads(wq, ws, xq, xs, min(16, os.cpu_count() or 1)) if N * K > 10 ** 8
+           else oracle.w4a8_linear(wq, ws, xq, xs))
+    a_o = oracle.argmax(y_o)
+    parent = sg.random_tree_parents(sg.stream_key(T, sg.TID_PARENT), T)
+    token = sg.tokens(sg.stream_key(T + 7, sg.TID_TOKEN), T, N)
+    for i in range(1, T):
+        if i % 3 != 2:
+            token[i] = a_o[parent[i]]
+    m_o, path_o, bonus_o = oracle.tree_accept(parent, token, a_o)
+    w = sv.pack_weights(to_dev(wq), to_dev(ws))
+    xq_d, xs_d = to_dev(xq), to_dev(xs)
+    L0 = 100
+    outs = []
+    for fused in (True, False):
+        ctrl = sv.new_ctrl(L0, T, 10 ** 6)
+        stats = torch.zeros(3, dtype=torch.int32, device="cuda")
+        ring = torch.zeros(64, dtype=torch.int32, device="cuda")
+        if fused:
+            amax, path = sv.linear_argmax_accept(w, xq_d, xs_d, to_dev(parent), to_dev(token), ctrl, stats=stats,
+                                                 ring=ring)
+        else:
+            amax = sv.linear_argmax(w, xq_d, xs_d)
+            path = sv.tree_accept(amax, to_dev(parent), to_dev(token), ctrl, stats=stats, ring=ring)
+        torch.cuda.synchronize()
+        outs.append((amax.cpu().numpy(), path.cpu().numpy()[: m_o + 1], ctrl.cpu().numpy(), stats.cpu().numpy(),
+                     ring.cpu().numpy()))
+    for amax, path, c, st, rg in outs:
+        assert np.array_equal(amax, a_o)
+        assert np.array_equal(path, path_o)
+        assert (c[0], c[4], c[5], c[6], c[7]) == (L0 + m_o + 1, m_o, bonus_o, 1, m_o + 1)
+        assert st.tolist() == [m_o, 0, T]
+        assert rg[: m_o + 1].tolist() == [int(token[p]) for p in path_o[1:]] + [bonus_o]
+    if T >= 8:
+        assert m_o >= 1
