@@ -243,11 +243,13 @@ def test_linear_layouts_sampled(sv, T, N, K):
     assert_bits(y[:, rows].copy(), oracle.w4a8_linear_rows(wq, ws, xq_o, xs_o, rows), f"T={T} N={N} K={K}")
 
 
-@pytest.mark.parametrize("T,N,K", [(1, 48, 1 << 20), (8, 48, 1 << 20), (2, (1 << 24) - 16, 32)])
+@pytest.mark.parametrize("T,N,K", [(1, 48, 1 << 20), (8, 48, 1 << 20), (2, (1 << 24) - 16, 32),
+                                   (32, 48, 1 << 20), (32, (1 << 24) - 16, 32)])
 def test_linear_maximum_sizes(sv, T, N, K):
     """The ABI's limits: K = 2^20 (the reloading layout, 2048 iterations per
     wave), every row against the oracle; N = 2^24 - 16 rows (a million
-    tiles over the grid), on sampled rows and the last tile's rows."""
+    tiles over the grid; at 32 tokens the dense kernel's workgroups walk
+    about 4096 tiles each), on sampled rows and the last tile's rows."""
     case(f"linear maximum sizes T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(13, T, N, K)
     xq_o, xs_o = oracle.quantize_act(x)
@@ -338,11 +340,13 @@ def test_linear_blocks_llama_sampled(sv, name, T):
     assert_bits(y[:, rows].copy(), oracle.w4a8_linear_blocks(wq[rows], ws[rows], xq_o, xs_o), f"{name} T={T}")
 
 
-def test_linear_degenerate_values(sv):
+@pytest.mark.parametrize("T", [4, 20])
+def test_linear_degenerate_values(sv, T):
     """All-zero token, negative and subnormal fp16 scales, tiny activations
-    with subnormal outputs, and an empty matrix."""
-    case("linear degenerate values")
-    T, N, K = 4, 37, 288
+    with subnormal outputs, and an empty matrix (at 20 tokens: the dense
+    32-token kernel, whose scaled products are one fma each)."""
+    case(f"linear degenerate values T={T}")
+    N, K = 37, 288
     wq, ws, x = sg.linear_case(9, T, N, K)
     x[0] = 0.0
     x[2] *= np.float32(1e-36)
