@@ -347,7 +347,11 @@ int kv_compact(uint16_t* k_cache, uint16_t* v_cache, int32_t n_layers, int32_t n
  *   w_qkv, s_qkv    [layers] x packed (QKV rows, K = H): q rows, then k
  *                   rows, then v rows
  *   w_o, s_o        [layers] x packed (H rows, K = A)
- *   w_gu, s_gu      [layers] x packed (2I rows, K = H): gate rows, then up
+ *   w_gu, s_gu      [layers] x packed (2I rows, K = H): gate and up rows
+ *                   alternating in blocks of 8 (gate rows 8b..8b+7, then up
+ *                   rows 8b..8b+7, for b = 0 .. I/8 - 1), so that each
+ *                   16-row tile of the linear holds gate row i and up row i
+ *                   and its epilogue writes silu(gate) * up
  *   w_down, s_down  [layers] x packed (H rows, K = I)
  *   norm_attn, norm_mlp  fp32 [layers][H]; norm_final fp32 [H]
  *   w_lm, s_lm      packed (V rows, K = H); the embedding of a token is its

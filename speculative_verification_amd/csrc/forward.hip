@@ -63,12 +63,9 @@ __device__ __forceinline__ uint16_t f32_to_f16(float x) {
 
 constexpr int kFwdThreads = 256;   // embedding and attention-chunk workgroups
 constexpr int kRowThreads = 1024;  // row kernels: norms, SiLU, attention merge
-// SiLU rows are produced by the down linear itself up to this many values
-// (tokens x intermediate): every workgroup recomputes them all, so the fused
-// prologue grows with the step and a separate row kernel wins past it.
-constexpr int64_t kSiluFuseMax = 6144;
-// Likewise RMSNorm rows up to this many tokens (one per wave): with two or
-// more per wave the redundant rows cost more than the row kernel's launch.
+// RMSNorm rows are produced by the linear that consumes them up to this many
+// tokens (one per wave): every workgroup recomputes them all, and with two
+// or more per wave the redundant rows cost more than the row kernel's launch.
 constexpr int kNormFuseMaxT = 4;
 constexpr int kRowRegs = 4;        // float4 chunks per thread: rows up to 16384 values
 constexpr int kMergeRegs = 8;      // values per thread in the merge: rows up to 8192
@@ -275,11 +272,12 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_quant_kernel(float* __res
     quantize_regs(y, H, xq + (size_t)i * H, xs + i, red);
 }
 
-// z = silu(gate) * up over a [n][2I] gate/up output, then quantisation.
-__global__ __launch_bounds__(kRowThreads) void silu_mul_quant_kernel(const float* __restrict__ gu, int I,
-                                                                     int8_t* __restrict__ xq,
-                                                                     float* __restrict__ xs,
-                                                                     const specv_ctrl* ctrl) {
+// Quantisation of the rows z = silu(gate) * up [n][I] that the gate_up
+// linear's epilogue wrote (for steps whose down projection does not
+// quantise them in its own prologue).
+__global__ __launch_bounds__(kRowThreads) void rows_quant_kernel(const float* __restrict__ zr, int I,
+                                                                 int8_t* __restrict__ xq, float* __restrict__ xs,
+                                                                 const specv_ctrl* ctrl) {
     __shared__ float red[kRowThreads / 64];
     const int i = blockIdx.x, tid = threadIdx.x, I4 = I / 4;
     if (ctrl->done) return;
@@ -287,24 +285,21 @@ __global__ __launch_bounds__(kRowThreads) void silu_mul_quant_kernel(const float
         zero_row(xq + (size_t)i * I, xs + i, I);
         return;
     }
-    const float* g = gu + (size_t)i * 2 * I;
-    float4 gv[kRowRegs], uv[kRowRegs];
+    const float* row = zr + (size_t)i * I;
+    float4 zv[kRowRegs];
 #pragma unroll
     for (int r = 0; r < kRowRegs; r++) {
         const int c = tid + r * kRowThreads;
-        if (c < I4) {
-            gv[r] = ld4(g + 4 * c);
-            uv[r] = ld4(g + I + 4 * c);
-        }
+        if (c < I4) zv[r] = ld4(row + 4 * c);
     }
     float z[kRowRegs][4];
 #pragma unroll
     for (int r = 0; r < kRowRegs; r++) {
         if (tid + r * kRowThreads >= I4) continue;
-        z[r][0] = silu(gv[r].x) * uv[r].x;
-        z[r][1] = silu(gv[r].y) * uv[r].y;
-        z[r][2] = silu(gv[r].z) * uv[r].z;
-        z[r][3] = silu(gv[r].w) * uv[r].w;
+        z[r][0] = zv[r].x;
+        z[r][1] = zv[r].y;
+        z[r][2] = zv[r].z;
+        z[r][3] = zv[r].w;
     }
     quantize_regs(z, I, xq + (size_t)i * I, xs + i, red);
 }
@@ -1234,10 +1229,10 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     // residual alternates between h and h2.
     float* hcur = h;
     auto norm_linear = [&](const float* resid, const float* w, const uint8_t* wq, const uint16_t* ws_,
-                           float* y, Best* am, int N, bool keep) -> int {
+                           float* y, Best* am, int N, bool keep, int epi) -> int {
         if (n <= kNormFuseMaxT && linear_fused_supported(kProdNorm, n, H)) {
             float* hnext = !resid || !keep ? nullptr : (hcur == h ? h2 : h);
-            ProdArgs pa{hcur, resid, w, hnext, m->eps, 0, ctrl};
+            ProdArgs pa{hcur, resid, w, hnext, m->eps, 0, ctrl, epi};
             const int rc = linear_enqueue_fused(kProdNorm, pa, wq, ws_, y, am, n, N, H, s);
             if (hnext) hcur = hnext;
             return rc;
@@ -1246,10 +1241,12 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
                            (size_t)16 * norm_slot_stride(H) * sizeof(float), s, hcur, resid, w,
                            H, m->eps, xq, xs, ctrl);
         SPECV_TRY(launch_status());
-        if (am) return linear_enqueue(wq, ws_, xq, xs, y, am, n, N, H, lin, s);
-        return w4a8_linear_T(wq, ws_, xq, xs, y, n, N, H, lin, linb, s);
+        return linear_enqueue(wq, ws_, xq, xs, y, am, n, N, H, lin, s, epi);
     };
-    const bool fuse_silu = (int64_t)n * I <= kSiluFuseMax && linear_fused_supported(kProdSilu, n, I);
+    // The gate_up epilogue writes z = silu(gate) * up (its rows alternate in
+    // blocks of 8 gate and 8 up rows); the down projection quantises z in
+    // its own prologue while that fits, else a row kernel does.
+    const bool fuse_rows = linear_fused_supported(kProdRows, n, I);
     const bool grouped = attn_grouped_ok(m);
     // small trees leave the grid short of workgroups: split each group's heads over two
     const int nsplit = nh / nkv > kGrpSets && n <= kGrpSplitMaxNodes ? 2 : 1;
@@ -1266,7 +1263,7 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
         const uint16_t* sd = m->s_down + (size_t)l * packed_scale_bytes(H, I) / 2;
 
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
-                              true));
+                              true, kEpiPlain));
         if (grouped) {  // chunks of every head of a KV group, the merge by the last workgroup of each node
             SPECV_TRY(launch_attn_group(hd, nsplit, dim3(nkv * nsplit, n, lay.nchunk_max), s, qkv, m->rope_cos, m->rope_sin,
                                         m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
@@ -1281,18 +1278,19 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
             SPECV_TRY(launch_status());
         }
         SPECV_TRY(w4a8_linear_T(wo, so, xq, xs, delta, n, H, A, lin, linb, s));
-        SPECV_TRY(norm_linear(delta, m->norm_mlp + (size_t)l * H, wgu, sgu, gu, nullptr, 2 * I, true));
-        if (fuse_silu) {
-            ProdArgs pa{gu, nullptr, nullptr, nullptr, 0.0f, 0, ctrl};
-            SPECV_TRY(linear_enqueue_fused(kProdSilu, pa, wd, sd, delta, nullptr, n, H, I, s));
+        SPECV_TRY(norm_linear(delta, m->norm_mlp + (size_t)l * H, wgu, sgu, gu, nullptr, 2 * I, true,
+                              kEpiSiluPairs));
+        if (fuse_rows) {
+            ProdArgs pa{gu, nullptr, nullptr, nullptr, 0.0f, 0, ctrl, kEpiPlain};
+            SPECV_TRY(linear_enqueue_fused(kProdRows, pa, wd, sd, delta, nullptr, n, H, I, s));
         } else {
-            hipLaunchKernelGGL(silu_mul_quant_kernel, dim3(n), dim3(kRowThreads), 0, s, gu, I, xq, xs, ctrl);
+            hipLaunchKernelGGL(rows_quant_kernel, dim3(n), dim3(kRowThreads), 0, s, gu, I, xq, xs, ctrl);
             SPECV_TRY(launch_status());
             SPECV_TRY(w4a8_linear_T(wd, sd, xq, xs, delta, n, H, I, lin, linb, s));
         }
     }
     // the residual is not needed after the final norm
-    return norm_linear(delta, m->norm_final, m->w_lm, m->s_lm, logits, amax, V, false);
+    return norm_linear(delta, m->norm_final, m->w_lm, m->s_lm, logits, amax, V, false, kEpiPlain);
 }
 
 int enqueue_step(const specv_model* m, int n, const int32_t* parent, const int32_t* token, float* logits,

@@ -21,10 +21,17 @@ StepLayout step_layout(const specv_model* m, int n_max);
 // tokens with the row kernel's arithmetic (so the codes are the same bits).
 //   kProdNorm: x = a (+ b), written to h_out by workgroup 0 when h_out is
 //              set; RMSNorm with weight w and eps; per-token quantisation.
-//   kProdSilu: z = silu(a[t][k]) * a[t][K + k]; per-token quantisation.
+//   kProdRows: the rows a[t][k] as they are (the SiLU-gated rows the
+//              gate_up epilogue wrote); per-token quantisation.
 // Tokens at or past ctrl->n_nodes, or all tokens once ctrl->done is set,
 // quantise to zero.
-enum { kProdNone = 0, kProdNorm = 1, kProdSilu = 2 };
+enum { kProdNone = 0, kProdNorm = 1, kProdRows = 2 };
+// What the linear writes: its outputs y[t][n] (kEpiPlain), or, for a matrix
+// whose rows alternate in blocks of 8 gate rows and 8 up rows (16-row tile
+// b: gate rows 8b..8b+7, then up rows 8b..8b+7), z[t][i] = silu(g) * u with
+// g and u the outputs of gate row i and up row i (kEpiSiluPairs; y is
+// [T][N/2]).
+enum { kEpiPlain = 0, kEpiSiluPairs = 1 };
 struct ProdArgs {
     const float* a;
     const float* b;
@@ -33,6 +40,7 @@ struct ProdArgs {
     float eps;
     int pad;
     const specv_ctrl* ctrl;
+    int epi;
 };
 
 // W4A8 linear whose activations the kernel produces (T <= 16, per-token
@@ -46,7 +54,7 @@ int validate_model(const specv_model* m);
 // W4A8 linear on validated arguments; y may be null when amax is set. The
 // argmax epilogue (amax: [T][chunks] partials) needs linear_argmax_supported.
 int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
-                   int T, int N, int K, void* workspace, hipStream_t s);
+                   int T, int N, int K, void* workspace, hipStream_t s, int epi = kEpiPlain);
 // The 32-token bucket with dense matrix products (17..32 tokens, per-token
 // scales, at most 10 x 16 groups per row), in csrc/linear_dense.hip.
 bool linear_dense_supported(int T, int K);

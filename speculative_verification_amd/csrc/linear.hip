@@ -176,8 +176,12 @@ struct SStage {
 // rint(v * 127 / absmax) clamped to +-127. Every row load of a token is
 // issued before its first use, so a token costs about one memory round trip.
 constexpr int kProdRegs = 4;       // float4 chunks per lane of a RMSNorm row kept in registers (K <= 1024)
-constexpr int kSiluRegs = 6;       // float4 chunks per thread of a SiLU row (K <= 6144)
-constexpr int kSiluTokens = 2;     // SiLU rows a fused linear produces at most
+constexpr int kRowsRegs = 6;       // float4 chunks per thread of a given row (K <= 6144)
+// Given rows a fused linear quantises at most: every workgroup quantises all
+// of them, and from two tokens on that costs more than a row kernel's launch
+// (measured on MI355X, 0.5B window, us per step, fused up to 1 / 2 / 4
+// tokens: width 2 800 / 802 / 803, width 4 843 / 843 / 901).
+constexpr int kRowsTokens = 1;
 
 __device__ __forceinline__ float tree16_lanes(float v) {
 #define SPECV_DPP_ADD(ctrl) \
@@ -384,25 +388,22 @@ __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP
     }
 }
 
-// SiLU rows (at most kSiluTokens): the whole workgroup, every load issued up
-// front, values in registers, each token's absmax met in LDS.
+// Given rows (at most kRowsTokens): the whole workgroup, every load issued
+// up front, values in registers, each token's absmax met in LDS.
 template <int T>
-__device__ void produce_silu(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
-                             float* part) {
-    constexpr int TS = T < kSiluTokens ? T : kSiluTokens;
+__device__ void produce_given(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
+                              float* part) {
+    constexpr int TS = T < kRowsTokens ? T : kRowsTokens;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K4 = K >> 2;
-    float4 gv[TS][kSiluRegs], uv[TS][kSiluRegs];
+    float4 zv[TS][kRowsRegs];
 #pragma unroll
     for (int t = 0; t < TS; t++)
         if (t < Tr) {
 #pragma unroll
-            for (int i = 0; i < kSiluRegs; i++) {
+            for (int i = 0; i < kRowsRegs; i++) {
                 const int c = tid + 256 * i;
-                if (c < K4) {
-                    gv[t][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * 2 * K + 4 * c);
-                    uv[t][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * 2 * K + K + 4 * c);
-                }
+                if (c < K4) zv[t][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * K + 4 * c);
             }
         }
     for (int t = 0; t < T; t++) zero_row_lds(act, t, JP, tid, 256);
@@ -412,13 +413,8 @@ __device__ void produce_silu(const ProdArgs& pa, int Tr, int live, int K, int JP
     for (int t = 0; t < TS; t++) {
         amax[t] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kSiluRegs; i++)
-            if (t < Tr && t < live && tid + 256 * i < K4) {
-                float4& z = gv[t][i];
-                z = make_float4(silu(z.x) * uv[t][i].x, silu(z.y) * uv[t][i].y, silu(z.z) * uv[t][i].z,
-                                silu(z.w) * uv[t][i].w);
-                amax[t] = fmaxf(amax[t], max4(z));
-            }
+        for (int i = 0; i < kRowsRegs; i++)
+            if (t < Tr && t < live && tid + 256 * i < K4) amax[t] = fmaxf(amax[t], max4(zv[t][i]));
         amax[t] = wave_max(amax[t]);
         if (lane == 0) part[4 * t + wave] = amax[t];
     }
@@ -431,13 +427,11 @@ __device__ void produce_silu(const ProdArgs& pa, int Tr, int live, int K, int JP
         if (tid == 0) s_xs[t] = m == 0.0f ? 0.0f : m / 127.0f;
         int8_t* rowb = act + (size_t)t * JP * 512;
 #pragma unroll
-        for (int i = 0; i < kSiluRegs; i++)
-            if (tid + 256 * i < K4) put_codes(rowb, tid + 256 * i, gv[t][i], qs);
+        for (int i = 0; i < kRowsRegs; i++)
+            if (tid + 256 * i < K4) put_codes(rowb, tid + 256 * i, zv[t][i], qs);
     }
 }
 
-// All rows of the step: zero the staged rows (padding groups, and tokens
-// past Tr or the live count, stay zero), then the producer.
 // All rows of the step; tokens past Tr or the live count, and padding
 // groups, stay zero. Each producer issues its row loads before it zeroes the
 // staged rows, so the two overlap.
@@ -448,7 +442,7 @@ __device__ void produce_rows(const ProdArgs& pa, int Tr, int K, int JP, int8_t* 
     if constexpr (PROD == kProdNorm)
         produce_norm<T>(pa, Tr, live, K, JP, act, s_xs, scratch);
     else
-        produce_silu<T>(pa, Tr, live, K, JP, act, s_xs, scratch);
+        produce_given<T>(pa, Tr, live, K, JP, act, s_xs, scratch);
 }
 
 template <int T, int P, bool AMAX, bool BS, bool RELOAD, int PROD>
@@ -672,19 +666,35 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
             for (int t = 0; t < T; t++) red[buf][wave][t][r] = s[t];
         }
         __syncthreads();
+        auto out = [&](int t, int rr, int kk) {  // output of row 16 tile + rr for token t
+            const float sum = (red[buf][0][t][rr] + red[buf][1][t][rr]) + (red[buf][2][t][rr] + red[buf][3][t][rr]);
+            return BS ? sum : (PROD != kProdNone ? s_xs[t] : fxs[kk]) * sum;
+        };
+        if (!AMAX && pa.epi == kEpiSiluPairs) {
+            // rows rr < 8 of the tile are gate rows 8 tile + rr, rows rr + 8
+            // the up rows of the same index: z = silu(g) * u
 #pragma unroll
-        for (int kk = 0; kk < FP; kk++) {
-            const int idx = tid + 256 * kk;
-            const int t = idx >> 4, rr = idx & 15;
-            const int row = 16 * tile + rr;
-            if (t < Tr && row < N) {
-                const float sum =
-                    (red[buf][0][t][rr] + red[buf][1][t][rr]) + (red[buf][2][t][rr] + red[buf][3][t][rr]);
-                const float val = BS ? sum : (PROD != kProdNone ? s_xs[t] : fxs[kk]) * sum;
-                if (!AMAX || write_y) y[(int64_t)t * N + row] = val;
-                if (AMAX && better(val, row, bv, bi)) {
-                    bv = val;
-                    bi = row;
+            for (int kk = 0; kk < FP; kk++) {
+                const int idx = tid + 256 * kk;
+                const int t = idx >> 4, rr = idx & 15;
+                if (t < Tr && rr < 8 && 16 * tile < N) {
+                    const float g = out(t, rr, kk), u = out(t, rr + 8, kk);
+                    y[(int64_t)t * (N >> 1) + 8 * tile + rr] = silu(g) * u;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < FP; kk++) {
+                const int idx = tid + 256 * kk;
+                const int t = idx >> 4, rr = idx & 15;
+                const int row = 16 * tile + rr;
+                if (t < Tr && row < N) {
+                    const float val = out(t, rr, kk);
+                    if (!AMAX || write_y) y[(int64_t)t * N + row] = val;
+                    if (AMAX && better(val, row, bv, bi)) {
+                        bv = val;
+                        bi = row;
+                    }
                 }
             }
         }
@@ -723,7 +733,7 @@ inline size_t stream_lds_bytes(int T, int K, bool bs, bool reload, int P = SPECV
 }
 // LDS of a producer: one row per wave (RMSNorm), the absmax exchange (SiLU).
 inline size_t prod_scratch_bytes(int prod, int K) {
-    return prod == kProdNorm ? (size_t)16 * norm_row_floats(K) : prod == kProdSilu ? 16 * kSiluTokens : 0;
+    return prod == kProdNorm ? (size_t)16 * norm_row_floats(K) : prod == kProdRows ? 16 * kRowsTokens : 0;
 }
 // Whether the activations of every iteration fit beside the reduction buffer.
 inline bool stream_keeps(int T, int K, bool bs) {
@@ -843,34 +853,34 @@ static int launch_exact(int P, const uint8_t* wq, const uint16_t* ws, const int8
 
 template <int T, bool BS>
 static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
-                    int Tr, int N, int K, hipStream_t s) {
+                    int Tr, int N, int K, hipStream_t s, const ProdArgs& pa) {
     const bool keep = stream_keeps(T, K, BS);
     if constexpr (T <= 16 && !BS) {
         if (deep_stream(T, N, K))
             return amax ? launch_one<T, true, false, false, kProdNone, kDeepStages>(wq, ws, xq, xs, y, amax, Tr, N,
-                                                                                    K, s)
+                                                                                    K, s, pa)
                         : launch_one<T, false, false, false, kProdNone, kDeepStages>(wq, ws, xq, xs, y, nullptr, Tr,
-                                                                                     N, K, s);
+                                                                                     N, K, s, pa);
         if (const int P = exact_stages(T, K))
-            return amax ? launch_exact<T, true>(P, wq, ws, xq, xs, y, amax, Tr, N, K, s)
-                        : launch_exact<T, false>(P, wq, ws, xq, xs, y, nullptr, Tr, N, K, s);
+            return amax ? launch_exact<T, true>(P, wq, ws, xq, xs, y, amax, Tr, N, K, s, pa)
+                        : launch_exact<T, false>(P, wq, ws, xq, xs, y, nullptr, Tr, N, K, s, pa);
     }
     if constexpr (T <= 16 && !BS) {
         if (amax)
-            return keep ? launch_one<T, true, false, false>(wq, ws, xq, xs, y, amax, Tr, N, K, s)
-                        : launch_one<T, true, false, true>(wq, ws, xq, xs, y, amax, Tr, N, K, s);
+            return keep ? launch_one<T, true, false, false>(wq, ws, xq, xs, y, amax, Tr, N, K, s, pa)
+                        : launch_one<T, true, false, true>(wq, ws, xq, xs, y, amax, Tr, N, K, s, pa);
     } else {
         if (amax) return SPECV_E_SHAPE;
     }
-    return keep ? launch_one<T, false, BS, false>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s)
-                : launch_one<T, false, BS, true>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s);
+    return keep ? launch_one<T, false, BS, false>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s, pa)
+                : launch_one<T, false, BS, true>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s, pa);
 }
 
 // Fused producers: T <= 16, per-token scales, every iteration's activations
 // (and, for RMSNorm, one row per wave) kept in LDS.
 bool linear_fused_supported(int prod, int T, int K) {
-    if (T < 1 || T > 16 || K < 32 || K % 32 || (prod != kProdNorm && prod != kProdSilu)) return false;
-    if (prod == kProdSilu && (K > 256 * 4 * kSiluRegs || T > kSiluTokens)) return false;
+    if (T < 1 || T > 16 || K < 32 || K % 32 || (prod != kProdNorm && prod != kProdRows)) return false;
+    if (prod == kProdRows && (K > 256 * 4 * kRowsRegs || T > kRowsTokens)) return false;
     return stream_lds_bytes(T, K, false, false) + prod_scratch_bytes(prod, K) + (size_t)T * 512 <= kLdsBudget;
 }
 
@@ -883,19 +893,20 @@ static int launch_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const u
             return amax ? launch_exact<T, true, kProdNorm>(P, wq, ws, nullptr, nullptr, y, amax, T, N, K, s, pa)
                         : launch_exact<T, false, kProdNorm>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
         if (amax) return SPECV_E_SHAPE;
-        return launch_exact<T, false, kProdSilu>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
+        return launch_exact<T, false, kProdRows>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
     }
     if (prod == kProdNorm)
         return amax ? launch_one<T, true, false, false, kProdNorm>(wq, ws, nullptr, nullptr, y, amax, T, N, K, s, pa)
                     : launch_one<T, false, false, false, kProdNorm>(wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s,
                                                                      pa);
     if (amax) return SPECV_E_SHAPE;
-    return launch_one<T, false, false, false, kProdSilu>(wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
+    return launch_one<T, false, false, false, kProdRows>(wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
 }
 
 int linear_enqueue_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const uint16_t* ws, float* y, Best* amax,
                          int T, int N, int K, hipStream_t s) {
     if (!linear_fused_supported(prod, T, K)) return SPECV_E_SHAPE;
+    if (pa.epi != kEpiPlain && (amax || N % 16)) return SPECV_E_SHAPE;
     switch (T) {
 #define SPECV_CASE(n) \
     case n: return launch_fused<n>(prod, pa, wq, ws, y, amax, N, K, s);
@@ -937,32 +948,38 @@ bool linear_argmax_supported(int T, int N, int K) { return T >= 1 && T <= 16 && 
 int linear_argmax_chunks(int T, int N, int K) { return linear_argmax_supported(T, N, K) ? stream_grid(N) : 0; }
 
 // Validated arguments. y may be null when amax is set (T <= 16, per-token
-// scales). bs: xs holds per-block scales [T][K/32].
+// scales). bs: xs holds per-block scales [T][K/32]. pa.epi chooses what the
+// linear writes (T <= 16).
 static int linear_dispatch(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
-                           Best* amax, int T, int N, int K, bool bs, hipStream_t s) {
+                           Best* amax, int T, int N, int K, bool bs, hipStream_t s,
+                           const ProdArgs& pa = ProdArgs{}) {
     switch (T) {
-#define SPECV_CASE(n)                                                  \
-    case n:                                                            \
-        return bs ? launch_T<n, true>(wq, ws, xq, xs, y, amax, n, N, K, s) \
-                  : launch_T<n, false>(wq, ws, xq, xs, y, amax, n, N, K, s);
+#define SPECV_CASE(n)                                                      \
+    case n:                                                                \
+        return bs ? launch_T<n, true>(wq, ws, xq, xs, y, amax, n, N, K, s, pa) \
+                  : launch_T<n, false>(wq, ws, xq, xs, y, amax, n, N, K, s, pa);
         SPECV_CASE(1) SPECV_CASE(2) SPECV_CASE(3) SPECV_CASE(4) SPECV_CASE(5) SPECV_CASE(6)
         SPECV_CASE(7) SPECV_CASE(8) SPECV_CASE(9) SPECV_CASE(10) SPECV_CASE(11) SPECV_CASE(12)
         SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
 #undef SPECV_CASE
         default:
             if (T > 16 && T <= 32) {  // the 32-token bucket: dense products where they apply
+                if (pa.epi != kEpiPlain) return SPECV_E_SHAPE;
                 if (!bs && !amax && linear_dense_supported(T, K))
                     return linear_dense_enqueue(wq, ws, xq, xs, y, T, N, K, s);
-                return bs ? launch_T<32, true>(wq, ws, xq, xs, y, amax, T, N, K, s)
-                          : launch_T<32, false>(wq, ws, xq, xs, y, amax, T, N, K, s);
+                return bs ? launch_T<32, true>(wq, ws, xq, xs, y, amax, T, N, K, s, pa)
+                          : launch_T<32, false>(wq, ws, xq, xs, y, amax, T, N, K, s, pa);
             }
             return SPECV_E_SHAPE;
     }
 }
 
 int linear_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, Best* amax,
-                   int T, int N, int K, void* /*workspace*/, hipStream_t s) {
-    return linear_dispatch(wq, ws, xq, xs, y, amax, T, N, K, false, s);
+                   int T, int N, int K, void* /*workspace*/, hipStream_t s, int epi) {
+    if (epi != kEpiPlain && (amax || N % 16)) return SPECV_E_SHAPE;
+    ProdArgs pa{};
+    pa.epi = epi;
+    return linear_dispatch(wq, ws, xq, xs, y, amax, T, N, K, false, s, pa);
 }
 
 // Shape and pointer checks shared by the linear entry points (N >= 1).

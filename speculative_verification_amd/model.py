@@ -2,9 +2,9 @@
 
 Packs a decoder given in the interchange layout (per layer: nibbles
 [rows][K/2] and scales [rows][K/32] for q, k, v, o, gate, up, down; norms;
-lm_head) into the library's device layout (q/k/v and gate/up rows
-concatenated, each matrix in the packed tile layout of w4a8_pack_weights,
-layers one after another), and exposes the step. Layout conversion only:
+lm_head) into the library's device layout (q/k/v rows concatenated, gate and
+up rows alternating in blocks of 8, each matrix in the packed tile layout of
+w4a8_pack_weights, layers one after another), and exposes the step. Layout conversion only:
 all arithmetic runs in libspecv.so.
 """
 from __future__ import annotations
@@ -17,6 +17,17 @@ import torch
 from ._lib import LIB, SpecvDrafter, SpecvModel, check, cm_params
 
 CFG_KEYS = ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "vocab", "max_pos")
+
+
+def _gate_up_blocks(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Gate and up rows [I][...] alternating in blocks of 8 (gate rows 8b..8b+7,
+    then up rows 8b..8b+7): the row order of the library's gate_up matrix,
+    whose epilogue pairs gate row i with up row i."""
+    I = g.shape[0]
+    if I % 8 or u.shape != g.shape:
+        raise ValueError("gate and up need the same shape with a multiple of 8 rows")
+    return np.ascontiguousarray(np.stack([g.reshape(I // 8, 8, -1), u.reshape(I // 8, 8, -1)], axis=1)
+                                .reshape(2 * I, -1))
 
 
 def _pack_layers(nl: int, wfn, sfn, dev) -> tuple[torch.Tensor, torch.Tensor]:
@@ -50,8 +61,8 @@ class DeviceModel:
         self.w_qkv, self.s_qkv = _pack_layers(nl, lambda l: np.concatenate([a["wq"][l], a["wk"][l], a["wv"][l]]),
                                               lambda l: np.concatenate([a["sq"][l], a["sk"][l], a["sv"][l]]), dev)
         self.w_o, self.s_o = _pack_layers(nl, lambda l: a["wo"][l], lambda l: a["so"][l], dev)
-        self.w_gu, self.s_gu = _pack_layers(nl, lambda l: np.concatenate([a["wg"][l], a["wu"][l]]),
-                                            lambda l: np.concatenate([a["sg"][l], a["su"][l]]), dev)
+        self.w_gu, self.s_gu = _pack_layers(nl, lambda l: _gate_up_blocks(a["wg"][l], a["wu"][l]),
+                                            lambda l: _gate_up_blocks(a["sg"][l], a["su"][l]), dev)
         self.w_down, self.s_down = _pack_layers(nl, lambda l: a["wd"][l], lambda l: a["sd"][l], dev)
         self.norm_attn = stack(lambda l: arrays["norm_attn"][l])
         self.norm_mlp = stack(lambda l: arrays["norm_mlp"][l])
