@@ -58,9 +58,9 @@ HBM_PEAK_GBS = 8000.0
 # source they were taken on: HBM bytes per linear launch of the T = 8 step
 # from the FETCH_SIZE and WRITE_SIZE counter passes (each scaled by a plain
 # 256 MiB device copy), and the kernel trace's mean duration per launch.
-LINEAR_PROFILE = {"source_sha256": "eb33503b17f06a0ce0408b43da2a5c097137cf448ffb8ca4685d57ff3f11a3ba",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33618740,
-                  "rocprof_mean_us": 8.110, "summary": "profiles/w4a8_linear_llama8b_T8.md"}
+LINEAR_PROFILE = {"source_sha256": "794a578499fad11ce01face431fab0d569d783866d75e6893f897ac175dffcf0",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33632822,
+                  "rocprof_mean_us": 8.087, "summary": "profiles/w4a8_linear_llama8b_T8.md"}
 
 
 def linear_profile(T, workload):
