@@ -578,13 +578,14 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
 // over one chunk of its visible sequence, with the merge fused: one
 // workgroup per (KV head g, node i, chunk c), so each value row is read and
 // widened once for the group's heads ([P1] Small-Batch Verification
-// Kernels). The workgroup's 1024 threads form four sets of 256; set k takes
-// the group's heads k, k + 4 (at most two), so the four SIMDs of a CU share
-// the heads' arithmetic. With nsplit = 2 (small trees, where the grid is
-// short of workgroups) two workgroups share a (KV head, node, chunk), the
-// first taking heads 0..3 and the second the rest, one head per set: the
-// rows are read twice (the second time mostly from L2) and each set's chain
-// of dependent arithmetic is halved. In a set, thread t owns position t of the chunk: its
+// Kernels). The workgroup's NT threads (1024, or 512 for wide trees) form
+// NT / 256 sets of 256; with S sets, set k takes the group's heads k,
+// k + S, ... (at most 8 / S), so the SIMDs of a CU share the heads'
+// arithmetic. With nsplit = 2 (small trees, where the grid is short of
+// workgroups) two workgroups share a (KV head, node, chunk), the first
+// taking heads 0..3 and the second the rest, one head per set: the rows are
+// read twice (the second time mostly from L2) and each set's chain of
+// dependent arithmetic is halved. In a set, thread t owns position t of the chunk: its
 // key row meets each of its heads' queries, s_{h,t} = R16_d(q_d * K_td) *
 // scale; each head's chunk maximum is taken over the set's waves (order-free);
 // e_{h,t} = E(s_{h,t} - m_h). For the value sums, lane s of the set's 16-lane
@@ -600,13 +601,19 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
 constexpr int kGrpThreads = 1024;
 constexpr int kGrpSets = kGrpThreads / kFwdThreads;  // sets of 256 threads
 constexpr int kGrpMaxHeads = 8;                        // query heads per KV head the grouped kernel takes
-constexpr int kGrpSetHeads = kGrpMaxHeads / kGrpSets;  // heads per set
 constexpr int kGrpMaxRow = kGrpThreads;                // attention row (heads x head dim) its merge takes
 constexpr int kGrpMaxChunks = 32;                      // chunks per node its merge takes
 constexpr int kGrpSplitMaxNodes = 4;                   // trees up to this size split a group's heads
+// Trees from this size take workgroups of 512 threads (two sets, up to four
+// heads each): two fit on a CU, so the up to 2 x 16 x 17 workgroups of a
+// wide tree run in one wave instead of two. Measured on the 0.5B window, us
+// per step at widths 8 / 16: 965 / 1230 with 1024 threads, 990 / 1164 with
+// 512 (980 / 1252 with 512 threads and the heads split over two
+// workgroups), so only trees of more than 8 nodes take them.
+constexpr int kGrpHalfMinNodes = 9;
 
-template <int HD>
-__global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
+template <int HD, int NT>
+__global__ __launch_bounds__(NT) void attn_group_kernel(
     const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
     int nh, int nkv, int nsplit, float scale, float* __restrict__ part, int nchunk_max,
@@ -616,13 +623,14 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     constexpr bool SWZ = attn_swizzle_ok(HD);
     constexpr int VS = attn_vstride(HD, SWZ);
     constexpr bool KF = HD <= 64;  // key row widened to fp32 registers once
-    constexpr int SH = kGrpSetHeads;
+    constexpr int SETS = NT / kFwdThreads;          // sets of 256 threads
+    constexpr int SH = kGrpMaxHeads / SETS;          // heads per set, at most
+    constexpr int EPT = (kGrpMaxRow + NT - 1) / NT;  // merge: attention row elements per thread
     const int g = blockIdx.x / nsplit, sp = blockIdx.x - g * nsplit;
     const int i = blockIdx.y, c = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int set = __builtin_amdgcn_readfirstlane(tid >> 8);  // uniform in a wave
     const int t8 = tid & 255;                                  // position / lane of the set
-    const int wset = wave & 3;                                 // wave within the set
     const int depth_raw = tinfo[i];  // issued with the control loads (i < 16)
     if (ctrl->done) return;
     const int K = nh * HD;
@@ -638,8 +646,8 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     if (j0 >= len) return;
     const int cnt = len - j0 < kAttnChunk ? len - j0 : kAttnChunk;
     const int G = nh / nkv;
-    const int hps = (G + nsplit * kGrpSets - 1) / (nsplit * kGrpSets);  // heads per set (1 or 2)
-    const int hbase = sp * kGrpSets * hps;                             // this workgroup's first head
+    const int hps = (G + nsplit * SETS - 1) / (nsplit * SETS);  // heads per set (1 or 2)
+    const int hbase = sp * SETS * hps;                             // this workgroup's first head
     const int QKV = (nh + 2 * nkv) * HD;
     __shared__ int anc[kMaxNodes];
     __shared__ __attribute__((aligned(16))) uint16_t tk[kMaxNodes][HD];
@@ -648,7 +656,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     // e of position s + 16k at Et[h][s][4 * ((k >> 2) ^ ((s >> 2) & 3)) + (k & 3)]: each lane s reads its
     // 16 values as four 16-byte words, and the 16 lanes of a group hit distinct banks
     __shared__ __attribute__((aligned(16))) float Et[kGrpMaxHeads][16][16];
-    __shared__ float wmax[kGrpThreads / 64][SH];
+    __shared__ float wmax[NT / 64][SH];
     __shared__ int s_last;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     uint16_t* Vs = reinterpret_cast<uint16_t*>(smem);  // [256][VS] value rows, then the key rows; later the
@@ -675,14 +683,14 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
                                           (ok ? 0u : kOOB));
         }
     }
-    for (int w = tid; w < G * HALF; w += kGrpThreads) {  // the group's rotated queries of node i
+    for (int w = tid; w < G * HALF; w += NT) {  // the group's rotated queries of node i
         const int h = w / HALF, d = w - h * HALF;
         const size_t tp = (size_t)(L + depth) * HALF + d;
         const float* src = qkv + (size_t)i * QKV + (g * G + h) * HD;
         rope_pair(src[d], src[d + HALF], cos_t[tp], sin_t[tp], qs[h][d], qs[h][d + HALF]);
     }
-    if (c == 0 && sp == 0 && tid >= kGrpThreads - HALF) {  // node i's key and value rows to the caches
-        const int d = tid - (kGrpThreads - HALF);
+    if (c == 0 && sp == 0 && tid >= NT - HALF) {  // node i's key and value rows to the caches
+        const int d = tid - (NT - HALF);
         const size_t tp = (size_t)(L + depth) * HALF + d;
         const float* ks = qkv + (size_t)i * QKV + (nh + g) * HD;
         const float* vsrc = qkv + (size_t)i * QKV + (nh + nkv + g) * HD;
@@ -708,7 +716,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     __syncthreads();
     if (j0 + cnt > L) {  // the chunk holds tree positions: their rows, made once into LDS
         // the ancestor at depth t has depth t itself, so its rotary position is L + t
-        for (int w = tid; w < (depth + 1) * HALF; w += kGrpThreads) {
+        for (int w = tid; w < (depth + 1) * HALF; w += NT) {
             const int t = w / HALF, d = w - t * HALF;
             const int a = anc[t];
             const float* ks = qkv + (size_t)a * QKV + (nh + g) * HD;
@@ -756,7 +764,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
         }
 #pragma unroll
         for (int u = 0; u < SH; u++) {
-            const int h = hbase + set + kGrpSets * u;
+            const int h = hbase + set + SETS * u;
             sc[u] = -__builtin_inff();
             if (u >= hps || h >= G || !live) continue;
             float slot[16];
@@ -801,7 +809,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     float mh[SH];
 #pragma unroll
     for (int u = 0; u < SH; u++) {
-        const int h = hbase + set + kGrpSets * u;
+        const int h = hbase + set + SETS * u;
         const int w0 = 4 * set;
         mh[u] = fmaxf(fmaxf(wmax[w0][u], wmax[w0 + 1][u]), fmaxf(wmax[w0 + 2][u], wmax[w0 + 3][u]));
         const int es = t8 & 15, ek = t8 >> 4;
@@ -835,7 +843,7 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
         }
 #pragma unroll
         for (int u = 0; u < SH; u++) {
-            const int h = hbase + set + kGrpSets * u;
+            const int h = hbase + set + SETS * u;
             if (u >= hps || h >= G) continue;
             float e[16];
 #pragma unroll
@@ -902,16 +910,27 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     };
     float* wts = reinterpret_cast<float*>(smem);  // [nh][nchunk_max], then l[nh]
     float* lsum = wts + (size_t)nh * nchunk_max;
-    const int hh0 = tid / HD, d0e = tid - hh0 * HD;
-    const bool own = tid < K;
-    const uint32_t ebase = (uint32_t)((size_t)hh0 * nchunk_max * stride + 2 + d0e) * 4u;
-    float slot[16];
+    // element e of this thread: idx = tid + NT e of the row, head idx / HD
+    int eh[EPT];
+    bool own[EPT];
+    uint32_t ebase[EPT];
+    float slot[EPT][16];
 #pragma unroll
-    for (int sl = 0; sl < 16; sl++) slot[sl] = 0.0f;
+    for (int e = 0; e < EPT; e++) {
+        const int idx = tid + NT * e;
+        eh[e] = idx / HD;
+        own[e] = idx < K;
+        ebase[e] = (uint32_t)((size_t)eh[e] * nchunk_max * stride + 2 + (idx - eh[e] * HD)) * 4u;
+#pragma unroll
+        for (int sl = 0; sl < 16; sl++) slot[e][sl] = 0.0f;
+    }
     for (int c0 = 0; c0 < nch; c0 += 16) {
-        float ov[16];
+        float ov[EPT][16];
 #pragma unroll
-        for (int sl = 0; sl < 16; sl++) ov[sl] = get(ebase + (uint32_t)(c0 + sl) * rec, own && c0 + sl < nch);
+        for (int e = 0; e < EPT; e++)
+#pragma unroll
+            for (int sl = 0; sl < 16; sl++)
+                ov[e][sl] = get(ebase[e] + (uint32_t)(c0 + sl) * rec, own[e] && c0 + sl < nch);
         if (c0 == 0) {
             const int hw = tid >> 4, sw = tid & 15;  // 16 lanes per head
             if (hw < nh) {
@@ -934,25 +953,32 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
             }
             __syncthreads();
         }
-        if (own) {
-            const float* wh = wts + hh0 * nchunk_max;
+#pragma unroll
+        for (int e = 0; e < EPT; e++) {
+            if (!own[e]) continue;
+            const float* wh = wts + eh[e] * nchunk_max;
 #pragma unroll
             for (int sl = 0; sl < 16; sl++) {
                 const float wc = c0 + sl < nch ? wh[c0 + sl] : 0.0f;
-                slot[sl] = slot[sl] + wc * ov[sl];
+                slot[e][sl] = slot[e][sl] + wc * ov[e][sl];
             }
         }
     }
-    float y = 0.0f;
-    if (own) {
+    float y[EPT];
+    float ya = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPT; e++) {
+        y[e] = 0.0f;
+        if (!own[e]) continue;
 #pragma unroll
         for (int w = 1; w < 16; w <<= 1)
 #pragma unroll
-            for (int sl = 0; sl < 16; sl += 2 * w) slot[sl] = slot[sl] + slot[sl + w];
-        y = slot[0] / lsum[hh0];
+            for (int sl = 0; sl < 16; sl += 2 * w) slot[e][sl] = slot[e][sl] + slot[e][sl + w];
+        y[e] = slot[e][0] / lsum[eh[e]];
+        ya = fmaxf(ya, fabsf(y[e]));
     }
     {
-        const float m16 = max16(fabsf(y));
+        const float m16 = max16(ya);
         const int b = __builtin_bit_cast(int, m16);
         const float mw = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
                                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
@@ -963,10 +989,12 @@ __global__ __launch_bounds__(kGrpThreads) void attn_group_kernel(
     __syncthreads();
     float a = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kGrpThreads / 64; w++) a = fmaxf(a, wmax[w][0]);
+    for (int w = 0; w < NT / 64; w++) a = fmaxf(a, wmax[w][0]);
     const QuantScale qsc = quant_scale(a);
     if (tid == 0) xs[i] = a == 0.0f ? 0.0f : a / 127.0f;
-    if (own) xq[(size_t)i * K + tid] = (int8_t)(int)quant_code(y, qsc);
+#pragma unroll
+    for (int e = 0; e < EPT; e++)
+        if (own[e]) xq[(size_t)i * K + tid + NT * e] = (int8_t)(int)quant_code(y[e], qsc);
 }
 
 // Merge of the chunks of each head of node i: m = max_c m_c,
@@ -1147,12 +1175,12 @@ inline size_t attn_group_lds_bytes(int hd, int nh, int nchunk_max) {  // key and
     return std::max(2 * attn_lds_bytes(hd, false, attn_swizzle_ok(hd)), merge_lds_bytes(nh, nchunk_max));
 }
 
-template <int HD>
-static int launch_attn_group_hd(dim3 grid, size_t lds, hipStream_t s, const float* qkv, const float* cos_t,
+template <int HD, int NT>
+static int launch_attn_group_nt(dim3 grid, size_t lds, hipStream_t s, const float* qkv, const float* cos_t,
                                 const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
                                 int cap, int nh, int nkv, int nsplit, float scale, float* part, int nchunk_max,
                                 uint32_t* arrivals, int8_t* xq, float* xs, const specv_ctrl* ctrl) {
-    auto kernel = &attn_group_kernel<HD>;
+    auto kernel = &attn_group_kernel<HD, NT>;
     static size_t enabled = 64 * 1024;  // dynamic LDS above 64 KB is enabled per kernel
     if (lds > enabled) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1162,21 +1190,35 @@ static int launch_attn_group_hd(dim3 grid, size_t lds, hipStream_t s, const floa
         }
         enabled = lds;
     }
-    hipLaunchKernelGGL(kernel, grid, dim3(kGrpThreads), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh,
-                       nkv, nsplit, scale, part, nchunk_max, arrivals, xq, xs, ctrl);
+    hipLaunchKernelGGL(kernel, grid, dim3(NT), lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv, nsplit,
+                       scale, part, nchunk_max, arrivals, xq, xs, ctrl);
     return launch_status();
 }
 
-static int launch_attn_group(int hd, int nsplit, dim3 grid, hipStream_t s, const float* qkv, const float* cos_t,
-                             const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
-                             int cap, int nh, int nkv, float scale, float* part, int nchunk_max, uint32_t* arrivals,
-                             int8_t* xq, float* xs, const specv_ctrl* ctrl) {
+template <int HD>
+static int launch_attn_group_hd(int threads, dim3 grid, size_t lds, hipStream_t s, const float* qkv,
+                                const float* cos_t, const float* sin_t, uint16_t* kc, uint16_t* vc,
+                                const int32_t* tinfo, int layer, int cap, int nh, int nkv, int nsplit, float scale,
+                                float* part, int nchunk_max, uint32_t* arrivals, int8_t* xq, float* xs,
+                                const specv_ctrl* ctrl) {
+    if (threads == kGrpThreads / 2)
+        return launch_attn_group_nt<HD, kGrpThreads / 2>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap,
+                                                         nh, nkv, nsplit, scale, part, nchunk_max, arrivals, xq, xs,
+                                                         ctrl);
+    return launch_attn_group_nt<HD, kGrpThreads>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv,
+                                                 nsplit, scale, part, nchunk_max, arrivals, xq, xs, ctrl);
+}
+
+static int launch_attn_group(int hd, int threads, int nsplit, dim3 grid, hipStream_t s, const float* qkv,
+                             const float* cos_t, const float* sin_t, uint16_t* kc, uint16_t* vc,
+                             const int32_t* tinfo, int layer, int cap, int nh, int nkv, float scale, float* part,
+                             int nchunk_max, uint32_t* arrivals, int8_t* xq, float* xs, const specv_ctrl* ctrl) {
     const size_t lds = attn_group_lds_bytes(hd, nh, nchunk_max);
     switch (hd) {
-#define SPECV_ATTN(HDV)                                                                                             \
-    case HDV:                                                                                                       \
-        return launch_attn_group_hd<HDV>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv, nsplit, \
-                                         scale, part, nchunk_max, arrivals, xq, xs, ctrl);
+#define SPECV_ATTN(HDV)                                                                                           \
+    case HDV:                                                                                                     \
+        return launch_attn_group_hd<HDV>(threads, grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, \
+                                         nkv, nsplit, scale, part, nchunk_max, arrivals, xq, xs, ctrl);
         SPECV_ATTN(16) SPECV_ATTN(32) SPECV_ATTN(48) SPECV_ATTN(64)
         SPECV_ATTN(80) SPECV_ATTN(96) SPECV_ATTN(112) SPECV_ATTN(128)
 #undef SPECV_ATTN
@@ -1249,7 +1291,10 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     const bool fuse_rows = linear_fused_supported(kProdRows, n, I);
     const bool grouped = attn_grouped_ok(m);
     // small trees leave the grid short of workgroups: split each group's heads over two
-    const int nsplit = nh / nkv > kGrpSets && n <= kGrpSplitMaxNodes ? 2 : 1;
+    // wide trees: half-size workgroups (the merge's chunk weights take 16 lanes per head)
+    const bool half = n >= kGrpHalfMinNodes && nh * 16 <= kGrpThreads / 2;
+    const int grp_threads = half ? kGrpThreads / 2 : kGrpThreads;
+    const int nsplit = !half && nh / nkv > kGrpSets && n <= kGrpSplitMaxNodes ? 2 : 1;
     uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + lay.arrivals);
     for (int l = 0; l < m->n_layers; l++) {
         // each layer's matrices in the packed tile layout, one after another
@@ -1265,9 +1310,9 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
         SPECV_TRY(norm_linear(l == 0 ? nullptr : delta, m->norm_attn + (size_t)l * H, wqkv, sqkv, qkv, nullptr, QKV,
                               true, kEpiPlain));
         if (grouped) {  // chunks of every head of a KV group, the merge by the last workgroup of each node
-            SPECV_TRY(launch_attn_group(hd, nsplit, dim3(nkv * nsplit, n, lay.nchunk_max), s, qkv, m->rope_cos, m->rope_sin,
-                                        m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,
-                                        arrivals, xq, xs, ctrl));
+            SPECV_TRY(launch_attn_group(hd, grp_threads, nsplit, dim3(nkv * nsplit, n, lay.nchunk_max), s, qkv,
+                                        m->rope_cos, m->rope_sin, m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv,
+                                        scale, attn, lay.nchunk_max, arrivals, xq, xs, ctrl));
         } else {
             SPECV_TRY(launch_attn_chunk(hd, dim3(nh, n, lay.nchunk_max), s, qkv, m->rope_cos, m->rope_sin,
                                         m->k_cache, m->v_cache, tinfo, l, cap, nh, nkv, scale, attn, lay.nchunk_max,

@@ -140,6 +140,15 @@ def test_grouped_head_split_parity(sv, name, seed, N, L):
     compare_step(sv, name, seed, N, L)
 
 
+@pytest.mark.parametrize("name,seed,N,L", [("g7", 68, 9, 300), ("g7", 69, 16, 520), ("g8", 70, 12, 255),
+                                            ("g8", 71, 16, 0)])
+def test_grouped_half_workgroups_parity(sv, name, seed, N, L):
+    """Trees of more than 8 nodes take the grouped attention in 512-thread
+    workgroups (two sets, up to four heads each)."""
+    case(f"{name} tree step seed={seed} N={N} L={L}")
+    compare_step(sv, name, seed, N, L)
+
+
 def test_tiny_unplanted_tree(sv):
     case("tiny tree step, random drafts")
     compare_step(sv, "tiny", 12, 8, 130, plant=False)
