@@ -443,8 +443,8 @@ def prefill_bench(model, T, steps, torch, reps=3):
         by_shape[nm] = round(float(np.mean(v)), 2)
     nb = model.prefill_bytes(T)
     out = {"workload": f"the same {model.m['layers']}-layer set at T={T} tokens (the dense 32-token bucket; down, "
-                       f"K = 14336, runs the block-diagonal form): quantisation + 128 layer linears + lm_head "
-                       f"writing logits, HIP-graph replay",
+                       f"K = 14336, streams its activation operands through LDS): quantisation + 128 layer "
+                       f"linears + lm_head writing logits, HIP-graph replay",
            "T": T, "us": round(us, 2), "GB/s": round(nb / us / 1e3, 1),
            "pct_hbm_peak": round(100 * nb / us / 1e3 / HBM_PEAK_GBS, 2), "bytes": nb, "by_shape_us": by_shape}
     print(f"[bench] prefill: {out}", file=sys.stderr, flush=True)

@@ -48,6 +48,13 @@ namespace specv {
 constexpr int kDenseThreads = 1024;  // 16 waves: one R16 slot each
 constexpr int kDenseMaxJ = 10;       // iterations per tile whose activation operands stay in registers
 constexpr int kDenseTokens = 32;
+// Tiles of weights in flight for up to 8 iterations per tile (measured on
+// MI355X at 32 tokens: three were no faster than two, and four spill).
+constexpr int kDenseLookahead = 2;
+// Passes of the streamed kernel whose activation and weight loads are in
+// flight (measured, the 14336-input down projection at 32 tokens: 21.0,
+// 21.4 and 22.8 us per launch with 2, 3 and 4).
+constexpr int kDensePassAhead = 2;
 
 // 8 activation codes (inputs 0..7) in the even-then-odd order of the decode.
 __device__ __forceinline__ long even_odd8(uint64_t raw) {
@@ -248,17 +255,189 @@ __global__ __launch_bounds__(kDenseThreads) void w4a8_linear_dense_kernel(
             if (ftok < Tr && row < N) y[(int64_t)ftok * N + row] = fxs * v[0];
         }
     };
-    if constexpr (LA == 1) {
-        for (int k = 0; k < ntiles; k++) tile_body(std::integral_constant<int, 0>{}, k);
-    } else {  // pairs of tiles, then the odd one (no branch inside the pair keeps the load counts exact)
-        int k = 0;
-        for (; k + 1 < ntiles; k += 2) {
-            tile_body(std::integral_constant<int, 0>{}, k);
-            tile_body(std::integral_constant<int, 1>{}, k + 1);
+    // groups of LA tiles, then the rest (no branch inside a group keeps the
+    // load counts exact)
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    int k = 0;
+    for (; k + LA <= ntiles; k += LA) {
+        tile_body(I0{}, k);
+        if constexpr (LA > 1) tile_body(I1{}, k + 1);
+        if constexpr (LA > 2) tile_body(I2{}, k + 2);
+        if constexpr (LA > 3) tile_body(I3{}, k + 3);
+    }
+    if constexpr (LA > 1)
+        if (k < ntiles) tile_body(I0{}, k);
+    if constexpr (LA > 2)
+        if (k + 1 < ntiles) tile_body(I1{}, k + 1);
+    if constexpr (LA > 3)
+        if (k + 2 < ntiles) tile_body(I2{}, k + 2);
+}
+
+// Longer rows (kDenseMaxJ < J <= kDensePassMaxJ iterations per tile, e.g.
+// the 14336-input down projection): the same dense products and order, but
+// the activation operands do not fit in registers, so for every tile they
+// stream through LDS in passes of one staging chunk (kStageGroups groups:
+// iterations 2c and 2c + 1). A pass stores its chunk and issues the loads of
+// the pass kDensePassAhead on: that chunk, and the weights of its two
+// iterations into the registers just consumed (past the tile's end, those
+// of the next tile), so every load has the same lead; then it issues both
+// iterations' products before it scales them. Measured on MI355X (the 8B
+// down projection, 32 tokens), the pass loop with no memory traffic at all
+// takes 12.4 of the 21.0 us: the two fp32 operations per scaled group
+// product (packed fp32 forms are not used) bound it, not the loads.
+constexpr int kDensePassMaxJ = 28;
+template <int JT>
+__global__ __launch_bounds__(kDenseThreads) void w4a8_linear_dense_pass_kernel(
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsg, const int8_t* __restrict__ xq, int N, int K,
+    int nwg, int Tr, const float* __restrict__ xs, float* __restrict__ y) {
+    constexpr int NP = JT / 2;              // passes per tile
+    constexpr int SA = kDensePassAhead;     // passes whose loads are in flight
+    constexpr int R = 2 * SA;               // weight iterations in flight: iteration j's registers take j + R next
+    static_assert(JT % 2 == 0 && NP >= SA, "a pass takes two iterations");
+    // two staging buffers, then two buffers of slot sums [slot][tt][i][q][row]
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    char* stg = reinterpret_cast<char*>(smem);
+    float* red = reinterpret_cast<float*>(stg + 2 * kStageBytes);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int s = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, q = lane >> 4;
+    const int G = K >> 5;
+    const int NT = (N + 15) >> 4;
+    const int b = blockIdx.x;
+    const int ntiles = b < NT ? (NT - b + nwg - 1) / nwg : 0;
+    if (ntiles == 0) return;
+
+    const auto rw = make_rsrc(wq, (uint32_t)packed_weight_bytes(N, K));
+    const auto rs = make_rsrc(wsg, (uint32_t)packed_scale_bytes(N, K));
+    const auto rx = make_rsrc(xq, (uint32_t)(Tr * K));
+    // lane offsets, and the same with the out-of-range bit: groups past G and
+    // tiles past the list read zeros through the range check
+    const uint32_t lw = 16u * (uint32_t)r + 4u * (uint32_t)q, ls = 2u * (uint32_t)r;
+    const uint32_t lwx = lw | kOOB, lsx = ls | kOOB;
+    uint32_t w[R];
+    uint16_t sc[R];
+    auto wload = [&](int slot, int j, int tile, bool past) {  // iteration j of a tile, as in the kernel above
+        const int g = 16 * j + s;
+        const bool bad = g >= G || past;
+        const uint32_t chunk = (uint32_t)tile * (uint32_t)G + (uint32_t)g;
+        w[slot] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, bad ? lwx : lw, bad ? 0u : chunk * 256u,
+                                                                 kCachePolicyNT);
+        sc[slot] = __builtin_amdgcn_raw_buffer_load_b16(rs, bad ? lsx : ls, bad ? 0u : chunk * 32u, kCachePolicyNT);
+    };
+    // chunk c: groups 32c .. 32c + 31 of every token, 2 x 16 bytes per thread,
+    // coalesced (each token's chunk is 1 KB in a row); tokens past Tr, groups
+    // past G and chunks of no further tile read zeros
+    constexpr int RND = 32 * kStageGroups * 32 / 16 / kDenseThreads;
+    v4i stage[SA][RND];
+    auto sload = [&](int sb, int c, bool none) {
+#pragma unroll
+        for (int i = 0; i < RND; i++) {
+            const int e = i * kDenseThreads + tid;
+            const int t = e / (2 * kStageGroups), u = e % (2 * kStageGroups);
+            const int g = c * kStageGroups + (u >> 1);
+            const bool ok = !none && t < Tr && g < G;
+            stage[sb][i] = load16(rx, ((uint32_t)(t * K + 32 * g + 16 * (u & 1))) | (ok ? 0u : kOOB));
         }
-        if (k < ntiles) tile_body(std::integral_constant<int, 0>{}, k);
+    };
+    auto sstore = [&](int sb, char* buf) {
+#pragma unroll
+        for (int i = 0; i < RND; i++) {
+            const int e = i * kDenseThreads + tid;
+            const int t = e / (2 * kStageGroups), u = e % (2 * kStageGroups);
+            *reinterpret_cast<v4i*>(buf + ((u >> 1) * 33 + t) * 32 + 16 * (u & 1)) = stage[sb][i];
+        }
+    };
+#pragma unroll
+    for (int c = 0; c < SA; c++) sload(c, c, false);
+#pragma unroll
+    for (int j = 0; j < R; j++) wload(j, j, b, false);
+    // the finishing thread's token scale (as in the register-resident kernel)
+    const int ftok = 16 * (tid >> 8) + 4 * ((tid >> 4) & 3) + ((tid >> 6) & 3);
+    const float fxs = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(xs, (uint32_t)(4 * Tr)),
+                                                    (4u * (uint32_t)ftok) | (tid < 512 ? 0u : kOOB), 0, 0));
+    const v4i bias = v4i{kMagic, kMagic, kMagic, kMagic};
+
+    for (int k = 0; k < ntiles; k++) {
+        const int tile = b + k * nwg;
+        const bool past = k + 1 >= ntiles;
+        float acc[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[tt][i] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NP; c++) {
+            char* buf = stg + (c & 1) * kStageBytes;
+            // (the last reads of this buffer, two passes ago, ended before
+            // every wave passed the previous pass's barrier)
+            sstore(c % SA, buf);
+            if (c + SA < NP)
+                sload(c % SA, c + SA, false);
+            else  // the next tile's first chunks: the same activation rows
+                sload(c % SA, c + SA - NP, past);
+            __syncthreads();
+            v4i d[2][2];
+            float s16[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                const int j = 2 * c + jj;  // group 16j + s = c * kStageGroups + 16jj + s
+                long a[2];
+#pragma unroll
+                for (int tt = 0; tt < 2; tt++) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(buf + ((16 * jj + s) * 33 + 16 * tt + r) * 32 + 8 * q);
+                    a[tt] = even_odd8((uint64_t)v.x | ((uint64_t)v.y << 32));
+                }
+                const long bw = decode_word(w[j % R]);
+                s16[jj] = (float)__builtin_bit_cast(_Float16, sc[j % R]) * 0.0625f;
+                d[jj][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[0], bw, bias, 0, 0, 0);
+                d[jj][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[1], bw, bias, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + R < JT)  // iteration j + R of this tile, or j + R - JT of the next
+                    wload(j % R, j + R, tile, false);
+                else
+                    wload(j % R, j + R - JT, tile + nwg, past);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                const float m = s16[jj];
+                const float cb = -(m * kMagicF);
+#pragma unroll
+                for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int di = d[jj][tt][i];
+                        acc[tt][i] = acc[tt][i] + __builtin_fmaf(m, __builtin_bit_cast(float, di), cb);
+                    }
+            }
+        }
+        // the 16 slot sums of each (token, row), added as the index-order tree
+        float* rb = red + (k & 1) * (16 * 512);
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) rb[s * 512 + ((tt * 4 + i) * 4 + q) * 16 + r] = acc[tt][i];
+        __syncthreads();
+        if (tid < 512) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) v[u] = rb[u * 512 + tid];
+#pragma unroll
+            for (int wd = 1; wd < 16; wd <<= 1)
+#pragma unroll
+                for (int u = 0; u < 16; u += 2 * wd) v[u] = v[u] + v[u + wd];
+            const int row = 16 * tile + (tid & 15);
+            if (ftok < Tr && row < N) y[(int64_t)ftok * N + row] = fxs * v[0];
+        }
     }
 }
+
+constexpr size_t kDensePassLds = (size_t)2 * kStageBytes + (size_t)2 * 16 * 512 * sizeof(float);
 
 // Dynamic LDS: the two activation staging buffers, later two buffers of 16
 // slots x 512 (token, row) sums.
@@ -282,7 +461,7 @@ template <int JT>
 static int launch_dense(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y, int Tr,
                         int N, int K, hipStream_t s) {
     // two tiles in flight where the registers allow it
-    auto kernel = &w4a8_linear_dense_kernel<JT, JT <= 8 ? 2 : 1>;
+    auto kernel = &w4a8_linear_dense_kernel<JT, JT <= 8 ? kDenseLookahead : 1>;
     static bool enabled = false;
     if (!enabled) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -304,9 +483,35 @@ static int launch_dense(const uint8_t* wq, const uint16_t* ws, const int8_t* xq,
     return launch_status();
 }
 
+template <int JT>
+static int launch_dense_pass(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
+                             int Tr, int N, int K, hipStream_t s) {
+    auto kernel = &w4a8_linear_dense_pass_kernel<JT>;
+    static bool enabled = false;
+    if (!enabled) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)kDensePassLds) != hipSuccess) {
+            (void)hipGetLastError();
+            return SPECV_E_HIP;
+        }
+        enabled = true;
+    }
+    const int NT = (N + 15) / 16;
+    const int cus = dense_cus();
+    const int grid = NT < cus ? NT : cus;
+    hipEvent_t e0, e1;
+    if (take_linear_timing(&e0, &e1))
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kDenseThreads), kDensePassLds, s, e0, e1, 0, wq, ws, xq, N, K,
+                              grid, Tr, xs, y);
+    else
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kDenseThreads), kDensePassLds, s, wq, ws, xq, N, K, grid, Tr, xs,
+                           y);
+    return launch_status();
+}
+
 bool linear_dense_supported(int T, int K) {
     const int J = (K / 32 + 15) / 16;
-    return T > 16 && T <= kDenseTokens && K >= 32 && K % 32 == 0 && J <= kDenseMaxJ;
+    return T > 16 && T <= kDenseTokens && K >= 32 && K % 32 == 0 && J <= kDensePassMaxJ;
 }
 
 // Iterations per tile rounded up to a compiled count (extra iterations read
@@ -319,7 +524,9 @@ int linear_dense_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq
     if (J <= 2) return launch_dense<2>(wq, ws, xq, xs, y, T, N, K, s);
     if (J <= 4) return launch_dense<4>(wq, ws, xq, xs, y, T, N, K, s);
     if (J <= 8) return launch_dense<8>(wq, ws, xq, xs, y, T, N, K, s);
-    return launch_dense<10>(wq, ws, xq, xs, y, T, N, K, s);
+    if (J <= kDenseMaxJ) return launch_dense<10>(wq, ws, xq, xs, y, T, N, K, s);
+    if (J <= 16) return launch_dense_pass<16>(wq, ws, xq, xs, y, T, N, K, s);
+    return launch_dense_pass<kDensePassMaxJ>(wq, ws, xq, xs, y, T, N, K, s);
 }
 
 }  // namespace specv

@@ -140,11 +140,16 @@ def test_quantize_misaligned_rows(sv):
                                    (8, 4100, 4864), (16, 4097, 8192), (1, 4111, 96), (2, 8211, 1056),
                                    # the 32-token bucket (17..32 tokens): dense products with 1, 2, 3
                                    # (padded to 4), 8 (ragged groups), 9 (padded to 10) and 10
-                                   # iterations per tile, more tiles than workgroups, and past 10
-                                   # iterations the block-diagonal form
+                                   # iterations per tile, more tiles than workgroups; 11..28
+                                   # iterations with the activations streamed through LDS (11 and
+                                   # 16 padded to 16, 19 with ragged groups and 28 padded to 28,
+                                   # one and two tiles per workgroup); past 28 iterations the
+                                   # block-diagonal form
                                    (20, 33, 896), (32, 100, 544), (25, 4100, 96), (17, 16, 32),
                                    (18, 50, 1536), (31, 300, 4352), (30, 77, 5120), (32, 4117, 4064),
-                                   (24, 70, 5152), (29, 8211, 2048), (32, 17, 4096)])
+                                   (24, 70, 5152), (29, 8211, 2048), (32, 17, 4096),
+                                   (19, 300, 8192), (27, 33, 9248), (32, 40, 14336), (17, 4100, 12288),
+                                   (21, 20, 14368)])
 def test_linear_parity_ragged(sv, T, N, K):
     case(f"linear ragged T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(50 + T, T, N, K)
@@ -230,7 +235,7 @@ def test_linear_run_to_run_identical(sv):
 
 @pytest.mark.parametrize("T,N,K", [(16, 16400, 10240), (16, 4096, 14336), (8, 4096, 14336), (8, 28672, 4096),
                                    (8, 6144, 4096), (32, 4096, 14336), (24, 9728, 4864), (32, 28672, 4096),
-                                   (17, 5000, 896)])
+                                   (17, 5000, 896), (32, 8211, 10240), (26, 4097, 14336)])
 def test_linear_layouts_sampled(sv, T, N, K):
     """Activations kept in LDS across a workgroup's tiles, and reloaded with
     every tile when T x K does not fit (T = 16 at K = 14336 or 10240, and
