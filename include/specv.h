@@ -160,9 +160,10 @@ int w4a8_pack_weights(const uint8_t* wq, const uint16_t* ws, int32_t N, int32_t 
  * T in [1, 32] (the buckets of [P1] are 1, 2, 4, 8, 16 and 32 tokens; 17..31
  * run in the 32-token kernel), N in [0, 2^24], K a multiple of 32 in
  * [32, 2^20], w4a8_packed_weight_bytes(N, K) < 2^31. N == 0 enqueues
- * nothing. The fp16 scales must be finite for T in 17..32: that bucket
- * forms each scaled product as one fused multiply-add, exact for every
- * finite scale, and an infinite scale gives NaN instead of +-inf.
+ * nothing. The fp16 scales must be finite for T in 8..32: those buckets
+ * form each scaled product as one fused multiply-add, exact for every
+ * finite scale, and an infinite or NaN scale gives NaN instead of +-inf
+ * (below 8 tokens every fp16 scale gives the IEEE product).
  * Alignment: wq and xq 16 bytes, ws 2, xs and y 4.
  */
 size_t w4a8_linear_workspace(int32_t T, int32_t N, int32_t K);

@@ -369,6 +369,32 @@ def test_linear_degenerate_values(sv, T):
     assert empty.shape == (1, 0)
 
 
+@pytest.mark.parametrize("T", [1, 4, 7])
+def test_linear_nonfinite_scales(sv, T):
+    """Below 8 tokens infinite and NaN fp16 scales give the IEEE products of
+    the plain definition: inf * d, inf * 0 = NaN, inf + -inf = NaN (from 8
+    tokens the scaled products are one fma each, which needs finite
+    scales)."""
+    case(f"linear non-finite scales T={T}")
+    N, K = 40, 544
+    wq, ws, x = sg.linear_case(14, T, N, K)
+    ws = ws.copy()
+    ws[0, 3] = np.uint16(0x7C00)                 # +inf
+    ws[1, 0] = np.uint16(0xFC00)                 # -inf
+    ws[2, 7] = np.uint16(0x7E00)                 # NaN
+    ws[5, 1] = np.uint16(0x7C00)
+    ws[5, 9] = np.uint16(0xFC00)                 # +inf and -inf in one row
+    ws[33, 16] = np.uint16(0x7C00)               # a later tile, slot 0 of iteration 1
+    x[0, :32] = 0.0                              # token 0's group 0 dots are 0: -inf * 0 = NaN
+    xq_o, xs_o = oracle.quantize_act(x)
+    y_o = oracle.w4a8_linear(wq, ws, xq_o, xs_o)
+    _, _, y = gpu_quant_linear(sv, wq, ws, x)
+    nan_o, nan_g = np.isnan(y_o), np.isnan(y)
+    assert np.array_equal(nan_g, nan_o), f"NaN positions differ: {np.argwhere(nan_g != nan_o)[:4]}"
+    assert nan_o.any() and np.isinf(y_o).any()
+    assert_bits(np.where(nan_g, 0, y).astype(np.float32), np.where(nan_o, 0, y_o).astype(np.float32), "non-NaN outputs")
+
+
 # ------------------------------------------------------------------ argmax + acceptance + compaction
 
 def _plant_tree(seed, n, amax_o, V, accept_path):
