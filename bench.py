@@ -58,9 +58,9 @@ HBM_PEAK_GBS = 8000.0
 # source they were taken on: HBM bytes per linear launch of the T = 8 step
 # from the FETCH_SIZE and WRITE_SIZE counter passes (each scaled by a plain
 # 256 MiB device copy), and the kernel trace's mean duration per launch.
-LINEAR_PROFILE = {"source_sha256": "794a578499fad11ce01face431fab0d569d783866d75e6893f897ac175dffcf0",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33632822,
-                  "rocprof_mean_us": 8.087, "summary": "profiles/w4a8_linear_llama8b_T8.md"}
+LINEAR_PROFILE = {"source_sha256": "9717e2d448980da311ec17eb327766a524753eaf4aa250253aea0c3f0f672553",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33627231,
+                  "rocprof_mean_us": 8.124, "summary": "profiles/w4a8_linear_llama8b_T8.md"}
 
 
 def linear_profile(T, workload):
@@ -977,8 +977,9 @@ def main():
                      "traffic": prof["bytes_per_launch"] if prof else None,
                      "frac_rocprof": (round(avg_b / (prof["rocprof_mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                       if prof else None),
-                     "profile_source": (f"stored, not of this run: rocprofv3 kernel trace (mean "
-                                        f"{prof['rocprof_mean_us']} us per launch) and FETCH_SIZE + WRITE_SIZE "
+                     "profile_source": (f"stored, not of this run: rocprofv3 kernel traces (mean "
+                                        f"{prof['rocprof_mean_us']} us per launch over two runs of this command on "
+                                        f"two devices) and FETCH_SIZE + WRITE_SIZE "
                                         f"counter passes of this command on linear.hip sha256 "
                                         f"{prof['source_sha256'][:16]}, {prof['summary']}") if prof else
                                        "none: linear.hip changed since the stored rocprofv3 figures were taken",
