@@ -1,7 +1,7 @@
 // Context-mixing drafter (GPU-Resident Speculative Decoding for In-Browser
 // LLM Inference with WebGPU, Draft-Free Drafting From Web Context): every
 // position of the token stream computes the length of its match with the
-// current suffix, a bitonic selection keeps the best positions of each
+// current suffix, a selection by rank keeps the best positions of each
 // workgroup, and one workgroup merges the continuations of the overall best
 // into a weighted trie and emits its most probable prefix-closed node set as
 // the next tree. Weights are a fixed integer function of the match length,
@@ -43,40 +43,49 @@ __device__ __forceinline__ int cm_stream_len(const specv_ctrl* ctrl, int n_given
     return n;
 }
 
-// Bitonic sort of 2^k keys in LDS, descending, by all threads of the block.
-__device__ void bitonic_desc(uint32_t* v, int count) {
-    for (int size = 2; size <= count; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < count / 2; i += blockDim.x) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint32_t a = v[lo], b = v[hi];
-                if (desc ? a < b : a > b) {
-                    v[lo] = b;
-                    v[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 // Match lengths of 256 positions and the workgroup's best `cands` keys.
+// Each thread loads its position's last 8 tokens and the suffix's at once
+// (one memory round trip), then counts the matching run. The best keys go
+// to their ranks, as in the tree kernel's merge (nonzero keys are
+// distinct); places no key takes hold zero.
 __global__ __launch_bounds__(kScanThreads) void cm_scan_kernel(const int32_t* __restrict__ s, int n_given, int cap,
                                                                const specv_ctrl* __restrict__ ctrl, int max_order,
                                                                int cands, uint32_t* __restrict__ part) {
-    __shared__ uint32_t key[kScanThreads];
+    __shared__ __attribute__((aligned(16))) uint32_t key[kScanThreads];
+    __shared__ uint32_t best[32];
     const int n = cm_stream_len(ctrl, n_given, cap, s);
     const int p = blockIdx.x * kScanThreads + threadIdx.x;
     int l = 0;
     if (p + 1 < n) {
-        while (l < max_order && l <= p && s[p - l] == s[n - 1 - l]) l++;
+        int cur[8], suf[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const bool in = i < max_order && i <= p;
+            cur[i] = in ? s[p - i] : 0;
+            suf[i] = in ? s[n - 1 - i] : 0;
+        }
+        bool run = true;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            run = run && i < max_order && i <= p && cur[i] == suf[i];
+            l += run;
+        }
     }
-    key[threadIdx.x] = cm_key(l, p);
+    const uint32_t x = cm_key(l, p);
+    key[threadIdx.x] = x;
+    if (threadIdx.x < 32) best[threadIdx.x] = 0u;
     __syncthreads();
-    bitonic_desc(key, kScanThreads);
-    if (threadIdx.x < cands) part[blockIdx.x * cands + threadIdx.x] = key[threadIdx.x];
+    if (x != 0u) {
+        int rank = 0;
+        const uint4* key4 = reinterpret_cast<const uint4*>(key);
+        for (int j = 0; j < kScanThreads / 4; j++) {  // every lane reads the same words
+            const uint4 v = key4[j];
+            rank += (v.x > x) + (v.y > x) + (v.z > x) + (v.w > x);
+        }
+        if (rank < cands) best[rank] = x;
+    }
+    __syncthreads();
+    if (threadIdx.x < cands) part[blockIdx.x * cands + threadIdx.x] = best[threadIdx.x];
 }
 
 // One workgroup: global best candidates, trie weights, selection and output.
@@ -90,7 +99,8 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
                                                       int32_t* __restrict__ best_match_out,
                                                       specv_step_stats* __restrict__ stats,
                                                       const int32_t* __restrict__ wcounter) {
-    __shared__ uint32_t keys[2 * kMergeChunk];
+    __shared__ __attribute__((aligned(16))) uint32_t pool[kMergeChunk + 32 + 4];
+    __shared__ uint32_t keys[32];
     __shared__ int32_t cont[32][8];
     __shared__ int clen[32];
     __shared__ uint32_t cw[32];
@@ -103,20 +113,36 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
     const int n = cm_stream_len(ctrl, n_given, cap, s);
 
     // running best `cands` keys over the parts that hold stream positions
-    // (later parts hold only the zero keys of positions without a match):
-    // [0, cands) holds them, the next chunk of parts follows, and the whole
-    // is sorted at the smallest power of two that holds it
+    // (later parts hold only the zero keys of positions without a match),
+    // a chunk of parts at a time: the chunk's keys and the best so far form
+    // a pool, and each nonzero key goes to its rank, the number of pool keys
+    // above it (nonzero keys are distinct, their positions differ), if that
+    // is below `cands`; the places no key takes stay zero. This is the
+    // descending order's first `cands` keys, as a sort of the pool gives.
     const int used = min(nparts, (n + kScanThreads - 1) / kScanThreads);
     const int total = used * cands;
-    for (int i = tid; i < cands; i += 256) keys[i] = 0u;
+    if (tid < 32) keys[tid] = 0u;
     for (int base = 0; base < total; base += kMergeChunk) {
         const int m = min(kMergeChunk, total - base);
-        int size = 2;
-        while (size < cands + m) size <<= 1;
-        for (int i = tid; i < size - cands; i += 256) keys[cands + i] = i < m ? part[base + i] : 0u;
+        const int np = m + cands, np4 = (np + 3) >> 2;
+        __syncthreads();  // the previous round's keys are written
+        for (int i = tid; i < 4 * np4; i += 256) pool[i] = i < m ? part[base + i] : i < np ? keys[i - m] : 0u;
         __syncthreads();
-        bitonic_desc(keys, size);
+        if (tid < 32) keys[tid] = 0u;
+        __syncthreads();
+        const uint4* pool4 = reinterpret_cast<const uint4*>(pool);
+        for (int i = tid; i < np; i += 256) {
+            const uint32_t x = pool[i];
+            if (x == 0u) continue;
+            int rank = 0;
+            for (int j = 0; j < np4; j++) {  // every lane reads the same words
+                const uint4 v = pool4[j];
+                rank += (v.x > x) + (v.y > x) + (v.z > x) + (v.w > x);
+            }
+            if (rank < cands) keys[rank] = x;
+        }
     }
+    __syncthreads();
     // candidates and their continuations
     if (tid < 32) {
         const uint32_t kk = tid < cands ? keys[tid] : 0u;
