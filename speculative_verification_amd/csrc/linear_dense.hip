@@ -520,6 +520,15 @@ int linear_dense_enqueue(const uint8_t* wq, const uint16_t* ws, const int8_t* xq
                          int N, int K, hipStream_t s) {
     if (!linear_dense_supported(T, K)) return SPECV_E_SHAPE;
     const int J = (K / 32 + 15) / 16;
+    // Workgroups of at most two tiles stream their activation operands too:
+    // staging all of them into registers up front costs more than a tile or
+    // two use (measured on MI355X at 32 tokens, K = 4096, per launch: qkv
+    // 11.8 -> 10.9 us, o 7.86 -> 7.35 us; with gate_up's 7 tiles per
+    // workgroup 27 -> 35 us, so longer walks keep the registers).
+    const int NT = (N + 15) / 16;
+    if (J > 4 && J <= kDenseMaxJ && NT <= 2 * dense_cus())
+        return J <= 8 ? launch_dense_pass<8>(wq, ws, xq, xs, y, T, N, K, s)
+                      : launch_dense_pass<10>(wq, ws, xq, xs, y, T, N, K, s);
     if (J <= 1) return launch_dense<1>(wq, ws, xq, xs, y, T, N, K, s);
     if (J <= 2) return launch_dense<2>(wq, ws, xq, xs, y, T, N, K, s);
     if (J <= 4) return launch_dense<4>(wq, ws, xq, xs, y, T, N, K, s);
