@@ -259,7 +259,13 @@ __device__ __forceinline__ void put_codes(int8_t* rowb, int c, const float4 y, Q
 
 // Floats of a wave's RMSNorm buffer: the row (long rows), or its squares as
 // 16 slots of a stride rounded up to whole float4s.
-__host__ __device__ inline int norm_row_floats(int K) { return 16 * (((K >> 4) + 3) & ~3); }
+// A row kept in registers (K <= 1024) leaves its squares in 16 slot rows of
+// kSlotStride floats, positions past K / 16 zero (68, not 64: the 16 summing
+// lanes then read distinct banks).
+constexpr int kSlotStride = 68;
+__host__ __device__ inline int norm_row_floats(int K) {
+    return K <= 1024 ? 16 * kSlotStride : 16 * (((K >> 4) + 3) & ~3);
+}
 
 // Zero the staged row of token t (by one wave, or by the workgroup).
 __device__ __forceinline__ void zero_row_lds(int8_t* act, int t, int JP, int first, int step) {
@@ -271,83 +277,164 @@ __device__ __forceinline__ void zero_row_lds(int8_t* act, int t, int JP, int fir
 // sq[s], sq[s + 16], ... in increasing k, then the lane tree. The squares
 // sit transposed in the wave's LDS buffer (slot s at sq[s * stride ...]), so
 // a slot lane reads its values as float4s, all issued before the adds.
-constexpr int kSlotRegs = 16;  // float4s per slot lane: rows up to 1024 values
 
-__device__ __forceinline__ float slot_sum_t(const float* sq, int K, int stride, int lane) {
+// Sum of the squares of a row in the fixed order: lane s < 16 adds the 64
+// positions of slot s in turn (the zeros past K / 16 leave a sum of squares
+// unchanged, bit for bit), then the 16 slot sums meet in index order.
+__device__ __forceinline__ float slot_sum64(const float* sq, int lane) {
     float acc = 0.0f;
     if (lane < 16) {
-        const int n16 = K >> 4;
-        float4 v[kSlotRegs];
+        float4 v[16];
 #pragma unroll
-        for (int i = 0; i < kSlotRegs; i++)
-            if (4 * i < n16) v[i] = *reinterpret_cast<const float4*>(sq + lane * stride + 4 * i);
+        for (int i = 0; i < 16; i++) v[i] = *reinterpret_cast<const float4*>(sq + lane * kSlotStride + 4 * i);
 #pragma unroll
-        for (int i = 0; i < kSlotRegs; i++) {
-            const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-                if (4 * i + u < n16) acc = acc + e[u];
-        }
+        for (int i = 0; i < 16; i++) acc = (((acc + v[i].x) + v[i].y) + v[i].z) + v[i].w;
     }
     acc = tree16_lanes(acc);
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, acc)));
 }
 
+// RMSNorm rows of fewer than 4 tokens, K <= 1024: thread i takes chunk i
+// (inputs 4i .. 4i+3) of every token, so the per-value work is spread over
+// the workgroup. The squares meet in LDS, where wave t sums token t's slots;
+// its scale and the four waves' absmaxes are exchanged there too.
+template <int T, typename Issue>
+__device__ void produce_norm_spread(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
+                                    float* scratch, Issue&& issue) {
+    static_assert(T < 4, "one token per summing wave");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = tid;
+    const bool in = c < (K >> 2);
+    const bool wb = pa.h_out && pa.b && blockIdx.x == 0;
+    const uint32_t rowb = (uint32_t)(Tr * K * 4);
+    const auto ra = make_rsrc(pa.a, rowb);
+    const auto rd = make_rsrc(pa.b ? pa.b : pa.a, pa.b ? rowb : 0u);
+    const auto rwn = make_rsrc(pa.w, (uint32_t)(K * 4));
+    float4 x[T], d[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        const uint32_t off = ((uint32_t)(t * K + 4 * c) * 4u) | (t < Tr && in ? 0u : kOOB);
+        x[t] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+        d[t] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+    }
+    const float4 wv = __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(rwn, ((uint32_t)c * 16u) | (in ? 0u : kOOB), 0, 0));
+    issue();
+    const auto rh = make_rsrc(pa.h_out, wb ? rowb : 0u);  // the summed residual, by workgroup 0
+    float* ex = scratch + 3 * 16 * kSlotStride;            // scales [T], absmaxes [T][4]
+    if (wave < T) {
+        zero_row_lds(act, wave, JP, lane, 64);
+        if (lane == 0) s_xs[wave] = 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        if (t >= Tr || t >= live) continue;
+        float4& v = x[t];
+        if (pa.b) v = make_float4(v.x + d[t].x, v.y + d[t].y, v.z + d[t].z, v.w + d[t].w);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rh,
+                                               ((uint32_t)(t * K + 4 * c) * 4u) | (in ? 0u : kOOB), 0, 0);
+        // slots (4c & 15) + e, position c >> 2; zero past K
+        float* q = scratch + t * 16 * kSlotStride + (4 * c & 15) * kSlotStride + (c >> 2);
+        q[0] = v.x * v.x;
+        q[kSlotStride] = v.y * v.y;
+        q[2 * kSlotStride] = v.z * v.z;
+        q[3 * kSlotStride] = v.w * v.w;
+    }
+    __syncthreads();
+    if (wave < T && wave < Tr && wave < live) {
+        const float ss = slot_sum64(scratch + wave * 16 * kSlotStride, lane);
+        if (lane == 0) ex[wave] = 1.0f / sqrtf(ss / (float)K + pa.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        if (t >= Tr || t >= live) continue;
+        const float rs = ex[t];
+        float4& v = x[t];
+        v = make_float4((v.x * rs) * wv.x, (v.y * rs) * wv.y, (v.z * rs) * wv.z, (v.w * rs) * wv.w);
+        const float amax = wave_max(in ? max4(v) : 0.0f);
+        if (lane == 0) ex[4 + 4 * t + wave] = amax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        if (t >= Tr || t >= live) continue;
+        const float* m4 = ex + 4 + 4 * t;
+        const float m = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        const QuantScale qs = quant_scale(m);
+        if (tid == 0) s_xs[t] = m == 0.0f ? 0.0f : m / 127.0f;
+        if (in) put_codes(act + (size_t)t * JP * 512, c, x[t], qs);
+    }
+}
+
 // RMSNorm rows: wave w takes tokens w, w + 4, ... Rows of up to 1024 values
 // live in registers, every load of the wave's tokens issued up front; longer
 // rows go through the wave's LDS row and read the weight twice.
-template <int T>
+template <int T, typename Issue>
 __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
-                             float* scratch) {
+                             float* scratch, Issue&& issue) {
     constexpr int TPW = (T + 3) / 4;  // tokens per wave
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K4 = K >> 2;
     const bool wb = pa.h_out && pa.b && blockIdx.x == 0;
     float* xr = scratch + (size_t)wave * norm_row_floats(K);
+    if constexpr (T < 4) {
+        if (K4 <= 64 * kProdRegs) return produce_norm_spread<T>(pa, Tr, live, K, JP, act, s_xs, scratch, issue);
+    }
     if (K4 <= 64 * kProdRegs) {
+        // Every row load is issued, out of range where there is no value (a
+        // token past Tr, a chunk past K, no residual), so the compiler counts
+        // them, and before the first weights: the rows are then waited for
+        // alone, while the weights stream (loads complete in order).
+        const uint32_t rowb = (uint32_t)(Tr * K * 4);
+        const auto ra = make_rsrc(pa.a, rowb);
+        const auto rd = make_rsrc(pa.b ? pa.b : pa.a, pa.b ? rowb : 0u);
+        const auto rwn = make_rsrc(pa.w, (uint32_t)(K * 4));
         float4 x[TPW][kProdRegs], d[TPW][kProdRegs], wv[kProdRegs];
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int t = wave + 4 * u;
-            if (t < T && t < Tr) {
 #pragma unroll
-                for (int i = 0; i < kProdRegs; i++) {
-                    const int c = lane + 64 * i;
-                    if (c < K4) {
-                        x[u][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * K + 4 * c);
-                        if (pa.b) d[u][i] = *reinterpret_cast<const float4*>(pa.b + (size_t)t * K + 4 * c);
-                    }
-                }
+            for (int i = 0; i < kProdRegs; i++) {
+                const int c = lane + 64 * i;
+                const uint32_t off = ((uint32_t)(t * K + 4 * c) * 4u) | (t < T && t < Tr && c < K4 ? 0u : kOOB);
+                x[u][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+                d[u][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
             }
         }
 #pragma unroll
-        for (int i = 0; i < kProdRegs; i++)
-            if (lane + 64 * i < K4) wv[i] = *reinterpret_cast<const float4*>(pa.w + 4 * (lane + 64 * i));
+        for (int i = 0; i < kProdRegs; i++) {
+            const int c = lane + 64 * i;
+            wv[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rwn, ((uint32_t)c * 16u) | (c < K4 ? 0u : kOOB), 0, 0));
+        }
+        issue();
+        const auto rh = make_rsrc(pa.h_out, wb ? rowb : 0u);  // the summed residual, by workgroup 0
         for (int t = wave; t < T; t += 4) {
             zero_row_lds(act, t, JP, lane, 64);
             if (lane == 0) s_xs[t] = 0.0f;
         }
-        const int stride = ((K >> 4) + 3) & ~3;
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int t = wave + 4 * u;
             if (t >= T || t >= Tr || t >= live) continue;
             int8_t* rowb = act + (size_t)t * JP * 512;
+            // every chunk of the 1024 positions, zero past K (its loads were out of range)
 #pragma unroll
             for (int i = 0; i < kProdRegs; i++) {
                 const int c = lane + 64 * i;
-                if (c >= K4) continue;
                 float4& v = x[u][i];
                 if (pa.b) v = make_float4(v.x + d[u][i].x, v.y + d[u][i].y, v.z + d[u][i].z, v.w + d[u][i].w);
-                if (wb) *reinterpret_cast<float4*>(pa.h_out + (size_t)t * K + 4 * c) = v;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rh,
+                                                       ((uint32_t)(t * K + 4 * c) * 4u) | (c < K4 ? 0u : kOOB), 0, 0);
                 // inputs 4c .. 4c+3: slots (4c & 15) + e, position 4c >> 4 within the slot
-                float* q = xr + (4 * c & 15) * stride + (c >> 2);
+                float* q = xr + (4 * c & 15) * kSlotStride + (c >> 2);
                 q[0] = v.x * v.x;
-                q[stride] = v.y * v.y;
-                q[2 * stride] = v.z * v.z;
-                q[3 * stride] = v.w * v.w;
+                q[kSlotStride] = v.y * v.y;
+                q[2 * kSlotStride] = v.z * v.z;
+                q[3 * kSlotStride] = v.w * v.w;
             }
-            const float ss = slot_sum_t(xr, K, stride, lane);
+            const float ss = slot_sum64(xr, lane);
             const float rs = 1.0f / sqrtf(ss / (float)K + pa.eps);
             float amax = 0.0f;
 #pragma unroll
@@ -367,6 +454,7 @@ __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP
         }
         return;
     }
+    issue();
     for (int t = wave; t < T; t += 4) {
         zero_row_lds(act, t, JP, lane, 64);
         if (lane == 0) s_xs[t] = 0.0f;
@@ -406,22 +494,26 @@ __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP
 
 // Given rows (at most kRowsTokens): the whole workgroup, every load issued
 // up front, values in registers, each token's absmax met in LDS.
-template <int T>
+template <int T, typename Issue>
 __device__ void produce_given(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
-                              float* part) {
+                              float* part, Issue&& issue) {
     constexpr int TS = T < kRowsTokens ? T : kRowsTokens;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K4 = K >> 2;
+    // every row load issued (out of range where there is no value), then the
+    // first weights, as for the RMSNorm rows
+    const auto ra = make_rsrc(pa.a, (uint32_t)(Tr * K * 4));
     float4 zv[TS][kRowsRegs];
 #pragma unroll
-    for (int t = 0; t < TS; t++)
-        if (t < Tr) {
+    for (int t = 0; t < TS; t++) {
 #pragma unroll
-            for (int i = 0; i < kRowsRegs; i++) {
-                const int c = tid + 256 * i;
-                if (c < K4) zv[t][i] = *reinterpret_cast<const float4*>(pa.a + (size_t)t * K + 4 * c);
-            }
+        for (int i = 0; i < kRowsRegs; i++) {
+            const int c = tid + 256 * i;
+            const uint32_t off = ((uint32_t)(t * K + 4 * c) * 4u) | (t < Tr && c < K4 ? 0u : kOOB);
+            zv[t][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
         }
+    }
+    issue();
     for (int t = 0; t < T; t++) zero_row_lds(act, t, JP, tid, 256);
     if (tid < T) s_xs[tid] = 0.0f;
     float amax[TS];
@@ -451,14 +543,15 @@ __device__ void produce_given(const ProdArgs& pa, int Tr, int live, int K, int J
 // All rows of the step; tokens past Tr or the live count, and padding
 // groups, stay zero. Each producer issues its row loads before it zeroes the
 // staged rows, so the two overlap.
-template <int T, int PROD>
-__device__ void produce_rows(const ProdArgs& pa, int Tr, int K, int JP, int8_t* act, float* s_xs, float* scratch) {
+template <int T, int PROD, typename Issue>
+__device__ void produce_rows(const ProdArgs& pa, int Tr, int K, int JP, int8_t* act, float* s_xs, float* scratch,
+                             Issue&& issue) {
     const bool done = pa.ctrl->done != 0;
     const int live = done ? 0 : pa.ctrl->n_nodes;
     if constexpr (PROD == kProdNorm)
-        produce_norm<T>(pa, Tr, live, K, JP, act, s_xs, scratch);
+        produce_norm<T>(pa, Tr, live, K, JP, act, s_xs, scratch, issue);
     else
-        produce_given<T>(pa, Tr, live, K, JP, act, s_xs, scratch);
+        produce_given<T>(pa, Tr, live, K, JP, act, s_xs, scratch, issue);
 }
 
 template <int T, int P, bool AMAX, bool BS, bool RELOAD, int PROD>
@@ -659,15 +752,19 @@ __global__ __launch_bounds__(256) void w4a8_linear_stream_kernel(
     };
 
     SStage<T, BS> st[P];
+    auto issue_first = [&]() {  // the first P iterations of the first tile
 #pragma unroll
-    for (int pp = 0; pp < P; pp++) {
-        load(st[pp], v, pp, PROD == kProdNone, 0u);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int pp = 0; pp < P; pp++) {
+            load(st[pp], v, pp, PROD == kProdNone, 0u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if constexpr (PROD == kProdNone) issue_first();
     if (tid < kStreamZero / 16) *reinterpret_cast<v4i*>(act + zero_off + 16 * tid) = v4i{0, 0, 0, 0};
-    if constexpr (PROD != kProdNone)  // the rows, while the first weights are in flight
+    if constexpr (PROD != kProdNone)  // the rows; the first weights go out right after their loads
         produce_rows<T, PROD>(pa, Tr, K, JP, act, s_xs,
-                              reinterpret_cast<float*>(act + zero_off + kStreamZero + (BS ? JA * 64 * T : 0)));
+                              reinterpret_cast<float*>(act + zero_off + kStreamZero + (BS ? JA * 64 * T : 0)),
+                              issue_first);
     __syncthreads();
 
     auto run_tile = [&](auto first_tag, int k, float (&acc)[T]) {
