@@ -64,9 +64,10 @@ __device__ __forceinline__ uint16_t f32_to_f16(float x) {
 constexpr int kFwdThreads = 256;   // embedding and attention-chunk workgroups
 constexpr int kRowThreads = 1024;  // row kernels: norms, SiLU, attention merge
 // RMSNorm rows are produced by the linear that consumes them up to this many
-// tokens (one per wave): every workgroup recomputes them all, and with two
-// or more per wave the redundant rows cost more than the row kernel's launch.
-constexpr int kNormFuseMaxT = 4;
+// tokens (every workgroup recomputing them all): rows of up to 1024 values
+// kept in registers, longer rows through LDS.
+constexpr int kNormFuseMaxT = 8;
+constexpr int kNormFuseMaxTLong = 4;
 constexpr int kRowRegs = 4;        // float4 chunks per thread: rows up to 16384 values
 constexpr int kMergeRegs = 8;      // values per thread in the merge: rows up to 8192
 constexpr int kMaxNodes = 16;
@@ -1272,7 +1273,7 @@ int enqueue_forward(const specv_model* m, int n, const int32_t* parent, const in
     float* hcur = h;
     auto norm_linear = [&](const float* resid, const float* w, const uint8_t* wq, const uint16_t* ws_,
                            float* y, Best* am, int N, bool keep, int epi) -> int {
-        if (n <= kNormFuseMaxT && linear_fused_supported(kProdNorm, n, H)) {
+        if (n <= (H <= 1024 ? kNormFuseMaxT : kNormFuseMaxTLong) && linear_fused_supported(kProdNorm, n, H)) {
             float* hnext = !resid || !keep ? nullptr : (hcur == h ? h2 : h);
             ProdArgs pa{hcur, resid, w, hnext, m->eps, 0, ctrl, epi};
             const int rc = linear_enqueue_fused(kProdNorm, pa, wq, ws_, y, am, n, N, H, s);

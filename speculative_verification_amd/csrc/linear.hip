@@ -194,10 +194,10 @@ struct SStage {
 constexpr int kProdRegs = 4;       // float4 chunks per lane of a RMSNorm row kept in registers (K <= 1024)
 constexpr int kRowsRegs = 6;       // float4 chunks per thread of a given row (K <= 6144)
 // Given rows a fused linear quantises at most: every workgroup quantises all
-// of them, and from two tokens on that costs more than a row kernel's launch
-// (measured on MI355X, 0.5B window, us per step, fused up to 1 / 2 / 4
-// tokens: width 2 800 / 802 / 803, width 4 843 / 843 / 901).
-constexpr int kRowsTokens = 1;
+// of them, and at four tokens that costs more than a row kernel's launch
+// (measured on MI355X, 0.5B window: fused up to 2 tokens, width 2 went from
+// 758 to 749 us per step; up to 4, width 4 lost 44 us per step).
+constexpr int kRowsTokens = 2;
 
 __device__ __forceinline__ float tree16_lanes(float v) {
 #define SPECV_DPP_ADD(ctrl) \
@@ -257,14 +257,22 @@ __device__ __forceinline__ void put_codes(int8_t* rowb, int c, const float4 y, Q
     }
 }
 
-// Floats of a wave's RMSNorm buffer: the row (long rows), or its squares as
-// 16 slots of a stride rounded up to whole float4s.
-// A row kept in registers (K <= 1024) leaves its squares in 16 slot rows of
-// kSlotStride floats, positions past K / 16 zero (68, not 64: the 16 summing
-// lanes then read distinct banks).
+// Floats of a wave's RMSNorm buffer: the row itself (rows longer than
+// 1024), or the squares of a row kept in registers as 16 slot rows of
+// kSlotStride floats, positions past K / 16 zero (68, not 64: the 16
+// summing lanes then read distinct banks).
 constexpr int kSlotStride = 68;
 __host__ __device__ inline int norm_row_floats(int K) {
     return K <= 1024 ? 16 * kSlotStride : 16 * (((K >> 4) + 3) & ~3);
+}
+// RMSNorm rows a fused linear produces at most, and at most spread over the
+// whole workgroup (below that each wave takes its own tokens). Rows of K <=
+// 1024 keep one slot area per token (4 per token of a wave), then 8 scales
+// and 4 absmaxes per token.
+constexpr int kNormMaxT = 8;
+constexpr int kNormSpreadMaxT = 3;
+__host__ __device__ inline int norm_scratch_floats(int T, int K) {
+    return K <= 1024 ? (T + 3) / 4 * 4 * norm_row_floats(K) + 8 + 4 * kNormMaxT : 4 * norm_row_floats(K);
 }
 
 // Zero the staged row of token t (by one wave, or by the workgroup).
@@ -278,30 +286,48 @@ __device__ __forceinline__ void zero_row_lds(int8_t* act, int t, int JP, int fir
 // sit transposed in the wave's LDS buffer (slot s at sq[s * stride ...]), so
 // a slot lane reads its values as float4s, all issued before the adds.
 
-// Sum of the squares of a row in the fixed order: lane s < 16 adds the 64
-// positions of slot s in turn (the zeros past K / 16 leave a sum of squares
-// unchanged, bit for bit), then the 16 slot sums meet in index order.
-__device__ __forceinline__ float slot_sum64(const float* sq, int lane) {
-    float acc = 0.0f;
+// Sums of the squares of N rows in the fixed order, the slot areas of row n
+// at sq + n * step: lane s < 16 adds the 64 positions of slot s in turn (the
+// zeros past K / 16 leave a sum of squares unchanged, bit for bit), then the
+// 16 slot sums meet in index order. The N chains interleave.
+template <int N>
+__device__ __forceinline__ void slot_sums(const float* sq, int step, int lane, float (&out)[N]) {
+    float acc[N];
+#pragma unroll
+    for (int n = 0; n < N; n++) acc[n] = 0.0f;
     if (lane < 16) {
-        float4 v[16];
+        constexpr int B = 16 / N;  // float4s of each row in flight per round
 #pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = *reinterpret_cast<const float4*>(sq + lane * kSlotStride + 4 * i);
+        for (int i0 = 0; i0 < 16; i0 += B) {
+            float4 v[N][B];
 #pragma unroll
-        for (int i = 0; i < 16; i++) acc = (((acc + v[i].x) + v[i].y) + v[i].z) + v[i].w;
+            for (int n = 0; n < N; n++)
+#pragma unroll
+                for (int i = 0; i < B; i++)
+                    v[n][i] = *reinterpret_cast<const float4*>(sq + n * step + lane * kSlotStride + 4 * (i0 + i));
+#pragma unroll
+            for (int i = 0; i < B; i++)
+#pragma unroll
+                for (int n = 0; n < N; n++) acc[n] = (((acc[n] + v[n][i].x) + v[n][i].y) + v[n][i].z) + v[n][i].w;
+        }
     }
-    acc = tree16_lanes(acc);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, acc)));
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+        const float a = tree16_lanes(acc[n]);
+        out[n] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a)));
+    }
 }
 
-// RMSNorm rows of fewer than 4 tokens, K <= 1024: thread i takes chunk i
-// (inputs 4i .. 4i+3) of every token, so the per-value work is spread over
-// the workgroup. The squares meet in LDS, where wave t sums token t's slots;
-// its scale and the four waves' absmaxes are exchanged there too.
+// RMSNorm rows of up to kNormSpreadMaxT tokens, K <= 1024: thread i takes
+// chunk i (inputs 4i .. 4i+3) of every token, so the per-value work is
+// spread over the workgroup. The squares meet in LDS, where wave t sums token
+// t's slots; its scale and the four waves' absmaxes are exchanged there too.
+// (From 4 tokens on, each wave's own serial chains per token, its absmax and
+// the scale's division, cost more than the spread saves.)
 template <int T, typename Issue>
 __device__ void produce_norm_spread(const ProdArgs& pa, int Tr, int live, int K, int JP, int8_t* act, float* s_xs,
                                     float* scratch, Issue&& issue) {
-    static_assert(T < 4, "one token per summing wave");
+    static_assert(T <= kNormSpreadMaxT, "one token per summing wave");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = tid;
     const bool in = c < (K >> 2);
@@ -321,10 +347,10 @@ __device__ void produce_norm_spread(const ProdArgs& pa, int Tr, int live, int K,
         float4, __builtin_amdgcn_raw_buffer_load_b128(rwn, ((uint32_t)c * 16u) | (in ? 0u : kOOB), 0, 0));
     issue();
     const auto rh = make_rsrc(pa.h_out, wb ? rowb : 0u);  // the summed residual, by workgroup 0
-    float* ex = scratch + 3 * 16 * kSlotStride;            // scales [T], absmaxes [T][4]
-    if (wave < T) {
-        zero_row_lds(act, wave, JP, lane, 64);
-        if (lane == 0) s_xs[wave] = 0.0f;
+    float* ex = scratch + T * 16 * kSlotStride;            // scales [8], absmaxes [T][4]
+    for (int t = wave; t < T; t += 4) {
+        zero_row_lds(act, t, JP, lane, 64);
+        if (lane == 0) s_xs[t] = 0.0f;
     }
 #pragma unroll
     for (int t = 0; t < T; t++) {
@@ -342,8 +368,9 @@ __device__ void produce_norm_spread(const ProdArgs& pa, int Tr, int live, int K,
     }
     __syncthreads();
     if (wave < T && wave < Tr && wave < live) {
-        const float ss = slot_sum64(scratch + wave * 16 * kSlotStride, lane);
-        if (lane == 0) ex[wave] = 1.0f / sqrtf(ss / (float)K + pa.eps);
+        float ss[1];
+        slot_sums<1>(scratch + wave * 16 * kSlotStride, 0, lane, ss);
+        if (lane == 0) ex[wave] = 1.0f / sqrtf(ss[0] / (float)K + pa.eps);
     }
     __syncthreads();
 #pragma unroll
@@ -353,13 +380,13 @@ __device__ void produce_norm_spread(const ProdArgs& pa, int Tr, int live, int K,
         float4& v = x[t];
         v = make_float4((v.x * rs) * wv.x, (v.y * rs) * wv.y, (v.z * rs) * wv.z, (v.w * rs) * wv.w);
         const float amax = wave_max(in ? max4(v) : 0.0f);
-        if (lane == 0) ex[4 + 4 * t + wave] = amax;
+        if (lane == 0) ex[8 + 4 * t + wave] = amax;
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < T; t++) {
         if (t >= Tr || t >= live) continue;
-        const float* m4 = ex + 4 + 4 * t;
+        const float* m4 = ex + 8 + 4 * t;
         const float m = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         const QuantScale qs = quant_scale(m);
         if (tid == 0) s_xs[t] = m == 0.0f ? 0.0f : m / 127.0f;
@@ -377,8 +404,9 @@ __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K4 = K >> 2;
     const bool wb = pa.h_out && pa.b && blockIdx.x == 0;
+    static_assert(T <= kNormMaxT, "RMSNorm rows of at most kNormMaxT tokens");
     float* xr = scratch + (size_t)wave * norm_row_floats(K);
-    if constexpr (T < 4) {
+    if constexpr (T <= kNormSpreadMaxT) {
         if (K4 <= 64 * kProdRegs) return produce_norm_spread<T>(pa, Tr, live, K, JP, act, s_xs, scratch, issue);
     }
     if (K4 <= 64 * kProdRegs) {
@@ -414,43 +442,58 @@ __device__ void produce_norm(const ProdArgs& pa, int Tr, int live, int K, int JP
             zero_row_lds(act, t, JP, lane, 64);
             if (lane == 0) s_xs[t] = 0.0f;
         }
+        // In phases over the wave's tokens, each in its own slot area, so
+        // that their serial chains (slot sums, absmaxes) interleave. A token
+        // past T, Tr or the live count goes through them on zeros, or on its
+        // row, and leaves nothing behind.
+        constexpr int kArea = 4 * 16 * kSlotStride;  // token wave + 4u: area u of the wave's
+        float* xa = scratch + (size_t)wave * 16 * kSlotStride;
+        bool ok[TPW];
 #pragma unroll
         for (int u = 0; u < TPW; u++) {
             const int t = wave + 4 * u;
-            if (t >= T || t >= Tr || t >= live) continue;
-            int8_t* rowb = act + (size_t)t * JP * 512;
+            ok[u] = t < T && t < Tr && t < live;
             // every chunk of the 1024 positions, zero past K (its loads were out of range)
 #pragma unroll
             for (int i = 0; i < kProdRegs; i++) {
                 const int c = lane + 64 * i;
                 float4& v = x[u][i];
                 if (pa.b) v = make_float4(v.x + d[u][i].x, v.y + d[u][i].y, v.z + d[u][i].z, v.w + d[u][i].w);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rh,
-                                                       ((uint32_t)(t * K + 4 * c) * 4u) | (c < K4 ? 0u : kOOB), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(v4i, v), rh, ((uint32_t)(t * K + 4 * c) * 4u) | (ok[u] && c < K4 ? 0u : kOOB),
+                    0, 0);
                 // inputs 4c .. 4c+3: slots (4c & 15) + e, position 4c >> 4 within the slot
-                float* q = xr + (4 * c & 15) * kSlotStride + (c >> 2);
+                float* q = xa + u * kArea + (4 * c & 15) * kSlotStride + (c >> 2);
                 q[0] = v.x * v.x;
                 q[kSlotStride] = v.y * v.y;
                 q[2 * kSlotStride] = v.z * v.z;
                 q[3 * kSlotStride] = v.w * v.w;
             }
-            const float ss = slot_sum64(xr, lane);
-            const float rs = 1.0f / sqrtf(ss / (float)K + pa.eps);
+        }
+        float ss[TPW], am[TPW];
+        slot_sums<TPW>(xa, kArea, lane, ss);
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            const float rs = 1.0f / sqrtf(ss[u] / (float)K + pa.eps);
             float amax = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kProdRegs; i++)
-                if (lane + 64 * i < K4) {
-                    float4& v = x[u][i];
-                    v = make_float4((v.x * rs) * wv[i].x, (v.y * rs) * wv[i].y, (v.z * rs) * wv[i].z,
-                                    (v.w * rs) * wv[i].w);
-                    amax = fmaxf(amax, max4(v));
-                }
-            amax = wave_max(amax);
-            const QuantScale qs = quant_scale(amax);
-            if (lane == 0) s_xs[t] = amax == 0.0f ? 0.0f : amax / 127.0f;
+            for (int i = 0; i < kProdRegs; i++) {
+                float4& v = x[u][i];
+                v = make_float4((v.x * rs) * wv[i].x, (v.y * rs) * wv[i].y, (v.z * rs) * wv[i].z,
+                                (v.w * rs) * wv[i].w);
+                amax = fmaxf(amax, lane + 64 * i < K4 ? max4(v) : 0.0f);
+            }
+            am[u] = wave_max(amax);
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; u++) {
+            if (!ok[u]) continue;
+            const int t = wave + 4 * u;
+            const QuantScale qs = quant_scale(am[u]);
+            if (lane == 0) s_xs[t] = am[u] == 0.0f ? 0.0f : am[u] / 127.0f;
 #pragma unroll
             for (int i = 0; i < kProdRegs; i++)
-                if (lane + 64 * i < K4) put_codes(rowb, lane + 64 * i, x[u][i], qs);
+                if (lane + 64 * i < K4) put_codes(act + (size_t)t * JP * 512, lane + 64 * i, x[u][i], qs);
         }
         return;
     }
@@ -872,8 +915,8 @@ inline size_t stream_lds_bytes(int T, int K, bool bs, bool reload, int P = SPECV
     return (size_t)T * JA * 512 + kStreamZero + (bs ? (size_t)JA * 64 * T : 0);
 }
 // LDS of a producer: one row per wave (RMSNorm), the absmax exchange (SiLU).
-inline size_t prod_scratch_bytes(int prod, int K) {
-    return prod == kProdNorm ? (size_t)16 * norm_row_floats(K) : prod == kProdRows ? 16 * kRowsTokens : 0;
+inline size_t prod_scratch_bytes(int prod, int T, int K) {
+    return prod == kProdNorm ? (size_t)4 * norm_scratch_floats(T, K) : prod == kProdRows ? 16 * kRowsTokens : 0;
 }
 // Whether the activations of every iteration fit beside the reduction buffer.
 inline bool stream_keeps(int T, int K, bool bs) {
@@ -942,7 +985,7 @@ template <int T, bool AMAX, bool BS, bool RELOAD, int PROD = kProdNone, int P = 
 static int launch_one(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, const float* xs, float* y,
                       Best* amax, int Tr, int N, int K, hipStream_t s, const ProdArgs& pa = ProdArgs{}) {
     static size_t lds_enabled = 64 * 1024;
-    const size_t lds = stream_lds_bytes(T, K, BS, RELOAD, P) + prod_scratch_bytes(PROD, K);
+    const size_t lds = stream_lds_bytes(T, K, BS, RELOAD, P) + prod_scratch_bytes(PROD, T, K);
     if (lds + (size_t)T * 512 > kLdsBudget) return SPECV_E_SHAPE;
     auto kernel = &w4a8_linear_stream_kernel<T, P, AMAX, BS, RELOAD, PROD>;
     const int rc = enable_lds(reinterpret_cast<const void*>(kernel), lds, lds_enabled);
@@ -1016,19 +1059,21 @@ static int launch_T(const uint8_t* wq, const uint16_t* ws, const int8_t* xq, con
                 : launch_one<T, false, BS, true>(wq, ws, xq, xs, y, nullptr, Tr, N, K, s, pa);
 }
 
-// Fused producers: T <= 16, per-token scales, every iteration's activations
-// (and, for RMSNorm, one row per wave) kept in LDS.
+// Fused producers: T <= kNormMaxT (RMSNorm) or kRowsTokens (given rows),
+// per-token scales, every iteration's activations and the producer's
+// scratch kept in LDS.
 bool linear_fused_supported(int prod, int T, int K) {
     if (T < 1 || T > 16 || K < 32 || K % 32 || (prod != kProdNorm && prod != kProdRows)) return false;
     if (prod == kProdRows && (K > 256 * 4 * kRowsRegs || T > kRowsTokens)) return false;
-    return stream_lds_bytes(T, K, false, false) + prod_scratch_bytes(prod, K) + (size_t)T * 512 <= kLdsBudget;
+    if (prod == kProdNorm && T > kNormMaxT) return false;
+    return stream_lds_bytes(T, K, false, false) + prod_scratch_bytes(prod, T, K) + (size_t)T * 512 <= kLdsBudget;
 }
 
 template <int T>
 static int launch_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const uint16_t* ws, float* y, Best* amax,
                         int N, int K, hipStream_t s) {
     if (const int P = exact_stages(T, K); P && stream_lds_bytes(T, K, false, false, P) +
-                                                          prod_scratch_bytes(prod, K) + (size_t)T * 512 <= kLdsBudget) {
+                                                          prod_scratch_bytes(prod, T, K) + (size_t)T * 512 <= kLdsBudget) {
         if (prod == kProdNorm)
             return amax ? launch_exact<T, true, kProdNorm>(P, wq, ws, nullptr, nullptr, y, amax, T, N, K, s, pa)
                         : launch_exact<T, false, kProdNorm>(P, wq, ws, nullptr, nullptr, y, nullptr, T, N, K, s, pa);
@@ -1051,8 +1096,7 @@ int linear_enqueue_fused(int prod, const ProdArgs& pa, const uint8_t* wq, const 
 #define SPECV_CASE(n) \
     case n: return launch_fused<n>(prod, pa, wq, ws, y, amax, N, K, s);
         SPECV_CASE(1) SPECV_CASE(2) SPECV_CASE(3) SPECV_CASE(4) SPECV_CASE(5) SPECV_CASE(6)
-        SPECV_CASE(7) SPECV_CASE(8) SPECV_CASE(9) SPECV_CASE(10) SPECV_CASE(11) SPECV_CASE(12)
-        SPECV_CASE(13) SPECV_CASE(14) SPECV_CASE(15) SPECV_CASE(16)
+        SPECV_CASE(7) SPECV_CASE(8)
 #undef SPECV_CASE
         default: return SPECV_E_SHAPE;
     }
