@@ -120,9 +120,15 @@ __device__ void quantize_regs(const float (&y)[R][V], int K, int8_t* __restrict_
     }
 }
 
-// Floats per slot row of the RMSNorm kernel's transposed squares: H/16
-// rounded up to whole float4s.
-inline __host__ __device__ int norm_slot_stride(int H) { return ((H >> 4) + 3) & ~3; }
+// Positions per slot row of the RMSNorm kernel's transposed squares (H/16
+// rounded up to whole blocks of 64, the tail zero), and the row's stride in
+// floats: 4 more, so the 16 summing lanes read distinct banks, except for the
+// longest rows (H = 16384), whose 16 rows then fill 64 KB exactly.
+inline __host__ __device__ int norm_slot_positions(int H) { return ((H >> 4) + 63) & ~63; }
+inline __host__ __device__ int norm_slot_stride(int H) {
+    const int n = norm_slot_positions(H);
+    return n < 1024 ? n + 4 : n;
+}
 
 // Rows of nodes past the live count quantise to zero, so the linears that
 // follow produce exact zeros for them. K is a multiple of 4.
@@ -220,15 +226,20 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_quant_kernel(float* __res
         }
     }
     float x[kRowRegs][4];
+    const int npos = norm_slot_positions(H);
 #pragma unroll
     for (int r = 0; r < kRowRegs; r++) {
         const int c = tid + r * kRowThreads;
-        if (c >= H4) continue;
-        x[r][0] = xv[r].x, x[r][1] = xv[r].y, x[r][2] = xv[r].z, x[r][3] = xv[r].w;
-        if (rr) {
-            x[r][0] = x[r][0] + rv[r].x, x[r][1] = x[r][1] + rv[r].y;
-            x[r][2] = x[r][2] + rv[r].z, x[r][3] = x[r][3] + rv[r].w;
-            *reinterpret_cast<float4*>(hr + 4 * c) = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
+        if (c >= 4 * npos) continue;
+        if (c < H4) {
+            x[r][0] = xv[r].x, x[r][1] = xv[r].y, x[r][2] = xv[r].z, x[r][3] = xv[r].w;
+            if (rr) {
+                x[r][0] = x[r][0] + rv[r].x, x[r][1] = x[r][1] + rv[r].y;
+                x[r][2] = x[r][2] + rv[r].z, x[r][3] = x[r][3] + rv[r].w;
+                *reinterpret_cast<float4*>(hr + 4 * c) = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
+            }
+        } else {  // the zero tail of the slot rows
+            x[r][0] = x[r][1] = x[r][2] = x[r][3] = 0.0f;
         }
         // input k = 4c + e sits at slot k mod 16, position k / 16 of the
         // slot's row of the transposed copy
@@ -240,21 +251,15 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_quant_kernel(float* __res
     }
     __syncthreads();
     if (tid < 16) {  // slot tid: its row in increasing k, read 16 float4s at a time
-        const int n16 = H >> 4;
+        // (the zeros past H / 16 leave a sum of squares unchanged, bit for bit)
         const float* row = sq + tid * sstride;
         float acc = 0.0f;
-        for (int b0 = 0; b0 < n16; b0 += 64) {
+        for (int b0 = 0; b0 < npos; b0 += 64) {
             float4 v[16];
 #pragma unroll
-            for (int u = 0; u < 16; u++)
-                if (b0 + 4 * u < n16) v[u] = *reinterpret_cast<const float4*>(row + b0 + 4 * u);
+            for (int u = 0; u < 16; u++) v[u] = *reinterpret_cast<const float4*>(row + b0 + 4 * u);
 #pragma unroll
-            for (int u = 0; u < 16; u++) {
-                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                for (int z = 0; z < 4; z++)
-                    if (b0 + 4 * u + z < n16) acc = acc + e[z];
-            }
+            for (int u = 0; u < 16; u++) acc = (((acc + v[u].x) + v[u].y) + v[u].z) + v[u].w;
         }
         acc = tree16(acc);
         if (tid == 0) s_ss = acc;
