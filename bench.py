@@ -58,9 +58,9 @@ HBM_PEAK_GBS = 8000.0
 # source they were taken on: HBM bytes per linear launch of the T = 8 step
 # from the FETCH_SIZE and WRITE_SIZE counter passes (each scaled by a plain
 # 256 MiB device copy), and the kernel trace's mean duration per launch.
-LINEAR_PROFILE = {"source_sha256": "7e330c8474591c13844c239d5261c4d96d5d53ea060ab156eadfc5ae3f53bf78",
-                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33626426,
-                  "rocprof_mean_us": 8.022, "summary": "profiles/w4a8_linear_llama8b_T8.md"}
+LINEAR_PROFILE = {"source_sha256": "2c3ddf8187a92a1296ebea7d5ce4c03aaa74ae7822172efec00270e8eae6d924",
+                  "T": 8, "workload": "llama3-8b", "bytes_per_launch": 33625599,
+                  "rocprof_mean_us": 7.961, "summary": "profiles/w4a8_linear_llama8b_T8.md"}
 
 
 def linear_profile(T, workload):
