@@ -149,7 +149,7 @@ def test_quantize_misaligned_rows(sv):
                                    (18, 50, 1536), (31, 300, 4352), (30, 77, 5120), (32, 4117, 4064),
                                    (24, 70, 5152), (29, 8211, 2048), (32, 17, 4096),
                                    (19, 300, 8192), (27, 33, 9248), (32, 40, 14336), (17, 4100, 12288),
-                                   (21, 20, 14368)])
+                                   (21, 20, 14368), (1, 900, 4864), (6, 4090, 4864), (8, 33, 4864)])
 def test_linear_parity_ragged(sv, T, N, K):
     case(f"linear ragged T={T} N={N} K={K}")
     wq, ws, x = sg.linear_case(50 + T, T, N, K)
