@@ -57,6 +57,11 @@ __device__ __forceinline__ float max16(float v) {
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
+// a * (float)h as one fused multiply-add with a +0 addend: the rounded
+// product itself (a zero product comes out +0, which a sum that starts at +0
+// cannot tell from -0), taken by v_fma_mix_f32 straight from the half of a
+// packed register, without a conversion.
+__device__ __forceinline__ float mul_f16(float a, uint16_t h) { return __builtin_fmaf(a, f16_to_f32(h), 0.0f); }
 __device__ __forceinline__ uint16_t f32_to_f16(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
 }
@@ -509,8 +514,8 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
             for (int e = 0; e < 4; e++) {
                 const uint32_t wd = (uint32_t)kr[t][e];
                 const int d = 8 * t + 2 * e;
-                slot[d & 15] = slot[d & 15] + qs[d] * f16_to_f32((uint16_t)(wd & 0xffff));
-                slot[(d + 1) & 15] = slot[(d + 1) & 15] + qs[d + 1] * f16_to_f32((uint16_t)(wd >> 16));
+                slot[d & 15] = slot[d & 15] + mul_f16(qs[d], (uint16_t)(wd & 0xffff));
+                slot[(d + 1) & 15] = slot[(d + 1) & 15] + mul_f16(qs[d + 1], (uint16_t)(wd >> 16));
             }
         }
 #pragma unroll
@@ -566,10 +571,10 @@ __global__ __launch_bounds__(kFwdThreads) void attn_chunk_kernel(
                 else
                     w = *reinterpret_cast<const uint2*>(
                         Vs + p * VS + (SWZ ? 8 * ((d0 >> 3) ^ ((p >> 1) & 7)) + (d0 & 7) : d0));
-                acc[0] = acc[0] + e[k] * f16_to_f32((uint16_t)(w.x & 0xffff));
-                acc[1] = acc[1] + e[k] * f16_to_f32((uint16_t)(w.x >> 16));
-                acc[2] = acc[2] + e[k] * f16_to_f32((uint16_t)(w.y & 0xffff));
-                acc[3] = acc[3] + e[k] * f16_to_f32((uint16_t)(w.y >> 16));
+                acc[0] = acc[0] + mul_f16(e[k], (uint16_t)(w.x & 0xffff));
+                acc[1] = acc[1] + mul_f16(e[k], (uint16_t)(w.x >> 16));
+                acc[2] = acc[2] + mul_f16(e[k], (uint16_t)(w.y & 0xffff));
+                acc[3] = acc[3] + mul_f16(e[k], (uint16_t)(w.y >> 16));
             }
         }
 #pragma unroll
@@ -618,7 +623,7 @@ constexpr int kGrpSplitMaxNodes = 4;                   // trees up to this size 
 // workgroups), so only trees of more than 8 nodes take them.
 constexpr int kGrpHalfMinNodes = 9;
 
-template <int HD, int NT>
+template <int HD, int NT, bool MIX>
 __global__ __launch_bounds__(NT) void attn_group_kernel(
     const float* __restrict__ qkv, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ tinfo, int layer, int cap,
@@ -628,7 +633,7 @@ __global__ __launch_bounds__(NT) void attn_group_kernel(
     constexpr int NB = (HD + 63) / 64;
     constexpr bool SWZ = attn_swizzle_ok(HD);
     constexpr int VS = attn_vstride(HD, SWZ);
-    constexpr bool KF = HD <= 64;  // key row widened to fp32 registers once
+    constexpr bool KF = HD <= 64;  // key row widened to fp32 registers once (more than one head per set)
     constexpr int SETS = NT / kFwdThreads;          // sets of 256 threads
     constexpr int SH = kGrpMaxHeads / SETS;          // heads per set, at most
     constexpr int EPT = (kGrpMaxRow + NT - 1) / NT;  // merge: attention row elements per thread
@@ -754,9 +759,40 @@ __global__ __launch_bounds__(NT) void attn_group_kernel(
         for (int t = 0; t < CH; t++)
             kr[t] = *reinterpret_cast<const v4i*>(Ks + t8 * VS + 8 * (SWZ ? t ^ ((t8 >> 1) & 7) : t));
     }
-    // scores of this thread's position for the set's heads h = hbase + set + 4u
+    // scores of this thread's position for the set's heads h = hbase + set + 4u:
+    // with one head per set (MIX, chosen by the host) each product comes
+    // straight from the key row's fp16 halves (v_fma_mix_f32: the products
+    // need no conversion); with more, the key row is widened to fp32 once
+    // (rows of up to 64 values) and shared by the heads, which costs less
+    // than mixed products for each head
     float sc[SH];
-    {
+    if constexpr (MIX) {
+#pragma unroll
+        for (int u = 0; u < SH; u++) sc[u] = -__builtin_inff();
+        const int h = hbase + set;
+        if (hps >= 1 && h < G && live) {
+            float slot[16];
+#pragma unroll
+            for (int r = 0; r < 16; r++) slot[r] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < HD / 8; t++) {
+                const float4 qa = *reinterpret_cast<const float4*>(&qs[h][8 * t]);
+                const float4 qb = *reinterpret_cast<const float4*>(&qs[h][8 * t + 4]);
+                const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int d = 8 * t + e;
+                    slot[d & 15] =
+                        slot[d & 15] + mul_f16(qv[e], (uint16_t)(((uint32_t)kr[t][e >> 1]) >> (16 * (e & 1))));
+                }
+            }
+#pragma unroll
+            for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2 * w) slot[r] = slot[r] + slot[r + w];
+            sc[0] = slot[0] * scale;
+        }
+    } else {
         float kf[KF ? HD : 1];
         if constexpr (KF) {
 #pragma unroll
@@ -830,27 +866,22 @@ __global__ __launch_bounds__(NT) void attn_group_kernel(
                                               kCachePolicySC1);
     };
     float* pnode = part + ((size_t)i * nh + (size_t)g * G) * nchunk_max * (HD + 2) + (size_t)c * (HD + 2);
+    if constexpr (MIX) {  // one head: the products straight from the value rows' fp16 halves
+        const int u = 0, h = hbase + set;
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-        const int d0 = 64 * b + 4 * q;
-        if (d0 >= HD) break;
-        float v[16][4];
+        for (int b = 0; b < NB; b++) {
+            const int d0 = 64 * b + 4 * q;
+            if (d0 >= HD) break;
+            if (h >= G) break;
+            uint2 vw[16];
 #pragma unroll
-        for (int k = 0; k < 16; k++) {
-            const int p = s + 16 * k;
-            uint2 w = make_uint2(0u, 0u);
-            if (p < cnt)
-                w = *reinterpret_cast<const uint2*>(Vs + p * VS + (SWZ ? 8 * ((d0 >> 3) ^ ((p >> 1) & 7)) + (d0 & 7)
-                                                                        : d0));
-            v[k][0] = f16_to_f32((uint16_t)(w.x & 0xffff));
-            v[k][1] = f16_to_f32((uint16_t)(w.x >> 16));
-            v[k][2] = f16_to_f32((uint16_t)(w.y & 0xffff));
-            v[k][3] = f16_to_f32((uint16_t)(w.y >> 16));
-        }
-#pragma unroll
-        for (int u = 0; u < SH; u++) {
-            const int h = hbase + set + SETS * u;
-            if (u >= hps || h >= G) continue;
+            for (int k = 0; k < 16; k++) {
+                const int p = s + 16 * k;
+                vw[k] = make_uint2(0u, 0u);
+                if (p < cnt)
+                    vw[k] = *reinterpret_cast<const uint2*>(
+                        Vs + p * VS + (SWZ ? 8 * ((d0 >> 3) ^ ((p >> 1) & 7)) + (d0 & 7) : d0));
+            }
             float e[16];
 #pragma unroll
             for (int k4 = 0; k4 < 4; k4++) {
@@ -864,10 +895,10 @@ __global__ __launch_bounds__(NT) void attn_group_kernel(
             float l = 0.0f;
 #pragma unroll
             for (int k = 0; k < 16; k++) {
-                acc[0] = acc[0] + e[k] * v[k][0];
-                acc[1] = acc[1] + e[k] * v[k][1];
-                acc[2] = acc[2] + e[k] * v[k][2];
-                acc[3] = acc[3] + e[k] * v[k][3];
+                acc[0] = acc[0] + mul_f16(e[k], (uint16_t)(vw[k].x & 0xffff));
+                acc[1] = acc[1] + mul_f16(e[k], (uint16_t)(vw[k].x >> 16));
+                acc[2] = acc[2] + mul_f16(e[k], (uint16_t)(vw[k].y & 0xffff));
+                acc[3] = acc[3] + mul_f16(e[k], (uint16_t)(vw[k].y >> 16));
                 if (b == 0) l = l + e[k];
             }
 #pragma unroll
@@ -882,6 +913,63 @@ __global__ __launch_bounds__(NT) void attn_group_kernel(
                 if (s == 0) {
                     put(o, mh[u]);
                     put(o + 1, l);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const int d0 = 64 * b + 4 * q;
+            if (d0 >= HD) break;
+            float v[16][4];
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                const int p = s + 16 * k;
+                uint2 w = make_uint2(0u, 0u);
+                if (p < cnt)
+                    w = *reinterpret_cast<const uint2*>(Vs + p * VS + (SWZ ? 8 * ((d0 >> 3) ^ ((p >> 1) & 7)) + (d0 & 7)
+                                                                            : d0));
+                v[k][0] = f16_to_f32((uint16_t)(w.x & 0xffff));
+                v[k][1] = f16_to_f32((uint16_t)(w.x >> 16));
+                v[k][2] = f16_to_f32((uint16_t)(w.y & 0xffff));
+                v[k][3] = f16_to_f32((uint16_t)(w.y >> 16));
+            }
+#pragma unroll
+            for (int u = 0; u < SH; u++) {
+                const int h = hbase + set + SETS * u;
+                if (u >= hps || h >= G) continue;
+                float e[16];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; k4++) {
+                    const float4 ev = *reinterpret_cast<const float4*>(&Et[h][s][4 * (k4 ^ ((s >> 2) & 3))]);
+                    e[4 * k4] = ev.x;
+                    e[4 * k4 + 1] = ev.y;
+                    e[4 * k4 + 2] = ev.z;
+                    e[4 * k4 + 3] = ev.w;
+                }
+                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                float l = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; k++) {
+                    acc[0] = acc[0] + e[k] * v[k][0];
+                    acc[1] = acc[1] + e[k] * v[k][1];
+                    acc[2] = acc[2] + e[k] * v[k][2];
+                    acc[3] = acc[3] + e[k] * v[k][3];
+                    if (b == 0) l = l + e[k];
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[r] = tree16(acc[r]);
+                float* o = pnode + (size_t)h * nchunk_max * (HD + 2);
+                if (s == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) put(o + 2 + d0 + r, acc[r]);
+                }
+                if (b == 0 && q == 0) {
+                    l = tree16(l);
+                    if (s == 0) {
+                        put(o, mh[u]);
+                        put(o + 1, l);
+                    }
                 }
             }
         }
@@ -1181,12 +1269,12 @@ inline size_t attn_group_lds_bytes(int hd, int nh, int nchunk_max) {  // key and
     return std::max(2 * attn_lds_bytes(hd, false, attn_swizzle_ok(hd)), merge_lds_bytes(nh, nchunk_max));
 }
 
-template <int HD, int NT>
+template <int HD, int NT, bool MIX>
 static int launch_attn_group_nt(dim3 grid, size_t lds, hipStream_t s, const float* qkv, const float* cos_t,
                                 const float* sin_t, uint16_t* kc, uint16_t* vc, const int32_t* tinfo, int layer,
                                 int cap, int nh, int nkv, int nsplit, float scale, float* part, int nchunk_max,
                                 uint32_t* arrivals, int8_t* xq, float* xs, const specv_ctrl* ctrl) {
-    auto kernel = &attn_group_kernel<HD, NT>;
+    auto kernel = &attn_group_kernel<HD, NT, MIX>;
     static size_t enabled = 64 * 1024;  // dynamic LDS above 64 KB is enabled per kernel
     if (lds > enabled) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1207,12 +1295,19 @@ static int launch_attn_group_hd(int threads, dim3 grid, size_t lds, hipStream_t 
                                 const int32_t* tinfo, int layer, int cap, int nh, int nkv, int nsplit, float scale,
                                 float* part, int nchunk_max, uint32_t* arrivals, int8_t* xq, float* xs,
                                 const specv_ctrl* ctrl) {
-    if (threads == kGrpThreads / 2)
-        return launch_attn_group_nt<HD, kGrpThreads / 2>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap,
-                                                         nh, nkv, nsplit, scale, part, nchunk_max, arrivals, xq, xs,
-                                                         ctrl);
-    return launch_attn_group_nt<HD, kGrpThreads>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv,
-                                                 nsplit, scale, part, nchunk_max, arrivals, xq, xs, ctrl);
+    // one query head per set (the kernel's hps) takes the mixed-precision products
+    const int sets = threads / kFwdThreads, G = nh / nkv;
+    const bool mix = (G + nsplit * sets - 1) / (nsplit * sets) == 1;
+#define SPECV_GRP(NTV, MIXV)                                                                                     \
+    return launch_attn_group_nt<HD, NTV, MIXV>(grid, lds, s, qkv, cos_t, sin_t, kc, vc, tinfo, layer, cap, nh, nkv, \
+                                               nsplit, scale, part, nchunk_max, arrivals, xq, xs, ctrl)
+    if (threads == kGrpThreads / 2) {
+        if (mix) SPECV_GRP(kGrpThreads / 2, true);
+        SPECV_GRP(kGrpThreads / 2, false);
+    }
+    if (mix) SPECV_GRP(kGrpThreads, true);
+    SPECV_GRP(kGrpThreads, false);
+#undef SPECV_GRP
 }
 
 static int launch_attn_group(int hd, int threads, int nsplit, dim3 grid, hipStream_t s, const float* qkv,
