@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
                                                       const int32_t* __restrict__ wcounter) {
     __shared__ __attribute__((aligned(16))) uint32_t pool[kMergeChunk + 32 + 4];
     __shared__ uint32_t keys[32];
-    __shared__ int32_t cont[32][8];
+    __shared__ __attribute__((aligned(16))) int32_t cont[32][8];
     __shared__ int clen[32];
     __shared__ uint32_t cw[32];
     __shared__ __attribute__((aligned(16))) uint32_t wt[32][8];
@@ -157,21 +157,31 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
     const int k = tid >> 3, d = tid & 7;
     const bool valid = d < clen[k];
     // representative: the first candidate with the same prefix; weight: the
-    // sum over every candidate with the same prefix
-    auto same_prefix = [&](int j, int upto) {
-        if (clen[j] <= upto) return false;
-        for (int e = 0; e <= upto; e++)
-            if (cont[j][e] != cont[k][e]) return false;
-        return true;
-    };
-    int rep = k;
+    // sum over every candidate with the same prefix; the parent's
+    // representative: the first candidate with the prefix shortened by one.
+    // Candidate j has the prefix of length e + 1 when it is longer than e
+    // and its continuation differs from this one at no depth up to e (a bit
+    // mask of the differing depths, from two 16-byte reads of its row).
+    int rep = k, prep = k;
     uint32_t w = 0;
     if (valid) {
-        for (int j = 31; j >= 0; j--)
-            if (same_prefix(j, d)) {
+        const int4 ka = *reinterpret_cast<const int4*>(&cont[k][0]);
+        const int4 kb = *reinterpret_cast<const int4*>(&cont[k][4]);
+        const uint32_t upto = (2u << d) - 1u, upto1 = (1u << d) - 1u;
+        for (int j = 31; j >= 0; j--) {
+            const int4 a = *reinterpret_cast<const int4*>(&cont[j][0]);
+            const int4 b = *reinterpret_cast<const int4*>(&cont[j][4]);
+            const uint32_t diff = (uint32_t)(a.x != ka.x) | (uint32_t)(a.y != ka.y) << 1 |
+                                  (uint32_t)(a.z != ka.z) << 2 | (uint32_t)(a.w != ka.w) << 3 |
+                                  (uint32_t)(b.x != kb.x) << 4 | (uint32_t)(b.y != kb.y) << 5 |
+                                  (uint32_t)(b.z != kb.z) << 6 | (uint32_t)(b.w != kb.w) << 7;
+            const int lj = clen[j];
+            if (lj > d && (diff & upto) == 0u) {
                 w += cw[j];
                 rep = j;  // ends at the smallest such j
             }
+            if (lj > d - 1 && (diff & upto1) == 0u) prep = j;
+        }
     }
     const bool is_node = valid && rep == k;
     wt[k][d] = is_node ? w : 0u;
@@ -216,14 +226,8 @@ __global__ __launch_bounds__(256) void cm_tree_kernel(const int32_t* __restrict_
     }
     __syncthreads();
     if (keep) {
-        int par = 0;
-        if (d > 0) {
-            // the parent node is the representative of this prefix shortened by one
-            int pr = k;
-            for (int j = 31; j >= 0; j--)
-                if (same_prefix(j, d - 1)) pr = j;
-            par = outi[pr][d - 1];
-        }
+        // the parent node is the representative of this prefix shortened by one
+        const int par = d > 0 ? outi[prep][d - 1] : 0;
         const int pos = outi[k][d];
         parent[pos] = par;
         token[pos] = cont[k][d];
