@@ -27,8 +27,10 @@ def sv():
     return m
 
 
-# Rows longer than 1024 values take the fused RMSNorm's LDS-row path, and an
-# intermediate of 2176 the fused SiLU up to 4 tokens.
+# Rows longer than 1024 values take the fused RMSNorm's LDS-row path (up to
+# 4 tokens; the row kernel beyond), and an intermediate of 2176 the fused
+# SiLU rows up to 2 tokens. Rows of up to 1024 values are spread over the
+# workgroup below 4 tokens and taken by their waves from 4 to 8.
 WIDE = dict(n_layers=2, hidden=1280, n_heads=10, n_kv_heads=2, head_dim=128, inter=2176, vocab=1000,
             eps=1e-6, max_pos=640)
 # Head dim 128 with an attention row of 1024 values: the grouped attention
